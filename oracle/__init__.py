@@ -1,0 +1,197 @@
+"""fp64 CPU oracle for the Mamba selective-scan layer core (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The product package never imports it.  The
+arithmetic lives in ``samba_oracle.c`` (plain C, double precision, sequential in time);
+this module only marshals numpy arrays and builds the shared object with gcc.
+
+Functions follow, in order, the steps stated on the page "Samba: Simple Hybrid State
+Space Models for Efficient Unlimited Context Language Modeling" (paper-graph-ui
+summary), section 3.4, subsections "Input Projection and Short Convolution",
+"Input-Dependent Selective Gating", "The State Space Model Update (S6)" and "Gated
+Output", with the conv tap order / padding, A = -exp(A_log) and the SiLU(z) gate taken
+from "Samba Guide: Hybrid Mamba & Sliding Window Architecture", "Step 1: The Selective
+State Space (Mamba) Layer".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "samba_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile samba_oracle.c with gcc (OpenMP) into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        _declare(lib)
+        _lib = lib
+    return _lib
+
+
+def _declare(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_softplus.restype = ctypes.c_double
+    lib.oracle_softplus.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_max_threads.restype = I
+    lib.oracle_scan_sequence.argtypes = [I, I, I, I, I] + [P] * 13
+    lib.oracle_prefill.argtypes = [I, I, I, I] + [P] * 13
+    lib.oracle_varlen.argtypes = [I, P, I, I] + [P] * 13
+    lib.oracle_decode_step.argtypes = [I, I, I] + [P] * 13
+    for f in (lib.oracle_scan_sequence, lib.oracle_prefill, lib.oracle_varlen, lib.oracle_decode_step):
+        f.restype = None
+
+
+def _use_library(path):
+    """Point the wrappers at another build of the oracle (used by the mutation tests,
+    which compile deliberately broken copies to show that the pins catch them)."""
+    global _lib
+    _lib = None
+    saved = globals()["_LIB"]
+    globals()["_LIB"] = path
+    try:
+        return _load_nobuild()
+    finally:
+        globals()["_LIB"] = saved
+
+
+def _load_nobuild():
+    global _lib
+    lib = ctypes.CDLL(_LIB)
+    _declare(lib)
+    _lib = lib
+    return lib
+
+
+def _reset():
+    global _lib
+    _lib = None
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def softplus(a: float) -> float:
+    return _load().oracle_softplus(float(a))
+
+
+def silu(v: float) -> float:
+    return _load().oracle_silu(float(v))
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def _params(A, Dskip, dt_bias, conv_w, conv_b, chans):
+    def sel(a, axis0=True):
+        if a is None:
+            return None
+        a = np.asarray(a)
+        return _f64(a if chans is None else a[chans])
+    return sel(A), sel(Dskip), sel(dt_bias), sel(conv_w), sel(conv_b)
+
+
+def prefill(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, chans=None):
+    """Fixed-length batch.  x, dt, z: [b, L, D]; B, C: [b, L, N]; A: [D, N]; Dskip,
+    dt_bias, conv_b: [D]; conv_w: [D, 4]; h0: [b, D, N] or None (zero state);
+    conv0: [b, 3, D] or None (zero history, oldest first).  ``chans`` restricts the
+    computation to a subset of channels (channels are independent, so the values are
+    exactly those of the full computation).  Returns (y [b, L, nch], h [b, nch, N],
+    hist [b, 3, nch]) in float64."""
+    lib = _load()
+    x = np.asarray(x)
+    b, L, D = x.shape
+    N = np.asarray(B).shape[-1]
+    assert N <= 64
+    sl = (slice(None), slice(None), chans) if chans is not None else (Ellipsis,)
+    xs, dts = _f64(x[sl]), _f64(np.asarray(dt)[sl])
+    zs = None if z is None else _f64(np.asarray(z)[sl])
+    nch = xs.shape[2]
+    Bs, Cs = _f64(B), _f64(C)
+    Ap, Dp, bp, wp, cbp = _params(A, Dskip, dt_bias, conv_w, conv_b, chans)
+    h = np.zeros((b, nch, N)) if h0 is None else _f64(np.asarray(h0)[:, chans, :] if chans is not None else h0).copy()
+    hist = np.zeros((b, 3, nch)) if conv0 is None else _f64(np.asarray(conv0)[:, :, chans] if chans is not None else conv0).copy()
+    y = np.empty((b, L, nch))
+    lib.oracle_prefill(b, L, nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
+                       _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h), _ptr(hist), _ptr(y))
+    return y, h, hist
+
+
+def varlen(cu_seqlens, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, chans=None):
+    """Packed batch.  x, dt, z: [T, D]; B, C: [T, N]; cu_seqlens: [nseq+1] int offsets.
+    Sequence s starts from h0[s] / conv0[s] (zeros if None).  Returns (y [T, nch],
+    h [nseq, nch, N], hist [nseq, 3, nch])."""
+    lib = _load()
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = cu.shape[0] - 1
+    x = np.asarray(x)
+    T, D = x.shape
+    N = np.asarray(B).shape[-1]
+    assert N <= 64
+    sl = (slice(None), chans) if chans is not None else (Ellipsis,)
+    xs, dts = _f64(x[sl]), _f64(np.asarray(dt)[sl])
+    zs = None if z is None else _f64(np.asarray(z)[sl])
+    nch = xs.shape[1]
+    Bs, Cs = _f64(B), _f64(C)
+    Ap, Dp, bp, wp, cbp = _params(A, Dskip, dt_bias, conv_w, conv_b, chans)
+    h = np.zeros((nseq, nch, N)) if h0 is None else _f64(np.asarray(h0)[:, chans, :] if chans is not None else h0).copy()
+    hist = np.zeros((nseq, 3, nch)) if conv0 is None else _f64(np.asarray(conv0)[:, :, chans] if chans is not None else conv0).copy()
+    y = np.empty((T, nch))
+    lib.oracle_varlen(nseq, _ptr(cu), nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
+                      _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h), _ptr(hist), _ptr(y))
+    return y, h, hist
+
+
+def decode_step(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, hist, chans=None):
+    """One token per sequence.  x, dt, z: [S, D]; B, C: [S, N]; h: [S, nch, N] and
+    hist: [S, 3, nch] (float64, already restricted to ``chans``) are updated in place.
+    Returns y [S, nch]."""
+    lib = _load()
+    x = np.asarray(x)
+    S, D = x.shape
+    N = np.asarray(B).shape[-1]
+    sl = (slice(None), chans) if chans is not None else (Ellipsis,)
+    xs, dts = _f64(x[sl]), _f64(np.asarray(dt)[sl])
+    zs = None if z is None else _f64(np.asarray(z)[sl])
+    nch = xs.shape[1]
+    assert h.dtype == np.float64 and h.flags.c_contiguous and h.shape == (S, nch, N)
+    assert hist.dtype == np.float64 and hist.flags.c_contiguous and hist.shape == (S, 3, nch)
+    Bs, Cs = _f64(B), _f64(C)
+    Ap, Dp, bp, wp, cbp = _params(A, Dskip, dt_bias, conv_w, conv_b, chans)
+    y = np.empty((S, nch))
+    lib.oracle_decode_step(S, nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
+                           _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h), _ptr(hist), _ptr(y))
+    return y
+
+
+def timed(fn, *args, **kw):
+    t0 = time.perf_counter()
+    out = fn(*args, **kw)
+    return out, time.perf_counter() - t0

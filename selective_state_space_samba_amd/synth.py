@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the selective-scan core.
+
+This module only draws random numbers; it holds none of the method's arithmetic and is
+shared by the HIP path's tests/benchmark and by the CPU oracle's callers, so both sides
+start from the same bytes.
+
+Recipe (distributions are those of the parameter initialisation stated on the page
+"Samba: Simple Hybrid State Space Models for Efficient Unlimited Context Language
+Modeling", section 3.4: A_ij = log j (S4D-Real) used as A = -exp(A_log) as in "Samba
+Guide: Hybrid Mamba & Sliding Window Architecture", Step 1; D initialised near 1; the
+Delta bias placing Delta in [0.001, 0.1]):
+
+* x, z, B, C ~ N(0, 1); conv weights ~ N(0, 0.5) (0.5 is the standard deviation);
+  conv bias 0; dt ~ N(0, 0.5); D ~ N(1, 0.1);
+* dt_bias[d] = softplus^-1(Delta0[d]) = log(expm1(Delta0[d])) with Delta0 log-uniform in
+  [1e-3, 1e-1];
+* A[d, n] = -exp(A_log[d, n]), A_log[d, n] = log(n + 1) (or, for the "random A"
+  variant, A_log ~ N(log(n + 1), 0.5));
+* values are drawn in float64, rounded to float32, and for bfloat16 I/O rounded to the
+  nearest bfloat16 (ties to even).  Arrays are returned as float32 holding exactly the
+  values the device receives.
+
+Every tensor has its own child stream of ``SeedSequence(seed)`` keyed by its name, so a
+tensor's values do not depend on which other tensors were drawn.
+"""
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+CONV_K = 4
+
+CONFIGS = {
+    # name: (batch, L, d_inner, d_state, io)
+    "tiny": dict(batch=1, L=512, D=256, N=16, io="f32"),
+    "train4k": dict(batch=4, L=4096, D=4096, N=16, io="bf16"),
+    "prompt128k": dict(batch=1, L=131072, D=4096, N=16, io="bf16"),
+    "decode256": dict(nseq=256, D=4096, N=16, io="bf16", steps=65536, warm_L=1024),
+    "varlen8": dict(nseq=8, lo=1024, hi=32768, total_max=131072, D=4096, N=16, io="bf16"),
+}
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    key = zlib.crc32(name.encode())
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, key])))
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    # leave NaN/Inf untouched (none are drawn here, but keep the function total)
+    special = (u & np.uint32(0x7F800000)) == np.uint32(0x7F800000)
+    r = np.where(special, u, r)
+    return r.view(np.float32)
+
+
+def _normal(seed, name, shape, mean=0.0, std=1.0, io="f32", chunk=1 << 24):
+    g = _rng(seed, name)
+    out = np.empty(int(np.prod(shape)), dtype=np.float32)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        v = g.standard_normal(e - s)  # float64
+        if std != 1.0:
+            v *= std
+        if mean != 0.0:
+            v += mean
+        out[s:e] = v
+        if io == "bf16":
+            out[s:e] = round_bf16(out[s:e])
+    return out.reshape(shape)
+
+
+@dataclass
+class Params:
+    A: np.ndarray        # [D, N] float32
+    Dskip: np.ndarray    # [D]
+    dt_bias: np.ndarray  # [D]
+    conv_w: np.ndarray   # [D, 4]; tap k multiplies x[t-3+k]
+    conv_b: np.ndarray   # [D]
+
+
+def make_params(seed: int, D: int, N: int, random_A: bool = False) -> Params:
+    conv_w = _normal(seed, "conv_w", (D, CONV_K), std=0.5)
+    conv_b = np.zeros(D, dtype=np.float32)
+    g = _rng(seed, "dt_bias")
+    delta0 = np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=D))
+    dt_bias = np.log(np.expm1(delta0)).astype(np.float32)
+    Dskip = _normal(seed, "D", (D,), mean=1.0, std=0.1)
+    A_log = np.tile(np.log(np.arange(1, N + 1, dtype=np.float64)), (D, 1))
+    if random_A:
+        A_log = A_log + 0.5 * _rng(seed, "A_log").standard_normal((D, N))
+    A = (-np.exp(A_log)).astype(np.float32)
+    return Params(A=A, Dskip=Dskip, dt_bias=dt_bias, conv_w=conv_w, conv_b=conv_b)
+
+
+@dataclass
+class Tokens:
+    x: np.ndarray
+    dt: np.ndarray
+    z: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+
+
+def make_tokens(seed: int, lead: tuple, D: int, N: int, io: str, tag: str = "") -> Tokens:
+    """Per-token tensors with leading shape ``lead`` (e.g. (b, L) or (T,) or (S,))."""
+    return Tokens(
+        x=_normal(seed, tag + "x", lead + (D,), io=io),
+        dt=_normal(seed, tag + "dt", lead + (D,), std=0.5, io=io),
+        z=_normal(seed, tag + "z", lead + (D,), io=io),
+        B=_normal(seed, tag + "B", lead + (N,), io=io),
+        C=_normal(seed, tag + "C", lead + (N,), io=io),
+    )
+
+
+def make_state(seed: int, nseq: int, D: int, N: int, io: str, scale: float = 1.0, tag: str = ""):
+    """A random resident state: h [nseq, D, N] float32 and conv history [nseq, 3, D] in
+    the I/O dtype (as float32 values)."""
+    h = _normal(seed, tag + "h0", (nseq, D, N), std=scale)
+    hist = _normal(seed, tag + "conv0", (nseq, 3, D), io=io)
+    return h, hist
+
+
+def varlen_lengths(seed: int, nseq: int = 8, lo: int = 1024, hi: int = 32768, total_max: int = 131072):
+    """Integer lengths uniform in [lo, hi] (inclusive); all nseq are redrawn from the same
+    stream until their sum is <= total_max."""
+    g = _rng(seed, "varlen_lengths")
+    while True:
+        lens = g.integers(lo, hi + 1, size=nseq)
+        if int(lens.sum()) <= total_max:
+            return lens.astype(np.int64)
+
+
+def cu_from_lengths(lens) -> np.ndarray:
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    return cu
+
+
+def seed_for(config_index: int) -> int:
+    return 20260000 + config_index

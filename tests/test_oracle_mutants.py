@@ -1,0 +1,84 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case compiles a copy of the oracle with one plausible mistake planted in it (a
+dropped term, a wrong sign or index, a reversed tap order ...) and checks that at least
+one pin in test_oracle_pins fails against that copy.  The real oracle is restored after
+every case.
+"""
+import inspect
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "samba_oracle.c")
+
+MUTANTS = {
+    "drop_D_skip": ("acc += dsk * u;", "acc += 0.0 * u;"),
+    "skip_uses_preconv_x": ("acc += dsk * u;", "acc += dsk * x[ix];"),
+    "A_sign_flipped": ("exp(delta * A[(size_t)d * N + n])", "exp(-delta * A[(size_t)d * N + n])"),
+    "Bbar_without_delta": ("du = delta * u;", "du = u;"),
+    "input_term_preconv": ("du = delta * u;", "du = delta * x[ix];"),
+    "conv_taps_reversed": ("pre += w[k] * win[k];", "pre += w[ORACLE_K - 1 - k] * win[k];"),
+    "conv_history_not_shifted": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = win[k + 1];", ";"),
+    "conv_bias_dropped": ("double pre = cb, u", "double pre = 0.0 * cb, u"),
+    "readout_uses_old_state": (
+        "hs[n] = abar * hs[n] + du * B[(size_t)t * N + n];\n                acc += C[(size_t)t * N + n] * hs[n];",
+        "acc += C[(size_t)t * N + n] * hs[n];\n                hs[n] = abar * hs[n] + du * B[(size_t)t * N + n];"),
+    "B_index_t_minus_1": ("du * B[(size_t)t * N + n]", "du * B[(size_t)(t > 0 ? t - 1 : 0) * N + n]"),
+    "C_transposed_with_B": ("acc += C[(size_t)t * N + n]", "acc += B[(size_t)t * N + n]"),
+    "softplus_missing_max": ("return (a > 0.0 ? a : 0.0) + log1p(exp(-fabs(a)));", "return log1p(exp(-fabs(a)));"),
+    "gate_is_sigmoid": ("y[ix] = z ? acc * oracle_silu(z[ix]) : acc;", "y[ix] = z ? acc / (1.0 + exp(-z[ix])) : acc;"),
+    "gate_missing": ("y[ix] = z ? acc * oracle_silu(z[ix]) : acc;", "y[ix] = acc;"),
+    "dt_bias_dropped": ("delta = oracle_softplus(dt[ix] + bias);", "delta = oracle_softplus(dt[ix]);"),
+    "silu_is_sigmoid": ("return v / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(-v));"),
+    "state_not_carried_in": ("for (n = 0; n < N; ++n) hs[n] = h[(size_t)d * N + n];", "for (n = 0; n < N; ++n) hs[n] = 0.0;"),
+    "history_not_carried_in": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];",
+                               "for (k = 0; k < ORACLE_K - 1; ++k) win[k] = 0.0;"),
+}
+
+PIN_TESTS = [(n, f) for n, f in inspect.getmembers(pins, inspect.isfunction) if n.startswith("test_")]
+
+
+def _run_pins():
+    failed = []
+    for name, fn in PIN_TESTS:
+        params = inspect.signature(fn).parameters
+        variants = [{}]
+        if "with_hist" in params:
+            variants = [{"with_hist": False}, {"with_hist": True}]
+        if "with_h0" in params:
+            variants = [{"with_h0": False}, {"with_h0": True}]
+        for kw in variants:
+            try:
+                fn(**kw)
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(mutant):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + mutant
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "mut.c")
+        so = os.path.join(td, "libmut.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", so, c, "-lm"])
+        oracle._use_library(so)
+        try:
+            failed = _run_pins()
+        finally:
+            oracle._reset()
+    assert failed, "no pin caught mutant " + mutant
+
+
+def test_unmutated_oracle_passes_all_pins():
+    oracle._reset()
+    assert _run_pins() == []

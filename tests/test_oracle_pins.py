@@ -1,0 +1,359 @@
+"""Pins for the fp64 oracle, independent of its own code.
+
+Each test checks the oracle against something the pages or plain mathematics fix:
+closed forms, textbook/library special cases, brute force on tiny inputs and exact
+invariances.  Formulas are from the page "Samba: Simple Hybrid State Space Models for
+Efficient Unlimited Context Language Modeling" (paper-graph-ui summary), section 3.4
+("Input Projection and Short Convolution", "Input-Dependent Selective Gating", "The
+State Space Model Update (S6)", "Gated Output"), with the conv padding / tap order, the
+A = -exp(A_log) parameterisation and the SiLU(z) gate from "Samba Guide: Hybrid Mamba &
+Sliding Window Architecture", "Step 1: The Selective State Space (Mamba) Layer".
+
+Independent tools used here: numpy's logaddexp / scipy's expit (softplus, sigmoid),
+torch's CPU conv1d in float64 (depthwise causal conv), numpy FFT (convolution),
+explicit products (brute force).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def np_softplus(a):
+    return np.logaddexp(0.0, a)
+
+
+def np_silu(v):
+    return v * scipy.special.expit(v)
+
+
+def torch_conv_silu(x, w, b, hist=None):
+    """u = SiLU(causal depthwise conv(x)) for one sequence, x [L, D], w [D, 4], b [D],
+    hist [3, D] (oldest first) or None.  torch conv1d with padding 3, keeping the first
+    L outputs, is the causal form of the p4 sketch."""
+    L, D = x.shape
+    xt = torch.from_numpy(np.ascontiguousarray(x.T, dtype=np.float64))[None]  # [1, D, L]
+    if hist is not None:
+        xt = torch.cat([torch.from_numpy(np.ascontiguousarray(hist.T, dtype=np.float64))[None], xt], dim=2)
+        pad = 0
+    else:
+        pad = 3
+    wt = torch.from_numpy(np.asarray(w, dtype=np.float64))[:, None, :]
+    bt = torch.from_numpy(np.asarray(b, dtype=np.float64))
+    out = torch.nn.functional.conv1d(xt, wt, bt, padding=pad, groups=D)[0, :, :L]
+    return torch.nn.functional.silu(out).numpy().T.copy()  # [L, D]
+
+
+def rand_case(rng, b, L, D, N, h0=False, hist=False):
+    c = dict(
+        x=rng.standard_normal((b, L, D)), dt=0.5 * rng.standard_normal((b, L, D)),
+        z=rng.standard_normal((b, L, D)), B=rng.standard_normal((b, L, N)),
+        C=rng.standard_normal((b, L, N)),
+        A=-np.exp(np.log(np.arange(1, N + 1))[None, :] + 0.3 * rng.standard_normal((D, N))),
+        Dskip=1.0 + 0.1 * rng.standard_normal(D),
+        dt_bias=np.log(np.expm1(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), D)))),
+        conv_w=0.5 * rng.standard_normal((D, 4)), conv_b=0.1 * rng.standard_normal(D),
+    )
+    c["h0"] = rng.standard_normal((b, D, N)) if h0 else None
+    c["conv0"] = rng.standard_normal((b, 3, D)) if hist else None
+    return c
+
+
+def run_prefill(c, **kw):
+    return oracle.prefill(c["x"], c["dt"], c["B"], c["C"], c["z"], c["A"], c["Dskip"], c["dt_bias"],
+                          c["conv_w"], c["conv_b"], h0=c["h0"], conv0=c["conv0"], **kw)
+
+
+# ---------------------------------------------------------------- P7: scalar maps
+def test_softplus_silu_match_library():
+    a = np.concatenate([np.linspace(-60, 60, 2401), [-700.0, -100.0, -37.5, 37.5, 100.0, 700.0, 0.0, 1e-300]])
+    sp = np.array([oracle.softplus(v) for v in a])
+    np.testing.assert_allclose(sp, np_softplus(a), rtol=1e-14, atol=0)
+    si = np.array([oracle.silu(v) for v in a])
+    np.testing.assert_allclose(si, np_silu(a), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------- P6: conv tap order
+@pytest.mark.parametrize("with_hist", [False, True])
+def test_conv_matches_torch_conv1d(with_hist):
+    rng = np.random.default_rng(6)
+    L, D, N = 37, 5, 4
+    c = rand_case(rng, 1, L, D, N, hist=with_hist)
+    c["B"][:] = 0.0          # state never moves from zero ...
+    c["Dskip"][:] = 1.0      # ... so y = D * u = u
+    c["z"] = None
+    y, h, hist = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"], None if c["conv0"] is None else c["conv0"][0])
+    np.testing.assert_allclose(y[0], u, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(h, 0.0)
+    np.testing.assert_array_equal(hist[0], c["x"][0, -3:, :])
+
+
+def test_conv_single_tap_delays():
+    """w = (1,0,0,0): u_t = SiLU(x_{t-3}), and SiLU(0) = 0 for t < 3 with zero history."""
+    rng = np.random.default_rng(7)
+    L, D, N = 12, 3, 2
+    c = rand_case(rng, 1, L, D, N)
+    c["conv_w"][:] = 0.0
+    c["conv_w"][:, 0] = 1.0
+    c["conv_b"][:] = 0.0
+    c["B"][:] = 0.0
+    c["Dskip"][:] = 1.0
+    c["z"] = None
+    y, _, _ = run_prefill(c)
+    np.testing.assert_array_equal(y[0, :3], 0.0)
+    np.testing.assert_allclose(y[0, 3:], np_silu(c["x"][0, :-3]), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- P1: geometric series
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_constant_inputs_geometric_series(with_h0):
+    rng = np.random.default_rng(1)
+    L, D, N = 64, 3, 16
+    xv, dtv, zv = rng.standard_normal(D), 0.5 * rng.standard_normal(D), rng.standard_normal(D)
+    Bv, Cv = rng.standard_normal(N), rng.standard_normal(N)
+    c = rand_case(rng, 1, L, D, N, h0=with_h0)
+    c["x"][:] = xv
+    c["dt"][:] = dtv
+    c["z"][:] = zv
+    c["B"][:] = Bv
+    c["C"][:] = Cv
+    c["conv_w"][:] = [0.0, 0.0, 0.0, 1.0]
+    c["conv_b"][:] = 0.0
+    y, h, _ = run_prefill(c)
+    u = np_silu(xv)                                   # [D]
+    delta = np_softplus(dtv + c["dt_bias"])           # [D]
+    abar = np.exp(delta[:, None] * c["A"])            # [D, N]
+    t = np.arange(L)[:, None, None] + 1               # t+1 powers
+    geo = (1.0 - abar[None] ** t) / (1.0 - abar[None])
+    ht = (delta * u)[None, :, None] * Bv[None, None, :] * geo
+    if with_h0:
+        ht = ht + abar[None] ** t * c["h0"][0][None]
+    yt = (np.einsum("tdn,n->td", ht, Cv) + c["Dskip"] * u) * np_silu(zv)
+    np.testing.assert_allclose(y[0], yt, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(h[0], ht[-1], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- P2 / P3: limits of Delta
+def test_delta_to_zero_freezes_state():
+    rng = np.random.default_rng(2)
+    L, D, N = 40, 4, 16
+    c = rand_case(rng, 1, L, D, N, h0=True, hist=True)
+    c["dt"][:] = -60.0
+    c["dt_bias"][:] = 0.0          # Delta = softplus(-60) ~ 8.8e-27
+    y, h, _ = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"], c["conv0"][0])
+    expect = (np.einsum("tn,dn->td", c["C"][0], c["h0"][0]) + c["Dskip"] * u) * np_silu(c["z"][0])
+    np.testing.assert_allclose(y[0], expect, rtol=1e-12, atol=1e-20)
+    np.testing.assert_allclose(h[0], c["h0"][0], rtol=1e-20, atol=1e-20)
+
+
+def test_delta_to_zero_zero_state_gives_gated_skip():
+    rng = np.random.default_rng(21)
+    L, D, N = 16, 3, 16
+    c = rand_case(rng, 1, L, D, N)
+    c["dt"][:] = -60.0
+    c["dt_bias"][:] = 0.0
+    y, _, _ = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"])
+    np.testing.assert_allclose(y[0], c["Dskip"] * u * np_silu(c["z"][0]), rtol=1e-12, atol=1e-20)
+
+
+def test_large_delta_is_memoryless():
+    rng = np.random.default_rng(3)
+    L, D, N = 30, 3, 16
+    c = rand_case(rng, 1, L, D, N, h0=True)
+    c["A"][:] = -np.arange(1, N + 1, dtype=np.float64)[None, :]
+    c["dt"][:] = 40.0
+    c["dt_bias"][:] = 0.0
+    y, _, _ = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"])
+    delta = np_softplus(40.0)
+    bc = np.sum(c["B"][0] * c["C"][0], axis=1)  # [L]
+    expect = (delta * u * bc[:, None] + c["Dskip"] * u) * np_silu(c["z"][0])
+    np.testing.assert_allclose(y[0], expect, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P4: time-invariant SSM = convolution
+def test_time_invariant_case_is_a_convolution():
+    """Delta, B, C constant in time: y_t = sum_k K_k u_{t-k} + D u_t with the unrolled
+    kernel K_k = sum_n C_n Abar_n^k Delta B_n.  Checked against a direct O(L^2) sum and
+    numpy's FFT convolution."""
+    rng = np.random.default_rng(4)
+    L, D, N = 200, 3, 16
+    c = rand_case(rng, 1, L, D, N)
+    dtv = 0.5 * rng.standard_normal(D)
+    c["dt"][:] = dtv
+    c["B"][:] = rng.standard_normal(N)
+    c["C"][:] = rng.standard_normal(N)
+    c["z"] = None
+    y, _, _ = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"])   # [L, D]
+    delta = np_softplus(dtv + c["dt_bias"])
+    Bv, Cv = c["B"][0, 0], c["C"][0, 0]
+    for d in range(D):
+        abar = np.exp(delta[d] * c["A"][d])
+        K = np.array([np.sum(Cv * abar ** k * delta[d] * Bv) for k in range(L)])
+        direct = np.array([sum(K[k] * u[t - k, d] for k in range(t + 1)) for t in range(L)])
+        nfft = 2 * L
+        fft = np.fft.irfft(np.fft.rfft(K, nfft) * np.fft.rfft(u[:, d], nfft), nfft)[:L]
+        scale = np.max(np.abs(direct))
+        np.testing.assert_allclose(y[0, :, d], direct + c["Dskip"][d] * u[:, d], rtol=1e-11, atol=1e-12 * scale)
+        np.testing.assert_allclose(y[0, :, d], fft + c["Dskip"][d] * u[:, d], rtol=0, atol=1e-10 * scale)
+
+
+# ---------------------------------------------------------------- P5: brute-force unrolled form
+def test_brute_force_unrolled_matrix_form():
+    rng = np.random.default_rng(5)
+    L, D, N = 7, 2, 3
+    c = rand_case(rng, 1, L, D, N, h0=True, hist=True)
+    y, h, _ = run_prefill(c)
+    u = torch_conv_silu(c["x"][0], c["conv_w"], c["conv_b"], c["conv0"][0])
+    delta = np_softplus(c["dt"][0] + c["dt_bias"][None, :])          # [L, D]
+    abar = np.exp(delta[:, :, None] * c["A"][None])                   # [L, D, N]
+    Bm, Cm, h0 = c["B"][0], c["C"][0], c["h0"][0]
+    for t in range(L):
+        for d in range(D):
+            acc = 0.0
+            for n in range(N):
+                prod_all = 1.0
+                for r in range(t + 1):
+                    prod_all *= abar[r, d, n]
+                acc += Cm[t, n] * prod_all * h0[d, n]
+                for s in range(t + 1):
+                    p = 1.0
+                    for r in range(s + 1, t + 1):
+                        p *= abar[r, d, n]
+                    acc += Cm[t, n] * p * delta[s, d] * Bm[s, n] * u[s, d]
+            expect = (acc + c["Dskip"][d] * u[t, d]) * np_silu(c["z"][0, t, d])
+            assert abs(y[0, t, d] - expect) <= 1e-12 * max(1.0, abs(expect))
+    # final state by the same brute force
+    for d in range(D):
+        for n in range(N):
+            hv = np.prod(abar[:, d, n]) * h0[d, n]
+            for s in range(L):
+                hv += np.prod(abar[s + 1:, d, n]) * delta[s, d] * Bm[s, n] * u[s, d]
+            assert abs(h[0, d, n] - hv) <= 1e-12 * max(1.0, abs(hv))
+
+
+# ---------------------------------------------------------------- page constants: decay per step
+def test_s4d_real_decay_matches_page_statement():
+    """With A_ij = log j used as A = -exp(A_log), state dimension j decays by exp(-j*Delta)
+    per step (page: eigenvalues -j, time constant 1/j)."""
+    g = json.load(open(os.path.join(HERE, "golden", "page_constants.json")))
+    N = g["d_state"]["value"]
+    assert g["conv_kernel_size"]["value"] == 4
+    L, D = 5, 1
+    A = -np.exp(np.log(np.arange(1, N + 1, dtype=np.float64)))[None, :]
+    delta = g["delta_max"]["value"]
+    rng = np.random.default_rng(8)
+    h0 = rng.standard_normal((1, D, N))
+    zeros = np.zeros((1, L, D))
+    _, h, _ = oracle.prefill(zeros, np.full((1, L, D), np.log(np.expm1(delta))), np.zeros((1, L, N)),
+                             np.zeros((1, L, N)), None, A, np.full(D, g["D_init"]["value"]), np.zeros(D),
+                             np.zeros((D, 4)), np.zeros(D), h0=h0)
+    j = np.arange(1, N + 1)
+    np.testing.assert_allclose(h[0, 0], h0[0, 0] * np.exp(-j * delta * L), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- P8: exact invariances
+def test_chunk_split_state_carry_is_exact():
+    rng = np.random.default_rng(9)
+    b, L, D, N = 2, 50, 4, 16
+    c = rand_case(rng, b, L, D, N, h0=True, hist=True)
+    y, h, hist = run_prefill(c)
+    for L1 in (0, 1, 2, 3, 17, 49, 50):
+        c1 = dict(c)
+        for k in ("x", "dt", "z", "B", "C"):
+            c1[k] = c[k][:, :L1]
+        y1, h1, hist1 = run_prefill(c1)
+        c2 = dict(c)
+        for k in ("x", "dt", "z", "B", "C"):
+            c2[k] = c[k][:, L1:]
+        c2["h0"], c2["conv0"] = h1, hist1
+        y2, h2, hist2 = run_prefill(c2)
+        np.testing.assert_array_equal(np.concatenate([y1, y2], axis=1), y)
+        np.testing.assert_array_equal(h2, h)
+        np.testing.assert_array_equal(hist2, hist)
+
+
+def test_decode_steps_equal_prefill_exactly():
+    rng = np.random.default_rng(10)
+    b, L, D, N = 3, 9, 5, 16
+    c = rand_case(rng, b, L, D, N, h0=True, hist=True)
+    y, h, hist = run_prefill(c)
+    hs, hi = c["h0"].copy(), c["conv0"].copy()
+    for t in range(L):
+        yt = oracle.decode_step(c["x"][:, t], c["dt"][:, t], c["B"][:, t], c["C"][:, t], c["z"][:, t], c["A"],
+                                c["Dskip"], c["dt_bias"], c["conv_w"], c["conv_b"], hs, hi)
+        np.testing.assert_array_equal(yt, y[:, t])
+    np.testing.assert_array_equal(hs, h)
+    np.testing.assert_array_equal(hi, hist)
+
+
+def test_varlen_equals_separate_prefills_exactly():
+    rng = np.random.default_rng(11)
+    D, N = 4, 16
+    lens = [5, 1, 2, 13, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    c = rand_case(rng, 1, T, D, N)
+    h0 = rng.standard_normal((len(lens), D, N))
+    conv0 = rng.standard_normal((len(lens), 3, D))
+    y, h, hist = oracle.varlen(cu, c["x"][0], c["dt"][0], c["B"][0], c["C"][0], c["z"][0], c["A"], c["Dskip"],
+                               c["dt_bias"], c["conv_w"], c["conv_b"], h0=h0, conv0=conv0)
+    for s, Ls in enumerate(lens):
+        sl = slice(cu[s], cu[s + 1])
+        ys, hs, his = oracle.prefill(c["x"][:, sl], c["dt"][:, sl], c["B"][:, sl], c["C"][:, sl], c["z"][:, sl],
+                                     c["A"], c["Dskip"], c["dt_bias"], c["conv_w"], c["conv_b"],
+                                     h0=h0[s:s + 1], conv0=conv0[s:s + 1])
+        np.testing.assert_array_equal(y[sl], ys[0])
+        np.testing.assert_array_equal(h[s], hs[0])
+        np.testing.assert_array_equal(hist[s], his[0])
+    # a length-1 sequence and a length-2 sequence keep older history entries
+    np.testing.assert_array_equal(hist[1][:2], conv0[1][1:])
+    np.testing.assert_array_equal(hist[1][2], c["x"][0, cu[1]])
+
+
+def test_channel_subset_is_exact():
+    rng = np.random.default_rng(12)
+    c = rand_case(rng, 2, 20, 9, 16, h0=True, hist=True)
+    y, h, hist = run_prefill(c)
+    chans = np.array([0, 4, 8, 3])
+    ys, hs, his = run_prefill(c, chans=chans)
+    np.testing.assert_array_equal(ys, y[:, :, chans])
+    np.testing.assert_array_equal(hs, h[:, chans])
+    np.testing.assert_array_equal(his, hist[:, :, chans])
+
+
+# ---------------------------------------------------------------- P9: batch independence
+def test_batch_permutation():
+    rng = np.random.default_rng(13)
+    c = rand_case(rng, 4, 15, 3, 16, h0=True, hist=True)
+    y, h, hist = run_prefill(c)
+    perm = np.array([2, 0, 3, 1])
+    cp = dict(c)
+    for k in ("x", "dt", "z", "B", "C", "h0", "conv0"):
+        cp[k] = c[k][perm]
+    yp, hp, histp = run_prefill(cp)
+    np.testing.assert_array_equal(yp, y[perm])
+    np.testing.assert_array_equal(hp, h[perm])
+    np.testing.assert_array_equal(histp, hist[perm])
+
+
+def test_no_gate_equals_unit_gate_division():
+    """z = None returns Y itself; with z given the output is Y * SiLU(z)."""
+    rng = np.random.default_rng(14)
+    c = rand_case(rng, 1, 25, 3, 16)
+    yg, _, _ = run_prefill(c)
+    c2 = dict(c)
+    c2["z"] = None
+    y, _, _ = run_prefill(c2)
+    np.testing.assert_allclose(yg, y * np_silu(c["z"]), rtol=1e-14, atol=1e-300)
