@@ -1,0 +1,149 @@
+/*
+ * samba_scan.h -- C ABI of the MI355X (gfx950) selective-scan core of a Mamba layer,
+ * as used in the Samba hybrid model.
+ *
+ * What is computed (page "Samba: Simple Hybrid State Space Models for Efficient
+ * Unlimited Context Language Modeling", paper-graph-ui summary, section 3.4), per
+ * sequence s, channel d and token t:
+ *
+ *   u_t   = SiLU(conv_b[d] + sum_{k=0..3} conv_w[d][k] * x_{t-3+k})   "Input Projection and
+ *                                                                     Short Convolution"
+ *   Delta = softplus(dt_t + dt_bias[d])                               "Input-Dependent
+ *                                                                     Selective Gating"
+ *   h_t[n] = exp(Delta * A[d][n]) * h_{t-1}[n] + Delta * B_t[n] * u_t  "The State Space
+ *   y_t    = sum_n C_t[n] * h_t[n] + D[d] * u_t                          Model Update (S6)"
+ *   out_t  = y_t * SiLU(z_t)                                           "Gated Output"
+ *
+ * The conv is causal with the previous three pre-conv inputs taken from the history
+ * (zeros at a fresh sequence start), tap k multiplying x_{t-3+k}; A is used as given
+ * (normally negative, A = -exp(A_log)); the gate is SiLU(z) -- these follow "Samba Guide:
+ * Hybrid Mamba & Sliding Window Architecture", "Step 1: The Selective State Space (Mamba)
+ * Layer".  The input projection, x_proj/dt_proj and out_proj GEMMs are not part of this
+ * library: x, dt, B, C and z are its inputs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer on the current HIP device, owned by the
+ *   caller; the library keeps no reference after the call returns.
+ * - Token tensors are token-major and contiguous: x, dt, z, out are [tokens][d_inner]
+ *   with the channel index fastest; B and C are [tokens][d_state] and shared by all
+ *   channels of their sequence.
+ * - I/O dtype `io` applies to x, dt, z, B, C, out and the conv history: SAMBA_F32
+ *   (float) or SAMBA_BF16 (bfloat16 bits, stored as uint16).  Outputs in bf16 are
+ *   rounded to nearest even.  Parameters and the state h are always float32; all
+ *   arithmetic is float32.
+ * - The recurrent state is [seq][d_inner][d_state] float32 (state index fastest).
+ * - The conv history is [seq][3][d_inner] in the I/O dtype, oldest token first.  A
+ *   prefill's conv_final can be passed unchanged as the next prefill's conv0 or as the
+ *   decode conv_state.
+ * - d_state must be in [1, 16]; d_inner >= 1; every pointer must be aligned to 16 bytes.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
+ *   return once the work is enqueued.  Outputs must not overlap inputs, except the
+ *   deliberately in/out arguments of samba_scan_decode.
+ * - Errors: arguments are checked on the host before anything is enqueued; a failing
+ *   check returns a non-zero samba_status, enqueues nothing and sets a thread-local
+ *   message readable with samba_last_error().  A launch failure returns SAMBA_ERR_HIP.
+ *   Faults inside a kernel surface at the caller's next synchronisation.  The library
+ *   never aborts the process.
+ */
+#ifndef SAMBA_SCAN_H
+#define SAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
+
+typedef enum {
+    SAMBA_OK = 0,
+    SAMBA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative or inconsistent size */
+    SAMBA_ERR_UNSUPPORTED = 2, /* valid request this build does not handle (d_state > 16) */
+    SAMBA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than samba_scan_workspace_bytes() */
+    SAMBA_ERR_HIP = 4          /* the HIP runtime reported an error; see samba_last_error() */
+} samba_status;
+
+/* Layer parameters, all float32 device pointers, read-only.
+ *   A       [d_inner][d_state]  multiplies Delta inside exp (page 1 section 3.4, "The State
+ *                               Space Model Update (S6)")
+ *   D       [d_inner]           skip weight; NULL means 0
+ *   dt_bias [d_inner]           bias inside softplus ("Input-Dependent Selective Gating");
+ *                               NULL means 0
+ *   conv_w  [d_inner][4]        depthwise taps; tap k multiplies x_{t-3+k}
+ *   conv_b  [d_inner]           conv bias; NULL means 0 */
+typedef struct {
+    const float *A;
+    const float *D;
+    const float *dt_bias;
+    const float *conv_w;
+    const float *conv_b;
+} samba_params;
+
+/* Size in bytes of the device workspace samba_scan_prefill / samba_scan_varlen need for
+ * this problem (0 means none: pass NULL).  nseq is the batch (or number of packed
+ * sequences), max_seqlen the longest sequence. */
+size_t samba_scan_workspace_bytes(int nseq, int max_seqlen, int d_inner, int d_state);
+
+/* Fixed-length prefill of `batch` sequences of `seqlen` tokens (the chunk-parallel form of
+ * the recurrence, page 1 section 3.4 "The State Space Model Update (S6)", last paragraph;
+ * passing the final state forward between chunks as in the Samba Guide's "Chunked
+ * Prefilling" practice).
+ *   x, dt, z, out [batch][seqlen][d_inner]; B, C [batch][seqlen][d_state]   (io dtype)
+ *   z        may be NULL: no gate (out = y)
+ *   h0       [batch][d_inner][d_state] float32 initial state; NULL = zeros
+ *   conv0    [batch][3][d_inner] (io dtype) history before token 0; NULL = zeros
+ *   h_final  [batch][d_inner][d_state] float32, may be NULL; may equal h0 (in place)
+ *   conv_final [batch][3][d_inner] (io dtype), may be NULL; may equal conv0
+ *   workspace / workspace_bytes: see samba_scan_workspace_bytes()
+ * seqlen == 0 copies h0/conv0 (or zeros) into h_final/conv_final.  batch == 0 is a no-op. */
+samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                                const void *x, const void *dt, const void *B, const void *C,
+                                const void *z, const samba_params *params,
+                                const float *h0, const void *conv0,
+                                void *out, float *h_final, void *conv_final,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Packed variable-length prefill: sequence s covers tokens [cu_seqlens[s], cu_seqlens[s+1])
+ * of the packed arrays (x, dt, z, out [total_tokens][d_inner]; B, C [total_tokens][d_state]).
+ * State and conv history restart at every sequence start from h0[s] / conv0[s] (zeros
+ * when NULL) and are never carried across a boundary; h_final[s] / conv_final[s] receive
+ * each sequence's final values.
+ *   cu_seqlens  DEVICE int32 [nseq + 1], non-decreasing, cu_seqlens[0] = 0 and
+ *               cu_seqlens[nseq] = total_tokens (the caller's contract; not re-read on
+ *               the host)
+ *   max_seqlen  host int >= every sequence length (sizes the launch) */
+samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
+                               int d_inner, int d_state, samba_dtype io,
+                               const void *x, const void *dt, const void *B, const void *C,
+                               const void *z, const samba_params *params,
+                               const float *h0, const void *conv0,
+                               void *out, float *h_final, void *conv_final,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decode step: one new token for each of nseq resident sequences (the constant
+ * per-token cost of the fixed-size state, page 1 section 5 "Experimental Analysis",
+ * generation throughput).
+ *   x, dt, z, out [nseq][d_inner]; B, C [nseq][d_state]   (io dtype); z may be NULL
+ *   h          [nseq][d_inner][d_state] float32, IN/OUT: updated in place
+ *   conv_state [nseq][3][d_inner] (io dtype), IN/OUT: the last three pre-conv inputs,
+ *              oldest first; shifted by one token in place */
+samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype io,
+                               const void *x, const void *dt, const void *B, const void *C,
+                               const void *z, const samba_params *params,
+                               float *h, void *conv_state, void *out, void *stream);
+
+/* Message describing the last failing call on this thread ("" if none).  The pointer
+ * stays valid until the next call into the library on the same thread. */
+const char *samba_last_error(void);
+
+/* Library version string. */
+const char *samba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMBA_SCAN_H */

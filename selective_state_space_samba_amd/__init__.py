@@ -1,0 +1,238 @@
+"""MI355X (gfx950) selective-scan core of a Mamba layer -- Python binding.
+
+A thin ctypes layer over ``libsamba_scan.so`` (C ABI declared in
+``include/samba_scan.h``).  It only marshals torch tensors into device pointers, sizes
+and the current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
+
+Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["prefill", "varlen", "decode", "workspace_bytes", "lib_path", "SambaError", "version"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
+_lib = None
+
+SAMBA_F32, SAMBA_BF16 = 0, 1
+_STATUS = {0: "OK", 1: "SAMBA_ERR_INVALID_ARG", 2: "SAMBA_ERR_UNSUPPORTED", 3: "SAMBA_ERR_WORKSPACE", 4: "SAMBA_ERR_HIP"}
+
+
+class SambaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), msg))
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsamba_scan.so is not built (run __graft_entry__.build()); "
+                               "there is no fallback path")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.samba_last_error.restype = ctypes.c_char_p
+        lib.samba_version.restype = ctypes.c_char_p
+        lib.samba_scan_workspace_bytes.restype = Z
+        lib.samba_scan_workspace_bytes.argtypes = [I, I, I, I]
+        lib.samba_scan_prefill.restype = I
+        lib.samba_scan_prefill.argtypes = [I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P, P, Z, P]
+        lib.samba_scan_varlen.restype = I
+        lib.samba_scan_varlen.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P,
+                                          P, Z, P]
+        lib.samba_scan_decode.restype = I
+        lib.samba_scan_decode.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return load().samba_version().decode()
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SAMBA_F32
+    if t.dtype == torch.bfloat16:
+        return SAMBA_BF16
+    raise TypeError("I/O tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N):
+    f = torch.float32
+    if A is None or conv_w is None:
+        raise ValueError("A and conv_w are required")
+    _shape(A, (D, N), "A")
+    _shape(Dskip, (D,), "Dskip")
+    _shape(dt_bias, (D,), "dt_bias")
+    _shape(conv_w, (D, 4), "conv_w")
+    _shape(conv_b, (D,), "conv_b")
+    return Params(_ptr(A, "A", f, dev), _ptr(Dskip, "Dskip", f, dev), _ptr(dt_bias, "dt_bias", f, dev),
+                  _ptr(conv_w, "conv_w", f, dev), _ptr(conv_b, "conv_b", f, dev))
+
+
+def _gpu_device(x: torch.Tensor) -> torch.device:
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("inputs must be tensors on a GPU (got %s); the library has no CPU path"
+                         % (getattr(x, "device", type(x))))
+    return x.device
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(st: int):
+    if st != 0:
+        raise SambaError(st, load().samba_last_error().decode())
+
+
+def workspace_bytes(nseq: int, max_seqlen: int, d_inner: int, d_state: int) -> int:
+    return int(load().samba_scan_workspace_bytes(nseq, max_seqlen, d_inner, d_state))
+
+
+def _workspace(nseq, max_seqlen, D, N, dev, workspace):
+    need = workspace_bytes(nseq, max_seqlen, D, N)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def prefill(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, *,
+            out=None, h_final=None, conv_final=None, want_state=True, workspace=None):
+    """Fixed-length prefill.  x, dt, z: [b, L, D]; B, C: [b, L, N] (float32 or bfloat16, all
+    the same dtype, on one GPU); A [D, N], Dskip/dt_bias/conv_b [D], conv_w [D, 4] float32;
+    h0 [b, D, N] float32 or None; conv0 [b, 3, D] (I/O dtype) or None.  Returns
+    (out, h_final, conv_final); the last two are None when want_state is False."""
+    dev = _gpu_device(x)
+    b, L, D = x.shape
+    N = B.shape[-1]
+    io = _io(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if want_state and h_final is None:
+        h_final = torch.empty((b, D, N), dtype=torch.float32, device=dev)
+    if want_state and conv_final is None:
+        conv_final = torch.empty((b, 3, D), dtype=x.dtype, device=dev)
+    for t, n in ((dt, "dt"), (z, "z"), (out, "out")):
+        _shape(t, (b, L, D), n)
+    _shape(C, (b, L, N), "C")
+    _shape(h0, (b, D, N), "h0")
+    _shape(h_final, (b, D, N), "h_final")
+    _shape(conv0, (b, 3, D), "conv0")
+    _shape(conv_final, (b, 3, D), "conv_final")
+    p = _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N)
+    ws, wsb = _workspace(b, L, D, N, dev, workspace)
+    st = load().samba_scan_prefill(
+        b, L, D, N, io, _ptr(x, "x", x.dtype, dev), _ptr(dt, "dt", x.dtype, dev), _ptr(B, "B", x.dtype, dev),
+        _ptr(C, "C", x.dtype, dev), _ptr(z, "z", x.dtype, dev), ctypes.byref(p),
+        _ptr(h0, "h0", torch.float32, dev), _ptr(conv0, "conv0", x.dtype, dev), _ptr(out, "out", x.dtype, dev),
+        _ptr(h_final, "h_final", torch.float32, dev), _ptr(conv_final, "conv_final", x.dtype, dev),
+        _ptr(ws, "workspace"), wsb, _stream(dev))
+    _check(st)
+    return out, h_final, conv_final
+
+
+def varlen(cu_seqlens, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, *,
+           max_seqlen=None, out=None, h_final=None, conv_final=None, workspace=None):
+    """Packed variable-length prefill.  cu_seqlens: int32 [nseq+1] on the GPU; x, dt, z:
+    [T, D]; B, C: [T, N].  ``max_seqlen`` (host int) is computed from cu_seqlens when not
+    given (that costs a device-to-host copy).  Returns (out, h_final [nseq, D, N],
+    conv_final [nseq, 3, D])."""
+    dev = _gpu_device(x)
+    T, D = x.shape
+    N = B.shape[-1]
+    nseq = cu_seqlens.numel() - 1
+    io = _io(x)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+    if out is None:
+        out = torch.empty_like(x)
+    if h_final is None:
+        h_final = torch.empty((nseq, D, N), dtype=torch.float32, device=dev)
+    if conv_final is None:
+        conv_final = torch.empty((nseq, 3, D), dtype=x.dtype, device=dev)
+    for t, n in ((dt, "dt"), (z, "z"), (out, "out")):
+        _shape(t, (T, D), n)
+    _shape(B, (T, N), "B")
+    _shape(C, (T, N), "C")
+    _shape(cu_seqlens, (nseq + 1,), "cu_seqlens")
+    _shape(h0, (nseq, D, N), "h0")
+    _shape(h_final, (nseq, D, N), "h_final")
+    _shape(conv0, (nseq, 3, D), "conv0")
+    _shape(conv_final, (nseq, 3, D), "conv_final")
+    p = _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N)
+    ws, wsb = _workspace(nseq, max_seqlen, D, N, dev, workspace)
+    st = load().samba_scan_varlen(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), T, int(max_seqlen), D, N, io,
+        _ptr(x, "x", x.dtype, dev), _ptr(dt, "dt", x.dtype, dev), _ptr(B, "B", x.dtype, dev),
+        _ptr(C, "C", x.dtype, dev), _ptr(z, "z", x.dtype, dev), ctypes.byref(p),
+        _ptr(h0, "h0", torch.float32, dev), _ptr(conv0, "conv0", x.dtype, dev), _ptr(out, "out", x.dtype, dev),
+        _ptr(h_final, "h_final", torch.float32, dev), _ptr(conv_final, "conv_final", x.dtype, dev),
+        _ptr(ws, "workspace"), wsb, _stream(dev))
+    _check(st)
+    return out, h_final, conv_final
+
+
+def decode(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, conv_state, *, out=None):
+    """One decode step for S sequences: x, dt, z [S, D]; B, C [S, N]; h [S, D, N] float32
+    and conv_state [S, 3, D] (I/O dtype) are updated in place.  Returns out [S, D]."""
+    dev = _gpu_device(x)
+    S, D = x.shape
+    N = B.shape[-1]
+    io = _io(x)
+    if out is None:
+        out = torch.empty_like(x)
+    for t, n in ((dt, "dt"), (z, "z"), (out, "out")):
+        _shape(t, (S, D), n)
+    _shape(B, (S, N), "B")
+    _shape(C, (S, N), "C")
+    _shape(h, (S, D, N), "h")
+    _shape(conv_state, (S, 3, D), "conv_state")
+    p = _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N)
+    st = load().samba_scan_decode(
+        S, D, N, io, _ptr(x, "x", x.dtype, dev), _ptr(dt, "dt", x.dtype, dev), _ptr(B, "B", x.dtype, dev),
+        _ptr(C, "C", x.dtype, dev), _ptr(z, "z", x.dtype, dev), ctypes.byref(p),
+        _ptr(h, "h", torch.float32, dev), _ptr(conv_state, "conv_state", x.dtype, dev),
+        _ptr(out, "out", x.dtype, dev), _stream(dev))
+    _check(st)
+    return out

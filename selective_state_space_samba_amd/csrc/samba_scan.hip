@@ -1,0 +1,237 @@
+// samba_scan.hip -- MI355X (gfx950) selective-scan core of a Mamba layer, C ABI.
+//
+// Operation (page "Samba: Simple Hybrid State Space Models for Efficient Unlimited
+// Context Language Modeling", paper-graph-ui summary, section 3.4): causal depthwise
+// conv (k = 4) + SiLU, Delta = softplus(dt + b), Abar = exp(Delta A),
+// h_t = Abar h_{t-1} + Delta B_t u_t, y_t = C_t . h_t + D u_t, out = y * SiLU(z).
+// Tap order, A = -exp(A_log) and the SiLU(z) gate as in "Samba Guide: Hybrid Mamba &
+// Sliding Window Architecture", Step 1.
+//
+// This file holds the host entry points (argument checks, launch) and includes the
+// kernels.  No CUDA, no compatibility layer: gfx950 only.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/samba_scan.h"
+#include "scan_common.h"
+#include "scan_lane.h"
+
+
+namespace {
+
+thread_local std::string g_err;
+
+samba_status fail(samba_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+samba_status fail(samba_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p, name)                                                               \
+    do {                                                                                   \
+        if ((p) == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: %s is NULL", fn, name); \
+        if (!aligned16(p)) return fail(SAMBA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name); \
+    } while (0)
+#define OPTIONAL_PTR(p, name)                                                              \
+    do {                                                                                   \
+        if ((p) != nullptr && !aligned16(p))                                               \
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name); \
+    } while (0)
+
+samba_status check_common(const char *fn, int d_inner, int d_state, samba_dtype io,
+                          const samba_params *p)
+{
+    if (d_inner < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: d_inner=%d must be >= 1", fn, d_inner);
+    if (d_state < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: d_state=%d must be >= 1", fn, d_state);
+    if (d_state > samba::kMaxState)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: d_state=%d exceeds the supported maximum %d", fn, d_state,
+                    samba::kMaxState);
+    if (io != SAMBA_F32 && io != SAMBA_BF16) return fail(SAMBA_ERR_INVALID_ARG, "%s: unknown io dtype %d", fn, (int)io);
+    if (p == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: params is NULL", fn);
+    REQUIRE_PTR(p->A, "params->A");
+    REQUIRE_PTR(p->conv_w, "params->conv_w");
+    OPTIONAL_PTR(p->D, "params->D");
+    OPTIONAL_PTR(p->dt_bias, "params->dt_bias");
+    OPTIONAL_PTR(p->conv_b, "params->conv_b");
+    return SAMBA_OK;
+}
+
+samba_status launched(const char *fn)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SAMBA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    g_err.clear();
+    return SAMBA_OK;
+}
+
+// Builds the argument block shared by every kernel.
+samba::ScanArgs make_args(int nseq, int seqlen, const int32_t *cu, int d_inner, int d_state,
+                          const void *x, const void *dt, const void *B, const void *C, const void *z,
+                          const samba_params *p, const float *h0, const void *conv0, void *out,
+                          float *h_final, void *conv_final)
+{
+    samba::ScanArgs a;
+    a.nseq = nseq;
+    a.seqlen = seqlen;
+    a.cu = cu;
+    a.total = 0;
+    a.D = d_inner;
+    a.N = d_state;
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.z = z;
+    a.A = p->A;
+    a.Dskip = p->D;
+    a.dt_bias = p->dt_bias;
+    a.conv_w = p->conv_w;
+    a.conv_b = p->conv_b;
+    a.h0 = h0;
+    a.conv0 = conv0;
+    a.out = out;
+    a.h_final = h_final;
+    a.conv_final = conv_final;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *samba_last_error(void) { return g_err.c_str(); }
+
+const char *samba_version(void) { return "samba_scan 0.1 (gfx950)"; }
+
+size_t samba_scan_workspace_bytes(int nseq, int max_seqlen, int d_inner, int d_state)
+{
+    (void)nseq;
+    (void)max_seqlen;
+    (void)d_inner;
+    (void)d_state;
+    return 0;
+}
+
+samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                                const void *x, const void *dt, const void *B, const void *C,
+                                const void *z, const samba_params *params,
+                                const float *h0, const void *conv0,
+                                void *out, float *h_final, void *conv_final,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "samba_scan_prefill";
+    (void)workspace;
+    (void)workspace_bytes;
+    if (batch < 0 || seqlen < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: batch=%d seqlen=%d must be >= 0", fn, batch, seqlen);
+    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    if (st != SAMBA_OK) return st;
+    if (batch == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    if ((size_t)batch * (size_t)seqlen > (size_t)INT32_MAX)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: batch*seqlen=%zu exceeds 2^31-1 tokens", fn,
+                    (size_t)batch * (size_t)seqlen);
+    if (seqlen > 0) {
+        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(dt, "dt");
+        REQUIRE_PTR(B, "B");
+        REQUIRE_PTR(C, "C");
+        REQUIRE_PTR(out, "out");
+        OPTIONAL_PTR(z, "z");
+    }
+    OPTIONAL_PTR(h0, "h0");
+    OPTIONAL_PTR(conv0, "conv0");
+    OPTIONAL_PTR(h_final, "h_final");
+    OPTIONAL_PTR(conv_final, "conv_final");
+    samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
+                                  conv0, out, h_final, conv_final);
+    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
+                               int d_inner, int d_state, samba_dtype io,
+                               const void *x, const void *dt, const void *B, const void *C,
+                               const void *z, const samba_params *params,
+                               const float *h0, const void *conv0,
+                               void *out, float *h_final, void *conv_final,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "samba_scan_varlen";
+    (void)workspace;
+    (void)workspace_bytes;
+    if (nseq < 0 || total_tokens < 0 || max_seqlen < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d total_tokens=%d max_seqlen=%d must be >= 0", fn, nseq,
+                    total_tokens, max_seqlen);
+    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    if (st != SAMBA_OK) return st;
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    if (cu_seqlens == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: cu_seqlens is NULL", fn);
+    if (max_seqlen > total_tokens)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total_tokens=%d", fn, max_seqlen, total_tokens);
+    if (total_tokens > 0) {
+        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(dt, "dt");
+        REQUIRE_PTR(B, "B");
+        REQUIRE_PTR(C, "C");
+        REQUIRE_PTR(out, "out");
+        OPTIONAL_PTR(z, "z");
+    }
+    OPTIONAL_PTR(h0, "h0");
+    OPTIONAL_PTR(conv0, "conv0");
+    OPTIONAL_PTR(h_final, "h_final");
+    OPTIONAL_PTR(conv_final, "conv_final");
+    samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
+                                  conv0, out, h_final, conv_final);
+    a.total = total_tokens;
+    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype io,
+                               const void *x, const void *dt, const void *B, const void *C,
+                               const void *z, const samba_params *params,
+                               float *h, void *conv_state, void *out, void *stream)
+{
+    const char *fn = "samba_scan_decode";
+    if (nseq < 0) return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d must be >= 0", fn, nseq);
+    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    if (st != SAMBA_OK) return st;
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(dt, "dt");
+    REQUIRE_PTR(B, "B");
+    REQUIRE_PTR(C, "C");
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(h, "h");
+    REQUIRE_PTR(conv_state, "conv_state");
+    OPTIONAL_PTR(z, "z");
+    // A decode step is the recurrence over a single token whose state and history are
+    // read and written in place.
+    samba::ScanArgs a = make_args(nseq, 1, nullptr, d_inner, d_state, x, dt, B, C, z, params, h, conv_state,
+                                  out, h, conv_state);
+    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// scan_common.h -- shared device helpers for the selective-scan kernels (gfx950).
+//
+// Arithmetic is float32 on the hardware transcendental units: v_exp_f32 (2^x),
+// v_log_f32 (log2 x) and v_rcp_f32 (1/x).  Natural-base quantities are carried in log2
+// units where that saves a multiply: with Lg = softplus(a) * log2(e) one has
+// exp(Delta * A) = 2^(Lg * A) and Delta = Lg * ln 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace samba {
+
+constexpr int kMaxState = 16;  // d_state = 16 on every configuration of the pages
+constexpr int kConvK = 4;      // short-conv kernel size k = 4
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Argument block shared by every scan kernel.  Pointers are device pointers.
+struct ScanArgs {
+    int nseq;            // sequences (batch)
+    int seqlen;          // tokens per sequence (fixed-length) or max_seqlen (varlen)
+    const int32_t *cu;   // varlen offsets [nseq + 1] or nullptr (fixed length)
+    int total;           // tokens in the packed arrays (varlen); offsets are clamped to it
+    int D;               // d_inner
+    int N;               // d_state (<= kMaxState)
+    const void *x, *dt, *B, *C, *z;
+    const float *A, *Dskip, *dt_bias, *conv_w, *conv_b;
+    const float *h0;
+    const void *conv0;
+    void *out;
+    float *h_final;
+    void *conv_final;
+};
+
+// Token range [t0, t1) of sequence s.  Varlen offsets are device data supplied by the
+// caller; they are clamped into [0, total] so that malformed offsets can never address
+// memory outside the packed arrays.
+__device__ inline void seq_range(const ScanArgs &a, int s, size_t &t0, size_t &t1)
+{
+    if (a.cu != nullptr) {
+        const int lo = min(max(a.cu[s], 0), a.total);
+        const int hi = min(max(a.cu[s + 1], lo), a.total);
+        t0 = static_cast<size_t>(lo);
+        t1 = static_cast<size_t>(hi);
+    } else {
+        t0 = static_cast<size_t>(s) * static_cast<size_t>(a.seqlen);
+        t1 = t0 + static_cast<size_t>(a.seqlen);
+    }
+}
+
+// ---------------------------------------------------------------- I/O element types
+struct IoF32 {
+    using T = float;
+    __device__ static inline float ld(const void *p, size_t i) { return static_cast<const float *>(p)[i]; }
+    __device__ static inline void st(void *p, size_t i, float v) { static_cast<float *>(p)[i] = v; }
+};
+
+struct IoBf16 {
+    using T = uint16_t;
+    __device__ static inline float ld(const void *p, size_t i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+    }
+    // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+    __device__ static inline void st(void *p, size_t i, float v)
+    {
+        static_cast<uint16_t *>(p)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    }
+};
+
+__device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint32_t pack_bf16(float lo, float hi)
+{
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi))) << 16);
+}
+
+// ---------------------------------------------------------------- scalar maps
+__device__ inline float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ inline float hw_log2(float v) { return __builtin_amdgcn_logf(v); }
+__device__ inline float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// SiLU(v) = v * sigmoid(v) = v / (1 + e^-v).  For v -> -inf, 2^(+big) = inf and
+// rcp(inf) = 0, so the result goes to -0 without NaN.
+__device__ inline float silu(float v) { return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// softplus(a) * log2(e), accurate in relative terms for all a:
+//   softplus(a) = max(a, 0) + log1p(e^-|a|).
+// With e = 2^(-|a| log2 e) in (0, 1]: for e >= 1/32, log2(1 + e) is evaluated directly
+// (1 + e >= 1.03, so rounding 1 + e costs < 2e-6 relative); below, the series
+// log1p(e) = e (1 - e/2 + e^2/3 - e^3/4) has truncation error < e^4/5 < 2e-7 relative.
+__device__ inline float softplus_log2(float a)
+{
+    const float a2 = a * kLog2e;
+    const float e = hw_exp2(-__builtin_fabsf(a2));
+    const float big = hw_log2(1.0f + e);
+    float q = __builtin_fmaf(e, -0.25f, 0.33333333f);
+    q = __builtin_fmaf(e, q, -0.5f);
+    q = __builtin_fmaf(e, q, 1.0f);
+    const float small = (e * kLog2e) * q;
+    return __builtin_fmaxf(a2, 0.0f) + (e >= 0.03125f ? big : small);
+}
+
+}  // namespace samba

@@ -1,0 +1,43 @@
+"""Shared test helpers: the tolerance metric and host<->device marshalling."""
+import numpy as np
+
+# Tolerance (read from the target: max relative error <= 1e-4 for float32 I/O, <= 2e-2 for
+# bfloat16 I/O with a float32 state).  "Relative" is taken against |r| + rms(r) of the
+# tensor, because y crosses zero constantly (x, B, C, z are zero-mean) and a pointwise
+# relative error is undefined there.
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel_err(g, r):
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(r * r)))
+    return float(np.max(np.abs(g - r) / (np.abs(r) + rms + 1e-300)))
+
+
+def plain_rel_err(g, r, floor=1e-2):
+    """Elementwise relative error over entries with |r| >= floor * max|r| (reported only)."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    m = np.abs(r) >= floor * np.max(np.abs(r))
+    return float(np.max(np.abs(g[m] - r[m]) / np.abs(r[m]))) if m.any() else 0.0
+
+
+def tdev(a, io, dev):
+    import torch
+    dt = torch.float32 if io == "f32" else torch.bfloat16
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return t.to(dt)
+
+
+def tf32(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def host(t):
+    return t.float().cpu().numpy()

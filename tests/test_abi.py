@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI library (no GPU needed): it loads, exports every function
+declared in include/*.h, and rejects bad arguments before touching the GPU."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import selective_state_space_samba_amd as ss
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(samba_\w+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("samba_scan_prefill", "samba_scan_varlen", "samba_scan_decode", "samba_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ss.lib_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_string():
+    assert "gfx950" in ss.version()
+
+
+def _call_prefill(lib, b=1, L=4, D=8, N=16, io=1, params=True, ptrs=True):
+    p = ss.Params(16, None, None, 32 if params else None, None) if params else None
+    fake = 4096 if ptrs else None
+    return lib.samba_scan_prefill(b, L, D, N, io, fake, fake, fake, fake, None,
+                                  ctypes.byref(p) if p is not None else None,
+                                  None, None, fake, None, None, None, 0, None)
+
+
+def test_argument_errors_are_reported_without_launching():
+    lib = ss.load()
+    assert _call_prefill(lib, params=False) == 1
+    assert b"params is NULL" in lib.samba_last_error()
+    assert _call_prefill(lib, N=17) == 2
+    assert b"d_state=17" in lib.samba_last_error()
+    assert _call_prefill(lib, N=0) == 1
+    assert _call_prefill(lib, D=0) == 1
+    assert _call_prefill(lib, b=-1) == 1
+    assert _call_prefill(lib, io=7) == 1
+    assert _call_prefill(lib, ptrs=False) == 1
+    assert b"x is NULL" in lib.samba_last_error()
+    # misaligned pointer
+    p = ss.Params(16, None, None, 32, None)
+    st = lib.samba_scan_prefill(1, 4, 8, 16, 1, 4098, 4096, 4096, 4096, None, ctypes.byref(p), None, None, 4096,
+                                None, None, None, 0, None)
+    assert st == 1 and b"aligned" in lib.samba_last_error()
+    # batch == 0 is a no-op that succeeds without touching any pointer
+    assert _call_prefill(lib, b=0, ptrs=False) == 0
+
+
+def test_varlen_and_decode_argument_errors():
+    lib = ss.load()
+    p = ss.Params(16, None, None, 32, None)
+    st = lib.samba_scan_varlen(2, None, 10, 5, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None, None,
+                               4096, None, None, None, 0, None)
+    assert st == 1 and b"cu_seqlens is NULL" in lib.samba_last_error()
+    st = lib.samba_scan_varlen(2, 4096, 10, 11, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None,
+                               None, 4096, None, None, None, 0, None)
+    assert st == 1 and b"max_seqlen" in lib.samba_last_error()
+    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None, 4096, 4096, None)
+    assert st == 1 and b"h is NULL" in lib.samba_last_error()
+    assert lib.samba_scan_decode(0, 8, 16, 1, None, None, None, None, None, ctypes.byref(p), None, None, None,
+                                 None) == 0
+
+
+def test_binding_refuses_cpu_tensors_before_calling():
+    import torch
+    x = torch.zeros((1, 4, 8), dtype=torch.bfloat16)
+    Bm = torch.zeros((1, 4, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on a GPU"):
+        ss.prefill(x, x, Bm, Bm, x, torch.zeros((8, 16)), None, None, torch.zeros((8, 4)), None)
+    with pytest.raises(ValueError, match="on a GPU"):
+        ss.decode(x[0], x[0], Bm[0], Bm[0], x[0], torch.zeros((8, 16)), None, None, torch.zeros((8, 4)), None,
+                  torch.zeros((4, 8, 16)), torch.zeros((4, 3, 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="on a GPU"):
+        ss.varlen(torch.zeros(2, dtype=torch.int32), x[0], x[0], Bm[0], Bm[0], x[0], torch.zeros((8, 16)), None,
+                  None, torch.zeros((8, 4)), None, max_seqlen=4)

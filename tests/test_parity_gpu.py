@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element.
+
+Sizes here are small enough for the oracle to finish in seconds while spanning several
+workgroups / tiles and ragged tails.  Full-size configurations are in
+test_full_configs_gpu.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_samba_amd as ss
+from selective_state_space_samba_amd import synth
+from tests.helpers import TOL, host, rel_err, tdev, tf32
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def make_case(seed, b, L, D, N, io, random_A=False, with_state=False, gate=True):
+    p = synth.make_params(seed, D, N, random_A=random_A)
+    tk = synth.make_tokens(seed, (b, L), D, N, io)
+    h0 = conv0 = None
+    if with_state:
+        h0, conv0 = synth.make_state(seed, b, D, N, io, scale=0.5)
+    return p, tk, h0, conv0, gate
+
+
+def run_both(p, tk, h0, conv0, gate, io):
+    z = tk.z if gate else None
+    print("case: x", tk.x.shape, "N", tk.B.shape[-1], "io", io, "state", h0 is not None, "gate", gate, flush=True)
+    y, hf, cf = ss.prefill(tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
+                           None if z is None else tdev(z, io, DEV), tf32(p.A, DEV), tf32(p.Dskip, DEV),
+                           tf32(p.dt_bias, DEV), tf32(p.conv_w, DEV), tf32(p.conv_b, DEV),
+                           None if h0 is None else tf32(h0, DEV), None if conv0 is None else tdev(conv0, io, DEV))
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b,
+                                h0=h0, conv0=conv0)
+    return (host(y), host(hf), host(cf)), (yr, hr, cr)
+
+
+def check(g, r, io):
+    (y, hf, cf), (yr, hr, cr) = g, r
+    ey, eh = rel_err(y, yr), rel_err(hf, hr)
+    print("  y err %.3e  h err %.3e  (tol %.0e)" % (ey, eh, TOL[io]), flush=True)
+    assert ey <= TOL[io]
+    assert eh <= TOL[io]
+    np.testing.assert_array_equal(cf, cr)  # the conv history is a copy: bit-exact
+
+
+def test_tiny_config_fp32():
+    """The tiny configuration exactly: batch 1, L=512, d_inner=256, d_state=16, fp32, zero state."""
+    p, tk, h0, c0, gate = make_case(synth.seed_for(0), 1, 512, 256, 16, "f32")
+    check(*run_both(p, tk, h0, c0, gate, "f32"), "f32")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_ragged_with_state_random_A(io):
+    p, tk, h0, c0, gate = make_case(101, 3, 333, 320, 16, io, random_A=True, with_state=True)
+    check(*run_both(p, tk, h0, c0, gate, io), io)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 4, 7])
+@pytest.mark.parametrize("N", [1, 5, 16])
+def test_short_sequences_and_small_state(L, N):
+    p, tk, h0, c0, gate = make_case(200 + L + 10 * N, 2, L, 96, N, "f32", with_state=True)
+    check(*run_both(p, tk, h0, c0, gate, "f32"), "f32")
+
+
+def test_no_gate():
+    p, tk, h0, c0, _ = make_case(300, 2, 150, 128, 16, "bf16")
+    check(*run_both(p, tk, h0, c0, False, "bf16"), "bf16")
+
+
+def test_chunked_prefill_carries_state():
+    """Prefill in three chunks, passing h_final / conv_final forward, equals one pass."""
+    io = "bf16"
+    p, tk, _, _, _ = make_case(400, 2, 700, 256, 16, io)
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    h = cs = None
+    ys = []
+    for lo, hi in ((0, 129), (129, 130), (130, 700)):
+        sl = lambda a: tdev(np.ascontiguousarray(a[:, lo:hi]), io, DEV)
+        y, h, cs = ss.prefill(sl(tk.x), sl(tk.dt), sl(tk.B), sl(tk.C), sl(tk.z), *args, h, cs)
+        ys.append(host(y))
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)
+    check((np.concatenate(ys, axis=1), host(h), host(cs)), (yr, hr, cr), io)
+
+
+def test_inplace_state_update():
+    """h_final may alias h0 and conv_final may alias conv0."""
+    io = "f32"
+    p, tk, h0, c0, _ = make_case(450, 2, 64, 128, 16, io, with_state=True)
+    h = tf32(h0, DEV)
+    cs = tdev(c0, io, DEV)
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    y, _, _ = ss.prefill(tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
+                         tdev(tk.z, io, DEV), *args, h, cs, h_final=h, conv_final=cs)
+    torch.cuda.synchronize()
+    r = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, h0=h0, conv0=c0)
+    check((host(y), host(h), host(cs)), r, io)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_varlen_ragged(io):
+    lens = [0, 1, 2, 3, 5, 100, 257, 0, 64]
+    cu = synth.cu_from_lengths(lens)
+    T, D, N = int(cu[-1]), 192, 16
+    seed = 500
+    p = synth.make_params(seed, D, N, random_A=True)
+    tk = synth.make_tokens(seed, (T,), D, N, io)
+    h0, c0 = synth.make_state(seed, len(lens), D, N, io, scale=0.5)
+    print("case: varlen", lens, io, flush=True)
+    y, hf, cf = ss.varlen(torch.from_numpy(cu).to(DEV), tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV),
+                          tdev(tk.B, io, DEV), tdev(tk.C, io, DEV), tdev(tk.z, io, DEV), tf32(p.A, DEV),
+                          tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV), tf32(p.conv_w, DEV), tf32(p.conv_b, DEV),
+                          tf32(h0, DEV), tdev(c0, io, DEV))
+    torch.cuda.synchronize()
+    r = oracle.varlen(cu, tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, h0=h0, conv0=c0)
+    check((host(y), host(hf), host(cf)), r, io)
+
+
+def test_varlen_fresh_sequences():
+    """No initial state: every sequence starts from zero state and zero history."""
+    lens = [17, 3, 40]
+    cu = synth.cu_from_lengths(lens)
+    T, D, N, io = int(cu[-1]), 64, 16, "bf16"
+    p = synth.make_params(510, D, N)
+    tk = synth.make_tokens(510, (T,), D, N, io)
+    y, hf, cf = ss.varlen(torch.from_numpy(cu).to(DEV), tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV),
+                          tdev(tk.B, io, DEV), tdev(tk.C, io, DEV), tdev(tk.z, io, DEV), tf32(p.A, DEV),
+                          tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV), tf32(p.conv_w, DEV), tf32(p.conv_b, DEV))
+    torch.cuda.synchronize()
+    r = oracle.varlen(cu, tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)
+    check((host(y), host(hf), host(cf)), r, io)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_steps(io):
+    S, D, N, steps = 5, 192, 16, 24
+    seed = 600
+    p = synth.make_params(seed, D, N, random_A=True)
+    h0, c0 = synth.make_state(seed, S, D, N, io, scale=0.5)
+    h = tf32(h0, DEV)
+    cs = tdev(c0, io, DEV)
+    hr = h0.astype(np.float64).copy()
+    cr = c0.astype(np.float64).copy()
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    for k in range(steps):
+        st = synth.make_tokens(seed, (S,), D, N, io, tag="s%d" % k)
+        y = ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
+                      tdev(st.z, io, DEV), *args, h, cs)
+        yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, hr, cr)
+        torch.cuda.synchronize()
+        e = rel_err(host(y), yr)
+        assert e <= TOL[io], "step %d err %.3e" % (k, e)
+    assert rel_err(host(h), hr) <= TOL[io]
+    np.testing.assert_array_equal(host(cs), cr)
+
+
+def test_decode_continues_prefill():
+    """GPU prefill then GPU decode equals the oracle's prefill then decode."""
+    io = "bf16"
+    b, L, D, N = 3, 300, 128, 16
+    seed = 700
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (b, L), D, N, io)
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    _, h, cs = ss.prefill(tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
+                          tdev(tk.z, io, DEV), *args)
+    _, hr, cr = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)
+    for k in range(5):
+        st = synth.make_tokens(seed, (b,), D, N, io, tag="d%d" % k)
+        y = ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
+                      tdev(st.z, io, DEV), *args, h, cs)
+        yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, hr, cr)
+        torch.cuda.synchronize()
+        assert rel_err(host(y), yr) <= TOL[io]
+    np.testing.assert_array_equal(host(cs), cr)
+
+
+def test_extreme_delta():
+    """Delta -> 0 (dt = -60) and Delta large (dt = +40) run through the same kernels."""
+    io = "f32"
+    for dtv in (-60.0, 40.0):
+        p, tk, h0, c0, gate = make_case(800, 1, 90, 64, 16, io, with_state=True)
+        tk.dt[:] = dtv
+        check(*run_both(p, tk, h0, c0, gate, io), io)
+
+
+def test_run_to_run_bitwise_deterministic():
+    io = "bf16"
+    p, tk, h0, c0, _ = make_case(900, 2, 1000, 512, 16, io, with_state=True)
+    ins = [tdev(a, io, DEV) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    ref = None
+    for _ in range(5):
+        y, hf, cf = ss.prefill(*ins, *args, tf32(h0, DEV), tdev(c0, io, DEV))
+        cur = (y.clone(), hf.clone(), cf.clone())
+        if ref is None:
+            ref = cur
+        else:
+            for a, b in zip(ref, cur):
+                assert torch.equal(a, b)
+
+
+def test_invalid_arguments_raise():
+    io = "bf16"
+    x = torch.zeros((1, 8, 16), dtype=torch.bfloat16, device=DEV)
+    Bm = torch.zeros((1, 8, 17), dtype=torch.bfloat16, device=DEV)
+    A = torch.zeros((16, 17), device=DEV)
+    w = torch.zeros((16, 4), device=DEV)
+    with pytest.raises(ss.SambaError) as ei:
+        ss.prefill(x, x, Bm, Bm, x, A, None, None, w, None)
+    assert ei.value.status == 2
