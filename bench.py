@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan core on one MI355X.
+
+Default workload: the long-prompt prefill -- batch 1, L = 131072 tokens, d_inner = 4096,
+d_state = 16, bfloat16 I/O with float32 state and arithmetic (seeded synthetic inputs,
+distributions of the layer's initialisation).  A "step" is one samba_scan_prefill call
+over the whole prompt (conv + SiLU, softplus, discretisation, recurrence, readout, skip,
+gate, final-state export), with inputs already resident in HBM.
+
+Also reported (extra fields on the same JSON line): decode tokens/s for 256 resident
+sequences (65536 single-token steps replayed from HIP graphs), and the packed-varlen and
+training-length prefills.  The CPU baseline is the fp64 oracle timed on a bounded sample
+of the same prompt (a subset of channels; channels are independent).
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Peaks used for the roofline fractions.
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+# Vector ALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-slots/s.
+# (The 157.3 TFLOP/s fp32 vector figure is this rate x 2 for FMA x 2 for packed fp32.)
+# One transcendental (v_exp/v_log/v_rcp_f32) costs two slots: measured half rate.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+D_INNER, D_STATE = 4096, 16
+# Algorithmic work per token.channel (prefill and decode alike):
+#   per state n (16x): mul (Delta*A) + exp (2 slots) + mul (Delta*u*B) + fma (state) + fma (readout) = 6
+#   per token.channel: conv 4 fma; SiLU 6 (exp 2, add, rcp 2, mul); softplus 5 (exp 2, add, log 2);
+#   dt+bias 1; Delta*u 1; D*u 1; gate 7 (SiLU(z) 6 + mul)                                          = 25
+SLOTS_PER_TC = 16 * 6 + 25
+# Algorithmic HBM bytes per token for bf16 I/O: read x, dt, z (2 B each per channel), write y
+# (2 B per channel), read B and C (2 B each per state).
+BYTES_PER_TOKEN = 8 * D_INNER + 4 * D_STATE
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the varlen / training-length timings")
+    ap.add_argument("--decode-steps", type=int, default=65536)
+    ap.add_argument("--cpu-channels", type=int, default=2048)
+    ap.add_argument("--prefill-only", action="store_true", help="time only the long-prompt prefill (profiling)")
+    return ap.parse_args()
+
+
+def to_dev(a, dev, bf16=True):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+def time_calls(fn, steps, warmup):
+    """Run fn() warmup + steps times on torch's current stream (the stream the library
+    launches on); returns (total seconds, per-call seconds from HIP events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return wall, per
+
+
+def bench_prefill(args, dev):
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+
+    seed = synth.seed_for(2)
+    b, L = 1, 131072
+    t0 = time.perf_counter()
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    tk = synth.make_tokens(seed, (b, L), D_INNER, D_STATE, "bf16")
+    log("generated prompt128k inputs in %.1fs" % (time.perf_counter() - t0))
+    x, dt, Bm, Cm, z = (to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z))
+    prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    out = torch.empty_like(x)
+    hf = torch.empty((b, D_INNER, D_STATE), dtype=torch.float32, device=dev)
+    cf = torch.empty((b, 3, D_INNER), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ss.prefill(x, dt, Bm, Cm, z, *prm, out=out, h_final=hf, conv_final=cf)
+
+    torch.cuda.synchronize()
+    wall, per = time_calls(step, args.steps, args.warmup)
+    log("prefill per-call ms:", " ".join("%.3f" % (s * 1e3) for s in per))
+    return dict(tokens=b * L, wall=wall, per=per, host=(p, tk))
+
+
+def bench_decode(args, dev):
+    """256 resident sequences, state from a random L=1024 prefill, then decode steps whose
+    inputs cycle through a pool of 256 pre-drawn steps (replayed from HIP graphs)."""
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+
+    S, Lw, P = 256, 1024, 256
+    seed = synth.seed_for(3)
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def randn(shape, std=1.0):
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    # warm-up prefill (random inputs drawn as in the tiny configuration's recipe)
+    x, z, Bm, Cm = randn((S, Lw, D_INNER)), randn((S, Lw, D_INNER)), randn((S, Lw, D_STATE)), randn((S, Lw, D_STATE))
+    dt = randn((S, Lw, D_INNER), 0.5)
+    _, h, cs = ss.prefill(x, dt, Bm, Cm, z, *prm)
+    del x, z, Bm, Cm, dt
+    pool = dict(x=randn((P, S, D_INNER)), dt=randn((P, S, D_INNER), 0.5), z=randn((P, S, D_INNER)),
+                B=randn((P, S, D_STATE)), C=randn((P, S, D_STATE)))
+    y = torch.empty((S, D_INNER), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def one(k):
+        ss.decode(pool["x"][k], pool["dt"][k], pool["B"][k], pool["C"][k], pool["z"][k], *prm, h, cs, out=y)
+
+    # eager per-step timing (a few steps) for the kernel duration
+    _, per = time_calls(lambda: one(0), 20, 5)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for k in range(P):
+            one(k)
+    torch.cuda.synchronize()
+    reps = max(1, args.decode_steps // P)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, bev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    bev.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(bev) / 1e3
+    steps = reps * P
+    return dict(S=S, steps=steps, seconds=t, per_step_eager=float(np.mean(per)))
+
+
+def bench_extra(dev, steps=5, warmup=2):
+    """Training-length prefill (4 x 4096) and packed varlen (8 sequences, <= 131072 tokens)."""
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+
+    res = {}
+    seed = synth.seed_for(1)
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    tk = synth.make_tokens(seed, (4, 4096), D_INNER, D_STATE, "bf16")
+    ins = [to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    out = torch.empty_like(ins[0])
+    _, per = time_calls(lambda: ss.prefill(*ins, *prm, out=out), steps, warmup)
+    res["train4k"] = dict(workload="batch 4, L=4096", ms=float(np.mean(per) * 1e3),
+                          mtok_s=4 * 4096 / float(np.mean(per)) / 1e6)
+    del ins, out
+    seed = synth.seed_for(4)
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    lens = synth.varlen_lengths(seed)
+    cu = synth.cu_from_lengths(lens)
+    T = int(cu[-1])
+    tk = synth.make_tokens(seed, (T,), D_INNER, D_STATE, "bf16")
+    ins = [to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    cu_d = torch.from_numpy(cu).to(dev)
+    out = torch.empty_like(ins[0])
+    _, per = time_calls(lambda: ss.varlen(cu_d, *ins, *prm, max_seqlen=int(lens.max()), out=out), steps, warmup)
+    res["varlen8"] = dict(workload="8 sequences, lengths %s, %d tokens" % (lens.tolist(), T),
+                          ms=float(np.mean(per) * 1e3), mtok_s=T / float(np.mean(per)) / 1e6)
+    return res
+
+
+def cpu_baseline(host, nch):
+    import oracle
+    p, tk = host
+    chans = np.arange(nch)
+    t0 = time.perf_counter()
+    oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, chans=chans)
+    sec = time.perf_counter() - t0
+    L = tk.x.shape[1]
+    return {"value": L * nch / D_INNER / sec / 1e6, "unit": "Mtok/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "fp64 oracle over all %d tokens of the prompt for %d of the %d channels (channels are "
+                      "independent); %.1f s wall; rate scaled to full-width tokens" % (L, nch, D_INNER, sec)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_samba_amd as ss
+    ss.load()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    pre = bench_prefill(args, dev)
+    per = np.array(pre["per"])
+    t_step = float(np.mean(per))
+    tokens = pre["tokens"]
+    value = tokens / t_step / 1e6
+    slots = tokens * D_INNER * SLOTS_PER_TC
+    achieved_alu = slots / t_step / 1e12
+    hbm_bytes = tokens * BYTES_PER_TOKEN
+    achieved_hbm = hbm_bytes / t_step / 1e9
+    line = {
+        "metric": "selective-scan Mtok/s at L=128K,d_inner=4096",
+        "value": round(value, 3),
+        "unit": "Mtok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prompt128k: batch 1, L=131072, d_inner=4096, d_state=16, bf16 I/O, fp32 state",
+                   "global_batch": 1, "seq_len": 131072, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "achieved": round(achieved_alu, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
+                     "unit": "T VALU-slots/s", "frac": round(achieved_alu / VALU_PEAK_TSLOTS, 4),
+                     "traffic": None,
+                     "work_per_launch": "%d tokens x %d channels x %d slots" % (tokens, D_INNER, SLOTS_PER_TC)},
+        "roofline_hbm": {"achieved": round(achieved_hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved_hbm / HBM_PEAK_GBS, 4), "bytes_per_launch": hbm_bytes},
+        "tok_ch_per_s": tokens * D_INNER / t_step,
+        "kernel": "samba_scan_prefill (one kernel launch per step)",
+    }
+    if not args.prefill_only and not args.no_decode:
+        dec = bench_decode(args, dev)
+        line["decode"] = {"tok_s": round(dec["S"] * dec["steps"] / dec["seconds"], 1), "sequences": dec["S"],
+                          "steps": dec["steps"], "us_per_step": round(dec["seconds"] / dec["steps"] * 1e6, 3),
+                          "us_per_step_eager": round(dec["per_step_eager"] * 1e6, 3),
+                          "note": "HIP-graph replay of 256-step graphs; state 67 MB fits the 256 MB MALL"}
+    if not args.prefill_only and not args.no_extra:
+        line["extra"] = bench_extra(dev)
+    if not args.prefill_only and not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(pre["host"], args.cpu_channels)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,11 +14,14 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/samba_scan.h"
 #include "scan_common.h"
 #include "scan_lane.h"
+#include "scan_rows.h"
 
 
 namespace {
@@ -35,6 +38,22 @@ samba_status fail(samba_status st, const char *fmt, ...)
     va_end(ap);
     g_err = buf;
     return st;
+}
+
+// Kernel choice for prefill / varlen.  The lane kernel (one lane per channel, 16 states
+// in registers) is the cheapest per token when sequences x channels alone give at least
+// four waves per SIMD; otherwise the row kernel (16 lanes per channel) supplies the
+// parallelism.  SAMBA_SCAN_PATH=lane|rows forces one of them (used by the tests to run
+// both kernels on every shape).
+bool use_rows(int nseq, int d_inner)
+{
+    const char *e = getenv("SAMBA_SCAN_PATH");
+    if (e != nullptr && e[0] != '\0') {
+        if (strcmp(e, "rows") == 0) return true;
+        if (strcmp(e, "lane") == 0) return false;
+    }
+    constexpr size_t kLaneThreshold = 256ull * 4 * 64 * 4;  // lanes for 4 waves on each SIMD
+    return static_cast<size_t>(nseq) * static_cast<size_t>(d_inner) < kLaneThreshold;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -159,7 +178,10 @@ samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state,
     OPTIONAL_PTR(conv_final, "conv_final");
     samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
-    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    if (use_rows(batch, d_inner))
+        samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
+    else
+        samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 
@@ -201,7 +223,10 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
     samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.total = total_tokens;
-    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    if (use_rows(nseq, d_inner))
+        samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
+    else
+        samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 

@@ -25,11 +25,15 @@ tensor's values do not depend on which other tensors were drawn.
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import zlib
-from dataclasses import dataclass, field
-from typing import Optional
+from dataclasses import dataclass
 
 import numpy as np
+
+_CHUNK = 1 << 22  # elements per independent child stream
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 CONV_K = 4
 
@@ -60,11 +64,18 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     return r.view(np.float32)
 
 
-def _normal(seed, name, shape, mean=0.0, std=1.0, io="f32", chunk=1 << 24):
-    g = _rng(seed, name)
+def _normal(seed, name, shape, mean=0.0, std=1.0, io="f32"):
+    """Normal draws; element block c (of _CHUNK elements) comes from its own child stream
+    SeedSequence([seed, crc32(name), c]), so the values do not depend on how many threads
+    fill the array."""
+    key = zlib.crc32(name.encode())
     out = np.empty(int(np.prod(shape)), dtype=np.float32)
-    for s in range(0, out.size, chunk):
-        e = min(out.size, s + chunk)
+    nchunk = (out.size + _CHUNK - 1) // _CHUNK
+
+    def fill(c):
+        s = c * _CHUNK
+        e = min(out.size, s + _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, key, c])))
         v = g.standard_normal(e - s)  # float64
         if std != 1.0:
             v *= std
@@ -73,6 +84,13 @@ def _normal(seed, name, shape, mean=0.0, std=1.0, io="f32", chunk=1 << 24):
         out[s:e] = v
         if io == "bf16":
             out[s:e] = round_bf16(out[s:e])
+
+    if nchunk <= 1:
+        for c in range(nchunk):
+            fill(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(_THREADS, nchunk)) as ex:
+            list(ex.map(fill, range(nchunk)))
     return out.reshape(shape)
 
 

@@ -17,6 +17,15 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
+@pytest.fixture(params=["rows", "lane"], autouse=True)
+def scan_path(request, monkeypatch):
+    """Run every prefill / varlen case on both kernels (the decode step always uses the
+    one-lane-per-channel kernel)."""
+    monkeypatch.setenv("SAMBA_SCAN_PATH", request.param)
+    print("path:", request.param, flush=True)
+    return request.param
+
+
 def make_case(seed, b, L, D, N, io, random_A=False, with_state=False, gate=True):
     p = synth.make_params(seed, D, N, random_A=random_A)
     tk = synth.make_tokens(seed, (b, L), D, N, io)
