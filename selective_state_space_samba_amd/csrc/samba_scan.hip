@@ -44,9 +44,14 @@ samba_status fail(samba_status st, const char *fmt, ...)
 // in registers) is the cheapest per token when sequences x channels alone give at least
 // four waves per SIMD; otherwise the row kernel (16 lanes per channel) supplies the
 // parallelism.  SAMBA_SCAN_PATH=lane|rows forces one of them (used by the tests to run
-// both kernels on every shape).
-bool use_rows(int nseq, int d_inner)
+// both kernels on every shape); the lane kernel is used whenever the row kernel's
+// alignment requirement is not met.
+bool use_rows(int nseq, int d_inner, samba_dtype io)
 {
+    // The row kernel moves 16-channel token rows as 16-byte vectors: every row must start
+    // 16-byte aligned, i.e. d_inner * sizeof(element) must be a multiple of 16.
+    const int elem = io == SAMBA_BF16 ? 2 : 4;
+    if ((d_inner * elem) % 16 != 0) return false;
     const char *e = getenv("SAMBA_SCAN_PATH");
     if (e != nullptr && e[0] != '\0') {
         if (strcmp(e, "rows") == 0) return true;
@@ -178,7 +183,7 @@ samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state,
     OPTIONAL_PTR(conv_final, "conv_final");
     samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
-    if (use_rows(batch, d_inner))
+    if (use_rows(batch, d_inner, io))
         samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
     else
         samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
@@ -223,7 +228,7 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
     samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.total = total_tokens;
-    if (use_rows(nseq, d_inner))
+    if (use_rows(nseq, d_inner, io))
         samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
     else
         samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));

@@ -71,6 +71,58 @@ struct IoBf16 {
     }
 };
 
+// Raw buffer access: a wave-uniform 128-bit resource (base, byte range) in SGPRs plus a
+// 32-bit per-lane byte offset.  The hardware returns 0 for loads and drops stores whose
+// offset falls outside the range, so a resource built from the exact extent of an
+// array bounds every access to it.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor flags
+
+__device__ inline Rsrc make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ inline void buf_ld(Rsrc r, uint32_t boff, float &v)
+{
+    v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, boff, 0, 0));
+}
+__device__ inline void buf_ld(Rsrc r, uint32_t boff, uint16_t &v)
+{
+    v = __builtin_amdgcn_raw_buffer_load_b16(r, boff, 0, 0);
+}
+__device__ inline uint4 buf_ld128(Rsrc r, uint32_t boff)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, boff, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline void buf_st(Rsrc r, uint32_t boff, float v, float *)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, boff, 0, 0);
+}
+__device__ inline void buf_st(Rsrc r, uint32_t boff, float v, uint16_t *)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), r, boff, 0, 0);
+}
+
+// Loads / stores at a 32-bit byte offset from a wave-uniform base pointer.
+template <class T>
+__device__ inline T ld_at(const T *base, uint32_t boff)
+{
+    return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + boff);
+}
+__device__ inline void st_at(float *base, uint32_t boff, float v)
+{
+    *reinterpret_cast<float *>(reinterpret_cast<char *>(base) + boff) = v;
+}
+__device__ inline void st_at(uint16_t *base, uint32_t boff, float v)
+{
+    *reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(base) + boff) = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+__device__ inline float to_f32(float v) { return v; }
+__device__ inline float to_f32(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
 __device__ inline float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ inline uint32_t pack_bf16(float lo, float hi)

@@ -7,15 +7,23 @@
 // the sequence in time, so a batch-1 prompt of d_inner = 4096 channels still yields
 // 65536 lanes with no cross-workgroup carry and no recomputation.
 //
-// Per block of 16 tokens, lane j of a row runs the per-token front end for token t0+j
-// (causal conv with the taps x_{t-1..t-3} fetched from neighbouring lanes by DPP row
-// rotations, SiLU, softplus(dt + b)), then all 16 lanes step their state through the 16
-// tokens, receiving Delta and Delta*u of token t from lane t by DPP row broadcast fused
-// into the multiply.  B and C of the block are staged once per workgroup into LDS as
-// float32, transposed to [state][token], so each lane reads its state's column with
-// 128-bit loads.  The 16 partial products C_t[n] h_t[n] of a lane are transposed through
-// LDS so that lane j sums the readout of token t0+j, adds D*u, applies the SiLU(z) gate
-// and stores the output.
+// Work is organised in blocks of 16 tokens (one per lane of a row) and stages of
+// kStage tokens:
+//  * per stage, the workgroup stages B and C (shared by its 16 channels) into LDS as
+//    float32, transposed to [state][token], while each lane prefetches into registers
+//    the x / dt / z words of its tokens of the next stage (buffer loads bounded by the
+//    stage's extent);
+//  * per block, lane j runs the per-token front end for token t0+j: causal conv with the
+//    taps x_{t-1..t-3} fetched from neighbouring lanes by DPP row rotations, SiLU,
+//    softplus(dt + b); then all 16 lanes step their state through the 16 tokens,
+//    receiving Delta and Delta*u of token t from lane t by DPP row broadcast fused into
+//    the multiply;
+//  * the 16 partial products C_t[n] h_t[n] of every lane are transposed through LDS so
+//    that lane j sums the readout of token t0+j, adds D*u, applies the SiLU(z) gate and
+//    stores the output.
+// The LDS traffic is software-pipelined: the B/C columns of block k+1 are read while
+// block k computes, and the transposed products of block k-1 are read before block k's
+// recurrence and consumed after it.
 #pragma once
 
 #include "scan_common.h"
@@ -28,19 +36,21 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kRowsPerWave = 4;           // channels per wave (4 rows of 16 lanes)
 constexpr int kChannels = kWaves * kRowsPerWave;  // channels per workgroup
 constexpr int kBlock = 16;                // tokens per block (one per lane of a row)
-constexpr int kStage = 64;                // tokens of B/C staged in LDS per stage
-constexpr int kStageBlocks = kStage / kBlock;
-constexpr int kBCPitch = kStage + 4;      // LDS pitch of one state's column (floats)
 constexpr int kPPitch = kBlock + 4;       // LDS pitch of one token's 16 partial products
+// LDS pitch of one row's 16x16 product tile: 16*20 + 16 floats puts the 4 rows of a
+// wave 16 banks apart, so a wave-wide store of one token's products does not conflict.
+constexpr int kRowPitch = kBlock * kPPitch + 16;
 
 // DPP controls (gfx9 encoding).
 constexpr int kRowRor = 0x120;      // row_ror:k = kRowRor + k  (k = 1..15)
 constexpr int kRowNewBcast = 0x150; // row_newbcast:k = kRowNewBcast + k
 
+// DPP move with every source lane valid (row rotations and row broadcasts), so the
+// compiler may fold it into the consuming VOP2 instruction.
 template <int kCtrl>
 __device__ inline float dpp(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
 }
 
 // x_{t-s} for the lane's token: from lane j-s of this block, or lane 16+j-s of the previous
@@ -52,67 +62,158 @@ __device__ inline float tap(float xcur, float xprev, int j)
     return dpp<kRowRor + kS>(r);
 }
 
-struct Smem {
-    float bc[2][2][kMaxState][kBCPitch];                        // [buffer][B|C][state][token]
-    float p[kWaves][kRowsPerWave][kBlock][kPPitch];             // [wave][row][token][state]
-};
-
-// Loads (into registers) this thread's share of a B/C stage: 2 tensors x kStage tokens x 16
-// states of bf16/f32.  Thread l handles tensor l/128, token (l%128)/2, states 8*(l%2)..+7.
-template <class Io>
-struct StageRegs {
-    float v[8];
-};
-
-template <class Io>
-__device__ inline void stage_load(const ScanArgs &a, size_t tbase, size_t t1, int N, int tid, StageRegs<Io> &r)
+// Compiler-level ordering point for the intra-wave LDS exchange (a wave executes its LDS
+// instructions in order, so nothing is needed in hardware).
+__device__ inline void wave_order()
 {
-    const int which = tid >> 7;
-    const int tt = (tid & 127) >> 1;
-    const int n0 = (tid & 1) * 8;
-    const size_t t = tbase + tt;
-    const void *src = which ? a.C : a.B;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Token tiles hold, per stage, x / dt / z for the workgroup's 16 channels: one row of
+// 16 I/O words per token, padded by 8 bytes so that the 16 tokens a wave reads at once
+// (one per lane of a row) fall in distinct banks.
+template <class T>
+constexpr int tok_pitch_bytes() { return kChannels * static_cast<int>(sizeof(T)) + 8; }
+
+template <class T, int kStage>
+struct Smem {
+    static constexpr int kBCPitch = kStage + 4;  // LDS pitch of one state's column (floats)
+    static constexpr int kTokPitch = tok_pitch_bytes<T>();
+    float bc[2][2][kMaxState][kBCPitch];         // [buffer][B|C][state][token]
+    float p[kWaves][kRowsPerWave * kRowPitch];   // [wave][row][token][state] (padded)
+    alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
+};
+
+// One B/C stage is 2 tensors x kStage tokens x 16 states.  The 256 threads cover the
+// 2*kStage (tensor, token) pairs with kParts threads per pair, each holding kPer states.
+// The raw words stay in registers while the current stage is computed and are converted
+// to float32 when written to LDS.  Tokens past the end of the sequence re-load the last
+// token (always in bounds); they only feed steps whose Delta is forced to 0.
+template <class Io, int kStage>
+struct Stager {
+    static constexpr int kPairs = 2 * kStage;           // (tensor, token) pairs per stage
+    static constexpr int kParts = 256 / kPairs;         // threads per pair
+    static constexpr int kPer = kMaxState / kParts;     // states per thread
+    static_assert(kPairs * kParts == 256 && kPer * kParts == kMaxState, "stage shape");
+    static constexpr int kWords = kPer * sizeof(typename Io::T) / 16;  // uint4 words (N == 16)
+    float v[kPer];
+    uint4 w[kWords > 0 ? kWords : 1];
+
+    __device__ inline void load(const ScanArgs &a, size_t tbase, size_t t1, int N, int tid)
+    {
+        const int pair = tid / kParts;
+        const int part = tid % kParts;
+        const int which = pair / kStage;
+        const int tt = pair % kStage;
+        size_t t = tbase + static_cast<size_t>(tt);
+        if (t >= t1) t = t1 - 1;  // t1 > tbase for every stage that exists
+        const void *src = which ? a.C : a.B;
+        const int n0 = part * kPer;
+        if (N == kMaxState && kWords > 0) {
+            const uint4 *q =
+                reinterpret_cast<const uint4 *>(static_cast<const typename Io::T *>(src) + t * kMaxState + n0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r.v[k] = 0.0f;
-    if (t < t1) {
-        if (N == kMaxState) {
+            for (int k = 0; k < kWords; ++k) w[k] = q[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) v[k] = (n0 + k) < N ? Io::ld(src, t * N + n0 + k) : 0.0f;
+        }
+    }
+
+    template <class T>
+    __device__ inline void store(Smem<T, kStage> &sm, int buf, int tid, int N) const
+    {
+        const int pair = tid / kParts;
+        const int part = tid % kParts;
+        const int which = pair / kStage;
+        const int tt = pair % kStage;
+        const int n0 = part * kPer;
+        float f[kPer];
+        if (N == kMaxState && kWords > 0) {
+            const uint32_t *u = reinterpret_cast<const uint32_t *>(w);
             if constexpr (sizeof(typename Io::T) == 2) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + t * kMaxState + n0);
-                r.v[0] = bf16lo(w.x); r.v[1] = bf16hi(w.x);
-                r.v[2] = bf16lo(w.y); r.v[3] = bf16hi(w.y);
-                r.v[4] = bf16lo(w.z); r.v[5] = bf16hi(w.z);
-                r.v[6] = bf16lo(w.w); r.v[7] = bf16hi(w.w);
+#pragma unroll
+                for (int k = 0; k < kPer / 2; ++k) {
+                    f[2 * k] = bf16lo(u[k]);
+                    f[2 * k + 1] = bf16hi(u[k]);
+                }
             } else {
-                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + t * kMaxState + n0);
-                const float4 u0 = p[0], u1 = p[1];
-                r.v[0] = u0.x; r.v[1] = u0.y; r.v[2] = u0.z; r.v[3] = u0.w;
-                r.v[4] = u1.x; r.v[5] = u1.y; r.v[6] = u1.z; r.v[7] = u1.w;
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) f[k] = __uint_as_float(u[k]);
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (n0 + k < N) r.v[k] = Io::ld(src, t * N + n0 + k);
+            for (int k = 0; k < kPer; ++k) f[k] = v[k];
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) sm.bc[buf][which][n0 + k][tt] = f[k];
+    }
+};
+
+// Token tiles of one stage: 3 tensors x kStage tokens x one 16-channel row (32 bytes for
+// bf16, 64 for fp32), moved as 16-byte buffer loads (16-channel rows are contiguous in
+// the token-major layout) and kept raw in registers until written to LDS at the end of
+// the current stage.  Tokens past the end of the sequence re-load the last token.
+template <class Io, int kStage>
+struct TokStager {
+    using T = typename Io::T;
+    static constexpr int kRowBytes = kChannels * static_cast<int>(sizeof(T));
+    static constexpr int kVecPerRow = kRowBytes / 16;
+    static constexpr int kPerTensor = kStage * kVecPerRow;
+    static constexpr int kVecs = 3 * kPerTensor;
+    static constexpr int kPerThread = (kVecs + 255) / 256;
+    uint4 v[kPerThread];
+
+    // rsrc[k]: resource of tensor k for this stage; c0: first channel of the workgroup.
+    __device__ inline void load(const Rsrc (&rsrc)[3], int last, int D, int c0, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int idx = i * 256 + tid;
+            if (kVecs % 256 == 0 || idx < kVecs) {
+                // the tensor index is uniform across a wave (256 % 64 == 0, kPerTensor % 64 == 0)
+                const int tensor = __builtin_amdgcn_readfirstlane(idx / kPerTensor);
+                const int rem = idx - tensor * kPerTensor;
+                const int tok = min(rem / kVecPerRow, last);
+                const int part = rem % kVecPerRow;
+                const uint32_t boff = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(D) + static_cast<uint32_t>(c0)) *
+                                          static_cast<uint32_t>(sizeof(T)) +
+                                      static_cast<uint32_t>(part * 16);
+                const Rsrc r = tensor == 0 ? rsrc[0] : (tensor == 1 ? rsrc[1] : rsrc[2]);
+                v[i] = buf_ld128(r, boff);
+            }
         }
     }
-}
 
-template <class Io>
-__device__ inline void stage_store(Smem &sm, int buf, int tid, const StageRegs<Io> &r)
-{
-    const int which = tid >> 7;
-    const int tt = (tid & 127) >> 1;
-    const int n0 = (tid & 1) * 8;
+    __device__ inline void store(Smem<T, kStage> &sm, int buf, int tid) const
+    {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sm.bc[buf][which][n0 + k][tt] = r.v[k];
-}
+        for (int i = 0; i < kPerThread; ++i) {
+            const int idx = i * 256 + tid;
+            if (kVecs % 256 == 0 || idx < kVecs) {
+                const int tensor = idx / kPerTensor;
+                const int rem = idx - tensor * kPerTensor;
+                const int tok = rem / kVecPerRow;
+                const int part = rem % kVecPerRow;
+                uint2 *d = reinterpret_cast<uint2 *>(&sm.tok[buf][tensor][tok][part * 16]);
+                d[0] = make_uint2(v[i].x, v[i].y);
+                d[1] = make_uint2(v[i].z, v[i].w);
+            }
+        }
+    }
+};
 
 }  // namespace rows
 
-template <class Io>
+template <class Io, int kStage>
 __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 {
     using namespace rows;
-    __shared__ Smem sm;
+    using T = typename Io::T;
+    constexpr int kStageBlocks = kStage / kBlock;
+    __shared__ Smem<T, kStage> sm;
 
     // Workgroup -> (sequence, block of 16 channels).  Consecutive hardware workgroup ids
     // go round-robin to the 8 XCDs; remap so that each XCD gets a contiguous range of
@@ -139,6 +240,7 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 
     size_t t0, t1;
     seq_range(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
 
     const float An = state_ok ? a.A[static_cast<size_t>(cc) * N + j] : 0.0f;
     const float w0 = a.conv_w[cc * kConvK + 0], w1 = a.conv_w[cc * kConvK + 1];
@@ -150,79 +252,151 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     float h = (a.h0 != nullptr && state_ok) ? a.h0[hidx] : 0.0f;
 
     // History: lanes 13, 14, 15 of the "previous block" hold x_{t0-3}, x_{t0-2}, x_{t0-1}.
+    // conv_final entry k receives x_{t1-3+k}: from the incoming history when t1-3+k < t0
+    // (sequences shorter than 3 tokens), else from the sequence itself.  Every source is
+    // read before any store, since conv_final may alias conv0.
     const size_t cbase = static_cast<size_t>(s) * 3 * D + cc;
     float xprev = 0.0f;
     if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
-    // conv_final entries that lie before t0 (sequences shorter than 3 tokens): copy the
-    // tail of the incoming history (read above, before any store can overwrite it).
-    const size_t L = t1 - t0;
-    if (a.conv_final != nullptr && chan_ok && L < 3 && j >= 13 && j - 13 + static_cast<int>(L) <= 2) {
-        // entry k = j - 13 receives x_{t1-3+k} = history entry k + L
+    if (a.conv_final != nullptr && chan_ok && j >= 13) {
         const int k = j - 13;
-        const float hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
+        const int tk = L - 3 + k;  // token index relative to t0
+        float hv;
+        if (tk >= 0)
+            hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
+        else
+            hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
         Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
     }
 
-    const size_t nblocks = (L + kBlock - 1) / kBlock;
-    const size_t nstages = (nblocks + kStageBlocks - 1) / kStageBlocks;
+    const int nstages = (L + kStage - 1) / kStage;
+    const bool has_z = a.z != nullptr;
+    const T *xs = static_cast<const T *>(a.x) + t0 * D;
+    const T *dts = static_cast<const T *>(a.dt) + t0 * D;
+    const T *zs = has_z ? static_cast<const T *>(a.z) + t0 * D : xs;
+    T *os = static_cast<T *>(a.out) + t0 * D;
 
-    // Prologue: stage 0 of B/C into LDS buffer 0.
-    StageRegs<Io> sr;
-    if (nstages > 0) {
-        stage_load<Io>(a, t0, t1, N, tid, sr);
-        stage_store<Io>(sm, 0, tid, sr);
-    }
-    __syncthreads();
+    // Byte extent of a stage's rows (the stage's tokens that belong to the sequence):
+    // buffer resources built on it bound every token access of the stage.
+    auto stage_bytes = [&](int base) {
+        return static_cast<uint32_t>(min(kStage, L - base)) * static_cast<uint32_t>(D) * static_cast<uint32_t>(sizeof(T));
+    };
+    auto tok_off = [&](int tr) {  // byte offset of (token tr of a stage, this lane's channel)
+        return (static_cast<uint32_t>(tr) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cc)) *
+               static_cast<uint32_t>(sizeof(T));
+    };
 
-    // Per-token inputs of the first block.
-    auto load_tok = [&](size_t tb, float &xv, float &dtv, float &zv) {
-        const size_t t = tb + j;
-        xv = dtv = zv = 0.0f;
-        if (t < t1) {
-            const size_t ix = t * D + cc;
-            xv = Io::ld(a.x, ix);
-            dtv = Io::ld(a.dt, ix);
-            zv = a.z ? Io::ld(a.z, ix) : 0.0f;
+    // Token tiles of one stage (x, dt, z for the workgroup's 16 channels).
+    const int c0 = cb * kChannels;
+    auto load_stage_tokens = [&](int st, TokStager<Io, kStage> &ts) {
+        const int base = st * kStage;
+        const uint32_t bytes = stage_bytes(base);
+        const Rsrc r[3] = {make_rsrc(xs + static_cast<size_t>(base) * D, bytes),
+                           make_rsrc(dts + static_cast<size_t>(base) * D, bytes),
+                           make_rsrc(zs + static_cast<size_t>(base) * D, bytes)};
+        ts.load(r, L - 1 - base, D, c0, tid);
+    };
+    // This lane's value of tensor k for token tr of the stage held in LDS buffer buf.
+    const int lane_ch = wave * kRowsPerWave + row;
+    auto tok_val = [&](int buf, int k, int tr) {
+        const T *p = reinterpret_cast<const T *>(&sm.tok[buf][k][tr][0]);
+        return to_f32(p[lane_ch]);
+    };
+
+    // B / C columns of one block for this lane's state, from the LDS stage buffer.
+    struct Cols {
+        float4 b[kBlock / 4], c[kBlock / 4];
+    };
+    auto read_cols = [&](int buf, int bk, Cols &cl) {
+        const float *bcol = &sm.bc[buf][0][j][bk * kBlock];
+        const float *ccol = &sm.bc[buf][1][j][bk * kBlock];
+#pragma unroll
+        for (int g = 0; g < kBlock / 4; ++g) {
+            cl.b[g] = *reinterpret_cast<const float4 *>(bcol + 4 * g);
+            cl.c[g] = *reinterpret_cast<const float4 *>(ccol + 4 * g);
         }
     };
-    float xn, dtn, zn;
-    if (nblocks > 0) load_tok(t0, xn, dtn, zn);
 
-    float *pw = &sm.p[wave][row][0][0];
+    float *pw = &sm.p[wave][row * kRowPitch];  // this row's 16x16 product tile
+    // Epilogue state of the block whose readout is in flight.
+    float pu = 0.0f, pz = 0.0f;
+    int pblk = -1;  // its first token relative to t0 (-1: none)
+    float4 py[kBlock / 4];
 
-    for (size_t st = 0; st < nstages; ++st) {
-        const int buf = static_cast<int>(st & 1);
+    // Sum the transposed products of the in-flight block (already read into py), finish
+    // its outputs and store them.
+    auto finish = [&]() {
+        float y = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kBlock / 4; ++g) y += (py[g].x + py[g].y) + (py[g].z + py[g].w);
+        y = __builtin_fmaf(dsk, pu, y);
+        const float o = has_z ? y * silu(pz) : y;
+        const int ta = pblk + j;
+        if (ta < L && chan_ok) {
+            const int sb = (pblk / kStage) * kStage;
+            const Rsrc ro = make_rsrc(os + static_cast<size_t>(sb) * D, stage_bytes(sb));
+            buf_st(ro, tok_off(ta - sb), o, static_cast<T *>(nullptr));
+        }
+    };
+    auto read_products = [&]() {
+        const float *pr = pw + j * kPPitch;
+#pragma unroll
+        for (int g = 0; g < kBlock / 4; ++g) py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
+    };
+
+    Stager<Io, kStage> stg;
+    TokStager<Io, kStage> tst;
+    Cols cl, cln;
+    if (nstages > 0) {
+        stg.load(a, t0, t1, N, tid);
+        load_stage_tokens(0, tst);
+        stg.store(sm, 0, tid, N);
+        tst.store(sm, 0, tid);
+    }
+    __syncthreads();
+    if (nstages > 0) read_cols(0, 0, cl);
+
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
         const bool more = st + 1 < nstages;
-        if (more) stage_load<Io>(a, t0 + (st + 1) * kStage, t1, N, tid, sr);
+        if (more) {
+            stg.load(a, t0 + static_cast<size_t>(st + 1) * kStage, t1, N, tid);
+            load_stage_tokens(st + 1, tst);
+        }
+        const int sbase = st * kStage;
 
+#pragma unroll
         for (int bk = 0; bk < kStageBlocks; ++bk) {
-            const size_t blk = st * kStageBlocks + bk;
-            if (blk >= nblocks) break;  // uniform across the workgroup
-            const size_t tb = t0 + blk * kBlock;
-            const float xv = xn, dtv = dtn, zv = zn;
-            if (blk + 1 < nblocks) load_tok(tb + kBlock, xn, dtn, zn);
-            const bool act = tb + j < t1;
+            const int tb = sbase + bk * kBlock;  // first token of the block (relative to t0)
+            if (bk > 0 && tb >= L) break;        // uniform: the last stage may be short
+            const bool act = tb + j < L;
+            const int tr = bk * kBlock + j;  // this lane's token within the stage
+            const float xv = tok_val(buf, 0, tr), dtv = tok_val(buf, 1, tr), zv = has_z ? tok_val(buf, 2, tr) : 0.0f;
 
             // ---- front end for token tb + j: conv taps, SiLU, softplus
             float pre = __builtin_fmaf(w3, xv, cbias);
-            pre = __builtin_fmaf(w2, tap<1>(xv, xprev, j), pre);
-            pre = __builtin_fmaf(w1, tap<2>(xv, xprev, j), pre);
-            pre = __builtin_fmaf(w0, tap<3>(xv, xprev, j), pre);
+            pre = __builtin_fmaf(tap<1>(xv, xprev, j), w2, pre);
+            pre = __builtin_fmaf(tap<2>(xv, xprev, j), w1, pre);
+            pre = __builtin_fmaf(tap<3>(xv, xprev, j), w0, pre);
             const float u = silu(pre);
             float lg = softplus_log2(dtv + bias);
             lg = act ? lg : 0.0f;
             const float du = act ? (lg * kLn2) * u : 0.0f;
+            xprev = xv;
+
+            // ---- products of the previous block: read now, consumed after this recurrence
+            wave_order();
+            if (pblk >= 0) read_products();
+            wave_order();
+            // ---- B/C columns of the next block of this stage
+            if (bk + 1 < kStageBlocks && tb + kBlock < L) read_cols(buf, bk + 1, cln);
 
             // ---- 16 recurrence steps; lane j holds state n = j
-            const float *bcol = &sm.bc[buf][0][j][bk * kBlock];
-            const float *ccol = &sm.bc[buf][1][j][bk * kBlock];
             float p[kBlock];
 #pragma unroll
             for (int g = 0; g < kBlock / 4; ++g) {
-                const float4 bq = *reinterpret_cast<const float4 *>(bcol + 4 * g);
-                const float4 cq = *reinterpret_cast<const float4 *>(ccol + 4 * g);
-                const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-                const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+                const float bv[4] = {cl.b[g].x, cl.b[g].y, cl.b[g].z, cl.b[g].w};
+                const float cv[4] = {cl.c[g].x, cl.c[g].y, cl.c[g].z, cl.c[g].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 4 * g + e;
@@ -241,36 +415,35 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
                 }
             }
 
-            // ---- readout: transpose the 16x16 partial products of the row through LDS
+            // ---- publish this block's products (the tile was read above, in order)
+            wave_order();
 #pragma unroll
             for (int t = 0; t < kBlock; ++t) pw[t * kPPitch + j] = p[t];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const float *pr = pw + j * kPPitch;
-            float y = 0.0f;
-#pragma unroll
-            for (int g = 0; g < kBlock / 4; ++g) {
-                const float4 v = *reinterpret_cast<const float4 *>(pr + 4 * g);
-                y += (v.x + v.y) + (v.z + v.w);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            y = __builtin_fmaf(dsk, u, y);
-            const float o = a.z ? y * silu(zv) : y;
-            if (act && chan_ok) {
-                const size_t t = tb + j;
-                Io::st(a.out, t * D + cc, o);
-                if (a.conv_final != nullptr && t + 3 >= t1) Io::st(a.conv_final, cbase + (t + 3 - t1) * D, xv);
-            }
-            xprev = xv;
+            wave_order();
+
+            // ---- finish the previous block
+            if (pblk >= 0) finish();
+            pu = u;
+            pz = zv;
+            pblk = tb;
+            cl = cln;
         }
 
-        if (more) stage_store<Io>(sm, buf ^ 1, tid, sr);
+        if (more) {
+            stg.store(sm, buf ^ 1, tid, N);
+            tst.store(sm, buf ^ 1, tid);
+        }
         __syncthreads();
+        if (more) read_cols(buf ^ 1, 0, cl);
     }
 
+    // Finish the last block.
+    if (pblk >= 0) {
+        wave_order();
+        read_products();
+        wave_order();
+        finish();
+    }
     if (a.h_final != nullptr && chan_ok && state_ok) a.h_final[hidx] = h;
 }
 
@@ -278,10 +451,21 @@ inline void launch_rows_scan(const ScanArgs &a, samba_dtype io, hipStream_t stre
 {
     const int ncb = (a.D + rows::kChannels - 1) / rows::kChannels;
     const dim3 grid(ncb * a.nseq), block(256);
-    if (io == SAMBA_BF16)
-        rows_scan_kernel<IoBf16><<<grid, block, 0, stream>>>(a, ncb);
-    else
-        rows_scan_kernel<IoF32><<<grid, block, 0, stream>>>(a, ncb);
+    // Few workgroups (one wave per SIMD): long stages so the next stage's loads have a
+    // whole stage of compute to arrive.  Many workgroups: short stages, smaller LDS and
+    // register footprint for more waves per SIMD.
+    const bool few = static_cast<size_t>(ncb) * a.nseq <= 512;
+    if (io == SAMBA_BF16) {
+        if (few)
+            rows_scan_kernel<IoBf16, 128><<<grid, block, 0, stream>>>(a, ncb);
+        else
+            rows_scan_kernel<IoBf16, 64><<<grid, block, 0, stream>>>(a, ncb);
+    } else {
+        if (few)
+            rows_scan_kernel<IoF32, 128><<<grid, block, 0, stream>>>(a, ncb);
+        else
+            rows_scan_kernel<IoF32, 64><<<grid, block, 0, stream>>>(a, ncb);
+    }
 }
 
 }  // namespace samba

@@ -76,6 +76,14 @@ def test_short_sequences_and_small_state(L, N):
     check(*run_both(p, tk, h0, c0, gate, "f32"), "f32")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_unaligned_channel_count(io):
+    """d_inner = 100 is not a multiple of 8: the row kernel's 16-byte token rows do not
+    apply and the one-lane-per-channel kernel serves the call."""
+    p, tk, h0, c0, gate = make_case(250, 2, 70, 100, 16, io, with_state=True)
+    check(*run_both(p, tk, h0, c0, gate, io), io)
+
+
 def test_no_gate():
     p, tk, h0, c0, _ = make_case(300, 2, 150, 128, 16, "bf16")
     check(*run_both(p, tk, h0, c0, False, "bf16"), "bf16")
