@@ -331,12 +331,15 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         for (int g = 0; g < kBlock / 4; ++g) y += (py[g].x + py[g].y) + (py[g].z + py[g].w);
         y = __builtin_fmaf(dsk, pu, y);
         const float o = has_z ? y * silu(pz) : y;
+        // Unconditional store: tokens past the end and padding channels get an offset
+        // beyond the resource's extent, which the hardware drops.  (A store inside a
+        // divergent branch makes the compiler's vector-memory counter tracking give up and
+        // wait for every outstanding store at the next use of loaded data.)
         const int ta = pblk + j;
-        if (ta < L && chan_ok) {
-            const int sb = (pblk / kStage) * kStage;
-            const Rsrc ro = make_rsrc(os + static_cast<size_t>(sb) * D, stage_bytes(sb));
-            buf_st(ro, tok_off(ta - sb), o, static_cast<T *>(nullptr));
-        }
+        const int sb = (pblk / kStage) * kStage;
+        const Rsrc ro = make_rsrc(os + static_cast<size_t>(sb) * D, stage_bytes(sb));
+        const uint32_t boff = (ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
+        buf_st(ro, boff, o, static_cast<T *>(nullptr));
     };
     auto read_products = [&]() {
         const float *pr = pw + j * kPPitch;
@@ -355,6 +358,10 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     }
     __syncthreads();
     if (nstages > 0) read_cols(0, 0, cl);
+    // Nothing loaded before the loop may still be in flight when it starts: otherwise the
+    // compiler cannot tell those loads apart from the next stage's prefetch at the loop
+    // header and waits for all of them at the first use.
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
