@@ -22,6 +22,7 @@
 #include "scan_common.h"
 #include "scan_lane.h"
 #include "scan_rows.h"
+#include "scan_decode.h"
 
 
 namespace {
@@ -260,7 +261,10 @@ samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype i
     // read and written in place.
     samba::ScanArgs a = make_args(nseq, 1, nullptr, d_inner, d_state, x, dt, B, C, z, params, h, conv_state,
                                   out, h, conv_state);
-    samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    if (d_state == samba::kMaxState)
+        samba::launch_decode16(a, io, static_cast<hipStream_t>(stream));
+    else
+        samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 
