@@ -296,12 +296,8 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
                            make_rsrc(zs + static_cast<size_t>(base) * D, bytes)};
         ts.load(r, L - 1 - base, D, c0, tid);
     };
-    // This lane's value of tensor k for token tr of the stage held in LDS buffer buf.
+    // This lane's channel within the workgroup's 16 (its column in the token tiles).
     const int lane_ch = wave * kRowsPerWave + row;
-    auto tok_val = [&](int buf, int k, int tr) {
-        const T *p = reinterpret_cast<const T *>(&sm.tok[buf][k][tr][0]);
-        return to_f32(p[lane_ch]);
-    };
 
     // B / C columns of one block for this lane's state, from the LDS stage buffer.
     struct Cols {
@@ -320,25 +316,25 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     float *pw = &sm.p[wave][row * kRowPitch];  // this row's 16x16 product tile
     // Epilogue state of the block whose readout is in flight.
     float pu = 0.0f, pz = 0.0f;
-    int pblk = -1;  // its first token relative to t0 (-1: none)
+    int pblk = -kBlock;  // its first token relative to t0 (negative: none yet)
     float4 py[kBlock / 4];
 
     // Sum the transposed products of the in-flight block (already read into py), finish
-    // its outputs and store them.
+    // its outputs and store them.  The store is unconditional: tokens past the end,
+    // padding channels and the not-yet-existing block get an offset beyond the resource's
+    // extent, which the hardware drops.  (A store inside a divergent branch makes the
+    // compiler's vector-memory counter tracking give up and wait for every outstanding
+    // store at the next use of loaded data.)
     auto finish = [&]() {
-        float y = 0.0f;
+        float y = (py[0].x + py[0].y) + (py[0].z + py[0].w);
 #pragma unroll
-        for (int g = 0; g < kBlock / 4; ++g) y += (py[g].x + py[g].y) + (py[g].z + py[g].w);
+        for (int g = 1; g < kBlock / 4; ++g) y += (py[g].x + py[g].y) + (py[g].z + py[g].w);
         y = __builtin_fmaf(dsk, pu, y);
         const float o = has_z ? y * silu(pz) : y;
-        // Unconditional store: tokens past the end and padding channels get an offset
-        // beyond the resource's extent, which the hardware drops.  (A store inside a
-        // divergent branch makes the compiler's vector-memory counter tracking give up and
-        // wait for every outstanding store at the next use of loaded data.)
         const int ta = pblk + j;
-        const int sb = (pblk / kStage) * kStage;
+        const int sb = max(pblk, 0) / kStage * kStage;
         const Rsrc ro = make_rsrc(os + static_cast<size_t>(sb) * D, stage_bytes(sb));
-        const uint32_t boff = (ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
+        const uint32_t boff = (pblk >= 0 && ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
         buf_st(ro, boff, o, static_cast<T *>(nullptr));
     };
     auto read_products = [&]() {
@@ -346,10 +342,21 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 #pragma unroll
         for (int g = 0; g < kBlock / 4; ++g) py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
     };
+    // Raw token words of one block for this lane (read from the LDS tile one block ahead).
+    struct TokRaw {
+        T x, dt, z;
+    };
+    auto read_tok = [&](int buf, int bk, TokRaw &r) {
+        const int tr = bk * kBlock + j;
+        r.x = reinterpret_cast<const T *>(&sm.tok[buf][0][tr][0])[lane_ch];
+        r.dt = reinterpret_cast<const T *>(&sm.tok[buf][1][tr][0])[lane_ch];
+        r.z = reinterpret_cast<const T *>(&sm.tok[buf][2][tr][0])[lane_ch];
+    };
 
     Stager<Io, kStage> stg;
     TokStager<Io, kStage> tst;
     Cols cl, cln;
+    TokRaw tkr, tkn;
     if (nstages > 0) {
         stg.load(a, t0, t1, N, tid);
         load_stage_tokens(0, tst);
@@ -357,7 +364,10 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         tst.store(sm, 0, tid);
     }
     __syncthreads();
-    if (nstages > 0) read_cols(0, 0, cl);
+    if (nstages > 0) {
+        read_cols(0, 0, cl);
+        read_tok(0, 0, tkr);
+    }
     // Nothing loaded before the loop may still be in flight when it starts: otherwise the
     // compiler cannot tell those loads apart from the next stage's prefetch at the loop
     // header and waits for all of them at the first use.
@@ -372,13 +382,18 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         }
         const int sbase = st * kStage;
 
+        // Every block of the stage runs, also past the end of a short last stage: there
+        // Delta is forced to 0 (the state does not move) and the stores are dropped.
 #pragma unroll
         for (int bk = 0; bk < kStageBlocks; ++bk) {
             const int tb = sbase + bk * kBlock;  // first token of the block (relative to t0)
-            if (bk > 0 && tb >= L) break;        // uniform: the last stage may be short
             const bool act = tb + j < L;
-            const int tr = bk * kBlock + j;  // this lane's token within the stage
-            const float xv = tok_val(buf, 0, tr), dtv = tok_val(buf, 1, tr), zv = has_z ? tok_val(buf, 2, tr) : 0.0f;
+            const float xv = to_f32(tkr.x), dtv = to_f32(tkr.dt), zv = to_f32(tkr.z);
+            // next block's token words and B/C columns (same stage buffer)
+            if (bk + 1 < kStageBlocks) {
+                read_tok(buf, bk + 1, tkn);
+                read_cols(buf, bk + 1, cln);
+            }
 
             // ---- front end for token tb + j: conv taps, SiLU, softplus
             float pre = __builtin_fmaf(w3, xv, cbias);
@@ -393,10 +408,8 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 
             // ---- products of the previous block: read now, consumed after this recurrence
             wave_order();
-            if (pblk >= 0) read_products();
+            read_products();
             wave_order();
-            // ---- B/C columns of the next block of this stage
-            if (bk + 1 < kStageBlocks && tb + kBlock < L) read_cols(buf, bk + 1, cln);
 
             // ---- 16 recurrence steps; lane j holds state n = j
             float p[kBlock];
@@ -429,11 +442,14 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
             wave_order();
 
             // ---- finish the previous block
-            if (pblk >= 0) finish();
+            finish();
             pu = u;
             pz = zv;
             pblk = tb;
-            cl = cln;
+            if (bk + 1 < kStageBlocks) {
+                cl = cln;
+                tkr = tkn;
+            }
         }
 
         if (more) {
@@ -441,11 +457,14 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
             tst.store(sm, buf ^ 1, tid);
         }
         __syncthreads();
-        if (more) read_cols(buf ^ 1, 0, cl);
+        if (more) {
+            read_cols(buf ^ 1, 0, cl);
+            read_tok(buf ^ 1, 0, tkr);
+        }
     }
 
     // Finish the last block.
-    if (pblk >= 0) {
+    if (nstages > 0) {
         wave_order();
         read_products();
         wave_order();
