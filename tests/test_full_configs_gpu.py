@@ -1,0 +1,156 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The oracle is evaluated on a sample of channels (every channel's recurrence is
+independent of the others, so a channel subset of the oracle is exactly the oracle's
+value for those channels).  Samples include the first and last channels, channel-block
+boundaries of the row kernel (multiples of 16) and random channels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_samba_amd as ss
+from selective_state_space_samba_amd import synth
+from tests.helpers import TOL, rel_err, tf32
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+D, N = 4096, 16
+
+
+def sample_channels(seed, k_random=12):
+    fixed = [0, 1, 15, 16, 17, 255, 256, 1023, 2048, 2049, 4079, 4080, 4095]
+    rng = np.random.default_rng(seed)
+    rnd = rng.choice(np.setdiff1d(np.arange(D), fixed), size=k_random, replace=False)
+    return np.sort(np.concatenate([fixed, rnd])).astype(np.int64)
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def params_dev(p):
+    return [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+
+
+def check(name, g, r, io="bf16"):
+    e = rel_err(g, r)
+    print("  %s err %.3e (tol %.0e)" % (name, e, TOL[io]), flush=True)
+    assert e <= TOL[io], name
+
+
+def run_prefill_case(cfg_index, b, L):
+    seed = synth.seed_for(cfg_index)
+    print("case: config %d batch %d L %d" % (cfg_index, b, L), flush=True)
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (b, L), D, N, "bf16")
+    y, hf, cf = ss.prefill(bf16(tk.x), bf16(tk.dt), bf16(tk.B), bf16(tk.C), bf16(tk.z), *params_dev(p))
+    chans = sample_channels(seed)
+    ci = torch.from_numpy(chans).to(DEV)
+    yg = y.index_select(2, ci).float().cpu().numpy()
+    hg = hf.index_select(1, ci).cpu().numpy()
+    cg = cf.index_select(2, ci).float().cpu().numpy()
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b,
+                                chans=chans)
+    check("y", yg, yr)
+    check("h_final", hg, hr)
+    np.testing.assert_array_equal(cg, cr)
+    return y
+
+
+def test_training_length_prefill_4x4096():
+    run_prefill_case(1, 4, 4096)
+
+
+def test_long_prompt_prefill_131072():
+    y = run_prefill_case(2, 1, 131072)
+    assert torch.isfinite(y.float()).all()
+
+
+def test_long_prompt_is_bitwise_deterministic():
+    seed = synth.seed_for(2)
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (1, 131072), D, N, "bf16")
+    ins = [bf16(a) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    prm = params_dev(p)
+    y1, h1, c1 = ss.prefill(*ins, *prm)
+    y2, h2, c2 = ss.prefill(*ins, *prm)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2) and torch.equal(c1, c2)
+
+
+def test_packed_varlen_8_sequences():
+    seed = synth.seed_for(4)
+    lens = synth.varlen_lengths(seed)
+    cu = synth.cu_from_lengths(lens)
+    T = int(cu[-1])
+    print("case: varlen lengths", lens.tolist(), "total", T, flush=True)
+    assert T <= 131072 and lens.min() >= 1024 and lens.max() <= 32768
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (T,), D, N, "bf16")
+    y, hf, cf = ss.varlen(torch.from_numpy(cu).to(DEV), bf16(tk.x), bf16(tk.dt), bf16(tk.B), bf16(tk.C),
+                          bf16(tk.z), *params_dev(p), max_seqlen=int(lens.max()))
+    chans = sample_channels(seed)
+    ci = torch.from_numpy(chans).to(DEV)
+    yg = y.index_select(1, ci).float().cpu().numpy()
+    hg = hf.index_select(1, ci).cpu().numpy()
+    cg = cf.index_select(2, ci).float().cpu().numpy()
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.varlen(cu, tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b,
+                               chans=chans)
+    check("y", yg, yr)
+    check("h_final", hg, hr)
+    np.testing.assert_array_equal(cg, cr)
+
+
+def test_streaming_decode_256_sequences_65536_steps():
+    """256 resident sequences, 65536 single-token steps.  Step inputs cycle through a pool
+    of 256 pre-drawn steps.  The starting state of the sampled (sequence, channel) pairs is
+    the oracle's state after a random 1024-token prefill; other entries start from a random
+    state of the same shape (channels and sequences are independent).  The oracle runs the
+    sampled sequences as one long prefill over the same token stream (decode steps equal
+    a prefill exactly in the oracle)."""
+    seed = synth.seed_for(3)
+    S, steps, P, Lw = 256, 65536, 256, 1024
+    p = synth.make_params(seed, D, N)
+    seqs = np.array([0, 1, 77, 128, 200, 255])
+    chans = sample_channels(seed, k_random=6)
+    # starting state
+    h0, conv0 = synth.make_state(seed, S, D, N, "bf16", scale=0.1, tag="bg")
+    warm = synth.make_tokens(seed, (len(seqs), Lw), D, N, "bf16", tag="warm")
+    _, hw, cw = oracle.prefill(warm.x, warm.dt, warm.B, warm.C, warm.z, p.A, p.Dskip, p.dt_bias, p.conv_w,
+                               p.conv_b, chans=chans)
+    for i, s in enumerate(seqs):
+        h0[s][chans] = hw[i].astype(np.float32)
+        conv0[s][:, chans] = cw[i].astype(np.float32)
+    pool = synth.make_tokens(seed, (P, S), D, N, "bf16", tag="pool")
+    # GPU: 65536 decode steps, gathering the sampled outputs on the device
+    h = tf32(h0, DEV)
+    cs = bf16(conv0)
+    px, pdt, pz, pB, pC = (bf16(a) for a in (pool.x, pool.dt, pool.z, pool.B, pool.C))
+    prm = params_dev(p)
+    si = torch.from_numpy(seqs).to(DEV)
+    ci = torch.from_numpy(chans).to(DEV)
+    y = torch.empty((S, D), dtype=torch.bfloat16, device=DEV)
+    ys = torch.empty((steps, len(seqs), len(chans)), dtype=torch.bfloat16, device=DEV)
+    print("case: decode S=%d steps=%d" % (S, steps), flush=True)
+    for k in range(steps):
+        q = k % P
+        ss.decode(px[q], pdt[q], pB[q], pC[q], pz[q], *prm, h, cs, out=y)
+        ys[k] = y.index_select(0, si).index_select(1, ci)
+    hg = h.index_select(0, si).index_select(1, ci).cpu().numpy()
+    cg = cs.index_select(0, si).index_select(2, ci).float().cpu().numpy()
+    yg = ys.float().cpu().numpy()
+    torch.cuda.synchronize()
+    # oracle: each sampled sequence as one prefill over its step stream
+    idx = np.arange(steps) % P
+    pc = [a[chans] for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    for i, s in enumerate(seqs):
+        stream = lambda a: a[:, s][:, chans][idx][None]     # [1, steps, nch]
+        bc = lambda a: a[:, s][idx][None]                   # [1, steps, N]
+        yr, hr, cr = oracle.prefill(stream(pool.x), stream(pool.dt), bc(pool.B), bc(pool.C), stream(pool.z),
+                                    *pc, h0=h0[s:s + 1][:, chans], conv0=conv0[s:s + 1][:, :, chans])
+        check("seq %d y (all steps)" % s, yg[:, i, :], yr[0])
+        check("seq %d h" % s, hg[i], hr[0])
+        np.testing.assert_array_equal(cg[i], cr[0])
