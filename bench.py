@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=65536)
     ap.add_argument("--cpu-channels", type=int, default=2048)
     ap.add_argument("--prefill-only", action="store_true", help="time only the long-prompt prefill (profiling)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the prefill and a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -200,6 +202,45 @@ def bench_extra(dev, steps=5, warmup=2):
     return res
 
 
+def traffic_probe(dev, steps=3):
+    """A plain device-to-device copy of exactly 2^30 bytes (bf16), the reference that scales
+    the FETCH_SIZE / WRITE_SIZE counters into bytes."""
+    import torch
+    src = torch.ones((1 << 29,), dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def kernel_source_hash():
+    import hashlib
+    from selective_state_space_samba_amd import build as b
+    h = hashlib.sha256()
+    for f in b.sources():
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(name):
+    """Bytes per launch measured by rocprofv3 counters, recorded in profiles/<name> together
+    with the hash of the kernel sources they were taken on; None when the sources changed."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("traffic_") or line.startswith("source_hash"):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(host, nch):
     import oracle
     p, tk = host
@@ -225,6 +266,10 @@ def main():
     dev = torch.device("cuda:0")
 
     pre = bench_prefill(args, dev)
+    if args.traffic_probe:
+        traffic_probe(dev)
+        print(json.dumps({"traffic_probe": "done", "source_hash": kernel_source_hash()}), flush=True)
+        return
     per = np.array(pre["per"])
     t_step = float(np.mean(per))
     tokens = pre["tokens"]
@@ -250,7 +295,7 @@ def main():
                    "global_batch": 1, "seq_len": 131072, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "alu", "achieved": round(achieved_alu, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU-slots/s", "frac": round(achieved_alu / VALU_PEAK_TSLOTS, 4),
-                     "traffic": None,
+                     "traffic": committed_traffic("rows_scan_prompt128k_traffic.md"),
                      "work_per_launch": "%d tokens x %d channels x %d slots" % (tokens, D_INNER, SLOTS_PER_TC)},
         "roofline_hbm": {"achieved": round(achieved_hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_hbm / HBM_PEAK_GBS, 4), "bytes_per_launch": hbm_bytes},
