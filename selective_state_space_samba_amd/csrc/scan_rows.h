@@ -79,10 +79,11 @@ constexpr int tok_pitch_bytes() { return kChannels * static_cast<int>(sizeof(T))
 
 template <class T, int kStage>
 struct Smem {
-    static constexpr int kBCPitch = kStage + 4;  // LDS pitch of one state's column (floats)
+    static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
     static constexpr int kTokPitch = tok_pitch_bytes<T>();
-    float bc[2][2][kMaxState][kBCPitch];         // [buffer][B|C][state][token]
-    float p[kWaves][kRowsPerWave * kRowPitch];   // [wave][row][token][state] (padded)
+    float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
+    float crow[2][kStage][kPPitch];              // [buffer][token][state]: C rows
+    float p[kWaves][kRowsPerWave * kRowPitch];   // [wave][row][token][state]: states h_t (padded)
     alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
 };
 
@@ -147,8 +148,17 @@ struct Stager {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) f[k] = v[k];
         }
+        if (which == 0) {
+            // B: transposed, one column per state (read by the lane that owns the state)
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) sm.bc[buf][which][n0 + k][tt] = f[k];
+            for (int k = 0; k < kPer; ++k) sm.bcol[buf][n0 + k][tt] = f[k];
+        } else {
+            // C: token rows (read by the lane that finishes the token's readout)
+#pragma unroll
+            for (int k = 0; k < kPer / 4; ++k)
+                *reinterpret_cast<float4 *>(&sm.crow[buf][tt][n0 + 4 * k]) =
+                    make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+        }
     }
 };
 
@@ -299,25 +309,21 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     // This lane's channel within the workgroup's 16 (its column in the token tiles).
     const int lane_ch = wave * kRowsPerWave + row;
 
-    // B / C columns of one block for this lane's state, from the LDS stage buffer.
+    // B column of one block for this lane's state, from the LDS stage buffer.
     struct Cols {
-        float4 b[kBlock / 4], c[kBlock / 4];
+        float4 b[kBlock / 4];
     };
     auto read_cols = [&](int buf, int bk, Cols &cl) {
-        const float *bcol = &sm.bc[buf][0][j][bk * kBlock];
-        const float *ccol = &sm.bc[buf][1][j][bk * kBlock];
+        const float *bcol = &sm.bcol[buf][j][bk * kBlock];
 #pragma unroll
-        for (int g = 0; g < kBlock / 4; ++g) {
-            cl.b[g] = *reinterpret_cast<const float4 *>(bcol + 4 * g);
-            cl.c[g] = *reinterpret_cast<const float4 *>(ccol + 4 * g);
-        }
+        for (int g = 0; g < kBlock / 4; ++g) cl.b[g] = *reinterpret_cast<const float4 *>(bcol + 4 * g);
     };
 
-    float *pw = &sm.p[wave][row * kRowPitch];  // this row's 16x16 product tile
+    float *pw = &sm.p[wave][row * kRowPitch];  // this row's 16x16 tile of states h_t[n]
     // Epilogue state of the block whose readout is in flight.
     float pu = 0.0f, pz = 0.0f;
     int pblk = -kBlock;  // its first token relative to t0 (negative: none yet)
-    float4 py[kBlock / 4];
+    float4 py[kBlock / 4], pc[kBlock / 4];  // its token's 16 states and C row (lane j: token j)
 
     // Sum the transposed products of the in-flight block (already read into py), finish
     // its outputs and store them.  The store is unconditional: tokens past the end,
@@ -326,9 +332,16 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     // compiler's vector-memory counter tracking give up and wait for every outstanding
     // store at the next use of loaded data.)
     auto finish = [&]() {
-        float y = (py[0].x + py[0].y) + (py[0].z + py[0].w);
+        // y = sum_n C_t[n] h_t[n] + D u_t  (four independent partial sums)
+        float ya = pc[0].x * py[0].x, yb = pc[0].y * py[0].y, yc = pc[0].z * py[0].z, yd = pc[0].w * py[0].w;
 #pragma unroll
-        for (int g = 1; g < kBlock / 4; ++g) y += (py[g].x + py[g].y) + (py[g].z + py[g].w);
+        for (int g = 1; g < kBlock / 4; ++g) {
+            ya = __builtin_fmaf(pc[g].x, py[g].x, ya);
+            yb = __builtin_fmaf(pc[g].y, py[g].y, yb);
+            yc = __builtin_fmaf(pc[g].z, py[g].z, yc);
+            yd = __builtin_fmaf(pc[g].w, py[g].w, yd);
+        }
+        float y = (ya + yb) + (yc + yd);
         y = __builtin_fmaf(dsk, pu, y);
         const float o = has_z ? y * silu(pz) : y;
         const int ta = pblk + j;
@@ -337,10 +350,17 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         const uint32_t boff = (pblk >= 0 && ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
         buf_st(ro, boff, o, static_cast<T *>(nullptr));
     };
+    // The in-flight block's states for this lane's token (transposed through the tile) and
+    // its C row (from the stage buffer that held the block).
     auto read_products = [&]() {
         const float *pr = pw + j * kPPitch;
+        const int cb_ = (max(pblk, 0) / kStage) & 1;
+        const float *cr = &sm.crow[cb_][(max(pblk, 0) % kStage) + j][0];
 #pragma unroll
-        for (int g = 0; g < kBlock / 4; ++g) py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
+        for (int g = 0; g < kBlock / 4; ++g) {
+            py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
+            pc[g] = *reinterpret_cast<const float4 *>(cr + 4 * g);
+        }
     };
     // Raw token words of one block for this lane (read from the LDS tile one block ahead).
     struct TokRaw {
@@ -353,10 +373,31 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         r.z = reinterpret_cast<const T *>(&sm.tok[buf][2][tr][0])[lane_ch];
     };
 
+    // Per-token front end of one block (lane j: token tb + j): causal conv with the taps
+    // x_{t-1..t-3} from neighbouring lanes (row rotations), SiLU, softplus(dt + b) in log2
+    // units, Delta * u.  Tokens past the end get Delta = 0 (the state does not move).
+    struct Front {
+        float x, u, zv, lg, du;
+    };
+    auto front = [&](const TokRaw &r, float xp, int tb, Front &f) {
+        const bool act = tb + j < L;
+        f.x = to_f32(r.x);
+        f.zv = to_f32(r.z);
+        float pre = __builtin_fmaf(w3, f.x, cbias);
+        pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
+        pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
+        pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
+        f.u = silu(pre);
+        const float lg = softplus_log2(to_f32(r.dt) + bias);
+        f.lg = act ? lg : 0.0f;
+        f.du = act ? (lg * kLn2) * f.u : 0.0f;
+    };
+
     Stager<Io, kStage> stg;
     TokStager<Io, kStage> tst;
     Cols cl, cln;
-    TokRaw tkr, tkn;
+    TokRaw tk1, tk2;  // token words of the next block and of the one after it
+    Front fe, fen;    // front end of the current block and of the next one
     if (nstages > 0) {
         stg.load(a, t0, t1, N, tid);
         load_stage_tokens(0, tst);
@@ -364,10 +405,6 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         tst.store(sm, 0, tid);
     }
     __syncthreads();
-    if (nstages > 0) {
-        read_cols(0, 0, cl);
-        read_tok(0, 0, tkr);
-    }
     // Nothing loaded before the loop may still be in flight when it starts: otherwise the
     // compiler cannot tell those loads apart from the next stage's prefetch at the loop
     // header and waits for all of them at the first use.
@@ -376,47 +413,43 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
         const bool more = st + 1 < nstages;
+        const int sbase = st * kStage;
+        // Stage prologue: B/C columns of block 0, token words of blocks 0 and 1, and the
+        // front end of block 0 (the one front end per stage not overlapped with a recurrence).
+        {
+            TokRaw tk0;
+            read_cols(buf, 0, cl);
+            read_tok(buf, 0, tk0);
+            read_tok(buf, 1, tk1);
+            front(tk0, xprev, sbase, fe);
+        }
         if (more) {
             stg.load(a, t0 + static_cast<size_t>(st + 1) * kStage, t1, N, tid);
             load_stage_tokens(st + 1, tst);
         }
-        const int sbase = st * kStage;
 
         // Every block of the stage runs, also past the end of a short last stage: there
         // Delta is forced to 0 (the state does not move) and the stores are dropped.
+        // Within one block: block bk's recurrence, block bk+1's front end and block
+        // bk-1's readout are independent, so the scheduler can interleave them.
 #pragma unroll
         for (int bk = 0; bk < kStageBlocks; ++bk) {
             const int tb = sbase + bk * kBlock;  // first token of the block (relative to t0)
-            const bool act = tb + j < L;
-            const float xv = to_f32(tkr.x), dtv = to_f32(tkr.dt), zv = to_f32(tkr.z);
-            // next block's token words and B/C columns (same stage buffer)
-            if (bk + 1 < kStageBlocks) {
-                read_tok(buf, bk + 1, tkn);
-                read_cols(buf, bk + 1, cln);
-            }
 
-            // ---- front end for token tb + j: conv taps, SiLU, softplus
-            float pre = __builtin_fmaf(w3, xv, cbias);
-            pre = __builtin_fmaf(tap<1>(xv, xprev, j), w2, pre);
-            pre = __builtin_fmaf(tap<2>(xv, xprev, j), w1, pre);
-            pre = __builtin_fmaf(tap<3>(xv, xprev, j), w0, pre);
-            const float u = silu(pre);
-            float lg = softplus_log2(dtv + bias);
-            lg = act ? lg : 0.0f;
-            const float du = act ? (lg * kLn2) * u : 0.0f;
-            xprev = xv;
-
-            // ---- products of the previous block: read now, consumed after this recurrence
+            // ---- states and C row of the previous block: read now, consumed below
             wave_order();
             read_products();
             wave_order();
+            // ---- LDS reads for the coming blocks (same stage buffer)
+            if (bk + 1 < kStageBlocks) read_cols(buf, bk + 1, cln);
+            if (bk + 2 < kStageBlocks) read_tok(buf, bk + 2, tk2);
 
             // ---- 16 recurrence steps; lane j holds state n = j
+            const float lg = fe.lg, du = fe.du;
             float p[kBlock];
 #pragma unroll
             for (int g = 0; g < kBlock / 4; ++g) {
                 const float bv[4] = {cl.b[g].x, cl.b[g].y, cl.b[g].z, cl.b[g].w};
-                const float cv[4] = {cl.c[g].x, cl.c[g].y, cl.c[g].z, cl.c[g].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 4 * g + e;
@@ -431,24 +464,28 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
                     }
                     const float ab = hw_exp2(lt * An);
                     h = __builtin_fmaf(ab, h, dut * bv[e]);
-                    p[t] = cv[e] * h;
+                    p[t] = h;
                 }
             }
+            // ---- front end of the next block (its token words were read a block ago)
+            if (bk + 1 < kStageBlocks) front(tk1, fe.x, tb + kBlock, fen);
+            // ---- finish the previous block
+            finish();
 
-            // ---- publish this block's products (the tile was read above, in order)
+            // ---- publish this block's states (the tile was read above, in order)
             wave_order();
 #pragma unroll
             for (int t = 0; t < kBlock; ++t) pw[t * kPPitch + j] = p[t];
             wave_order();
 
-            // ---- finish the previous block
-            finish();
-            pu = u;
-            pz = zv;
+            pu = fe.u;
+            pz = fe.zv;
             pblk = tb;
+            xprev = fe.x;
             if (bk + 1 < kStageBlocks) {
+                fe = fen;
                 cl = cln;
-                tkr = tkn;
+                tk1 = tk2;
             }
         }
 
@@ -457,10 +494,6 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
             tst.store(sm, buf ^ 1, tid);
         }
         __syncthreads();
-        if (more) {
-            read_cols(buf ^ 1, 0, cl);
-            read_tok(buf ^ 1, 0, tkr);
-        }
     }
 
     // Finish the last block.
