@@ -165,51 +165,56 @@ struct Stager {
 // Token tiles of one stage: 3 tensors x kStage tokens x one 16-channel row (32 bytes for
 // bf16, 64 for fp32), moved as 16-byte buffer loads (16-channel rows are contiguous in
 // the token-major layout) and kept raw in registers until written to LDS at the end of
-// the current stage.  Tokens past the end of the sequence re-load the last token.
+// the current stage.  Tokens past the end of the sequence re-load the last token.  Each
+// tensor's resource is chosen at compile time (a resource picked from an array by a
+// runtime index is not provably uniform and costs a waterfall loop per load).
 template <class Io, int kStage>
 struct TokStager {
     using T = typename Io::T;
     static constexpr int kRowBytes = kChannels * static_cast<int>(sizeof(T));
     static constexpr int kVecPerRow = kRowBytes / 16;
-    static constexpr int kPerTensor = kStage * kVecPerRow;
-    static constexpr int kVecs = 3 * kPerTensor;
-    static constexpr int kPerThread = (kVecs + 255) / 256;
-    uint4 v[kPerThread];
+    static constexpr int kPerTensor = kStage * kVecPerRow;  // 16-byte vectors per tensor
+    static constexpr int kPerThread = (kPerTensor + 255) / 256;
+    static_assert(kPerTensor % 64 == 0, "whole waves per vector slot");
+    uint4 v[3][kPerThread];
 
-    // rsrc[k]: resource of tensor k for this stage; c0: first channel of the workgroup.
-    __device__ inline void load(const Rsrc (&rsrc)[3], int last, int D, int c0, int tid)
+    __device__ inline void load_one(Rsrc r, int k, int last, int D, int c0, int tid)
     {
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
             const int idx = i * 256 + tid;
-            if (kVecs % 256 == 0 || idx < kVecs) {
-                // the tensor index is uniform across a wave (256 % 64 == 0, kPerTensor % 64 == 0)
-                const int tensor = __builtin_amdgcn_readfirstlane(idx / kPerTensor);
-                const int rem = idx - tensor * kPerTensor;
-                const int tok = min(rem / kVecPerRow, last);
-                const int part = rem % kVecPerRow;
+            if (kPerTensor % 256 == 0 || idx < kPerTensor) {  // uniform across each wave
+                const int tok = min(idx / kVecPerRow, last);
+                const int part = idx % kVecPerRow;
                 const uint32_t boff = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(D) + static_cast<uint32_t>(c0)) *
                                           static_cast<uint32_t>(sizeof(T)) +
                                       static_cast<uint32_t>(part * 16);
-                const Rsrc r = tensor == 0 ? rsrc[0] : (tensor == 1 ? rsrc[1] : rsrc[2]);
-                v[i] = buf_ld128(r, boff);
+                v[k][i] = buf_ld128(r, boff);
             }
         }
+    }
+
+    __device__ inline void load(Rsrc rx, Rsrc rd, Rsrc rz, int last, int D, int c0, int tid)
+    {
+        load_one(rx, 0, last, D, c0, tid);
+        load_one(rd, 1, last, D, c0, tid);
+        load_one(rz, 2, last, D, c0, tid);
     }
 
     __device__ inline void store(Smem<T, kStage> &sm, int buf, int tid) const
     {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int idx = i * 256 + tid;
-            if (kVecs % 256 == 0 || idx < kVecs) {
-                const int tensor = idx / kPerTensor;
-                const int rem = idx - tensor * kPerTensor;
-                const int tok = rem / kVecPerRow;
-                const int part = rem % kVecPerRow;
-                uint2 *d = reinterpret_cast<uint2 *>(&sm.tok[buf][tensor][tok][part * 16]);
-                d[0] = make_uint2(v[i].x, v[i].y);
-                d[1] = make_uint2(v[i].z, v[i].w);
+        for (int k = 0; k < 3; ++k) {
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) {
+                const int idx = i * 256 + tid;
+                if (kPerTensor % 256 == 0 || idx < kPerTensor) {
+                    const int tok = idx / kVecPerRow;
+                    const int part = idx % kVecPerRow;
+                    uint2 *d = reinterpret_cast<uint2 *>(&sm.tok[buf][k][tok][part * 16]);
+                    d[0] = make_uint2(v[k][i].x, v[k][i].y);
+                    d[1] = make_uint2(v[k][i].z, v[k][i].w);
+                }
             }
         }
     }
@@ -301,10 +306,8 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     auto load_stage_tokens = [&](int st, TokStager<Io, kStage> &ts) {
         const int base = st * kStage;
         const uint32_t bytes = stage_bytes(base);
-        const Rsrc r[3] = {make_rsrc(xs + static_cast<size_t>(base) * D, bytes),
-                           make_rsrc(dts + static_cast<size_t>(base) * D, bytes),
-                           make_rsrc(zs + static_cast<size_t>(base) * D, bytes)};
-        ts.load(r, L - 1 - base, D, c0, tid);
+        ts.load(make_rsrc(xs + static_cast<size_t>(base) * D, bytes), make_rsrc(dts + static_cast<size_t>(base) * D, bytes),
+                make_rsrc(zs + static_cast<size_t>(base) * D, bytes), L - 1 - base, D, c0, tid);
     };
     // This lane's channel within the workgroup's 16 (its column in the token tiles).
     const int lane_ch = wave * kRowsPerWave + row;
@@ -444,9 +447,11 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
             if (bk + 1 < kStageBlocks) read_cols(buf, bk + 1, cln);
             if (bk + 2 < kStageBlocks) read_tok(buf, bk + 2, tk2);
 
-            // ---- 16 recurrence steps; lane j holds state n = j
+            // ---- 16 recurrence steps; lane j holds state n = j.  First the 16 decay
+            // factors exp(Delta_t A_n) and inputs Delta_t u_t B_t[n] (independent of the
+            // state: 16 parallel chains), then the state chain itself (16 dependent FMAs).
             const float lg = fe.lg, du = fe.du;
-            float p[kBlock];
+            float ab[kBlock], bu[kBlock], p[kBlock];
 #pragma unroll
             for (int g = 0; g < kBlock / 4; ++g) {
                 const float bv[4] = {cl.b[g].x, cl.b[g].y, cl.b[g].z, cl.b[g].w};
@@ -462,10 +467,14 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
                         SAMBA_BCAST(12) SAMBA_BCAST(13) SAMBA_BCAST(14) SAMBA_BCAST(15)
 #undef SAMBA_BCAST
                     }
-                    const float ab = hw_exp2(lt * An);
-                    h = __builtin_fmaf(ab, h, dut * bv[e]);
-                    p[t] = h;
+                    ab[t] = hw_exp2(lt * An);
+                    bu[t] = dut * bv[e];
                 }
+            }
+#pragma unroll
+            for (int t = 0; t < kBlock; ++t) {
+                h = __builtin_fmaf(ab[t], h, bu[t]);
+                p[t] = h;
             }
             // ---- front end of the next block (its token words were read a block ago)
             if (bk + 1 < kStageBlocks) front(tk1, fe.x, tb + kBlock, fen);
