@@ -295,7 +295,7 @@ def main():
                    "global_batch": 1, "seq_len": 131072, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "alu", "achieved": round(achieved_alu, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU-slots/s", "frac": round(achieved_alu / VALU_PEAK_TSLOTS, 4),
-                     "traffic": committed_traffic("rows_scan_prompt128k_traffic.md"),
+                     "traffic": committed_traffic("rows_split_prompt128k_traffic.md"),
                      "work_per_launch": "%d tokens x %d channels x %d slots" % (tokens, D_INNER, SLOTS_PER_TC)},
         "roofline_hbm": {"achieved": round(achieved_hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_hbm / HBM_PEAK_GBS, 4), "bytes_per_launch": hbm_bytes},

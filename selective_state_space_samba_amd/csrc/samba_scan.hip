@@ -21,7 +21,7 @@
 #include "../../include/samba_scan.h"
 #include "scan_common.h"
 #include "scan_lane.h"
-#include "scan_rows.h"
+#include "scan_split.h"
 #include "scan_decode.h"
 
 
@@ -43,23 +43,42 @@ samba_status fail(samba_status st, const char *fmt, ...)
 
 // Kernel choice for prefill / varlen.  The lane kernel (one lane per channel, 16 states
 // in registers) is the cheapest per token when sequences x channels alone give at least
-// four waves per SIMD; otherwise the row kernel (16 lanes per channel) supplies the
-// parallelism.  SAMBA_SCAN_PATH=lane|rows forces one of them (used by the tests to run
-// both kernels on every shape); the lane kernel is used whenever the row kernel's
-// alignment requirement is not met.
-bool use_rows(int nseq, int d_inner, samba_dtype io)
+// four waves per SIMD; otherwise the row kernels (16 lanes per channel) supply the
+// parallelism: the two-role row kernel while the grid has at most one workgroup per CU,
+// the single-role one (two workgroups per CU) beyond that.  SAMBA_SCAN_PATH=lane|single|
+// split forces one of them (the tests run every kernel on every shape); the lane kernel is
+// used whenever the row kernels' alignment requirement is not met.
+enum class ScanPath { kLane, kSingle, kSplit };
+
+ScanPath scan_path(int nseq, int d_inner, samba_dtype io)
 {
-    // The row kernel moves 16-channel token rows as 16-byte vectors: every row must start
+    // The row kernels move 16-channel token rows as 16-byte vectors: every row must start
     // 16-byte aligned, i.e. d_inner * sizeof(element) must be a multiple of 16.
     const int elem = io == SAMBA_BF16 ? 2 : 4;
-    if ((d_inner * elem) % 16 != 0) return false;
+    if ((d_inner * elem) % 16 != 0) return ScanPath::kLane;
+    const size_t row_grid = static_cast<size_t>(nseq) * static_cast<size_t>((d_inner + samba::rows::kChannels - 1) /
+                                                                              samba::rows::kChannels);
+    const ScanPath rows = row_grid <= static_cast<size_t>(samba::split::kMaxSplitGrid) ? ScanPath::kSplit
+                                                                                       : ScanPath::kSingle;
     const char *e = getenv("SAMBA_SCAN_PATH");
     if (e != nullptr && e[0] != '\0') {
-        if (strcmp(e, "rows") == 0) return true;
-        if (strcmp(e, "lane") == 0) return false;
+        if (strcmp(e, "lane") == 0) return ScanPath::kLane;
+        if (strcmp(e, "single") == 0) return ScanPath::kSingle;
+        if (strcmp(e, "split") == 0) return ScanPath::kSplit;
+        if (strcmp(e, "rows") == 0) return rows;
     }
     constexpr size_t kLaneThreshold = 256ull * 4 * 64 * 4;  // lanes for 4 waves on each SIMD
-    return static_cast<size_t>(nseq) * static_cast<size_t>(d_inner) < kLaneThreshold;
+    return static_cast<size_t>(nseq) * static_cast<size_t>(d_inner) < kLaneThreshold ? rows : ScanPath::kLane;
+}
+
+void launch_scan(const samba::ScanArgs &a, samba_dtype io, void *stream)
+{
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (scan_path(a.nseq, a.D, io)) {
+    case ScanPath::kLane: samba::launch_lane_scan(a, io, s); break;
+    case ScanPath::kSingle: samba::launch_rows_single(a, io, s); break;
+    case ScanPath::kSplit: samba::launch_rows_split(a, io, s); break;
+    }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -184,10 +203,7 @@ samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state,
     OPTIONAL_PTR(conv_final, "conv_final");
     samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
-    if (use_rows(batch, d_inner, io))
-        samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
-    else
-        samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    launch_scan(a, io, stream);
     return launched(fn);
 }
 
@@ -229,10 +245,7 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
     samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.total = total_tokens;
-    if (use_rows(nseq, d_inner, io))
-        samba::launch_rows_scan(a, io, static_cast<hipStream_t>(stream));
-    else
-        samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    launch_scan(a, io, stream);
     return launched(fn);
 }
 

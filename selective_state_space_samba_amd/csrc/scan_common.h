@@ -78,10 +78,17 @@ struct IoBf16 {
 using Rsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer descriptor flags
 
+// base and bytes must be the same in every lane of the wave.  They are read from the
+// first active lane: a value the compiler happens to compute in vector registers would
+// otherwise make it wrap every access in a loop over the distinct values.
 __device__ inline Rsrc make_rsrc(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), kRsrcWord3);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    void *ub = reinterpret_cast<void *>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
+                                             static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kRsrcWord3);
 }
 __device__ inline void buf_ld(Rsrc r, uint32_t boff, float &v)
 {

@@ -1,29 +1,32 @@
-// scan_rows.h -- prefill with one 16-lane DPP row per channel (one lane per state).
+// scan_rows.h -- prefill with one 16-lane DPP row per channel (one lane per state):
+// the pieces shared by the row kernels and the single-role row kernel.
 //
 // The recurrence of page 1 section 3.4 ("The State Space Model Update (S6)") is
 // independent across channels and, within a channel, across the d_state = 16 state
-// components; only the readout y_t = sum_n C_t[n] h_t[n] couples the states.  This
-// kernel therefore gives every channel a row of 16 lanes (lane n owns state n) and walks
+// components; only the readout y_t = sum_n C_t[n] h_t[n] couples the states.  The row
+// kernels therefore give every channel a row of 16 lanes (lane n owns state n) and walk
 // the sequence in time, so a batch-1 prompt of d_inner = 4096 channels still yields
 // 65536 lanes with no cross-workgroup carry and no recomputation.
 //
-// Work is organised in blocks of 16 tokens (one per lane of a row) and stages of
-// kStage tokens:
+// In the single-role kernel below every wave does all the work of its 4 channels; it is
+// the row kernel for grids of more than one workgroup per CU, where two workgroups share
+// each CU (scan_split.h holds the two-role kernel for smaller grids).  Work is organised
+// in blocks of 16 tokens (one per lane of a row) and stages of kStage tokens:
 //  * per stage, the workgroup stages B and C (shared by its 16 channels) into LDS as
-//    float32, transposed to [state][token], while each lane prefetches into registers
-//    the x / dt / z words of its tokens of the next stage (buffer loads bounded by the
-//    stage's extent);
+//    float32 (B transposed to [state][token], C as token rows) and the x / dt / z rows
+//    of its 16 channels (16-byte buffer loads bounded by the stage's extent), with the
+//    loads of the next stage issued at the start of the current one;
 //  * per block, lane j runs the per-token front end for token t0+j: causal conv with the
 //    taps x_{t-1..t-3} fetched from neighbouring lanes by DPP row rotations, SiLU,
 //    softplus(dt + b); then all 16 lanes step their state through the 16 tokens,
 //    receiving Delta and Delta*u of token t from lane t by DPP row broadcast fused into
 //    the multiply;
-//  * the 16 partial products C_t[n] h_t[n] of every lane are transposed through LDS so
-//    that lane j sums the readout of token t0+j, adds D*u, applies the SiLU(z) gate and
+//  * the 16x16 tile of states h_t[n] is transposed through LDS so that lane j sums the
+//    readout of token t0+j against its C row, adds D*u, applies the SiLU(z) gate and
 //    stores the output.
-// The LDS traffic is software-pipelined: the B/C columns of block k+1 are read while
-// block k computes, and the transposed products of block k-1 are read before block k's
-// recurrence and consumed after it.
+// The LDS traffic is software-pipelined: the B columns of block k+1 are read while block
+// k computes, and the states of block k-1 are read before block k's recurrence and
+// consumed after it.
 #pragma once
 
 #include "scan_common.h"
@@ -40,6 +43,7 @@ constexpr int kPPitch = kBlock + 4;       // LDS pitch of one token's 16 partial
 // LDS pitch of one row's 16x16 product tile: 16*20 + 16 floats puts the 4 rows of a
 // wave 16 banks apart, so a wave-wide store of one token's products does not conflict.
 constexpr int kRowPitch = kBlock * kPPitch + 16;
+constexpr int kStagerThreads = 256;       // threads that move one stage (B/C or token words)
 
 // DPP controls (gfx9 encoding).
 constexpr int kRowRor = 0x120;      // row_ror:k = kRowRor + k  (k = 1..15)
@@ -71,6 +75,19 @@ __device__ inline void wave_order()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Values loaded from LDS one step ahead pass through an empty asm statement after the
+// step's barrier: the compiler then cannot start the next step's arithmetic on them inside
+// the current step, right after the loads, where it would wait for their latency.
+__device__ inline void hold(float &v) { asm volatile("" : "+v"(v)); }
+__device__ inline void hold(uint16_t &v) { asm volatile("" : "+v"(v)); }
+__device__ inline void hold(float4 &v)
+{
+    hold(v.x);
+    hold(v.y);
+    hold(v.z);
+    hold(v.w);
+}
+
 // Token tiles hold, per stage, x / dt / z for the workgroup's 16 channels: one row of
 // 16 I/O words per token, padded by 8 bytes so that the 16 tokens a wave reads at once
 // (one per lane of a row) fall in distinct banks.
@@ -87,32 +104,34 @@ struct Smem {
     alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
 };
 
-// One B/C stage is 2 tensors x kStage tokens x 16 states.  The 256 threads cover the
-// 2*kStage (tensor, token) pairs with kParts threads per pair, each holding kPer states.
-// The raw words stay in registers while the current stage is computed and are converted
-// to float32 when written to LDS.  Tokens past the end of the sequence re-load the last
-// token (always in bounds); they only feed steps whose Delta is forced to 0.
-template <class Io, int kStage>
+// One B/C stage is 2 tensors x kStage tokens x 16 states.  kStagerThreads threads cover
+// the 2*kStage (tensor, token) pairs with kParts threads per pair, each holding kPer
+// states.  The raw words stay in registers while the current stage is computed and
+// are converted to float32 when written to LDS.  Tokens past the end of the sequence
+// re-load the last token (always in bounds); they only feed steps whose Delta is 0.
+// kFullN: d_state == 16, rows of 16 states moved as 16-byte vectors.
+template <class Io, int kStage, bool kFullN>
 struct Stager {
-    static constexpr int kPairs = 2 * kStage;           // (tensor, token) pairs per stage
-    static constexpr int kParts = 256 / kPairs;         // threads per pair
-    static constexpr int kPer = kMaxState / kParts;     // states per thread
-    static_assert(kPairs * kParts == 256 && kPer * kParts == kMaxState, "stage shape");
-    static constexpr int kWords = kPer * sizeof(typename Io::T) / 16;  // uint4 words (N == 16)
-    float v[kPer];
-    uint4 w[kWords > 0 ? kWords : 1];
+    static constexpr int kPairs = 2 * kStage;               // (tensor, token) pairs per stage
+    static constexpr int kParts = kStagerThreads / kPairs;    // threads per pair
+    static constexpr int kPer = kMaxState / kParts;         // states per thread
+    static_assert(kPairs * kParts == kStagerThreads && kPer * kParts == kMaxState, "stage shape");
+    static constexpr int kWords = kPer * static_cast<int>(sizeof(typename Io::T)) / 16;  // uint4 words
+    static_assert(!kFullN || kWords > 0, "16-byte rows");
+    float v[kFullN ? 1 : kPer];
+    uint4 w[kFullN ? kWords : 1];
 
-    __device__ inline void load(const ScanArgs &a, size_t tbase, size_t t1, int N, int tid)
+    __device__ inline void load(const ScanArgs &a, size_t tbase, size_t t1, int N, int rtid)
     {
-        const int pair = tid / kParts;
-        const int part = tid % kParts;
+        const int pair = rtid / kParts;
+        const int part = rtid % kParts;
         const int which = pair / kStage;
         const int tt = pair % kStage;
         size_t t = tbase + static_cast<size_t>(tt);
-        if (t >= t1) t = t1 - 1;  // t1 > tbase for every stage that exists
+        if (t >= t1) t = t1 - 1;  // only called for non-empty sequences
         const void *src = which ? a.C : a.B;
         const int n0 = part * kPer;
-        if (N == kMaxState && kWords > 0) {
+        if constexpr (kFullN) {
             const uint4 *q =
                 reinterpret_cast<const uint4 *>(static_cast<const typename Io::T *>(src) + t * kMaxState + n0);
 #pragma unroll
@@ -123,16 +142,16 @@ struct Stager {
         }
     }
 
-    template <class T>
-    __device__ inline void store(Smem<T, kStage> &sm, int buf, int tid, int N) const
+    template <class S>  // LDS layout with bcol[2][kMaxState][>= kStage] and crow[2][kStage][kPPitch]
+    __device__ inline void store(S &sm, int buf, int rtid) const
     {
-        const int pair = tid / kParts;
-        const int part = tid % kParts;
+        const int pair = rtid / kParts;
+        const int part = rtid % kParts;
         const int which = pair / kStage;
         const int tt = pair % kStage;
         const int n0 = part * kPer;
         float f[kPer];
-        if (N == kMaxState && kWords > 0) {
+        if constexpr (kFullN) {
             const uint32_t *u = reinterpret_cast<const uint32_t *>(w);
             if constexpr (sizeof(typename Io::T) == 2) {
 #pragma unroll
@@ -163,10 +182,10 @@ struct Stager {
 };
 
 // Token tiles of one stage: 3 tensors x kStage tokens x one 16-channel row (32 bytes for
-// bf16, 64 for fp32), moved as 16-byte buffer loads (16-channel rows are contiguous in
-// the token-major layout) and kept raw in registers until written to LDS at the end of
-// the current stage.  Tokens past the end of the sequence re-load the last token.  Each
-// tensor's resource is chosen at compile time (a resource picked from an array by a
+// bf16, 64 for fp32), moved as 16-byte buffer loads (16-channel rows are
+// contiguous in the token-major layout) and kept raw in registers until written to LDS.
+// Tokens past the end of the sequence fall outside the resource's extent and load 0.
+// Each tensor's resource is chosen at compile time (a resource picked from an array by a
 // runtime index is not provably uniform and costs a waterfall loop per load).
 template <class Io, int kStage>
 struct TokStager {
@@ -174,17 +193,17 @@ struct TokStager {
     static constexpr int kRowBytes = kChannels * static_cast<int>(sizeof(T));
     static constexpr int kVecPerRow = kRowBytes / 16;
     static constexpr int kPerTensor = kStage * kVecPerRow;  // 16-byte vectors per tensor
-    static constexpr int kPerThread = (kPerTensor + 255) / 256;
+    static constexpr int kPerThread = (kPerTensor + kStagerThreads - 1) / kStagerThreads;
     static_assert(kPerTensor % 64 == 0, "whole waves per vector slot");
     uint4 v[3][kPerThread];
 
-    __device__ inline void load_one(Rsrc r, int k, int last, int D, int c0, int tid)
+    __device__ inline void load_one(Rsrc r, int k, int D, int c0, int rtid)
     {
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-            const int idx = i * 256 + tid;
-            if (kPerTensor % 256 == 0 || idx < kPerTensor) {  // uniform across each wave
-                const int tok = min(idx / kVecPerRow, last);
+            const int idx = i * kStagerThreads + rtid;
+            if (kPerTensor % kStagerThreads == 0 || idx < kPerTensor) {  // uniform across each wave
+                const int tok = idx / kVecPerRow;
                 const int part = idx % kVecPerRow;
                 const uint32_t boff = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(D) + static_cast<uint32_t>(c0)) *
                                           static_cast<uint32_t>(sizeof(T)) +
@@ -194,21 +213,22 @@ struct TokStager {
         }
     }
 
-    __device__ inline void load(Rsrc rx, Rsrc rd, Rsrc rz, int last, int D, int c0, int tid)
+    __device__ inline void load(Rsrc rx, Rsrc rd, Rsrc rz, int D, int c0, int rtid)
     {
-        load_one(rx, 0, last, D, c0, tid);
-        load_one(rd, 1, last, D, c0, tid);
-        load_one(rz, 2, last, D, c0, tid);
+        load_one(rx, 0, D, c0, rtid);
+        load_one(rd, 1, D, c0, rtid);
+        load_one(rz, 2, D, c0, rtid);
     }
 
-    __device__ inline void store(Smem<T, kStage> &sm, int buf, int tid) const
+    template <class S>  // LDS layout with tok[2][3][kStage][>= 16 I/O words]
+    __device__ inline void store(S &sm, int buf, int rtid) const
     {
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
-                const int idx = i * 256 + tid;
-                if (kPerTensor % 256 == 0 || idx < kPerTensor) {
+                const int idx = i * kStagerThreads + rtid;
+                if (kPerTensor % kStagerThreads == 0 || idx < kPerTensor) {
                     const int tok = idx / kVecPerRow;
                     const int part = idx % kVecPerRow;
                     uint2 *d = reinterpret_cast<uint2 *>(&sm.tok[buf][k][tok][part * 16]);
@@ -222,7 +242,7 @@ struct TokStager {
 
 }  // namespace rows
 
-template <class Io, int kStage>
+template <class Io, int kStage, bool kFullN>
 __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 {
     using namespace rows;
@@ -291,8 +311,9 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     const T *zs = has_z ? static_cast<const T *>(a.z) + t0 * D : xs;
     T *os = static_cast<T *>(a.out) + t0 * D;
 
-    // Byte extent of a stage's rows (the stage's tokens that belong to the sequence):
-    // buffer resources built on it bound every token access of the stage.
+    // Byte extent of a stage's rows (the stage's tokens that belong to the sequence; only
+    // stages that start inside it are addressed): buffer resources built on it bound every
+    // token access of the stage.
     auto stage_bytes = [&](int base) {
         return static_cast<uint32_t>(min(kStage, L - base)) * static_cast<uint32_t>(D) * static_cast<uint32_t>(sizeof(T));
     };
@@ -306,8 +327,8 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     auto load_stage_tokens = [&](int st, TokStager<Io, kStage> &ts) {
         const int base = st * kStage;
         const uint32_t bytes = stage_bytes(base);
-        ts.load(make_rsrc(xs + static_cast<size_t>(base) * D, bytes), make_rsrc(dts + static_cast<size_t>(base) * D, bytes),
-                make_rsrc(zs + static_cast<size_t>(base) * D, bytes), L - 1 - base, D, c0, tid);
+        const size_t off = static_cast<size_t>(base) * D;
+        ts.load(make_rsrc(xs + off, bytes), make_rsrc(dts + off, bytes), make_rsrc(zs + off, bytes), D, c0, tid);
     };
     // This lane's channel within the workgroup's 16 (its column in the token tiles).
     const int lane_ch = wave * kRowsPerWave + row;
@@ -396,7 +417,7 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         f.du = act ? (lg * kLn2) * f.u : 0.0f;
     };
 
-    Stager<Io, kStage> stg;
+    Stager<Io, kStage, kFullN> stg;
     TokStager<Io, kStage> tst;
     Cols cl, cln;
     TokRaw tk1, tk2;  // token words of the next block and of the one after it
@@ -404,7 +425,7 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     if (nstages > 0) {
         stg.load(a, t0, t1, N, tid);
         load_stage_tokens(0, tst);
-        stg.store(sm, 0, tid, N);
+        stg.store(sm, 0, tid);
         tst.store(sm, 0, tid);
     }
     __syncthreads();
@@ -499,7 +520,7 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         }
 
         if (more) {
-            stg.store(sm, buf ^ 1, tid, N);
+            stg.store(sm, buf ^ 1, tid);
             tst.store(sm, buf ^ 1, tid);
         }
         __syncthreads();
@@ -515,24 +536,23 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     if (a.h_final != nullptr && chan_ok && state_ok) a.h_final[hidx] = h;
 }
 
-inline void launch_rows_scan(const ScanArgs &a, samba_dtype io, hipStream_t stream)
+// One wave per channel group, four waves per workgroup; used when the grid has enough
+// workgroups for two or more waves per SIMD.  kStage 64 keeps two workgroups per CU.
+inline void launch_rows_single(const ScanArgs &a, samba_dtype io, hipStream_t stream)
 {
     const int ncb = (a.D + rows::kChannels - 1) / rows::kChannels;
     const dim3 grid(ncb * a.nseq), block(256);
-    // Few workgroups (one wave per SIMD): long stages so the next stage's loads have a
-    // whole stage of compute to arrive.  Many workgroups: short stages, smaller LDS and
-    // register footprint for more waves per SIMD.
-    const bool few = static_cast<size_t>(ncb) * a.nseq <= 512;
+    const bool full = a.N == kMaxState;
     if (io == SAMBA_BF16) {
-        if (few)
-            rows_scan_kernel<IoBf16, 128><<<grid, block, 0, stream>>>(a, ncb);
+        if (full)
+            rows_scan_kernel<IoBf16, 64, true><<<grid, block, 0, stream>>>(a, ncb);
         else
-            rows_scan_kernel<IoBf16, 64><<<grid, block, 0, stream>>>(a, ncb);
+            rows_scan_kernel<IoBf16, 64, false><<<grid, block, 0, stream>>>(a, ncb);
     } else {
-        if (few)
-            rows_scan_kernel<IoF32, 128><<<grid, block, 0, stream>>>(a, ncb);
+        if (full)
+            rows_scan_kernel<IoF32, 64, true><<<grid, block, 0, stream>>>(a, ncb);
         else
-            rows_scan_kernel<IoF32, 64><<<grid, block, 0, stream>>>(a, ncb);
+            rows_scan_kernel<IoF32, 64, false><<<grid, block, 0, stream>>>(a, ncb);
     }
 }
 

@@ -1,0 +1,426 @@
+// scan_split.h -- prefill with one 16-lane DPP row per channel (one lane per state), the
+// work of every channel split between two waves of different roles.
+//
+// The recurrence of page 1 section 3.4 ("The State Space Model Update (S6)") is
+// independent across channels and, within a channel, across the d_state = 16 state
+// components; only the readout y_t = sum_n C_t[n] h_t[n] couples the states.  This
+// kernel therefore gives every channel a row of 16 lanes (lane n owns state n) and walks
+// the sequence in time, so a batch-1 prompt of d_inner = 4096 channels still yields
+// 65536 lanes with no cross-workgroup carry and no recomputation.
+//
+// 65536 lanes are one wave per SIMD, and a single wave issues at most one instruction per
+// issue cycle of its SIMD: its LDS, scalar and memory instructions would each cost a
+// VALU slot.  So every channel gets two waves on the same SIMD, one per role:
+//  * the token wave (lane j of a row = token j of a block of 16) runs the per-token work:
+//    causal conv (taps from neighbouring lanes by DPP row rotations), SiLU,
+//    softplus(dt + b), Delta and Delta*u, which it hands to the scan wave through LDS;
+//    and the readout of a finished block (C_t . h_t + D u_t, SiLU(z) gate, store);
+//  * the scan wave (lane n of a row = state n) steps the 16 states through the block,
+//    receiving Delta and Delta*u of token t from lane t by DPP row broadcast fused into
+//    the multiply, and writes the 16x16 tile of states h_t[n] to LDS, where the token
+//    wave reads it transposed (lane j: token j's 16 states).
+// Both roles of a workgroup advance in lockstep, one 16-token block per step and one
+// workgroup barrier per step: at step k the scan waves run block k while the token waves
+// run the front end of block k+2 and the readout of block k-1.  The VALU work of the two
+// roles then shares the SIMD while each role's LDS / memory / scalar instructions and
+// stalls are covered by the other role.
+//
+// Per stage of kStage tokens the scan waves stage B and C (shared by the workgroup's 16
+// channels) into LDS as float32 (B transposed to [state][token], C as token rows) and the
+// token waves stage the x / dt / z rows of the 16 channels (16-byte buffer loads), both
+// into the other half of double buffers, with the loads issued one stage ahead.
+#pragma once
+
+#include "scan_rows.h"
+
+namespace samba {
+
+namespace split {
+
+constexpr int kRoleWaves = 4;                                  // waves per role
+constexpr int kRoleThreads = kRoleWaves * 64;                  // threads per role
+constexpr int kThreads = 2 * kRoleThreads;                     // threads per workgroup
+constexpr int kExSlots = 4;                                    // Delta hand-over slots (blocks in flight)
+constexpr int kMaxSplitGrid = 256;                             // workgroups: one per CU
+static_assert(kRoleWaves * rows::kRowsPerWave == rows::kChannels && kRoleThreads == rows::kStagerThreads,
+              "roles cover the 16 channels of a workgroup");
+
+template <class T, int kStage>
+struct SplitSmem {
+    static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
+    static constexpr int kTokPitch = rows::tok_pitch_bytes<T>();
+    float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
+    float crow[2][kStage][rows::kPPitch];        // [buffer][token][state]: C rows
+    float hs[2][rows::kChannels * rows::kRowPitch];  // [block parity][channel][token][state]: h_t
+    float lg[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * log2(e)
+    float du[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * u
+    alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
+};
+
+}  // namespace split
+
+template <class Io, int kStage, bool kFullN>
+__global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a, int ncb)
+{
+    using namespace rows;
+    using namespace split;
+    using T = typename Io::T;
+    constexpr int kSB = kStage / kBlock;  // blocks (steps) per stage
+    // Stage data for stage s+1 is written to LDS at step kStoreStep of stage s: after the
+    // last read of the buffers' previous contents (token words of stage s-1 are read up to
+    // step kSB-4 of stage s-1, C rows of stage s-1 at step 0 of stage s) and before the
+    // first read of the new contents (token words of stage s+1 from step kSB-3 on).
+    constexpr int kStoreStep = kSB - 4;
+    static_assert(kSB >= 8 && kSB % kExSlots == 0, "stage length");
+    __shared__ SplitSmem<T, kStage> sm;
+
+    // Workgroup -> (sequence, block of 16 channels).  Consecutive hardware workgroup ids
+    // go round-robin to the 8 XCDs; remap so that each XCD gets a contiguous range of
+    // channel blocks, and the 128-byte lines shared by 4 neighbouring blocks meet in
+    // one L2.
+    const int nb = gridDim.x;
+    const int q = nb >> 3;
+    int bid = blockIdx.x;
+    if (bid < (q << 3)) bid = (bid & 7) * q + (bid >> 3);
+    const int s = bid / ncb;
+    const int cb = bid - s * ncb;
+
+    const int tid = threadIdx.x;
+    // Role of the wave: uniform, so the role branch is a scalar branch; both roles pass
+    // the same sequence of workgroup barriers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool scan_role = wave >= kRoleWaves;
+    const int rtid = tid & (kRoleThreads - 1);  // thread index within the role
+    const int lane = tid & 63;
+    const int row = lane >> 4;
+    const int j = lane & 15;  // state n (scan role) or token of the block (token role)
+    const int ch = (wave & (kRoleWaves - 1)) * kRowsPerWave + row;  // channel within the workgroup
+    const int D = a.D;
+    const int N = a.N;
+    const int c = cb * kChannels + ch;
+    const bool chan_ok = c < D;
+    const int cc = chan_ok ? c : D - 1;  // clamped channel for loads; results discarded
+
+    size_t t0, t1;
+    seq_range(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
+    const int nstages = (L + kStage - 1) / kStage;
+    const int c0 = cb * kChannels;
+
+    if (scan_role) {
+        // ================================================================ scan role
+        const bool state_ok = j < N;
+        const float An = state_ok ? a.A[static_cast<size_t>(cc) * N + j] : 0.0f;
+        const size_t hidx = (static_cast<size_t>(s) * D + cc) * N + j;
+        float h = (a.h0 != nullptr && state_ok) ? a.h0[hidx] : 0.0f;
+        float *hw = &sm.hs[0][ch * kRowPitch + j];  // this lane's state column of the tile
+
+        struct Cols {
+            float4 b[kBlock / 4];
+        };
+        auto read_cols = [&](int buf, int bk, Cols &cl) {
+            const float *bcol = &sm.bcol[buf][j][bk * kBlock];
+#pragma unroll
+            for (int g = 0; g < kBlock / 4; ++g) cl.b[g] = *reinterpret_cast<const float4 *>(bcol + 4 * g);
+        };
+
+        Stager<Io, kStage, kFullN> stg;
+        if (nstages > 0) {
+            stg.load(a, t0, t1, N, rtid);
+            stg.store(sm, 0, rtid);
+        }
+        __syncthreads();  // stage 0 in LDS
+        __syncthreads();  // Delta of blocks 0 and 1 published
+        // Delta, Delta*u (lane n: token n) and B columns of the block about to run.
+        float lgc = sm.lg[0][ch * kBlock + j], duc = sm.du[0][ch * kBlock + j];
+        Cols cl;
+        read_cols(0, 0, cl);
+
+        // States of the previous block, published at the start of the next step (so that
+        // the step's barrier never waits for fresh stores).
+        float pp[kBlock];
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) pp[t] = 0.0f;
+        for (int st = 0; st < nstages; ++st) {
+            const int buf = st & 1;
+            // Next stage's B/C rows (past the last stage: clamped re-loads, never used).
+            stg.load(a, t0 + static_cast<size_t>(st + 1) * kStage, t1, N, rtid);
+#pragma unroll
+            for (int bk = 0; bk < kSB; ++bk) {
+                // ---- publish block k-1 (tile of parity (k-1) & 1; zeros before block 0)
+                {
+                    float *hp = hw + ((bk + 1) & 1) * (kChannels * kRowPitch);
+#pragma unroll
+                    for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
+                }
+                // ---- next block's inputs (published by the token role a step ago)
+                const int nslot = (bk + 1) % kExSlots;
+                const float lgn = sm.lg[nslot][ch * kBlock + j], dun = sm.du[nslot][ch * kBlock + j];
+                Cols cln;
+                if (bk + 1 < kSB)
+                    read_cols(buf, bk + 1, cln);
+                else
+                    read_cols(buf ^ 1, 0, cln);
+                // keep the LDS traffic at the top of the step
+                __builtin_amdgcn_sched_barrier(0);
+
+                // ---- 16 recurrence steps; lane j holds state n = j.  First the 16 decay
+                // factors exp(Delta_t A_n) and inputs Delta_t u_t B_t[n] (independent of the
+                // state: 16 parallel chains), then the state chain itself (16 dependent FMAs).
+                float ab[kBlock], bu[kBlock];
+#pragma unroll
+                for (int g = 0; g < kBlock / 4; ++g) {
+                    const float bv[4] = {cl.b[g].x, cl.b[g].y, cl.b[g].z, cl.b[g].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * g + e;
+                        float lt, dut;
+                        switch (t) {
+#define SAMBA_BCAST(k) case k: lt = dpp<kRowNewBcast + k>(lgc); dut = dpp<kRowNewBcast + k>(duc); break;
+                            SAMBA_BCAST(0) SAMBA_BCAST(1) SAMBA_BCAST(2) SAMBA_BCAST(3)
+                            SAMBA_BCAST(4) SAMBA_BCAST(5) SAMBA_BCAST(6) SAMBA_BCAST(7)
+                            SAMBA_BCAST(8) SAMBA_BCAST(9) SAMBA_BCAST(10) SAMBA_BCAST(11)
+                            SAMBA_BCAST(12) SAMBA_BCAST(13) SAMBA_BCAST(14) SAMBA_BCAST(15)
+#undef SAMBA_BCAST
+                        }
+                        ab[t] = hw_exp2(lt * An);
+                        bu[t] = dut * bv[e];
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < kBlock; ++t) {
+                    h = __builtin_fmaf(ab[t], h, bu[t]);
+                    pp[t] = h;
+                }
+                if (bk == kStoreStep) stg.store(sm, buf ^ 1, rtid);
+                __syncthreads();
+                lgc = lgn;
+                duc = dun;
+                cl = cln;
+                hold(lgc);
+                hold(duc);
+#pragma unroll
+                for (int g = 0; g < kBlock / 4; ++g) hold(cl.b[g]);
+            }
+        }
+        // Publish the last block.
+        if (nstages > 0) {
+            float *hp = hw + ((nstages * kSB - 1) & 1) * (kChannels * kRowPitch);
+#pragma unroll
+            for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
+        }
+        __syncthreads();
+        if (a.h_final != nullptr && chan_ok && state_ok) a.h_final[hidx] = h;
+        return;
+    }
+
+    // ==================================================================== token role
+    const float w0 = a.conv_w[cc * kConvK + 0], w1 = a.conv_w[cc * kConvK + 1];
+    const float w2 = a.conv_w[cc * kConvK + 2], w3 = a.conv_w[cc * kConvK + 3];
+    const float cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+    const float dsk = a.Dskip ? a.Dskip[cc] : 0.0f;
+    const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
+
+    // History: lanes 13, 14, 15 of the "previous block" hold x_{t0-3}, x_{t0-2}, x_{t0-1}.
+    // conv_final entry k receives x_{t1-3+k}: from the incoming history when t1-3+k < t0
+    // (sequences shorter than 3 tokens), else from the sequence itself.  Every source is
+    // read before any store, since conv_final may alias conv0.
+    const size_t cbase = static_cast<size_t>(s) * 3 * D + cc;
+    float xprev = 0.0f;
+    if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
+    if (a.conv_final != nullptr && chan_ok && j >= 13) {
+        const int k = j - 13;
+        const int tk = L - 3 + k;  // token index relative to t0
+        float hv;
+        if (tk >= 0)
+            hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
+        else
+            hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
+        Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
+    }
+
+    const bool has_z = a.z != nullptr;
+    const T *xs = static_cast<const T *>(a.x) + t0 * D;
+    const T *dts = static_cast<const T *>(a.dt) + t0 * D;
+    const T *zs = has_z ? static_cast<const T *>(a.z) + t0 * D : xs;
+    T *os = static_cast<T *>(a.out) + t0 * D;
+
+    // Byte extent of a stage's rows (the stage's tokens that belong to the sequence; 0 for
+    // a stage past the end): buffer resources built on it bound every token access.
+    auto stage_bytes = [&](int base) {
+        return static_cast<uint32_t>(max(0, min(kStage, L - base))) * static_cast<uint32_t>(D) *
+               static_cast<uint32_t>(sizeof(T));
+    };
+    auto tok_off = [&](int tr) {  // byte offset of (token tr of a stage, this lane's channel)
+        return (static_cast<uint32_t>(tr) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cc)) *
+               static_cast<uint32_t>(sizeof(T));
+    };
+    TokStager<Io, kStage> tst;
+    auto load_stage_tokens = [&](int st) {
+        const int base = st * kStage;
+        const uint32_t bytes = stage_bytes(base);
+        const size_t off = static_cast<size_t>(min(base, L)) * D;
+        tst.load(make_rsrc(xs + off, bytes), make_rsrc(dts + off, bytes), make_rsrc(zs + off, bytes), D, c0, rtid);
+    };
+
+    // Raw token words of one block for this lane (token j of the block, channel ch).
+    struct TokRaw {
+        T x, dt, z;
+    };
+    auto read_tok = [&](int buf, int bk, TokRaw &r) {
+        const int tr = bk * kBlock + j;
+        r.x = reinterpret_cast<const T *>(&sm.tok[buf][0][tr][0])[ch];
+        r.dt = reinterpret_cast<const T *>(&sm.tok[buf][1][tr][0])[ch];
+        r.z = reinterpret_cast<const T *>(&sm.tok[buf][2][tr][0])[ch];
+    };
+    // Per-token front end of one block (lane j: token tb + j): causal conv with the taps
+    // x_{t-1..t-3} from neighbouring lanes (row rotations), SiLU, softplus(dt + b) in log2
+    // units and Delta * u, published to the scan role.  Tokens past the end get Delta = 0
+    // (the state does not move).
+    struct Front {
+        float x, u, zv;
+    };
+    auto front = [&](const TokRaw &r, float xp, int tb, int slot, Front &f) {
+        const bool act = tb + j < L;
+        f.x = to_f32(r.x);
+        f.zv = to_f32(r.z);
+        float pre = __builtin_fmaf(w3, f.x, cbias);
+        pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
+        pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
+        pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
+        f.u = silu(pre);
+        const float lg = softplus_log2(to_f32(r.dt) + bias);
+        sm.lg[slot][ch * kBlock + j] = act ? lg : 0.0f;
+        sm.du[slot][ch * kBlock + j] = act ? (lg * kLn2) * f.u : 0.0f;
+    };
+    // Readout of the block whose first token is pb (relative to t0; negative: none): lane j
+    // sums token j's 16 states against its C row, adds D*u, gates and stores.  The store is
+    // unconditional: tokens past the end, padding channels and the not-yet-existing block
+    // get an offset beyond the resource's extent, which the hardware drops.
+    auto finish = [&](const float4 *py, const float4 *pc, float pu, float pz, int pb) {
+        float ya = pc[0].x * py[0].x, yb = pc[0].y * py[0].y, yc = pc[0].z * py[0].z, yd = pc[0].w * py[0].w;
+#pragma unroll
+        for (int g = 1; g < kBlock / 4; ++g) {
+            ya = __builtin_fmaf(pc[g].x, py[g].x, ya);
+            yb = __builtin_fmaf(pc[g].y, py[g].y, yb);
+            yc = __builtin_fmaf(pc[g].z, py[g].z, yc);
+            yd = __builtin_fmaf(pc[g].w, py[g].w, yd);
+        }
+        float y = (ya + yb) + (yc + yd);
+        y = __builtin_fmaf(dsk, pu, y);
+        const float o = has_z ? y * silu(pz) : y;
+        const int ta = pb + j;
+        const int sb = max(pb, 0) / kStage * kStage;
+        const Rsrc ro = make_rsrc(os + static_cast<size_t>(sb) * D, stage_bytes(sb));
+        const uint32_t boff = (pb >= 0 && ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
+        buf_st(ro, boff, o, static_cast<T *>(nullptr));
+    };
+    // A finished block's states for this lane's token (tile of step parity par) and the
+    // token's C row (block cbk of stage buffer cbuf).
+    const float *hr = &sm.hs[0][ch * kRowPitch + j * kPPitch];
+    auto read_states = [&](int par, int cbuf, int cbk, float4 *py, float4 *pc) {
+        const float *pr = hr + par * (kChannels * kRowPitch);
+        const float *cr = &sm.crow[cbuf][cbk * kBlock + j][0];
+#pragma unroll
+        for (int g = 0; g < kBlock / 4; ++g) {
+            py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
+            pc[g] = *reinterpret_cast<const float4 *>(cr + 4 * g);
+        }
+    };
+
+    if (nstages > 0) {
+        load_stage_tokens(0);
+        tst.store(sm, 0, rtid);
+    }
+    __syncthreads();  // stage 0 in LDS
+    // Fronts of the blocks in flight: fm2 (block k-2, read out at step k), fm1, f0 (block k)
+    // and f1 (block k+1); step k computes block k+2 from its token words rn (read a step
+    // ahead).
+    Front fm2{}, fm1{}, f0{}, f1{};
+    TokRaw rn;
+    {
+        TokRaw r0, r1;
+        read_tok(0, 0, r0);
+        read_tok(0, 1, r1);
+        read_tok(0, 2, rn);
+        front(r0, xprev, 0, 0, f0);
+        front(r1, f0.x, kBlock, 1, f1);
+    }
+    __syncthreads();  // Delta of blocks 0 and 1 published
+
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
+        const int sbase = st * kStage;
+        load_stage_tokens(st + 1);  // past the last stage: empty extent, the loads return 0
+#pragma unroll
+        for (int bk = 0; bk < kSB; ++bk) {
+            const int tb = sbase + bk * kBlock;  // first token of block k (relative to t0)
+            // ---- LDS reads: states and C row of block k-2 (published at step k-1), token
+            // words of block k+3
+            float4 py[kBlock / 4], pc[kBlock / 4];
+            if (bk >= 2)
+                read_states(bk & 1, buf, bk - 2, py, pc);
+            else
+                read_states(bk & 1, buf ^ 1, kSB + bk - 2, py, pc);
+            TokRaw r3;
+            if (bk + 3 < kSB)
+                read_tok(buf, bk + 3, r3);
+            else
+                read_tok(buf ^ 1, bk + 3 - kSB, r3);
+            __builtin_amdgcn_sched_barrier(0);  // issue the reads before the arithmetic
+            // ---- front end of block k+2, published for the scan role
+            Front f2;
+            front(rn, f1.x, tb + 2 * kBlock, (bk + 2) % kExSlots, f2);
+            // ---- readout of block k-2 (after the front end, which covers the reads' latency)
+            __builtin_amdgcn_sched_barrier(0);
+            finish(py, pc, fm2.u, fm2.zv, tb - 2 * kBlock);
+            if (bk == kStoreStep) tst.store(sm, buf ^ 1, rtid);
+            __syncthreads();
+            fm2 = fm1;
+            fm1 = f0;
+            f0 = f1;
+            f1 = f2;
+            rn = r3;
+            hold(rn.x);
+            hold(rn.dt);
+            hold(rn.z);
+        }
+    }
+    // Readout of the last two blocks: block nb-2 was published at the last step, block nb-1
+    // after the loop.
+    if (nstages > 0) {
+        const int last = nstages * kSB - 1;
+        const int lbuf = (nstages - 1) & 1;
+        float4 py[kBlock / 4], pc[kBlock / 4];
+        read_states((last - 1) & 1, lbuf, kSB - 2, py, pc);
+        finish(py, pc, fm2.u, fm2.zv, (last - 1) * kBlock);
+    }
+    __syncthreads();
+    if (nstages > 0) {
+        const int last = nstages * kSB - 1;
+        const int lbuf = (nstages - 1) & 1;
+        float4 py[kBlock / 4], pc[kBlock / 4];
+        read_states(last & 1, lbuf, kSB - 1, py, pc);
+        finish(py, pc, fm1.u, fm1.zv, last * kBlock);
+    }
+}
+
+inline void launch_rows_split(const ScanArgs &a, samba_dtype io, hipStream_t stream)
+{
+    const int ncb = (a.D + rows::kChannels - 1) / rows::kChannels;
+    const dim3 grid(ncb * a.nseq), block(split::kThreads);
+    const bool full = a.N == kMaxState;
+    if (io == SAMBA_BF16) {
+        if (full)
+            rows_split_kernel<IoBf16, 128, true><<<grid, block, 0, stream>>>(a, ncb);
+        else
+            rows_split_kernel<IoBf16, 128, false><<<grid, block, 0, stream>>>(a, ncb);
+    } else {
+        if (full)
+            rows_split_kernel<IoF32, 128, true><<<grid, block, 0, stream>>>(a, ncb);
+        else
+            rows_split_kernel<IoF32, 128, false><<<grid, block, 0, stream>>>(a, ncb);
+    }
+}
+
+}  // namespace samba

@@ -17,10 +17,11 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-@pytest.fixture(params=["rows", "lane"], autouse=True)
+@pytest.fixture(params=["split", "single", "lane"], autouse=True)
 def scan_path(request, monkeypatch):
-    """Run every prefill / varlen case on both kernels (the decode step always uses the
-    one-lane-per-channel kernel)."""
+    """Run every prefill / varlen case on each prefill kernel: the two-role and the
+    single-role row kernels and the one-lane-per-channel kernel (the decode step has a
+    kernel of its own)."""
     monkeypatch.setenv("SAMBA_SCAN_PATH", request.param)
     print("path:", request.param, flush=True)
     return request.param
