@@ -80,6 +80,14 @@ __device__ inline void wave_order()
 // the current step, right after the loads, where it would wait for their latency.
 __device__ inline void hold(float &v) { asm volatile("" : "+v"(v)); }
 __device__ inline void hold(uint16_t &v) { asm volatile("" : "+v"(v)); }
+__device__ inline void hold(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ inline void hold(uint4 &v)
+{
+    hold(v.x);
+    hold(v.y);
+    hold(v.z);
+    hold(v.w);
+}
 __device__ inline void hold(float4 &v)
 {
     hold(v.x);
@@ -139,6 +147,19 @@ struct Stager {
         } else {
 #pragma unroll
             for (int k = 0; k < kPer; ++k) v[k] = (n0 + k) < N ? Io::ld(src, t * N + n0 + k) : 0.0f;
+        }
+    }
+
+    // Pins the raw words to this point of the program: their conversion (in store) cannot
+    // be hoisted up to the loads, where it would wait for the memory latency.
+    __device__ inline void hold_raw()
+    {
+        if constexpr (kFullN) {
+#pragma unroll
+            for (int k = 0; k < kWords; ++k) hold(w[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) hold(v[k]);
         }
     }
 

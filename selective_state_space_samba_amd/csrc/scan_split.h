@@ -66,11 +66,13 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     using namespace split;
     using T = typename Io::T;
     constexpr int kSB = kStage / kBlock;  // blocks (steps) per stage
-    // Stage data for stage s+1 is written to LDS at step kStoreStep of stage s: after the
-    // last read of the buffers' previous contents (token words of stage s-1 are read up to
-    // step kSB-4 of stage s-1, C rows of stage s-1 at step 0 of stage s) and before the
-    // first read of the new contents (token words of stage s+1 from step kSB-3 on).
-    constexpr int kStoreStep = kSB - 4;
+    // The token role stages the data of stage s+1 during stage s (the scan role is the
+    // longer one).  Token words are written to LDS at step kStoreStep: after their buffer's
+    // last read of stage s-1 words (step kSB-4 of stage s-1) and before the first read of
+    // the new ones (step kSB-3).  B columns and C rows are written a step later, spreading
+    // the LDS writes: after the last read of stage s-1's C rows (step 1 of stage s) and
+    // before the first read of the new B columns (step kSB-1).
+    constexpr int kStoreStep = kSB - 4, kStoreStepBC = kSB - 3;
     static_assert(kSB >= 8 && kSB % kExSlots == 0, "stage length");
     __shared__ SplitSmem<T, kStage> sm;
 
@@ -124,11 +126,6 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
             for (int g = 0; g < kBlock / 4; ++g) cl.b[g] = *reinterpret_cast<const float4 *>(bcol + 4 * g);
         };
 
-        Stager<Io, kStage, kFullN> stg;
-        if (nstages > 0) {
-            stg.load(a, t0, t1, N, rtid);
-            stg.store(sm, 0, rtid);
-        }
         __syncthreads();  // stage 0 in LDS
         __syncthreads();  // Delta of blocks 0 and 1 published
         // Delta, Delta*u (lane n: token n) and B columns of the block about to run.
@@ -143,8 +140,6 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         for (int t = 0; t < kBlock; ++t) pp[t] = 0.0f;
         for (int st = 0; st < nstages; ++st) {
             const int buf = st & 1;
-            // Next stage's B/C rows (past the last stage: clamped re-loads, never used).
-            stg.load(a, t0 + static_cast<size_t>(st + 1) * kStage, t1, N, rtid);
 #pragma unroll
             for (int bk = 0; bk < kSB; ++bk) {
                 // ---- publish block k-1 (tile of parity (k-1) & 1; zeros before block 0)
@@ -192,7 +187,6 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
                     h = __builtin_fmaf(ab[t], h, bu[t]);
                     pp[t] = h;
                 }
-                if (bk == kStoreStep) stg.store(sm, buf ^ 1, rtid);
                 __syncthreads();
                 lgc = lgn;
                 duc = dun;
@@ -328,8 +322,12 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         }
     };
 
+    Stager<Io, kStage, kFullN> stg;
     if (nstages > 0) {
+        stg.load(a, t0, t1, N, rtid);
         load_stage_tokens(0);
+        stg.hold_raw();
+        stg.store(sm, 0, rtid);
         tst.store(sm, 0, rtid);
     }
     __syncthreads();  // stage 0 in LDS
@@ -351,7 +349,10 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
         const int sbase = st * kStage;
-        load_stage_tokens(st + 1);  // past the last stage: empty extent, the loads return 0
+        // Next stage's token words (past the last stage: empty extent, the loads return 0)
+        // and B/C rows (past the last stage: clamped re-loads, never used).
+        load_stage_tokens(st + 1);
+        stg.load(a, t0 + static_cast<size_t>(st + 1) * kStage, t1, N, rtid);
 #pragma unroll
         for (int bk = 0; bk < kSB; ++bk) {
             const int tb = sbase + bk * kBlock;  // first token of block k (relative to t0)
@@ -375,6 +376,10 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
             __builtin_amdgcn_sched_barrier(0);
             finish(py, pc, fm2.u, fm2.zv, tb - 2 * kBlock);
             if (bk == kStoreStep) tst.store(sm, buf ^ 1, rtid);
+            if (bk == kStoreStepBC) {
+                stg.hold_raw();
+                stg.store(sm, buf ^ 1, rtid);
+            }
             __syncthreads();
             fm2 = fm1;
             fm1 = f0;
