@@ -45,6 +45,18 @@ constexpr int kPPitch = kBlock + 4;       // LDS pitch of one token's 16 partial
 constexpr int kRowPitch = kBlock * kPPitch + 16;
 constexpr int kStagerThreads = 256;       // threads that move one stage (B/C or token words)
 
+// Logical workgroup index (sequence-major, then 16-channel block) of hardware workgroup h.
+// Consecutive hardware ids go round-robin to the 8 XCDs, each with its own L2.  Groups of
+// 4 consecutive logical blocks (64 channels: the 128-byte bf16 rows of x, dt, z and y they
+// share) are placed on one XCD, and logical order otherwise follows dispatch order, so that
+// a grid of several sequences is spread evenly over the XCDs.
+__device__ inline int logical_block(int h, int nb)
+{
+    if (h >= (nb & ~31)) return h;
+    const int i = h >> 5, x = h & 7, k = (h >> 3) & 3;
+    return (i << 5) | (x << 2) | k;
+}
+
 // DPP controls (gfx9 encoding).
 constexpr int kRowRor = 0x120;      // row_ror:k = kRowRor + k  (k = 1..15)
 constexpr int kRowNewBcast = 0x150; // row_newbcast:k = kRowNewBcast + k
@@ -271,14 +283,8 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     constexpr int kStageBlocks = kStage / kBlock;
     __shared__ Smem<T, kStage> sm;
 
-    // Workgroup -> (sequence, block of 16 channels).  Consecutive hardware workgroup ids
-    // go round-robin to the 8 XCDs; remap so that each XCD gets a contiguous range of
-    // channel blocks, and the 128-byte lines shared by 4 neighbouring blocks meet in
-    // one L2.
-    const int nb = gridDim.x;
-    const int q = nb >> 3;
-    int bid = blockIdx.x;
-    if (bid < (q << 3)) bid = (bid & 7) * q + (bid >> 3);
+    // Workgroup -> (sequence, block of 16 channels).
+    const int bid = logical_block(blockIdx.x, gridDim.x);
     const int s = bid / ncb;
     const int cb = bid - s * ncb;
 

@@ -76,14 +76,8 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     static_assert(kSB >= 8 && kSB % kExSlots == 0, "stage length");
     __shared__ SplitSmem<T, kStage> sm;
 
-    // Workgroup -> (sequence, block of 16 channels).  Consecutive hardware workgroup ids
-    // go round-robin to the 8 XCDs; remap so that each XCD gets a contiguous range of
-    // channel blocks, and the 128-byte lines shared by 4 neighbouring blocks meet in
-    // one L2.
-    const int nb = gridDim.x;
-    const int q = nb >> 3;
-    int bid = blockIdx.x;
-    if (bid < (q << 3)) bid = (bid & 7) * q + (bid >> 3);
+    // Workgroup -> (sequence, block of 16 channels).
+    const int bid = logical_block(blockIdx.x, gridDim.x);
     const int s = bid / ncb;
     const int cb = bid - s * ncb;
 
