@@ -154,9 +154,12 @@ def test_varlen_fresh_sequences():
     check((host(y), host(hf), host(cf)), r, io)
 
 
-@pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_decode_steps(io):
-    S, D, N, steps = 5, 192, 16, 24
+@pytest.mark.parametrize("io,D,gate", [("f32", 192, True), ("bf16", 192, True), ("bf16", 200, True),
+                                         ("f32", 72, False)])
+def test_decode_steps(io, D, gate):
+    """24 decode steps on 5 sequences; D = 200 and 72 leave a partly filled last wave of 64
+    channels, and z = None exercises the ungated output."""
+    S, N, steps = 5, 16, 24
     seed = 600
     p = synth.make_params(seed, D, N, random_A=True)
     h0, c0 = synth.make_state(seed, S, D, N, io, scale=0.5)
@@ -168,8 +171,9 @@ def test_decode_steps(io):
     for k in range(steps):
         st = synth.make_tokens(seed, (S,), D, N, io, tag="s%d" % k)
         y = ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
-                      tdev(st.z, io, DEV), *args, h, cs)
-        yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, hr, cr)
+                      tdev(st.z, io, DEV) if gate else None, *args, h, cs)
+        yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z if gate else None, p.A, p.Dskip, p.dt_bias,
+                                p.conv_w, p.conv_b, hr, cr)
         torch.cuda.synchronize()
         e = rel_err(host(y), yr)
         assert e <= TOL[io], "step %d err %.3e" % (k, e)
