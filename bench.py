@@ -77,9 +77,10 @@ def to_dev(a, dev, bf16=True):
     return t.to(torch.bfloat16) if bf16 else t
 
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps, warmup, flush=None):
     """Run fn() warmup + steps times on torch's current stream (the stream the library
-    launches on); returns (total seconds, per-call seconds from HIP events)."""
+    launches on); returns (total seconds, per-call seconds from HIP events).  flush, if
+    given, runs before every timed call, outside its events."""
     import torch
     for _ in range(warmup):
         fn()
@@ -87,6 +88,8 @@ def time_calls(fn, steps, warmup):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in ev:
+        if flush is not None:
+            flush()
         a.record()
         fn()
         b.record()
@@ -122,14 +125,15 @@ def bench_prefill(args, dev):
     return dict(tokens=b * L, wall=wall, per=per, host=(p, tk))
 
 
-def bench_decode(args, dev):
-    """256 resident sequences, state from a random L=1024 prefill, then decode steps whose
-    inputs cycle through a pool of 256 pre-drawn steps (replayed from HIP graphs)."""
+def bench_decode(args, dev, S=256, P=256, warm_prefill=True, steps=None):
+    """S resident sequences, state from a random L=1024 prefill (or, for the out-of-cache
+    control, a random state), then decode steps whose inputs cycle through a pool of P
+    pre-drawn steps (replayed from HIP graphs of P steps)."""
     import torch
     import selective_state_space_samba_amd as ss
     from selective_state_space_samba_amd import synth
 
-    S, Lw, P = 256, 1024, 256
+    Lw = 1024
     seed = synth.seed_for(3)
     p = synth.make_params(seed, D_INNER, D_STATE)
     prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
@@ -139,11 +143,16 @@ def bench_decode(args, dev):
     def randn(shape, std=1.0):
         return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
 
-    # warm-up prefill (random inputs drawn as in the tiny configuration's recipe)
-    x, z, Bm, Cm = randn((S, Lw, D_INNER)), randn((S, Lw, D_INNER)), randn((S, Lw, D_STATE)), randn((S, Lw, D_STATE))
-    dt = randn((S, Lw, D_INNER), 0.5)
-    _, h, cs = ss.prefill(x, dt, Bm, Cm, z, *prm)
-    del x, z, Bm, Cm, dt
+    if warm_prefill:
+        # warm-up prefill (random inputs drawn as in the tiny configuration's recipe)
+        x, z, Bm, Cm = (randn((S, Lw, D_INNER)), randn((S, Lw, D_INNER)), randn((S, Lw, D_STATE)),
+                        randn((S, Lw, D_STATE)))
+        dt = randn((S, Lw, D_INNER), 0.5)
+        _, h, cs = ss.prefill(x, dt, Bm, Cm, z, *prm)
+        del x, z, Bm, Cm, dt
+    else:
+        h = torch.randn((S, D_INNER, D_STATE), generator=g, device=dev, dtype=torch.float32) * 0.1
+        cs = randn((S, 3, D_INNER))
     pool = dict(x=randn((P, S, D_INNER)), dt=randn((P, S, D_INNER), 0.5), z=randn((P, S, D_INNER)),
                 B=randn((P, S, D_STATE)), C=randn((P, S, D_STATE)))
     y = torch.empty((S, D_INNER), dtype=torch.bfloat16, device=dev)
@@ -161,7 +170,7 @@ def bench_decode(args, dev):
         for k in range(P):
             one(k)
     torch.cuda.synchronize()
-    reps = max(1, args.decode_steps // P)
+    reps = max(1, (steps if steps is not None else args.decode_steps) // P)
     graph.replay()
     torch.cuda.synchronize()
     a, bev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -188,10 +197,14 @@ def bench_extra(dev, steps=5, warmup=2):
     tk = synth.make_tokens(seed, (4, 4096), D_INNER, D_STATE, "bf16")
     ins = [to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
     out = torch.empty_like(ins[0])
-    _, per = time_calls(lambda: ss.prefill(*ins, *prm, out=out), steps, warmup)
+    # 539 MB of inputs and outputs: more than the 256 MB MALL, but a 512 MB write between the
+    # timed calls makes sure none of it is left there
+    scratch = torch.empty((256 << 20,), dtype=torch.bfloat16, device=dev)
+    _, per = time_calls(lambda: ss.prefill(*ins, *prm, out=out), steps, warmup, flush=lambda: scratch.fill_(1.0))
     res["train4k"] = dict(workload="batch 4, L=4096", ms=float(np.mean(per) * 1e3),
-                          mtok_s=4 * 4096 / float(np.mean(per)) / 1e6)
-    del ins, out
+                          ms_median=float(np.median(per) * 1e3), mtok_s=4 * 4096 / float(np.mean(per)) / 1e6,
+                          note="512 MB scratch write between timed calls")
+    del ins, out, scratch
     seed = synth.seed_for(4)
     p = synth.make_params(seed, D_INNER, D_STATE)
     prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
@@ -204,7 +217,8 @@ def bench_extra(dev, steps=5, warmup=2):
     out = torch.empty_like(ins[0])
     _, per = time_calls(lambda: ss.varlen(cu_d, *ins, *prm, max_seqlen=int(lens.max()), out=out), steps, warmup)
     res["varlen8"] = dict(workload="8 sequences, lengths %s, %d tokens" % (lens.tolist(), T),
-                          ms=float(np.mean(per) * 1e3), mtok_s=T / float(np.mean(per)) / 1e6)
+                          ms=float(np.mean(per) * 1e3), ms_median=float(np.median(per) * 1e3),
+                          mtok_s=T / float(np.mean(per)) / 1e6)
     return res
 
 
@@ -247,18 +261,42 @@ def committed_traffic(name):
         return None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(host, nch):
+    """The oracle timed on the host: OpenMP over all its threads on nch channels, and one
+    thread on nch / 32 channels (channels are independent, so both are exact samples)."""
     import oracle
     p, tk = host
-    chans = np.arange(nch)
-    t0 = time.perf_counter()
-    oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, chans=chans)
-    sec = time.perf_counter() - t0
     L = tk.x.shape[1]
-    return {"value": L * nch / D_INNER / sec / 1e6, "unit": "Mtok/s", "cores": oracle.max_threads(),
+    threads = oracle.max_threads()
+
+    def run(n):
+        t0 = time.perf_counter()
+        oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b,
+                       chans=np.arange(n))
+        return time.perf_counter() - t0
+
+    sec = run(nch)
+    n1 = max(1, nch // 32)
+    oracle.set_threads(1)
+    sec1 = run(n1)
+    oracle.set_threads(threads)
+    return {"value": L * nch / D_INNER / sec / 1e6, "unit": "Mtok/s", "cores": threads,
             "kind": "oracle",
             "sample": "fp64 oracle over all %d tokens of the prompt for %d of the %d channels (channels are "
-                      "independent); %.1f s wall; rate scaled to full-width tokens" % (L, nch, D_INNER, sec)}
+                      "independent); %.1f s wall; rate scaled to full-width tokens" % (L, nch, D_INNER, sec),
+            "single_thread": {"value": L * n1 / D_INNER / sec1 / 1e6, "unit": "Mtok/s",
+                              "sample": "%d channels, %.1f s" % (n1, sec1)},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count()}
 
 
 def decode_summary(dec):
@@ -308,6 +346,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 4),
+        "ms_median": round(float(np.median(per)) * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -326,6 +365,10 @@ def main():
     }
     if not args.prefill_only and not args.no_decode:
         line["decode"] = decode_summary(bench_decode(args, dev))
+        # out-of-cache control: 1024 sequences (268 MB of state, more than the 256 MB MALL)
+        ctl = decode_summary(bench_decode(args, dev, S=1024, P=16, warm_prefill=False, steps=1024))
+        ctl["note"] = "control: random start state, inputs from a pool of 16 steps; state exceeds the MALL"
+        line["decode_s1024"] = ctl
     if not args.prefill_only and not args.no_extra:
         line["extra"] = bench_extra(dev)
     if not args.prefill_only and not args.no_cpu:

@@ -109,6 +109,13 @@ def max_threads() -> int:
     return _load().oracle_max_threads()
 
 
+def set_threads(n: int) -> None:
+    """Thread count of the channel-parallel loops (used to time the CPU baseline)."""
+    lib = _load()
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads(int(n))
+
+
 def _params(A, Dskip, dt_bias, conv_w, conv_b, chans):
     def sel(a, axis0=True):
         if a is None:

@@ -169,3 +169,14 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the channel-parallel loops (timing of the CPU baseline only). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
