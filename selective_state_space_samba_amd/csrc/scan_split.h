@@ -45,13 +45,13 @@ constexpr int kMaxSplitGrid = 256;                             // workgroups: on
 static_assert(kRoleWaves * rows::kRowsPerWave == rows::kChannels && kRoleThreads == rows::kStagerThreads,
               "roles cover the 16 channels of a workgroup");
 
-template <class T, int kStage>
+template <class T, int kStage, int kHsSlots>
 struct SplitSmem {
     static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
     static constexpr int kTokPitch = rows::tok_pitch_bytes<T>();
     float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
     float crow[2][kStage][rows::kPPitch];        // [buffer][token][state]: C rows
-    float hs[2][rows::kChannels * rows::kRowPitch];  // [block parity][channel][token][state]: h_t
+    float hs[kHsSlots][rows::kChannels * rows::kRowPitch];  // [block slot][channel][token][state]: h_t
     float lg[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * log2(e)
     float du[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * u
     alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
@@ -59,22 +59,36 @@ struct SplitSmem {
 
 }  // namespace split
 
-template <class Io, int kStage, bool kFullN>
+template <class Io, int kStage, bool kFullN, int kDist>
 __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a, int ncb)
 {
     using namespace rows;
     using namespace split;
     using T = typename Io::T;
     constexpr int kSB = kStage / kBlock;  // blocks (steps) per stage
-    // The token role stages the data of stage s+1 during stage s (the scan role is the
-    // longer one).  Token words are written to LDS at step kStoreStep: after their buffer's
-    // last read of stage s-1 words (step kSB-4 of stage s-1) and before the first read of
-    // the new ones (step kSB-3).  B columns and C rows are written a step later, spreading
-    // the LDS writes: after the last read of stage s-1's C rows (step 1 of stage s) and
-    // before the first read of the new B columns (step kSB-1).
-    constexpr int kStoreStep = kSB - 4, kStoreStepBC = kSB - 3;
-    static_assert(kSB >= 8 && kSB % kExSlots == 0, "stage length");
-    __shared__ SplitSmem<T, kStage> sm;
+    // Hand-over distance: a value written in step k is read in step k + kDist, and the
+    // workgroup barrier runs after every kDist-th step (after steps kDist-1, 2 kDist-1, ...),
+    // so exactly one barrier lies between every write and its read.  At step k the scan
+    // role runs block k (its Delta and B columns were read in step k-1) and publishes block
+    // k-1's states; the token role computes the front end of block k+1+kDist (from token
+    // words read in step k-1) and reads out block k-1-kDist.  State tiles live in 2 kDist
+    // slots, so that no tile is rewritten before a barrier has passed after its last read.
+    constexpr int kHsSlots = 2 * kDist;
+    // The token role stages the data of stage s+1 during stage s.  Token words are first
+    // read (a step ahead) at step kSB-2-kDist; they are written at the last step before the
+    // barrier preceding that (their buffer's previous contents were last read in stage s-1).
+    // B columns and C rows are written later, spreading the LDS writes: after a barrier
+    // that follows the last readout of stage s-1's C rows (step kDist) and before the
+    // barrier preceding the first read of the new B columns (step kSB-1).
+    constexpr int kStoreStep = ((kSB - 2 - kDist) / kDist) * kDist - 1;
+    constexpr int kStoreStepBC = ((kSB - 1) / kDist) * kDist - 1;
+    static_assert(kDist == 1 || kDist == 2, "hand-over distance");
+    static_assert(kSB >= 8 && kSB % kExSlots == 0 && kSB % kDist == 0, "stage length");
+    static_assert(kStoreStep >= 0 && kStoreStepBC >= 2 * kDist && kStoreStepBC >= kStoreStep, "stage store steps");
+    __shared__ SplitSmem<T, kStage, kHsSlots> sm;
+    auto step_barrier = [](int bk) {
+        if (bk % kDist == kDist - 1) __syncthreads();
+    };
 
     // Workgroup -> (sequence, block of 16 channels).
     const int bid = logical_block(blockIdx.x, gridDim.x);
@@ -121,7 +135,7 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         };
 
         __syncthreads();  // stage 0 in LDS
-        __syncthreads();  // Delta of blocks 0 and 1 published
+        __syncthreads();  // Delta of blocks 0 .. kDist published
         // Delta, Delta*u (lane n: token n) and B columns of the block about to run.
         float lgc = sm.lg[0][ch * kBlock + j], duc = sm.du[0][ch * kBlock + j];
         Cols cl;
@@ -136,13 +150,13 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
             const int buf = st & 1;
 #pragma unroll
             for (int bk = 0; bk < kSB; ++bk) {
-                // ---- publish block k-1 (tile of parity (k-1) & 1; zeros before block 0)
+                // ---- publish block k-1 (its slot; zeros before block 0)
                 {
-                    float *hp = hw + ((bk + 1) & 1) * (kChannels * kRowPitch);
+                    float *hp = hw + ((bk + kHsSlots - 1) % kHsSlots) * (kChannels * kRowPitch);
 #pragma unroll
                     for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
                 }
-                // ---- next block's inputs (published by the token role a step ago)
+                // ---- next block's inputs (published by the token role kDist steps ago)
                 const int nslot = (bk + 1) % kExSlots;
                 const float lgn = sm.lg[nslot][ch * kBlock + j], dun = sm.du[nslot][ch * kBlock + j];
                 Cols cln;
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
                     h = __builtin_fmaf(ab[t], h, bu[t]);
                     pp[t] = h;
                 }
-                __syncthreads();
+                step_barrier(bk);
                 lgc = lgn;
                 duc = dun;
                 cl = cln;
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         }
         // Publish the last block.
         if (nstages > 0) {
-            float *hp = hw + ((nstages * kSB - 1) & 1) * (kChannels * kRowPitch);
+            float *hp = hw + ((nstages * kSB - 1) % kHsSlots) * (kChannels * kRowPitch);
 #pragma unroll
             for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
         }
@@ -303,11 +317,11 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         const uint32_t boff = (pb >= 0 && ta < L && chan_ok) ? tok_off(ta - sb) : 0xfffffff0u;
         buf_st(ro, boff, o, static_cast<T *>(nullptr));
     };
-    // A finished block's states for this lane's token (tile of step parity par) and the
-    // token's C row (block cbk of stage buffer cbuf).
+    // A finished block's states for this lane's token (tile slot hslot) and the token's C
+    // row (block cbk of stage buffer cbuf).
     const float *hr = &sm.hs[0][ch * kRowPitch + j * kPPitch];
-    auto read_states = [&](int par, int cbuf, int cbk, float4 *py, float4 *pc) {
-        const float *pr = hr + par * (kChannels * kRowPitch);
+    auto read_states = [&](int hslot, int cbuf, int cbk, float4 *py, float4 *pc) {
+        const float *pr = hr + hslot * (kChannels * kRowPitch);
         const float *cr = &sm.crow[cbuf][cbk * kBlock + j][0];
 #pragma unroll
         for (int g = 0; g < kBlock / 4; ++g) {
@@ -325,20 +339,23 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         tst.store(sm, 0, rtid);
     }
     __syncthreads();  // stage 0 in LDS
-    // Fronts of the blocks in flight: fm2 (block k-2, read out at step k), fm1, f0 (block k)
-    // and f1 (block k+1); step k computes block k+2 from its token words rn (read a step
-    // ahead).
-    Front fm2{}, fm1{}, f0{}, f1{};
+    // Fronts of the blocks in flight, fr[i] = block k-1-kDist+i at step k: fr[0] is read out,
+    // fr[2 kDist + 2] is computed (from token words rn, read a step ahead).
+    constexpr int kFronts = 2 * kDist + 3;
+    Front fr[kFronts] = {};
     TokRaw rn;
     {
-        TokRaw r0, r1;
-        read_tok(0, 0, r0);
-        read_tok(0, 1, r1);
-        read_tok(0, 2, rn);
-        front(r0, xprev, 0, 0, f0);
-        front(r1, f0.x, kBlock, 1, f1);
+        TokRaw r;
+        float xp = xprev;
+#pragma unroll
+        for (int m = 0; m <= kDist; ++m) {
+            read_tok(0, m, r);
+            front(r, xp, m * kBlock, m, fr[kDist + 1 + m]);
+            xp = fr[kDist + 1 + m].x;
+        }
+        read_tok(0, kDist + 1, rn);
     }
-    __syncthreads();  // Delta of blocks 0 and 1 published
+    __syncthreads();  // Delta of blocks 0 .. kDist published
 
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
@@ -350,57 +367,60 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
 #pragma unroll
         for (int bk = 0; bk < kSB; ++bk) {
             const int tb = sbase + bk * kBlock;  // first token of block k (relative to t0)
-            // ---- LDS reads: states and C row of block k-2 (published at step k-1), token
-            // words of block k+3
+            // ---- LDS reads: states and C row of block k-1-kDist (published at step
+            // k-kDist), token words of block k+2+kDist
+            constexpr int kLag = 1 + kDist;
             float4 py[kBlock / 4], pc[kBlock / 4];
-            if (bk >= 2)
-                read_states(bk & 1, buf, bk - 2, py, pc);
+            const int hslot = (bk + kHsSlots * 2 - kLag) % kHsSlots;
+            if (bk >= kLag)
+                read_states(hslot, buf, bk - kLag, py, pc);
             else
-                read_states(bk & 1, buf ^ 1, kSB + bk - 2, py, pc);
+                read_states(hslot, buf ^ 1, kSB + bk - kLag, py, pc);
             TokRaw r3;
-            if (bk + 3 < kSB)
-                read_tok(buf, bk + 3, r3);
+            if (bk + kLag + 1 < kSB)
+                read_tok(buf, bk + kLag + 1, r3);
             else
-                read_tok(buf ^ 1, bk + 3 - kSB, r3);
+                read_tok(buf ^ 1, bk + kLag + 1 - kSB, r3);
             __builtin_amdgcn_sched_barrier(0);  // issue the reads before the arithmetic
-            // ---- front end of block k+2, published for the scan role
-            Front f2;
-            front(rn, f1.x, tb + 2 * kBlock, (bk + 2) % kExSlots, f2);
-            // ---- readout of block k-2 (after the front end, which covers the reads' latency)
+            // ---- front end of block k+1+kDist, published for the scan role
+            front(rn, fr[kFronts - 2].x, tb + kLag * kBlock, (bk + kLag) % kExSlots, fr[kFronts - 1]);
+            // ---- readout of block k-1-kDist (after the front end, which covers the reads'
+            // latency)
             __builtin_amdgcn_sched_barrier(0);
-            finish(py, pc, fm2.u, fm2.zv, tb - 2 * kBlock);
+            finish(py, pc, fr[0].u, fr[0].zv, tb - kLag * kBlock);
             if (bk == kStoreStep) tst.store(sm, buf ^ 1, rtid);
             if (bk == kStoreStepBC) {
                 stg.hold_raw();
                 stg.store(sm, buf ^ 1, rtid);
             }
-            __syncthreads();
-            fm2 = fm1;
-            fm1 = f0;
-            f0 = f1;
-            f1 = f2;
+            step_barrier(bk);
+#pragma unroll
+            for (int i = 0; i + 1 < kFronts; ++i) fr[i] = fr[i + 1];
             rn = r3;
             hold(rn.x);
             hold(rn.dt);
             hold(rn.z);
         }
     }
-    // Readout of the last two blocks: block nb-2 was published at the last step, block nb-1
-    // after the loop.
+    // Readout of the last 1 + kDist blocks: all but the last were published in the loop,
+    // the last one after it.
     if (nstages > 0) {
-        const int last = nstages * kSB - 1;
+        const int nb = nstages * kSB;
         const int lbuf = (nstages - 1) & 1;
-        float4 py[kBlock / 4], pc[kBlock / 4];
-        read_states((last - 1) & 1, lbuf, kSB - 2, py, pc);
-        finish(py, pc, fm2.u, fm2.zv, (last - 1) * kBlock);
+#pragma unroll
+        for (int i = 0; i < kDist; ++i) {
+            const int m = nb - 1 - kDist + i;
+            float4 py[kBlock / 4], pc[kBlock / 4];
+            read_states(m % kHsSlots, lbuf, kSB - 1 - kDist + i, py, pc);
+            finish(py, pc, fr[i].u, fr[i].zv, m * kBlock);
+        }
     }
     __syncthreads();
     if (nstages > 0) {
-        const int last = nstages * kSB - 1;
-        const int lbuf = (nstages - 1) & 1;
+        const int nb = nstages * kSB;
         float4 py[kBlock / 4], pc[kBlock / 4];
-        read_states(last & 1, lbuf, kSB - 1, py, pc);
-        finish(py, pc, fm1.u, fm1.zv, last * kBlock);
+        read_states((nb - 1) % kHsSlots, (nstages - 1) & 1, kSB - 1, py, pc);
+        finish(py, pc, fr[kDist].u, fr[kDist].zv, (nb - 1) * kBlock);
     }
 }
 
@@ -409,16 +429,18 @@ inline void launch_rows_split(const ScanArgs &a, samba_dtype io, hipStream_t str
     const int ncb = (a.D + rows::kChannels - 1) / rows::kChannels;
     const dim3 grid(ncb * a.nseq), block(split::kThreads);
     const bool full = a.N == kMaxState;
+    // Hand-over distance 2 (a barrier every other step) needs 4 state-tile slots, which fit
+    // next to the 2-byte token tiles; with 4-byte token tiles the kernel syncs every step.
     if (io == SAMBA_BF16) {
         if (full)
-            rows_split_kernel<IoBf16, 128, true><<<grid, block, 0, stream>>>(a, ncb);
+            rows_split_kernel<IoBf16, 128, true, 2><<<grid, block, 0, stream>>>(a, ncb);
         else
-            rows_split_kernel<IoBf16, 128, false><<<grid, block, 0, stream>>>(a, ncb);
+            rows_split_kernel<IoBf16, 128, false, 2><<<grid, block, 0, stream>>>(a, ncb);
     } else {
         if (full)
-            rows_split_kernel<IoF32, 128, true><<<grid, block, 0, stream>>>(a, ncb);
+            rows_split_kernel<IoF32, 128, true, 1><<<grid, block, 0, stream>>>(a, ncb);
         else
-            rows_split_kernel<IoF32, 128, false><<<grid, block, 0, stream>>>(a, ncb);
+            rows_split_kernel<IoF32, 128, false, 1><<<grid, block, 0, stream>>>(a, ncb);
     }
 }
 
