@@ -8,8 +8,8 @@ over the whole prompt (conv + SiLU, softplus, discretisation, recurrence, readou
 gate, final-state export), with inputs already resident in HBM.
 
 Also reported (extra fields on the same JSON line): decode tokens/s for 256 resident
-sequences (65536 single-token steps replayed from HIP graphs), and the packed-varlen and
-training-length prefills.  The CPU baseline is the fp64 oracle timed on a bounded sample
+sequences (65536 single-token steps replayed from HIP graphs), and the packed-varlen,
+training-length and batch-64 prefills.  The CPU baseline is the fp64 oracle timed on a bounded sample
 of the same prompt (a subset of channels; channels are independent).
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-decode] [--no-cpu]
@@ -185,7 +185,8 @@ def bench_decode(args, dev, S=256, P=256, warm_prefill=True, steps=None):
 
 
 def bench_extra(dev, steps=5, warmup=2):
-    """Training-length prefill (4 x 4096) and packed varlen (8 sequences, <= 131072 tokens)."""
+    """Training-length prefill (4 x 4096), batch 64 x 2048, and packed varlen (8 sequences,
+    <= 131072 tokens)."""
     import torch
     import selective_state_space_samba_amd as ss
     from selective_state_space_samba_amd import synth
@@ -205,6 +206,17 @@ def bench_extra(dev, steps=5, warmup=2):
                           ms_median=float(np.median(per) * 1e3), mtok_s=4 * 4096 / float(np.mean(per)) / 1e6,
                           note="512 MB scratch write between timed calls")
     del ins, out, scratch
+    # Many mid-length sequences (batch 64, L = 2048): the same 131072 tokens as the long
+    # prompt, spread over enough (sequence, channel) pairs to give one lane each.
+    tk = synth.make_tokens(seed, (64, 2048), D_INNER, D_STATE, "bf16")
+    ins = [to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    out = torch.empty_like(ins[0])
+    _, per = time_calls(lambda: ss.prefill(*ins, *prm, out=out), steps, warmup)
+    sec = float(np.median(per))
+    res["batch64"] = dict(workload="batch 64, L=2048", ms=float(np.mean(per) * 1e3), ms_median=sec * 1e3,
+                          mtok_s=64 * 2048 / sec / 1e6,
+                          valu_frac=64 * 2048 * D_INNER * SLOTS_PER_TC / sec / 1e12 / VALU_PEAK_TSLOTS)
+    del ins, out
     seed = synth.seed_for(4)
     p = synth.make_params(seed, D_INNER, D_STATE)
     prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
