@@ -67,7 +67,7 @@ ScanPath scan_path(int nseq, int d_inner, samba_dtype io)
         if (strcmp(e, "split") == 0) return ScanPath::kSplit;
         if (strcmp(e, "rows") == 0) return rows;
     }
-    constexpr size_t kLaneThreshold = 256ull * 4 * 64 * 4;  // lanes for 4 waves on each SIMD
+    constexpr size_t kLaneThreshold = 256ull * 4 * 64 * 2;  // lanes for 2 waves on each SIMD
     return static_cast<size_t>(nseq) * static_cast<size_t>(d_inner) < kLaneThreshold ? rows : ScanPath::kLane;
 }
 

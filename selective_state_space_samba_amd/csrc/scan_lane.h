@@ -9,8 +9,12 @@
 //    of one sequence, so they are read with scalar loads through the constant address space
 //    (the kernel never writes them) and widened on the scalar unit: no vector-memory or VALU
 //    work per state for them.
-//  * x, dt and z are read kAhead tokens ahead into a small register ring, so a token's
-//    loads have kAhead tokens of arithmetic to arrive.
+//  * x, dt and z are read kAhead tokens ahead into two register banks that take turns, so a
+//    token's loads have kAhead tokens of arithmetic to arrive and no register is copied;
+//    B and C are read one token ahead.
+//  * token rows are addressed through buffer resources rebased once per group of tokens,
+//    so the per-token address arithmetic is gone from the vector ALU and rows past the
+//    sequence end read as 0 without a clamp.
 #pragma once
 
 #include "scan_common.h"
@@ -24,31 +28,48 @@ constexpr int kAhead = 4;  // tokens of x / dt / z in flight
 template <class T>
 using ConstPtr = const __attribute__((address_space(4))) T *;
 
-// B_t and C_t (d_state = 16) as 32 uniform floats.
+// B_t and C_t (d_state = 16) as raw 32-bit words: 8 + 8 for bf16, 16 + 16 for fp32.
 template <class Io>
-__device__ inline void bc_row(const ScanArgs &a, size_t t, float *b, float *c)
-{
-    if constexpr (sizeof(typename Io::T) == 2) {
-        const ConstPtr<uint32_t> pb = (ConstPtr<uint32_t>)(static_cast<const uint16_t *>(a.B) + t * kMaxState);
-        const ConstPtr<uint32_t> pc = (ConstPtr<uint32_t>)(static_cast<const uint16_t *>(a.C) + t * kMaxState);
+struct BcWords {
+    static constexpr int kWords = kMaxState * static_cast<int>(sizeof(typename Io::T)) / 4;
+    uint32_t b[kWords], c[kWords];
+
+    __device__ inline void load(const ScanArgs &a, size_t t)
+    {
+        using T = typename Io::T;
+        const ConstPtr<uint32_t> pb = (ConstPtr<uint32_t>)(static_cast<const T *>(a.B) + t * kMaxState);
+        const ConstPtr<uint32_t> pc = (ConstPtr<uint32_t>)(static_cast<const T *>(a.C) + t * kMaxState);
 #pragma unroll
-        for (int k = 0; k < kMaxState / 2; ++k) {
-            const uint32_t wb = pb[k], wc = pc[k];
-            b[2 * k] = bf16lo(wb);
-            b[2 * k + 1] = bf16hi(wb);
-            c[2 * k] = bf16lo(wc);
-            c[2 * k + 1] = bf16hi(wc);
-        }
-    } else {
-        const ConstPtr<float> pb = (ConstPtr<float>)(static_cast<const float *>(a.B) + t * kMaxState);
-        const ConstPtr<float> pc = (ConstPtr<float>)(static_cast<const float *>(a.C) + t * kMaxState);
-#pragma unroll
-        for (int k = 0; k < kMaxState; ++k) {
+        for (int k = 0; k < kWords; ++k) {
             b[k] = pb[k];
             c[k] = pc[k];
         }
     }
-}
+
+    // Makes the loaded words available here (the wait for them goes here, not at the load).
+    __device__ inline void settle()
+    {
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) asm volatile("" : "+s"(b[k]), "+s"(c[k]));
+    }
+
+    // Widened to 16 + 16 uniform floats.
+    __device__ inline void widen(float *fb, float *fc) const
+    {
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) {
+            if constexpr (kWords == kMaxState / 2) {
+                fb[2 * k] = bf16lo(b[k]);
+                fb[2 * k + 1] = bf16hi(b[k]);
+                fc[2 * k] = bf16lo(c[k]);
+                fc[2 * k + 1] = bf16hi(c[k]);
+            } else {
+                fb[k] = __uint_as_float(b[k]);
+                fc[k] = __uint_as_float(c[k]);
+            }
+        }
+    }
+};
 
 }  // namespace lane
 
@@ -92,7 +113,7 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
     const T *zs = has_z ? static_cast<const T *>(a.z) : xs;
 
     // One token of the recurrence; B_t / C_t in b / c.
-    auto step = [&](size_t t, float xv, float dtv, float zv, const float *b, const float *c) {
+    auto step = [&](float xv, float dtv, float zv, const float *b, const float *c) -> float {
         float pre = __builtin_fmaf(w0, x0, cb);
         pre = __builtin_fmaf(w1, x1, pre);
         pre = __builtin_fmaf(w2, x2, pre);
@@ -111,43 +132,73 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
             h[n] = __builtin_fmaf(ab, h[n], du * b[n]);
             acc = __builtin_fmaf(c[n], h[n], acc);
         }
-        const float o = has_z ? acc * silu(zv) : acc;
-        Io::st(a.out, t * D + d, o);
+        return has_z ? acc * silu(zv) : acc;
     };
 
     if constexpr (kFullN) {
         if (t1 <= t0) goto done;  // empty sequence: nothing to read
-        // Token words kAhead tokens ahead (clamped re-loads past the end, never used).
+        // Token rows are addressed through buffer resources rebased on each group of kAhead
+        // tokens and sized to the rows the group touches (at most 2 kAhead, none past the
+        // sequence end): row i of the group is at the constant lane offset vo[i], loads past
+        // the end return 0 and are never used, and nothing is recomputed per token.
+        const uint32_t row = static_cast<uint32_t>(D) * sizeof(T);
+        uint32_t vo[2 * kAhead];
+#pragma unroll
+        for (int i = 0; i < 2 * kAhead; ++i) vo[i] = static_cast<uint32_t>(d) * sizeof(T) + i * row;
+        auto group_rsrc = [&](const void *p, size_t tg) {
+            const size_t rows = min(t1 - tg, static_cast<size_t>(2 * kAhead));
+            return make_rsrc(static_cast<const char *>(p) + tg * row, static_cast<uint32_t>(rows * row));
+        };
+        // x / dt / z words kAhead tokens ahead in two register banks that take turns (a group
+        // reads one bank while the next group's words arrive in the other: no copies), B / C
+        // words one token ahead.
+        struct Bank {
+            T x[kAhead], dt[kAhead], z[kAhead];
+        };
+        auto fill = [&](Bank &k, size_t tg, int first) {  // rows first .. first+kAhead-1 of group tg
+            const Rsrc gx = group_rsrc(xs, tg), gd = group_rsrc(dts, tg), gz = group_rsrc(zs, tg);
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) {
+                buf_ld(gx, vo[first + i], k.x[i]);
+                buf_ld(gd, vo[first + i], k.dt[i]);
+                buf_ld(gz, vo[first + i], k.z[i]);
+            }
+        };
         const size_t last = t1 - 1;
-        T rx[kAhead], rd[kAhead], rz[kAhead];
+        BcWords<Io> nw;
+        nw.load(a, t0);
+        auto token = [&](size_t t, T xr, T dr, T zr, Rsrc go, uint32_t voff) {
+            BcWords<Io> cw = nw;
+            if constexpr (BcWords<Io>::kWords == kMaxState / 2) cw.settle();  // wait here for the words loaded a token ago
+            nw.load(a, min(t + 1, last));
+            float b[kMaxState], c[kMaxState];
+            cw.widen(b, c);
+            buf_st(go, voff, step(to_f32(xr), to_f32(dr), to_f32(zr), b, c), static_cast<T *>(nullptr));
+        };
+        // kAhead tokens of group tg from bank k (only the first n when n < kAhead).
+        auto run = [&](const Bank &k, size_t tg, int n) {
+            const Rsrc go = group_rsrc(a.out, tg);
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) {
-            const size_t ix = min(t0 + i, last) * D + d;
-            rx[i] = xs[ix];
-            rd[i] = dts[ix];
-            rz[i] = zs[ix];
+            for (int i = 0; i < kAhead; ++i)
+                if (i < n) token(tg + i, k.x[i], k.dt[i], k.z[i], go, vo[i]);
+        };
+        Bank b0, b1;
+        fill(b0, t0, 0);
+        // Pairs of whole groups: straight-line code, no per-token branch.
+        size_t tg = t0;
+        for (; tg + 2 * kAhead <= t1; tg += 2 * kAhead) {
+            fill(b1, tg, kAhead);
+            run(b0, tg, kAhead);
+            fill(b0, tg + kAhead, kAhead);
+            run(b1, tg + kAhead, kAhead);
         }
-        for (size_t tg = t0; tg < t1; tg += kAhead) {
-            T cx[kAhead], cd[kAhead], cz[kAhead];
-#pragma unroll
-            for (int i = 0; i < kAhead; ++i) {
-                cx[i] = rx[i];
-                cd[i] = rd[i];
-                cz[i] = rz[i];
-                const size_t ix = min(tg + kAhead + i, last) * D + d;
-                rx[i] = xs[ix];
-                rd[i] = dts[ix];
-                rz[i] = zs[ix];
-            }
-#pragma unroll
-            for (int i = 0; i < kAhead; ++i) {
-                const size_t t = tg + i;
-                if (t < t1) {  // uniform: every lane of the workgroup is in the same sequence
-                    float b[kMaxState], c[kMaxState];
-                    bc_row<Io>(a, t, b, c);
-                    step(t, to_f32(cx[i]), to_f32(cd[i]), to_f32(cz[i]), b, c);
-                }
-            }
+        // The last t1 - tg < 2 kAhead tokens; rows tg .. tg+kAhead-1 are in b0.
+        if (tg + kAhead <= t1) {
+            fill(b1, tg, kAhead);
+            run(b0, tg, kAhead);
+            run(b1, tg + kAhead, static_cast<int>(t1 - tg - kAhead));
+        } else if (tg < t1) {
+            run(b0, tg, static_cast<int>(t1 - tg));
         }
     } else {
         for (size_t t = t0; t < t1; ++t) {
@@ -159,7 +210,7 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
                 b[n] = on ? Io::ld(a.B, t * N + n) : 0.0f;
                 c[n] = on ? Io::ld(a.C, t * N + n) : 0.0f;
             }
-            step(t, Io::ld(a.x, ix), Io::ld(a.dt, ix), has_z ? Io::ld(a.z, ix) : 0.0f, b, c);
+            Io::st(a.out, ix, step(Io::ld(a.x, ix), Io::ld(a.dt, ix), has_z ? Io::ld(a.z, ix) : 0.0f, b, c));
         }
     }
 

@@ -64,6 +64,11 @@ def test_training_length_prefill_4x4096():
     run_prefill_case(1, 4, 4096)
 
 
+def test_batch64_prefill_2048():
+    """Many mid-length sequences: the one-lane-per-channel kernel's shape."""
+    run_prefill_case(1, 64, 2048)
+
+
 def test_long_prompt_prefill_131072():
     y = run_prefill_case(2, 1, 131072)
     assert torch.isfinite(y.float()).all()
