@@ -59,6 +59,8 @@ def _declare(lib):
     lib.oracle_prefill.argtypes = [I, I, I, I] + [P] * 13
     lib.oracle_varlen.argtypes = [I, P, I, I] + [P] * 13
     lib.oracle_decode_step.argtypes = [I, I, I] + [P] * 13
+    lib.oracle_conv_silu_varlen.argtypes = [I, P, I, P, P, P, P, P]
+    lib.oracle_conv_silu_varlen.restype = None
     for f in (lib.oracle_scan_sequence, lib.oracle_prefill, lib.oracle_varlen, lib.oracle_decode_step):
         f.restype = None
 
@@ -196,6 +198,34 @@ def decode_step(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, hist, chan
     lib.oracle_decode_step(S, nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
                            _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h), _ptr(hist), _ptr(y))
     return y
+
+
+def conv_silu(x, conv_w, conv_b, conv0=None, cu_seqlens=None, chans=None):
+    """The short convolution + SiLU alone (the activation u a full layer feeds to x_proj).
+    Fixed length: x [b, L, D], conv0 [b, 3, D] or None.  Packed: x [T, D] with cu_seqlens
+    [nseq+1], conv0 [nseq, 3, D] or None.  Returns (u shaped like x restricted to
+    ``chans``, hist [nseq, 3, nch]) in float64; hist holds each sequence's last three
+    inputs, oldest first."""
+    lib = _load()
+    x = np.asarray(x)
+    if cu_seqlens is None:
+        b, L, D = x.shape
+        cu = (np.arange(b + 1) * L).astype(np.int32)
+        xt = x.reshape(b * L, D)
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        xt = x
+    nseq = cu.shape[0] - 1
+    xs = _f64(xt if chans is None else xt[:, chans])
+    nch = xs.shape[1]
+    _, _, _, wp, cbp = _params(None, None, None, conv_w, conv_b, chans)
+    hist = np.zeros((nseq, 3, nch)) if conv0 is None else \
+        _f64(np.asarray(conv0)[:, :, chans] if chans is not None else conv0).copy()
+    u = np.empty_like(xs)
+    lib.oracle_conv_silu_varlen(nseq, _ptr(cu), nch, _ptr(xs), _ptr(wp), _ptr(cbp), _ptr(hist), _ptr(u))
+    if cu_seqlens is None:
+        u = u.reshape(x.shape[0], x.shape[1], nch)
+    return u, hist
 
 
 def timed(fn, *args, **kw):

@@ -160,6 +160,50 @@ void oracle_decode_step(int nseq, int nch, int N,
     oracle_prefill(nseq, 1, nch, N, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, hist, y);
 }
 
+/*
+ * The short convolution and its SiLU alone, U = SiLU(DepthwiseConv(H, W_conv)) ([P1]
+ * "Input Projection and Short Convolution"; causal, tap k multiplying x[t-3+k], per [P4]
+ * Step 1): the activation a full layer feeds to its x_proj as well as to the scan.  One
+ * sequence of L tokens, conventions as in oracle_scan_sequence: x, u [L][ldx];
+ * hist [3][ldh] in: the 3 inputs before token 0 (oldest first), out: the last 3 inputs.
+ */
+void oracle_conv_silu_sequence(int L, int nch, int ldx, int ldh, const double *x,
+                               const double *conv_w, const double *conv_b, double *hist, double *u)
+{
+    int d;
+#pragma omp parallel for schedule(static)
+    for (d = 0; d < nch; ++d) {
+        double win[ORACLE_K]; /* win[0..2] = x[t-3..t-1], win[3] = x[t] */
+        const double *w = conv_w + (size_t)d * ORACLE_K;
+        const double cb = conv_b ? conv_b[d] : 0.0;
+        int t, k;
+        for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];
+        for (t = 0; t < L; ++t) {
+            const size_t ix = (size_t)t * ldx + d;
+            double pre = cb;
+            win[ORACLE_K - 1] = x[ix];
+            for (k = 0; k < ORACLE_K; ++k) pre += w[k] * win[k];
+            u[ix] = oracle_silu(pre);
+            for (k = 0; k < ORACLE_K - 1; ++k) win[k] = win[k + 1];
+        }
+        for (k = 0; k < ORACLE_K - 1; ++k) hist[(size_t)k * ldh + d] = win[k];
+    }
+}
+
+/* Packed sequences for the conv alone: sequence s covers tokens [cu[s], cu[s+1]) of x / u
+ * ([T][nch]); its history starts from hist[s] ([3][nch]; the caller zeroes it for fresh
+ * sequences) and ends there. */
+void oracle_conv_silu_varlen(int nseq, const int32_t *cu, int nch, const double *x,
+                             const double *conv_w, const double *conv_b, double *hist, double *u)
+{
+    int s;
+    for (s = 0; s < nseq; ++s) {
+        const size_t t0 = (size_t)cu[s];
+        oracle_conv_silu_sequence(cu[s + 1] - cu[s], nch, nch, nch, x + t0 * nch, conv_w, conv_b,
+                                  hist + (size_t)s * 3 * nch, u + t0 * nch);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -37,6 +37,10 @@ MUTANTS = {
     "dt_bias_dropped": ("delta = oracle_softplus(dt[ix] + bias);", "delta = oracle_softplus(dt[ix]);"),
     "silu_is_sigmoid": ("return v / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(-v));"),
     "state_not_carried_in": ("for (n = 0; n < N; ++n) hs[n] = h[(size_t)d * N + n];", "for (n = 0; n < N; ++n) hs[n] = 0.0;"),
+    "conv_alone_bias_dropped": ("double pre = cb;\n", "double pre = 0.0 * cb;\n"),
+    "conv_alone_current_token_late": (
+        "double pre = cb;\n            win[ORACLE_K - 1] = x[ix];\n            for (k = 0; k < ORACLE_K; ++k) pre += w[k] * win[k];",
+        "double pre = cb;\n            for (k = 0; k < ORACLE_K; ++k) pre += w[k] * win[k];\n            win[ORACLE_K - 1] = x[ix];"),
     "history_not_carried_in": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];",
                                "for (k = 0; k < ORACLE_K - 1; ++k) win[k] = 0.0;"),
 }

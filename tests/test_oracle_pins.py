@@ -112,6 +112,55 @@ def test_conv_single_tap_delays():
     np.testing.assert_allclose(y[0, 3:], np_silu(c["x"][0, :-3]), rtol=1e-14)
 
 
+# ---------------------------------------------------------------- P6b: the conv alone
+@pytest.mark.parametrize("with_hist", [False, True])
+def test_conv_silu_alone_matches_torch_conv1d(with_hist):
+    """The conv-only oracle (the activation u a full layer feeds to x_proj) against torch's
+    float64 depthwise conv1d + SiLU, batch of two, with and without an incoming history."""
+    rng = np.random.default_rng(61)
+    b, L, D = 2, 29, 6
+    x = rng.standard_normal((b, L, D))
+    w, cb = 0.5 * rng.standard_normal((D, 4)), 0.1 * rng.standard_normal(D)
+    h0 = rng.standard_normal((b, 3, D)) if with_hist else None
+    u, hist = oracle.conv_silu(x, w, cb, conv0=h0)
+    for s in range(b):
+        ref = torch_conv_silu(x[s], w, cb, None if h0 is None else h0[s])
+        np.testing.assert_allclose(u[s], ref, rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(hist[s], x[s, -3:, :])
+
+
+def test_conv_silu_alone_packed_short_sequences():
+    """Packed sequences of 0, 1, 2, 5 and 9 tokens: each restarts from its own history, and
+    the outgoing history of a sequence shorter than 3 tokens keeps the older history
+    entries (the window simply slides)."""
+    rng = np.random.default_rng(62)
+    lens = [0, 1, 2, 5, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    D = 4
+    x = rng.standard_normal((int(cu[-1]), D))
+    w, cb = 0.5 * rng.standard_normal((D, 4)), 0.1 * rng.standard_normal(D)
+    h0 = rng.standard_normal((len(lens), 3, D))
+    u, hist = oracle.conv_silu(x, w, cb, conv0=h0, cu_seqlens=cu)
+    for s, n in enumerate(lens):
+        xs = x[cu[s]:cu[s + 1]]
+        if n:
+            np.testing.assert_allclose(u[cu[s]:cu[s + 1]], torch_conv_silu(xs, w, cb, h0[s]), rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(hist[s], np.concatenate([h0[s], xs])[-3:])
+
+
+def test_conv_silu_alone_one_tap_shift():
+    """w = (0, 0, 1, 0), no bias: u_t = SiLU(x_{t-1}), with x_{-1} taken from the history."""
+    rng = np.random.default_rng(63)
+    L, D = 10, 3
+    x = rng.standard_normal((1, L, D))
+    w = np.zeros((D, 4))
+    w[:, 2] = 1.0
+    h0 = rng.standard_normal((1, 3, D))
+    u, _ = oracle.conv_silu(x, w, np.zeros(D), conv0=h0)
+    np.testing.assert_allclose(u[0, 0], np_silu(h0[0, 2]), rtol=1e-14)
+    np.testing.assert_allclose(u[0, 1:], np_silu(x[0, :-1]), rtol=1e-14)
+
+
 # ---------------------------------------------------------------- P1: geometric series
 @pytest.mark.parametrize("with_h0", [False, True])
 def test_constant_inputs_geometric_series(with_h0):
