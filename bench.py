@@ -185,8 +185,8 @@ def bench_decode(args, dev, S=256, P=256, warm_prefill=True, steps=None):
 
 
 def bench_extra(dev, steps=5, warmup=2):
-    """Training-length prefill (4 x 4096), batch 64 x 2048, and packed varlen (8 sequences,
-    <= 131072 tokens)."""
+    """Training-length prefill (4 x 4096), batch 64 x 2048, the conv alone on the long
+    prompt, and packed varlen (8 sequences, <= 131072 tokens)."""
     import torch
     import selective_state_space_samba_amd as ss
     from selective_state_space_samba_amd import synth
@@ -217,6 +217,28 @@ def bench_extra(dev, steps=5, warmup=2):
                           mtok_s=64 * 2048 / sec / 1e6,
                           valu_frac=64 * 2048 * D_INNER * SLOTS_PER_TC / sec / 1e12 / VALU_PEAK_TSLOTS)
     del ins, out
+    # The conv + SiLU alone on the long prompt (HBM-bound: x read, u written, 2 B each).
+    seed = synth.seed_for(2)
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    tk = synth.make_tokens(seed, (1, 131072), D_INNER, D_STATE, "bf16")
+    x = to_dev(tk.x, dev)
+    w, cb = to_dev(p.conv_w, dev, bf16=False), to_dev(p.conv_b, dev, bf16=False)
+    u = torch.empty_like(x)
+    cf = torch.empty((1, 3, D_INNER), dtype=torch.bfloat16, device=dev)
+    _, per = time_calls(lambda: ss.conv_silu(x, w, cb, out=u, conv_final=cf), steps, warmup)
+    sec = float(np.median(per))
+    nbytes = 131072 * D_INNER * 4
+    # the same bytes moved by a plain device copy (torch's copy kernel): the practical
+    # ceiling of a read-once, write-once stream on this GPU
+    _, cper = time_calls(lambda: u.copy_(x), steps, warmup)
+    copy_gbs = nbytes / float(np.median(cper)) / 1e9
+    res["conv_silu"] = dict(workload="conv + SiLU alone, batch 1, L=131072", ms=float(np.mean(per) * 1e3),
+                            ms_median=sec * 1e3, mtok_s=131072 / sec / 1e6,
+                            roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1), peak=HBM_PEAK_GBS,
+                                          unit="GB/s", frac=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                          bytes_per_launch=nbytes),
+                            copy_same_bytes_gbs=round(copy_gbs, 1), frac_of_copy=round(nbytes / sec / 1e9 / copy_gbs, 4))
+    del x, u
     seed = synth.seed_for(4)
     p = synth.make_params(seed, D_INNER, D_STATE)
     prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]

@@ -135,6 +135,27 @@ samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype i
                                const void *z, const samba_params *params,
                                float *h, void *conv_state, void *out, void *stream);
 
+/* The short causal convolution and its SiLU alone (page 1 section 3.4, "Input Projection
+ * and Short Convolution"): u_t = SiLU(conv_b + sum_k conv_w[k] x_{t-3+k}), the activation a
+ * full Mamba layer feeds to its x_proj (whose outputs dt, B, C the scan consumes).  The
+ * scan entry points recompute u from x internally; this call exists for x_proj's input.
+ *   cu_seqlens NULL: nseq sequences of seqlen tokens, x and u [nseq][seqlen][d_inner];
+ *              total_tokens is ignored.
+ *   cu_seqlens non-NULL (DEVICE int32 [nseq + 1], as for samba_scan_varlen): packed
+ *              sequences, x and u [total_tokens][d_inner]; seqlen is the longest
+ *              sequence (max_seqlen, sizes the launch).
+ *   conv_w [d_inner][4], conv_b [d_inner] (NULL = 0): float32, as in samba_params
+ *   conv0  [nseq][3][d_inner] (io dtype) history before each sequence; NULL = zeros
+ *   u      (io dtype) output; must not overlap x
+ *   conv_final [nseq][3][d_inner] (io dtype), may be NULL: each sequence's last three
+ *              inputs, oldest first (the history for the next chunk or for decode);
+ *              must not overlap conv0.
+ * Returns SAMBA_ERR_INVALID_ARG for negative sizes, NULL or misaligned required pointers
+ * and overlapping outputs; nseq == 0 is a no-op. */
+samba_status samba_conv_silu(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int d_inner,
+                             samba_dtype io, const void *x, const float *conv_w, const float *conv_b,
+                             const void *conv0, void *u, void *conv_final, void *stream);
+
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char *samba_last_error(void);

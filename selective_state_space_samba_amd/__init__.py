@@ -5,7 +5,7 @@ A thin ctypes layer over ``libsamba_scan.so`` (C ABI declared in
 and the current HIP stream; every step of the computation runs in the library's HIP
 kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
 
-Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``.
+Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode`` and ``conv_silu``.
 """
 from __future__ import annotations
 
@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "workspace_bytes", "lib_path", "SambaError", "version"]
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "workspace_bytes", "lib_path", "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
@@ -60,6 +60,8 @@ def load():
                                           P, Z, P]
         lib.samba_scan_decode.restype = I
         lib.samba_scan_decode.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P]
+        lib.samba_conv_silu.restype = I
+        lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -236,3 +238,42 @@ def decode(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, conv_state, *, 
         _ptr(out, "out", x.dtype, dev), _stream(dev))
     _check(st)
     return out
+
+
+def conv_silu(x, conv_w, conv_b=None, conv0=None, *, cu_seqlens=None, max_seqlen=None, out=None,
+              conv_final=None, want_state=True):
+    """The short causal conv + SiLU alone: u = SiLU(conv_b + sum_k conv_w[:, k] x_{t-3+k}),
+    the activation a full layer feeds to x_proj.  Fixed length: x [b, L, D], conv0
+    [b, 3, D] or None.  Packed: x [T, D] with cu_seqlens (int32 [nseq+1] on the GPU) and
+    ``max_seqlen`` (computed from cu_seqlens when not given, at the cost of a copy to the
+    host).  conv_w [D, 4], conv_b [D] float32.  Returns (u, conv_final [nseq, 3, D] or
+    None when want_state is False)."""
+    dev = _gpu_device(x)
+    io = _io(x)
+    f = torch.float32
+    if cu_seqlens is None:
+        b, L, D = x.shape
+        nseq, total = b, b * L
+    else:
+        T, D = x.shape
+        nseq = cu_seqlens.numel() - 1
+        total = T
+        _shape(cu_seqlens, (nseq + 1,), "cu_seqlens")
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+        L = int(max_seqlen)
+    if out is None:
+        out = torch.empty_like(x)
+    if want_state and conv_final is None:
+        conv_final = torch.empty((nseq, 3, D), dtype=x.dtype, device=dev)
+    _shape(out, tuple(x.shape), "out")
+    _shape(conv_w, (D, 4), "conv_w")
+    _shape(conv_b, (D,), "conv_b")
+    _shape(conv0, (nseq, 3, D), "conv0")
+    _shape(conv_final, (nseq, 3, D), "conv_final")
+    st = load().samba_conv_silu(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), L, total, D, io, _ptr(x, "x", x.dtype, dev),
+        _ptr(conv_w, "conv_w", f, dev), _ptr(conv_b, "conv_b", f, dev), _ptr(conv0, "conv0", x.dtype, dev),
+        _ptr(out, "out", x.dtype, dev), _ptr(conv_final, "conv_final", x.dtype, dev), _stream(dev))
+    _check(st)
+    return out, conv_final

@@ -11,6 +11,7 @@
 // kernels.  No CUDA, no compatibility layer: gfx950 only.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
@@ -23,6 +24,7 @@
 #include "scan_lane.h"
 #include "scan_split.h"
 #include "scan_decode.h"
+#include "scan_conv.h"
 
 
 namespace {
@@ -121,6 +123,14 @@ samba_status launched(const char *fn)
 }
 
 // Builds the argument block shared by every kernel.
+// Whether the byte ranges [p, p + pb) and [q, q + qb) share a byte.
+bool overlaps(const void *p, size_t pb, const void *q, size_t qb)
+{
+    if (p == nullptr || q == nullptr || pb == 0 || qb == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + qb && b < a + pb;
+}
+
 samba::ScanArgs make_args(int nseq, int seqlen, const int32_t *cu, int d_inner, int d_state,
                           const void *x, const void *dt, const void *B, const void *C, const void *z,
                           const samba_params *p, const float *h0, const void *conv0, void *out,
@@ -278,6 +288,65 @@ samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype i
         samba::launch_decode16(a, io, static_cast<hipStream_t>(stream));
     else
         samba::launch_lane_scan(a, io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+samba_status samba_conv_silu(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int d_inner,
+                             samba_dtype io, const void *x, const float *conv_w, const float *conv_b,
+                             const void *conv0, void *u, void *conv_final, void *stream)
+{
+    const char *fn = "samba_conv_silu";
+    if (nseq < 0 || seqlen < 0 || (cu_seqlens != nullptr && total_tokens < 0))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d seqlen=%d total_tokens=%d must be >= 0", fn, nseq, seqlen,
+                    total_tokens);
+    if (d_inner < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: d_inner=%d must be >= 1", fn, d_inner);
+    if (io != SAMBA_F32 && io != SAMBA_BF16) return fail(SAMBA_ERR_INVALID_ARG, "%s: unknown io dtype %d", fn, (int)io);
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    const size_t elem = io == SAMBA_BF16 ? 2 : 4;
+    size_t tokens;
+    if (cu_seqlens != nullptr) {
+        if (seqlen > total_tokens)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total_tokens=%d", fn, seqlen, total_tokens);
+        tokens = static_cast<size_t>(total_tokens);
+    } else {
+        tokens = static_cast<size_t>(nseq) * static_cast<size_t>(seqlen);
+        if (tokens > static_cast<size_t>(INT32_MAX))
+            return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq*seqlen=%zu exceeds 2^31-1 tokens", fn, tokens);
+    }
+    REQUIRE_PTR(conv_w, "conv_w");
+    OPTIONAL_PTR(conv_b, "conv_b");
+    if (tokens > 0) {
+        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(u, "u");
+    }
+    OPTIONAL_PTR(conv0, "conv0");
+    OPTIONAL_PTR(conv_final, "conv_final");
+    const size_t tok_bytes = tokens * static_cast<size_t>(d_inner) * elem;
+    const size_t hist_bytes = static_cast<size_t>(nseq) * 3 * static_cast<size_t>(d_inner) * elem;
+    if (overlaps(u, tok_bytes, x, tok_bytes))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: u overlaps x (runs of tokens re-read the rows before them)", fn);
+    if (overlaps(conv_final, hist_bytes, conv0, hist_bytes))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: conv_final overlaps conv0", fn);
+    const long long run = std::max<long long>(samba::conv::kMinRun, (static_cast<long long>(seqlen) + 65534) / 65535);
+    const long long nruns = std::max<long long>(1, (seqlen + run - 1) / run);
+    if (static_cast<long long>(nseq) * nruns > INT32_MAX)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d x %lld runs exceeds the launch limit", fn, nseq, nruns);
+    samba::ConvArgs a{};
+    a.nseq = nseq;
+    a.seqlen = seqlen;
+    a.cu = cu_seqlens;
+    a.total = total_tokens;
+    a.D = d_inner;
+    a.x = x;
+    a.conv_w = conv_w;
+    a.conv_b = conv_b;
+    a.conv0 = conv0;
+    a.u = u;
+    a.conv_final = conv_final;
+    samba::launch_conv_silu(a, io, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 

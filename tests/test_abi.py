@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("samba_scan_prefill", "samba_scan_varlen", "samba_scan_decode", "samba_last_error"):
+    for n in ("samba_scan_prefill", "samba_scan_varlen", "samba_scan_decode", "samba_conv_silu", "samba_last_error"):
         assert n in names
 
 
@@ -94,3 +94,25 @@ def test_binding_refuses_cpu_tensors_before_calling():
     with pytest.raises(ValueError, match="on a GPU"):
         ss.varlen(torch.zeros(2, dtype=torch.int32), x[0], x[0], Bm[0], Bm[0], x[0], torch.zeros((8, 16)), None,
                   None, torch.zeros((8, 4)), None, max_seqlen=4)
+
+
+def test_conv_silu_argument_errors():
+    lib = ss.load()
+    # nseq, cu, seqlen, total, D, io, x, conv_w, conv_b, conv0, u, conv_final, stream
+    assert lib.samba_conv_silu(1, None, 4, 0, 8, 1, 4096, None, None, None, 8192, None, None) == 1
+    assert b"conv_w is NULL" in lib.samba_last_error()
+    assert lib.samba_conv_silu(1, None, 4, 0, 8, 1, None, 4096, None, None, 8192, None, None) == 1
+    assert b"x is NULL" in lib.samba_last_error()
+    # u overlapping x (4 tokens x 8 channels x 2 bytes = 64 bytes)
+    assert lib.samba_conv_silu(1, None, 4, 0, 8, 1, 4096, 4096, None, None, 4096 + 48, None, None) == 1
+    assert b"overlaps x" in lib.samba_last_error()
+    # conv_final overlapping conv0 (3 x 8 x 2 = 48 bytes)
+    assert lib.samba_conv_silu(1, None, 4, 0, 8, 1, 4096, 4096, None, 1 << 20, 8192, (1 << 20) + 32, None) == 1
+    assert b"conv_final overlaps conv0" in lib.samba_last_error()
+    assert lib.samba_conv_silu(2, 4096, 11, 10, 8, 1, 4096, 4096, None, None, 8192, None, None) == 1
+    assert b"max_seqlen" in lib.samba_last_error()
+    assert lib.samba_conv_silu(-1, None, 4, 0, 8, 1, None, None, None, None, None, None, None) == 1
+    assert lib.samba_conv_silu(0, None, 4, 0, 8, 1, None, None, None, None, None, None, None) == 0
+    with pytest.raises(ValueError, match="on a GPU"):
+        import torch
+        ss.conv_silu(torch.zeros((1, 4, 8)), torch.zeros((8, 4)))

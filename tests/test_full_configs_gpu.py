@@ -74,6 +74,24 @@ def test_long_prompt_prefill_131072():
     assert torch.isfinite(y.float()).all()
 
 
+def test_long_prompt_conv_silu_alone():
+    """The conv-only entry point on the long prompt (the launch bench.py times)."""
+    seed = synth.seed_for(2)
+    print("case: conv alone, batch 1 L 131072", flush=True)
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (1, 131072), D, N, "bf16")
+    cb = (0.1 * np.random.default_rng(seed).standard_normal(D)).astype(np.float32)
+    u, cf = ss.conv_silu(bf16(tk.x), tf32(p.conv_w, DEV), tf32(cb, DEV))
+    chans = sample_channels(seed)
+    ci = torch.from_numpy(chans).to(DEV)
+    ug = u.index_select(2, ci).float().cpu().numpy()
+    cg = cf.index_select(2, ci).float().cpu().numpy()
+    torch.cuda.synchronize()
+    ur, cr = oracle.conv_silu(tk.x, p.conv_w, cb, chans=chans)
+    check("u", ug, ur)
+    np.testing.assert_array_equal(cg, cr)
+
+
 def test_long_prompt_is_bitwise_deterministic():
     seed = synth.seed_for(2)
     p = synth.make_params(seed, D, N)
