@@ -61,6 +61,8 @@ def _declare(lib):
     lib.oracle_decode_step.argtypes = [I, I, I] + [P] * 13
     lib.oracle_conv_silu_varlen.argtypes = [I, P, I, P, P, P, P, P]
     lib.oracle_conv_silu_varlen.restype = None
+    lib.oracle_backward.argtypes = [I, P, I, I] + [P] * 27
+    lib.oracle_backward.restype = None
     for f in (lib.oracle_scan_sequence, lib.oracle_prefill, lib.oracle_varlen, lib.oracle_decode_step):
         f.restype = None
 
@@ -226,6 +228,59 @@ def conv_silu(x, conv_w, conv_b, conv0=None, cu_seqlens=None, chans=None):
     if cu_seqlens is None:
         u = u.reshape(x.shape[0], x.shape[1], nch)
     return u, hist
+
+
+def backward(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, dout, h0=None, conv0=None,
+             dh_final=None, dconv_final=None, cu_seqlens=None, chans=None):
+    """Gradients of the layer (reverse-mode, from the same formulas as ``prefill``).  The
+    incoming gradients are dout (shaped like x), dh_final [nseq, D, N] and dconv_final
+    [nseq, 3, D] (None = zero).  Fixed length: x, dt, z, dout [b, L, D], B, C [b, L, N];
+    packed: [T, D] / [T, N] with cu_seqlens.  ``chans`` restricts the channels: token and
+    parameter gradients of those channels are exact, while dB and dC (sums over all
+    channels) are then only those channels' share.  Returns a dict of float64 arrays: dx,
+    ddt, dz (shaped like x, restricted to chans; dz None without a gate), dB, dC (shaped
+    like B), dA [nch, N], dD, ddt_bias, dconv_b [nch], dconv_w [nch, 4], dh0 [nseq, nch, N],
+    dconv0 [nseq, 3, nch]."""
+    lib = _load()
+    x = np.asarray(x)
+    fixed = cu_seqlens is None
+    if fixed:
+        b, L, D = x.shape
+        cu = (np.arange(b + 1) * L).astype(np.int32)
+        flat = lambda a: None if a is None else np.asarray(a).reshape((b * L,) + np.asarray(a).shape[2:])
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        flat = lambda a: None if a is None else np.asarray(a)
+    nseq = cu.shape[0] - 1
+    T = int(cu[-1])
+    N = np.asarray(B).shape[-1]
+    assert N <= 64
+    sel = (lambda a: None if a is None else _f64(a if chans is None else a[:, chans]))
+    xs, dts, zs, gs = sel(flat(x)), sel(flat(dt)), sel(flat(z)), sel(flat(dout))
+    nch = xs.shape[1]
+    Bs, Cs = _f64(flat(B)), _f64(flat(C))
+    Ap, Dp, bp, wp, cbp = _params(A, Dskip, dt_bias, conv_w, conv_b, chans)
+    per_seq = lambda a, shape, ax: np.zeros(shape) if a is None else \
+        _f64(np.take(np.asarray(a), chans, axis=ax) if chans is not None else a)
+    h0s = per_seq(h0, (nseq, nch, N), 1)
+    c0s = per_seq(conv0, (nseq, 3, nch), 2)
+    dhf = None if dh_final is None else per_seq(dh_final, None, 1)
+    dcf = None if dconv_final is None else per_seq(dconv_final, None, 2)
+    out = dict(dx=np.zeros((T, nch)), ddt=np.zeros((T, nch)), dz=None if zs is None else np.zeros((T, nch)),
+               dB=np.zeros((T, N)), dC=np.zeros((T, N)), dA=np.zeros((nch, N)), dD=np.zeros(nch),
+               ddt_bias=np.zeros(nch), dconv_w=np.zeros((nch, 4)), dconv_b=np.zeros(nch),
+               dh0=np.zeros((nseq, nch, N)), dconv0=np.zeros((nseq, 3, nch)))
+    lib.oracle_backward(nseq, _ptr(cu), nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
+                        _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h0s), _ptr(c0s), _ptr(gs), _ptr(dhf), _ptr(dcf),
+                        *[_ptr(out[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dA", "dD", "ddt_bias", "dconv_w",
+                                                 "dconv_b", "dh0", "dconv0")])
+    if fixed:
+        for k in ("dx", "ddt", "dz"):
+            if out[k] is not None:
+                out[k] = out[k].reshape(b, L, nch)
+        for k in ("dB", "dC"):
+            out[k] = out[k].reshape(b, L, N)
+    return out
 
 
 def timed(fn, *args, **kw):

@@ -35,6 +35,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #define ORACLE_K 4 /* short-convolution kernel size k = 4 ([P1] "Input Projection and Short Convolution") */
 
@@ -202,6 +203,192 @@ void oracle_conv_silu_varlen(int nseq, const int32_t *cu, int nch, const double 
         oracle_conv_silu_sequence(cu[s + 1] - cu[s], nch, nch, nch, x + t0 * nch, conv_w, conv_b,
                                   hist + (size_t)s * 3 * nch, u + t0 * nch);
     }
+}
+
+/*
+ * Gradients of one sequence (reverse-mode differentiation of oracle_scan_sequence, written
+ * step by step from the same formulas).  The loss is taken to be
+ *     sum_t dout[t] . y[t]  +  dh_final . h_final  +  dconv_final . hist_final,
+ * i.e. dout, dh_final and dconv_final are the incoming gradients of the layer output,
+ * the final state and the outgoing conv history (either of the last two may be NULL).
+ * Conventions as in oracle_scan_sequence; in addition
+ *   dout, dx, ddt, dz [L][ldx]   dz may be NULL when z is NULL
+ *   dB, dC [L][N]                accumulated (+=) over the channels
+ *   dA [nch][N], dD, ddt_bias, dconv_b [nch], dconv_w [nch][4]   accumulated (+=)
+ *   dh0 [nch][N], dconv0 [3][ldh]   overwritten: gradients of the initial state / history
+ * work must hold L * (N + 5) doubles (the recomputed forward values).
+ *
+ * For each token, in reverse: with G[n] = dLoss/dh_t[n] (from y_t and from h_{t+1}),
+ *   y_t = sum_n C h_t + D u_t, out = y SiLU(z):  dz = dout y SiLU'(z),  gy = dout SiLU(z)
+ *   G[n] = gy C_t[n] + (adjoint from h_{t+1}[n]);  dC_t[n] += gy h_t[n]
+ *   h_t = Abar h_{t-1} + Delta u B,  Abar = exp(Delta A):
+ *     dB_t[n] += G Delta u,  dA[n] += G Abar h_{t-1} Delta,  adjoint to h_{t-1}[n] = G Abar
+ *     dDelta = sum_n G (A Abar h_{t-1} + u B),  du = gy D + Delta sum_n G B
+ *   Delta = softplus(a), a = dt + b:  da = dDelta sigmoid(a) = ddt = (share of) ddt_bias
+ *   u = SiLU(pre):  dpre = du SiLU'(pre);  pre = b + sum_k w_k x_{t-3+k}:
+ *     dconv_b += dpre,  dconv_w[k] += dpre x_{t-3+k},  dx_{t-3+k} += w_k dpre
+ * with SiLU'(v) = s (1 + v (1 - s)), s = sigmoid(v).
+ */
+static double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+void oracle_backward_sequence(int L, int nch, int N, int ldx, int ldh,
+                              const double *x, const double *dt, const double *B, const double *C,
+                              const double *z, const double *A, const double *Dskip,
+                              const double *dt_bias, const double *conv_w, const double *conv_b,
+                              const double *h0, const double *hist0, const double *dout,
+                              const double *dh_final, const double *dconv_final,
+                              double *dx, double *ddt, double *dz, double *dB, double *dC,
+                              double *dA, double *dD, double *ddt_bias, double *dconv_w, double *dconv_b,
+                              double *dh0, double *dconv0, double *work)
+{
+    int d, t, n, k;
+    for (d = 0; d < nch; ++d) {
+        /* forward recompute: hs[t][n] = h_t[n]; pre, u, a, delta, y per token */
+        double *hs = work, *pre = work + (size_t)L * N, *u = pre + L, *av = u + L, *delta = av + L, *y = delta + L;
+        const double *w = conv_w + (size_t)d * ORACLE_K;
+        const double cb = conv_b ? conv_b[d] : 0.0;
+        const double dsk = Dskip ? Dskip[d] : 0.0;
+        const double bias = dt_bias ? dt_bias[d] : 0.0;
+        double hcur[64], R[64], P1, P2, P3;
+        for (n = 0; n < N; ++n) hcur[n] = h0[(size_t)d * N + n];
+        {
+            double win[ORACLE_K];
+            for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist0[(size_t)k * ldh + d];
+            for (t = 0; t < L; ++t) {
+                const size_t ix = (size_t)t * ldx + d;
+                double p = cb, acc = 0.0;
+                win[ORACLE_K - 1] = x[ix];
+                for (k = 0; k < ORACLE_K; ++k) p += w[k] * win[k];
+                for (k = 0; k < ORACLE_K - 1; ++k) win[k] = win[k + 1];
+                pre[t] = p;
+                u[t] = oracle_silu(p);
+                av[t] = dt[ix] + bias;
+                delta[t] = oracle_softplus(av[t]);
+                for (n = 0; n < N; ++n) {
+                    hcur[n] = exp(delta[t] * A[(size_t)d * N + n]) * hcur[n] + delta[t] * u[t] * B[(size_t)t * N + n];
+                    hs[(size_t)t * N + n] = hcur[n];
+                    acc += C[(size_t)t * N + n] * hcur[n];
+                }
+                y[t] = acc + dsk * u[t];
+            }
+        }
+        /* reverse */
+        for (n = 0; n < N; ++n) R[n] = dh_final ? dh_final[(size_t)d * N + n] : 0.0;
+        /* P1, P2, P3: pending gradient of x_{t}, x_{t-1}, x_{t-2} before step t */
+        P1 = dconv_final ? dconv_final[(size_t)2 * ldh + d] : 0.0;
+        P2 = dconv_final ? dconv_final[(size_t)1 * ldh + d] : 0.0;
+        P3 = dconv_final ? dconv_final[(size_t)0 * ldh + d] : 0.0;
+        for (t = L - 1; t >= 0; --t) {
+            const size_t ix = (size_t)t * ldx + d;
+            double gy, du, S1 = 0.0, S2 = 0.0, ddel, da, sp, dpre, xin[ORACLE_K];
+            if (z) {
+                const double sz = sigm(z[ix]);
+                dz[ix] = dout[ix] * y[t] * sz * (1.0 + z[ix] * (1.0 - sz));
+                gy = dout[ix] * z[ix] * sz;
+            } else {
+                gy = dout[ix];
+            }
+            dD[d] += gy * u[t];
+            du = gy * dsk;
+            for (n = 0; n < N; ++n) {
+                const double an = A[(size_t)d * N + n];
+                const double abar = exp(delta[t] * an);
+                const double hp = t > 0 ? hs[(size_t)(t - 1) * N + n] : h0[(size_t)d * N + n];
+                const double G = gy * C[(size_t)t * N + n] + R[n];
+                dC[(size_t)t * N + n] += gy * hs[(size_t)t * N + n];
+                dB[(size_t)t * N + n] += G * delta[t] * u[t];
+                dA[(size_t)d * N + n] += G * abar * hp * delta[t];
+                S1 += G * an * abar * hp;
+                S2 += G * B[(size_t)t * N + n];
+                R[n] = G * abar;
+            }
+            ddel = S1 + u[t] * S2;
+            du += delta[t] * S2;
+            da = ddel * sigm(av[t]);
+            ddt[ix] = da;
+            ddt_bias[d] += da;
+            sp = sigm(pre[t]);
+            dpre = du * sp * (1.0 + pre[t] * (1.0 - sp));
+            dconv_b[d] += dpre;
+            for (k = 0; k < ORACLE_K; ++k) {
+                const int tk = t - 3 + k;
+                xin[k] = tk >= 0 ? x[(size_t)tk * ldx + d] : hist0[(size_t)(tk + 3) * ldh + d];
+                dconv_w[(size_t)d * ORACLE_K + k] += dpre * xin[k];
+            }
+            dx[ix] = P1 + w[3] * dpre;
+            P1 = P2 + w[2] * dpre;
+            P2 = P3 + w[1] * dpre;
+            P3 = w[0] * dpre;
+        }
+        for (n = 0; n < N; ++n) dh0[(size_t)d * N + n] = R[n];
+        dconv0[(size_t)0 * ldh + d] = P3;
+        dconv0[(size_t)1 * ldh + d] = P2;
+        dconv0[(size_t)2 * ldh + d] = P1;
+    }
+}
+
+/* Packed sequences (cu as in oracle_varlen; fixed length is cu[s] = s * L): arrays as in
+ * oracle_backward_sequence with the token arrays packed [T][nch] / [T][N], and h0, hist0,
+ * dh_final, dconv_final, dh0, dconv0 per sequence ([nseq][nch][N], [nseq][3][nch]).
+ * Parameter gradients are summed over the sequences.  Channels are split over threads;
+ * each thread accumulates its own dB / dC, and the per-thread sums are added in thread
+ * order afterwards. */
+void oracle_backward(int nseq, const int32_t *cu, int nch, int N,
+                     const double *x, const double *dt, const double *B, const double *C,
+                     const double *z, const double *A, const double *Dskip,
+                     const double *dt_bias, const double *conv_w, const double *conv_b,
+                     const double *h0, const double *hist0, const double *dout,
+                     const double *dh_final, const double *dconv_final,
+                     double *dx, double *ddt, double *dz, double *dB, double *dC,
+                     double *dA, double *dD, double *ddt_bias, double *dconv_w, double *dconv_b,
+                     double *dh0, double *dconv0)
+{
+    const int T = cu[nseq];
+    int maxL = 0, s, nt = 1, i, th;
+    double **lB, **lC;
+    for (s = 0; s < nseq; ++s)
+        if (cu[s + 1] - cu[s] > maxL) maxL = cu[s + 1] - cu[s];
+#ifdef _OPENMP
+    {
+        extern int omp_get_max_threads(void);
+        nt = omp_get_max_threads();
+    }
+#endif
+    if (nt > nch) nt = nch > 0 ? nch : 1;
+    lB = (double **)calloc((size_t)nt, sizeof(double *));
+    lC = (double **)calloc((size_t)nt, sizeof(double *));
+#pragma omp parallel for schedule(static, 1) num_threads(nt)
+    for (th = 0; th < nt; ++th) {
+        const int d0 = (int)((long long)nch * th / nt), d1 = (int)((long long)nch * (th + 1) / nt);
+        double *work = (double *)calloc((size_t)maxL * (N + 5) + 1, sizeof(double));
+        int ss;
+        lB[th] = (double *)calloc((size_t)T * N + 1, sizeof(double));
+        lC[th] = (double *)calloc((size_t)T * N + 1, sizeof(double));
+        for (ss = 0; ss < nseq && d1 > d0; ++ss) {
+            const size_t t0 = (size_t)cu[ss];
+            const int L = cu[ss + 1] - cu[ss];
+            const size_t o = t0 * nch + d0, oh = (size_t)ss * nch * N + (size_t)d0 * N, oc = (size_t)ss * 3 * nch + d0;
+            oracle_backward_sequence(L, d1 - d0, N, nch, nch, x + o, dt + o, B + t0 * N, C + t0 * N,
+                                     z ? z + o : NULL, A + (size_t)d0 * N, Dskip ? Dskip + d0 : NULL,
+                                     dt_bias ? dt_bias + d0 : NULL, conv_w + (size_t)d0 * ORACLE_K,
+                                     conv_b ? conv_b + d0 : NULL, h0 + oh, hist0 + oc, dout + o,
+                                     dh_final ? dh_final + oh : NULL, dconv_final ? dconv_final + oc : NULL,
+                                     dx + o, ddt + o, dz ? dz + o : NULL, lB[th] + t0 * N, lC[th] + t0 * N,
+                                     dA + (size_t)d0 * N, dD + d0, ddt_bias + d0, dconv_w + (size_t)d0 * ORACLE_K,
+                                     dconv_b + d0, dh0 + oh, dconv0 + oc, work);
+        }
+        free(work);
+    }
+    for (th = 0; th < nt; ++th) {
+        for (i = 0; i < T * N; ++i) {
+            dB[i] += lB[th][i];
+            dC[i] += lC[th][i];
+        }
+        free(lB[th]);
+        free(lC[th]);
+    }
+    free(lB);
+    free(lC);
 }
 
 int oracle_max_threads(void)

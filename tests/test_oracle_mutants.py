@@ -41,6 +41,19 @@ MUTANTS = {
     "conv_alone_current_token_late": (
         "double pre = cb;\n            win[ORACLE_K - 1] = x[ix];\n            for (k = 0; k < ORACLE_K; ++k) pre += w[k] * win[k];",
         "double pre = cb;\n            for (k = 0; k < ORACLE_K; ++k) pre += w[k] * win[k];\n            win[ORACLE_K - 1] = x[ix];"),
+    "bwd_adjoint_not_decayed": ("R[n] = G * abar;", "R[n] = G;"),
+    "bwd_dA_without_delta": ("dA[(size_t)d * N + n] += G * abar * hp * delta[t];",
+                             "dA[(size_t)d * N + n] += G * abar * hp;"),
+    "bwd_gate_derivative_sigmoid_only": ("dz[ix] = dout[ix] * y[t] * sz * (1.0 + z[ix] * (1.0 - sz));",
+                                         "dz[ix] = dout[ix] * y[t] * sz;"),
+    "bwd_silu_derivative_dropped": ("dpre = du * sp * (1.0 + pre[t] * (1.0 - sp));", "dpre = du * sp;"),
+    "bwd_conv_transpose_taps_reversed": ("dx[ix] = P1 + w[3] * dpre;", "dx[ix] = P1 + w[0] * dpre;"),
+    "bwd_dB_missing_u": ("dB[(size_t)t * N + n] += G * delta[t] * u[t];", "dB[(size_t)t * N + n] += G * delta[t];"),
+    "bwd_du_missing_skip": ("du = gy * dsk;", "du = 0.0;"),
+    "bwd_previous_state_is_current": (
+        "const double hp = t > 0 ? hs[(size_t)(t - 1) * N + n] : h0[(size_t)d * N + n];",
+        "const double hp = hs[(size_t)t * N + n];"),
+    "bwd_softplus_derivative_dropped": ("da = ddel * sigm(av[t]);", "da = ddel;"),
     "history_not_carried_in": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];",
                                "for (k = 0; k < ORACLE_K - 1; ++k) win[k] = 0.0;"),
 }
@@ -57,6 +70,8 @@ def _run_pins():
             variants = [{"with_hist": False}, {"with_hist": True}]
         if "with_h0" in params:
             variants = [{"with_h0": False}, {"with_h0": True}]
+        if "gate" in params:
+            variants = [{"gate": True}, {"gate": False}]
         for kw in variants:
             try:
                 fn(**kw)

@@ -406,3 +406,79 @@ def test_no_gate_equals_unit_gate_division():
     c2["z"] = None
     y, _, _ = run_prefill(c2)
     np.testing.assert_allclose(yg, y * np_silu(c["z"]), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------- P9: gradients
+def _fd_check(case, packed_lens=None, eps=1e-6, tol=2e-7):
+    """Every gradient of oracle.backward against central finite differences of the
+    forward oracle, for the loss sum(dout * y) + sum(dh_final * h_final) +
+    sum(dconv_final * hist_final).  The finite differences use only the forward oracle, so
+    they pin the backward formulas independently."""
+    c = case
+    names = ["x", "dt", "B", "C", "z", "A", "Dskip", "dt_bias", "conv_w", "conv_b", "h0", "conv0"]
+
+    def loss(v):
+        if packed_lens is None:
+            y, h, hist = oracle.prefill(v["x"], v["dt"], v["B"], v["C"], v["z"], v["A"], v["Dskip"], v["dt_bias"],
+                                        v["conv_w"], v["conv_b"], h0=v["h0"], conv0=v["conv0"])
+        else:
+            y, h, hist = oracle.varlen(c["cu"], v["x"], v["dt"], v["B"], v["C"], v["z"], v["A"], v["Dskip"],
+                                       v["dt_bias"], v["conv_w"], v["conv_b"], h0=v["h0"], conv0=v["conv0"])
+        return float(np.sum(c["dout"] * y) + np.sum(c["dh_final"] * h) + np.sum(c["dconv_final"] * hist))
+
+    g = oracle.backward(c["x"], c["dt"], c["B"], c["C"], c["z"], c["A"], c["Dskip"], c["dt_bias"], c["conv_w"],
+                        c["conv_b"], c["dout"], h0=c["h0"], conv0=c["conv0"], dh_final=c["dh_final"],
+                        dconv_final=c["dconv_final"], cu_seqlens=c.get("cu"))
+    gname = dict(x="dx", dt="ddt", B="dB", C="dC", z="dz", A="dA", Dskip="dD", dt_bias="ddt_bias",
+                 conv_w="dconv_w", conv_b="dconv_b", h0="dh0", conv0="dconv0")
+    for nm in names:
+        if c[nm] is None:
+            continue
+        base = {k: (None if c[k] is None else np.array(c[k], dtype=np.float64)) for k in names}
+        fd = np.zeros_like(base[nm])
+        flat = base[nm].reshape(-1)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + eps
+            lp = loss(base)
+            flat[i] = keep - eps
+            lm = loss(base)
+            flat[i] = keep
+            fd.reshape(-1)[i] = (lp - lm) / (2 * eps)
+        got = np.asarray(g[gname[nm]]).reshape(fd.shape)
+        err = np.max(np.abs(got - fd)) / (np.max(np.abs(fd)) + 1e-30)
+        assert err < tol, (nm, err)
+
+
+def _grad_case(rng, b, L, D, N, gate=True, packed_lens=None):
+    if packed_lens is not None:
+        T = int(sum(packed_lens))
+        lead = (T,)
+        nseq = len(packed_lens)
+    else:
+        lead = (b, L)
+        nseq = b
+    c = dict(
+        x=rng.standard_normal(lead + (D,)), dt=0.5 * rng.standard_normal(lead + (D,)),
+        z=rng.standard_normal(lead + (D,)) if gate else None, B=rng.standard_normal(lead + (N,)),
+        C=rng.standard_normal(lead + (N,)),
+        A=-np.exp(np.log(np.arange(1, N + 1))[None, :] + 0.3 * rng.standard_normal((D, N))),
+        Dskip=1.0 + 0.1 * rng.standard_normal(D), dt_bias=0.3 * rng.standard_normal(D),
+        conv_w=0.5 * rng.standard_normal((D, 4)), conv_b=0.1 * rng.standard_normal(D),
+        h0=rng.standard_normal((nseq, D, N)), conv0=rng.standard_normal((nseq, 3, D)),
+        dout=rng.standard_normal(lead + (D,)), dh_final=rng.standard_normal((nseq, D, N)),
+        dconv_final=rng.standard_normal((nseq, 3, D)))
+    if packed_lens is not None:
+        c["cu"] = np.concatenate([[0], np.cumsum(packed_lens)]).astype(np.int32)
+    return c
+
+
+@pytest.mark.parametrize("gate", [True, False])
+def test_backward_matches_finite_differences(gate):
+    _fd_check(_grad_case(np.random.default_rng(90), 2, 6, 3, 4, gate=gate))
+
+
+def test_backward_packed_short_sequences_match_finite_differences():
+    """Packed sequences of 0, 1, 2 and 5 tokens: gradients reach the incoming history and
+    state through sequences shorter than the conv window."""
+    _fd_check(_grad_case(np.random.default_rng(91), None, None, 2, 3, packed_lens=[0, 1, 2, 5]), packed_lens=True)
