@@ -156,6 +156,43 @@ samba_status samba_conv_silu(int nseq, const int32_t *cu_seqlens, int seqlen, in
                              samba_dtype io, const void *x, const float *conv_w, const float *conv_b,
                              const void *conv0, void *u, void *conv_final, void *stream);
 
+/* Size in bytes of the device workspace samba_scan_backward needs (nseq sequences of at
+ * most seqlen tokens, total_tokens tokens in all). */
+size_t samba_scan_backward_workspace_bytes(int nseq, int seqlen, int total_tokens, int d_inner, int d_state);
+
+/* Gradients of the layer for training: reverse-mode differentiation of the computation
+ * above (page 1 section 3.4, the steps from "Input Projection and Short Convolution" to
+ * "Gated Output"; the pages train the model at 4K tokens, "Training Configurations and
+ * Scaling").  The loss is taken as sum(dout . out) + sum(dh_final . h_final) +
+ * sum(dconv_final . conv_final): dout is the gradient of the layer output, dh_final and
+ * dconv_final (NULL = zero) those of the final state and outgoing conv history.
+ *   cu_seqlens NULL: nseq sequences of seqlen tokens (token tensors [nseq][seqlen][...]);
+ *              total_tokens is ignored.  Non-NULL: packed as for samba_scan_varlen, seqlen
+ *              = the longest sequence.
+ *   x, dt, B, C, z, params, h0, conv0: the forward call's inputs (the forward is
+ *              recomputed; nothing from the forward call is needed)
+ *   dout [tokens][d_inner] (io dtype); dh_final [nseq][d_inner][d_state] float32;
+ *   dconv_final [nseq][3][d_inner] (io dtype)
+ * Outputs (overwritten, not accumulated):
+ *   dx, ddt, dz [tokens][d_inner], dB, dC [tokens][d_state]   io dtype; dz required when
+ *              z is given (ignored otherwise)
+ *   dA [d_inner][d_state], dD, ddt_bias, dconv_b [d_inner], dconv_w [d_inner][4]   float32,
+ *              summed over all sequences and tokens (dD / ddt_bias / dconv_b are the
+ *              gradients of a zero parameter when its pointer in params is NULL)
+ *   dh0 [nseq][d_inner][d_state] float32, dconv0 [nseq][3][d_inner] io dtype: gradients of
+ *              the initial state and history; either may be NULL
+ *   workspace: at least samba_scan_backward_workspace_bytes() bytes, 256-byte aligned,
+ *              contents irrelevant (SAMBA_ERR_WORKSPACE otherwise)
+ * Outputs must not overlap inputs or each other.  Limits: nseq <= 65535 and seqlen <=
+ * 65535 * 16 (SAMBA_ERR_UNSUPPORTED beyond). */
+samba_status samba_scan_backward(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int d_inner,
+                                 int d_state, samba_dtype io, const void *x, const void *dt, const void *B,
+                                 const void *C, const void *z, const samba_params *params, const float *h0,
+                                 const void *conv0, const void *dout, const float *dh_final,
+                                 const void *dconv_final, void *dx, void *ddt, void *dB, void *dC, void *dz,
+                                 float *dA, float *dD, float *ddt_bias, float *dconv_w, float *dconv_b,
+                                 float *dh0, void *dconv0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char *samba_last_error(void);

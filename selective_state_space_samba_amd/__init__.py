@@ -5,7 +5,8 @@ A thin ctypes layer over ``libsamba_scan.so`` (C ABI declared in
 and the current HIP stream; every step of the computation runs in the library's HIP
 kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
 
-Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode`` and ``conv_silu``.
+Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``, ``conv_silu`` and
+``backward``.
 """
 from __future__ import annotations
 
@@ -15,7 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "workspace_bytes", "lib_path", "SambaError", "version"]
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "workspace_bytes", "lib_path", "SambaError",
+           "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
@@ -60,6 +62,11 @@ def load():
                                           P, Z, P]
         lib.samba_scan_decode.restype = I
         lib.samba_scan_decode.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P]
+        lib.samba_scan_backward_workspace_bytes.restype = Z
+        lib.samba_scan_backward_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.samba_scan_backward.restype = I
+        lib.samba_scan_backward.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P,
+                                            P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.samba_conv_silu.restype = I
         lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
         _lib = lib
@@ -277,3 +284,59 @@ def conv_silu(x, conv_w, conv_b=None, conv0=None, *, cu_seqlens=None, max_seqlen
         _ptr(out, "out", x.dtype, dev), _ptr(conv_final, "conv_final", x.dtype, dev), _stream(dev))
     _check(st)
     return out, conv_final
+
+
+def backward(dout, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, *,
+             dh_final=None, dconv_final=None, cu_seqlens=None, max_seqlen=None, want_state_grads=True,
+             workspace=None):
+    """Gradients of the layer.  dout is the gradient of the output (shaped like x); dh_final
+    [nseq, D, N] and dconv_final [nseq, 3, D] those of the final state and history (None =
+    zero).  Fixed length: x, dt, z, dout [b, L, D], B, C [b, L, N]; packed: [T, D] / [T, N]
+    with cu_seqlens (int32 [nseq+1] on the GPU) and max_seqlen.  Returns a dict: dx, ddt,
+    dz (None without a gate), dB, dC (I/O dtype, shaped like their inputs), dA, dD,
+    ddt_bias, dconv_w, dconv_b (float32, summed over sequences), dh0, dconv0 (None when
+    want_state_grads is False)."""
+    dev = _gpu_device(x)
+    io = _io(x)
+    f = torch.float32
+    N = B.shape[-1]
+    if cu_seqlens is None:
+        b, L, D = x.shape
+        nseq, total = b, b * L
+    else:
+        T, D = x.shape
+        nseq = cu_seqlens.numel() - 1
+        total = T
+        _shape(cu_seqlens, (nseq + 1,), "cu_seqlens")
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+        L = int(max_seqlen)
+    for t, n in ((dt, "dt"), (z, "z"), (dout, "dout")):
+        _shape(t, tuple(x.shape), n)
+    _shape(C, tuple(B.shape), "C")
+    _shape(h0, (nseq, D, N), "h0")
+    _shape(conv0, (nseq, 3, D), "conv0")
+    _shape(dh_final, (nseq, D, N), "dh_final")
+    _shape(dconv_final, (nseq, 3, D), "dconv_final")
+    p = _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N)
+    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(x), dz=None if z is None else torch.empty_like(x),
+             dB=torch.empty_like(B), dC=torch.empty_like(C), dA=torch.empty((D, N), dtype=f, device=dev),
+             dD=torch.empty(D, dtype=f, device=dev), ddt_bias=torch.empty(D, dtype=f, device=dev),
+             dconv_w=torch.empty((D, 4), dtype=f, device=dev), dconv_b=torch.empty(D, dtype=f, device=dev),
+             dh0=torch.empty((nseq, D, N), dtype=f, device=dev) if want_state_grads else None,
+             dconv0=torch.empty((nseq, 3, D), dtype=x.dtype, device=dev) if want_state_grads else None)
+    need = int(load().samba_scan_backward_workspace_bytes(nseq, L, total, D, N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    st = load().samba_scan_backward(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), L, total, D, N, io,
+        _ptr(x, "x", x.dtype, dev), _ptr(dt, "dt", x.dtype, dev), _ptr(B, "B", x.dtype, dev),
+        _ptr(C, "C", x.dtype, dev), _ptr(z, "z", x.dtype, dev), ctypes.byref(p),
+        _ptr(h0, "h0", f, dev), _ptr(conv0, "conv0", x.dtype, dev), _ptr(dout, "dout", x.dtype, dev),
+        _ptr(dh_final, "dh_final", f, dev), _ptr(dconv_final, "dconv_final", x.dtype, dev),
+        *[_ptr(g[k], k) for k in ("dx", "ddt", "dB", "dC", "dz", "dA", "dD", "ddt_bias", "dconv_w", "dconv_b",
+                                  "dh0", "dconv0")],
+        _ptr(workspace, "workspace"), wsb, _stream(dev))
+    _check(st)
+    return g

@@ -25,6 +25,7 @@
 #include "scan_split.h"
 #include "scan_decode.h"
 #include "scan_conv.h"
+#include "scan_bwd.h"
 
 
 namespace {
@@ -347,6 +348,112 @@ samba_status samba_conv_silu(int nseq, const int32_t *cu_seqlens, int seqlen, in
     a.u = u;
     a.conv_final = conv_final;
     samba::launch_conv_silu(a, io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+size_t samba_scan_backward_workspace_bytes(int nseq, int seqlen, int total_tokens, int d_inner, int d_state)
+{
+    (void)d_state;
+    if (nseq <= 0 || seqlen < 0 || total_tokens < 0 || d_inner <= 0) return 0;
+    return samba::bwd_workspace(nseq, seqlen, total_tokens, d_inner).total_bytes;
+}
+
+samba_status samba_scan_backward(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int d_inner,
+                                 int d_state, samba_dtype io, const void *x, const void *dt, const void *B,
+                                 const void *C, const void *z, const samba_params *params, const float *h0,
+                                 const void *conv0, const void *dout, const float *dh_final,
+                                 const void *dconv_final, void *dx, void *ddt, void *dB, void *dC, void *dz,
+                                 float *dA, float *dD, float *ddt_bias, float *dconv_w, float *dconv_b,
+                                 float *dh0, void *dconv0, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "samba_scan_backward";
+    if (nseq < 0 || seqlen < 0 || (cu_seqlens != nullptr && total_tokens < 0))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d seqlen=%d total_tokens=%d must be >= 0", fn, nseq, seqlen,
+                    total_tokens);
+    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    if (st != SAMBA_OK) return st;
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    size_t tokens;
+    if (cu_seqlens != nullptr) {
+        if (seqlen > total_tokens)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total_tokens=%d", fn, seqlen, total_tokens);
+        tokens = static_cast<size_t>(total_tokens);
+    } else {
+        tokens = static_cast<size_t>(nseq) * static_cast<size_t>(seqlen);
+        if (tokens > static_cast<size_t>(INT32_MAX))
+            return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq*seqlen=%zu exceeds 2^31-1 tokens", fn, tokens);
+    }
+    if (nseq > 65535 || (seqlen + samba::bwd::kChunk - 1) / samba::bwd::kChunk > 65535)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d or seqlen=%d exceeds the launch limits (65535 sequences, "
+                    "65535 chunks of %d tokens)", fn, nseq, seqlen, samba::bwd::kChunk);
+    if (tokens > 0) {
+        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(dt, "dt");
+        REQUIRE_PTR(B, "B");
+        REQUIRE_PTR(C, "C");
+        REQUIRE_PTR(dout, "dout");
+        REQUIRE_PTR(dx, "dx");
+        REQUIRE_PTR(ddt, "ddt");
+        REQUIRE_PTR(dB, "dB");
+        REQUIRE_PTR(dC, "dC");
+        OPTIONAL_PTR(z, "z");
+        if (z != nullptr) REQUIRE_PTR(dz, "dz");
+    }
+    REQUIRE_PTR(dA, "dA");
+    REQUIRE_PTR(dD, "dD");
+    REQUIRE_PTR(ddt_bias, "ddt_bias");
+    REQUIRE_PTR(dconv_w, "dconv_w");
+    REQUIRE_PTR(dconv_b, "dconv_b");
+    OPTIONAL_PTR(h0, "h0");
+    OPTIONAL_PTR(conv0, "conv0");
+    OPTIONAL_PTR(dh_final, "dh_final");
+    OPTIONAL_PTR(dconv_final, "dconv_final");
+    OPTIONAL_PTR(dh0, "dh0");
+    OPTIONAL_PTR(dconv0, "dconv0");
+    const size_t need = samba::bwd_workspace(nseq, seqlen, static_cast<int>(tokens), d_inner).total_bytes;
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    samba::BwdArgs a{};
+    a.nseq = nseq;
+    a.seqlen = seqlen;
+    a.cu = cu_seqlens;
+    a.total = static_cast<int>(tokens);
+    a.D = d_inner;
+    a.N = d_state;
+    a.x = x;
+    a.dt = dt;
+    a.B = B;
+    a.C = C;
+    a.z = z;
+    a.A = params->A;
+    a.Dskip = params->D;
+    a.dt_bias = params->dt_bias;
+    a.conv_w = params->conv_w;
+    a.conv_b = params->conv_b;
+    a.h0 = h0;
+    a.conv0 = conv0;
+    a.dout = dout;
+    a.dh_final = dh_final;
+    a.dconv_final = dconv_final;
+    a.dx = dx;
+    a.ddt = ddt;
+    a.dB = dB;
+    a.dC = dC;
+    a.dz = dz;
+    a.dA = dA;
+    a.dD = dD;
+    a.ddt_bias = ddt_bias;
+    a.dconv_w = dconv_w;
+    a.dconv_b = dconv_b;
+    a.dh0 = dh0;
+    a.dconv0 = dconv0;
+    samba::launch_backward(a, static_cast<float *>(workspace), io, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 

@@ -1,0 +1,691 @@
+// scan_bwd.h -- gradients of the selective-scan layer core (training).
+//
+// Reverse-mode differentiation of the recurrence of page 1 section 3.4 ("Input Projection
+// and Short Convolution" ... "Gated Output"): for the loss sum(dout . out) + dh_final .
+// h_final + dconv_final . conv_final, with G_t[n] = dLoss/dh_t[n],
+//   gy = dout SiLU(z),  dz = dout y SiLU'(z),  G_t = gy C_t + Abar_{t+1} G_{t+1},
+//   dC_t[n] += gy h_t[n],  dB_t[n] += G Delta u,  dA[n] += G Abar h_{t-1} Delta,
+//   dDelta = sum_n G (A Abar h_{t-1} + u B),  du = gy D + Delta sum_n G B,
+//   ddt = dDelta sigmoid(dt + b),  dpre = du SiLU'(pre),
+//   dx_{t-3+k} += w_k dpre,  dconv_w[k] += dpre x_{t-3+k},  dconv_b += dpre.
+//
+// Parallel in time: the sequence is cut into chunks of kChunk tokens and every (sequence,
+// chunk, channel) gets a lane (one lane per channel, the 16 states in registers, as in the
+// lane prefill kernel), so a training batch of 4 x 4096 tokens x 4096 channels gives 1M
+// lanes.  Both recurrences are linear, so a chunk only needs two carries:
+//   1. local pass (one lane per chunk): the chunk's state from a zero start, H, its
+//      decay sum S = sum_t Delta_t log2(e) (the chunk maps h to exp2(A S) h + H), and its
+//      adjoint from a zero end, E (maps R to exp2(A S) R + E);
+//   2. carry pass (one lane per sequence and channel, sequential over chunks): the true
+//      state entering each chunk and the true adjoint entering it from the right, the
+//      gradient of h0 falls out at the end;
+//   3. full pass (one lane per chunk): the forward recomputed from the true start (kSub
+//      tokens at a time, the sub-chunk starts kept in registers), then the reverse with
+//      every per-token gradient; dB / dC (sums over channels) are reduced over the wave's
+//      64 channels through LDS and written as per-wave partials; dA, dD, dbias as
+//      per-chunk partials; the conv-output gradient dpre goes to a float32 workspace;
+//   4. conv pass: dx (the conv transposed over dpre), dconv0, dconv_w / dconv_b partials;
+//   5. reductions of the partials.
+#pragma once
+
+#include "scan_common.h"
+
+namespace samba {
+
+namespace bwd {
+
+constexpr int kChunk = 16;  // tokens per time chunk
+constexpr int kSub = 4;     // tokens recomputed at a time in the full pass
+constexpr int kNSub = kChunk / kSub;
+constexpr int kLanes = 64;  // one wave per workgroup: 64 consecutive channels
+constexpr int kRun = 64;    // tokens per thread in the conv pass
+constexpr int kPar = 18;    // per-chunk parameter partials: dA[16], dD, ddt_bias
+constexpr int kConvPar = 5; // per-run conv partials: dconv_w[4], dconv_b
+constexpr int kBC = 2 * kMaxState;  // per-token dB[16], dC[16]
+constexpr int kTilePitch = kBC + 1;  // LDS tile pitch (floats): conflict-free columns
+
+template <class T>
+using ConstPtr = const __attribute__((address_space(4))) T *;
+
+}  // namespace bwd
+
+struct BwdArgs {
+    int nseq, seqlen;   // seqlen: tokens per sequence (fixed) or max_seqlen (packed)
+    const int32_t *cu;  // packed offsets or nullptr
+    int total;          // tokens in the packed arrays (packed) / nseq * seqlen
+    int D, N;
+    int nchunk;         // chunks per sequence slot = ceil(seqlen / kChunk)
+    int nrun;           // conv-pass runs per sequence slot = ceil(seqlen / kRun)
+    int nwave;          // channel waves = ceil(D / 64)
+    const void *x, *dt, *B, *C, *z;
+    const float *A, *Dskip, *dt_bias, *conv_w, *conv_b;
+    const float *h0;
+    const void *conv0;
+    const void *dout;
+    const float *dh_final;
+    const void *dconv_final;
+    void *dx, *ddt, *dB, *dC, *dz;
+    float *dA, *dD, *ddt_bias, *dconv_w, *dconv_b, *dh0;
+    void *dconv0;
+    // workspace
+    float *hck;   // [nseq][nchunk][D][16]  local end state -> true state entering the chunk
+    float *eck;   // [nseq][nchunk][D][16]  local adjoint carry -> adjoint entering from the right
+    float *lsum;  // [nseq][nchunk][D]      sum of Delta log2(e) over the chunk
+    float *dpre;  // [total][D]             gradient of the conv output before SiLU
+    float *ppar;  // [nseq][nchunk][D][kPar]
+    float *pbc;   // [total][nwave][kBC]
+    float *pconv; // [nseq][nrun][D][kConvPar]
+};
+
+namespace bwd {
+
+__device__ inline void seq_bounds(const BwdArgs &a, int s, size_t &t0, size_t &t1)
+{
+    if (a.cu != nullptr) {
+        const int lo = min(max(a.cu[s], 0), a.total);
+        const int hi = min(max(a.cu[s + 1], lo), a.total);
+        t0 = static_cast<size_t>(lo);
+        t1 = static_cast<size_t>(hi);
+    } else {
+        t0 = static_cast<size_t>(s) * static_cast<size_t>(a.seqlen);
+        t1 = t0 + static_cast<size_t>(a.seqlen);
+    }
+}
+
+__device__ inline float sigmoid(float v) { return hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// B_t or C_t row as 16 uniform floats (zeros past N).
+template <class Io, bool kFullN>
+__device__ inline void row16(const void *p, size_t t, int N, float *f)
+{
+    using T = typename Io::T;
+    if constexpr (kFullN) {
+        if constexpr (sizeof(T) == 2) {
+            const ConstPtr<uint32_t> q = (ConstPtr<uint32_t>)(static_cast<const T *>(p) + t * kMaxState);
+#pragma unroll
+            for (int k = 0; k < kMaxState / 2; ++k) {
+                const uint32_t w = q[k];
+                f[2 * k] = bf16lo(w);
+                f[2 * k + 1] = bf16hi(w);
+            }
+        } else {
+            const ConstPtr<float> q = (ConstPtr<float>)(static_cast<const float *>(p) + t * kMaxState);
+#pragma unroll
+            for (int k = 0; k < kMaxState; ++k) f[k] = q[k];
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) f[n] = n < N ? Io::ld(p, t * N + n) : 0.0f;
+    }
+}
+
+// Per-lane constants of a channel.
+struct Chan {
+    float A[kMaxState];
+    float w0, w1, w2, w3, cb, dsk, bias;
+};
+
+__device__ inline void load_chan(const BwdArgs &a, int dc, Chan &ch)
+{
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) ch.A[n] = n < a.N ? a.A[static_cast<size_t>(dc) * a.N + n] : 0.0f;
+    const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + static_cast<size_t>(dc) * kConvK);
+    ch.w0 = w.x;
+    ch.w1 = w.y;
+    ch.w2 = w.z;
+    ch.w3 = w.w;
+    ch.cb = a.conv_b ? a.conv_b[dc] : 0.0f;
+    ch.dsk = a.Dskip ? a.Dskip[dc] : 0.0f;
+    ch.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
+}
+
+// Input x of token tt of the sequence starting at t0 (tt may be -3..-1: the history).
+template <class Io>
+__device__ inline float x_at(const BwdArgs &a, int s, size_t t0, int tt, int dc)
+{
+    if (tt >= 0) return Io::ld(a.x, (t0 + static_cast<size_t>(tt)) * a.D + dc);
+    if (a.conv0 == nullptr) return 0.0f;
+    return Io::ld(a.conv0, (static_cast<size_t>(s) * 3 + static_cast<size_t>(3 + tt)) * a.D + dc);
+}
+
+// Front end of one token: pre-activation, u = SiLU(pre), a = dt + b, lg = softplus(a) log2 e.
+struct Front {
+    float pre, u, a, lg;
+};
+
+__device__ inline void front(const Chan &ch, float xm3, float xm2, float xm1, float xt, float dtv, Front &f)
+{
+    float pre = __builtin_fmaf(ch.w0, xm3, ch.cb);
+    pre = __builtin_fmaf(ch.w1, xm2, pre);
+    pre = __builtin_fmaf(ch.w2, xm1, pre);
+    pre = __builtin_fmaf(ch.w3, xt, pre);
+    f.pre = pre;
+    f.u = silu(pre);
+    f.a = dtv + ch.bias;
+    f.lg = softplus_log2(f.a);
+}
+
+// gy = dout SiLU(z) (or dout without a gate).
+__device__ inline float gate_grad(float g, bool has_z, float zv)
+{
+    return has_z ? g * (zv * sigmoid(zv)) : g;
+}
+
+}  // namespace bwd
+
+// ---------------------------------------------------------------- 1. local pass
+// grid (nwave, nchunk, nseq), 64 threads.  Chunk-local state H (zero start), decay sum S,
+// chunk-local adjoint E (zero end).
+template <class Io, bool kFullN>
+__global__ __launch_bounds__(bwd::kLanes) void bwd_local_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    const int s = blockIdx.z, c = blockIdx.y;
+    const int d = blockIdx.x * kLanes + threadIdx.x;
+    const bool dok = d < a.D;
+    const int dc = dok ? d : a.D - 1;
+    size_t t0, t1;
+    seq_bounds(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
+    const int cs = c * kChunk;
+    if (cs >= L) return;  // chunk past this sequence's end (uniform)
+    const int n_t = min(kChunk, L - cs);
+    Chan ch;
+    load_chan(a, dc, ch);
+
+    // forward from zero
+    float xm3 = x_at<Io>(a, s, t0, cs - 3, dc), xm2 = x_at<Io>(a, s, t0, cs - 2, dc), xm1 = x_at<Io>(a, s, t0, cs - 1, dc);
+    float h[kMaxState], lgs[kChunk];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
+    float S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        lgs[i] = 0.0f;
+        if (i < n_t) {
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            const float xt = Io::ld(a.x, t * a.D + dc);
+            Front f;
+            front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
+            xm3 = xm2;
+            xm2 = xm1;
+            xm1 = xt;
+            float b[kMaxState];
+            row16<Io, kFullN>(a.B, t, a.N, b);
+            const float du = (f.lg * kLn2) * f.u;
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
+            lgs[i] = f.lg;
+            S += f.lg;
+        }
+    }
+    // reverse from zero
+    const bool has_z = a.z != nullptr;
+    float R[kMaxState];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) R[n] = 0.0f;
+#pragma unroll
+    for (int i = kChunk - 1; i >= 0; --i) {
+        if (i < n_t) {
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            const float g = Io::ld(a.dout, t * a.D + dc);
+            const float gy = gate_grad(g, has_z, has_z ? Io::ld(a.z, t * a.D + dc) : 0.0f);
+            float cr[kMaxState];
+            row16<Io, kFullN>(a.C, t, a.N, cr);
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n)
+                R[n] = hw_exp2(lgs[i] * ch.A[n]) * __builtin_fmaf(gy, cr[n], R[n]);
+        }
+    }
+    if (dok) {
+        const size_t o = ((static_cast<size_t>(s) * a.nchunk + c) * a.D + d);
+        float4 *ph = reinterpret_cast<float4 *>(a.hck + o * kMaxState);
+        float4 *pe = reinterpret_cast<float4 *>(a.eck + o * kMaxState);
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            ph[g] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+            pe[g] = make_float4(R[4 * g], R[4 * g + 1], R[4 * g + 2], R[4 * g + 3]);
+        }
+        a.lsum[o] = S;
+    }
+}
+
+// ---------------------------------------------------------------- 2. carry pass
+// grid (nwave, nseq), 64 threads: one lane per (sequence, channel), sequential over chunks.
+// hck becomes the state entering each chunk, eck the adjoint entering it from the right.
+__global__ __launch_bounds__(bwd::kLanes) void bwd_carry_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    const int s = blockIdx.y;
+    const int d = blockIdx.x * kLanes + threadIdx.x;
+    if (d >= a.D) return;  // no barriers: an early exit is safe
+    size_t t0, t1;
+    seq_bounds(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
+    // chunks of this sequence (clamped to the slot: offsets are caller data)
+    const int nc = min((L + kChunk - 1) / kChunk, a.nchunk);
+    float A[kMaxState], h[kMaxState], R[kMaxState];
+    const size_t hb = (static_cast<size_t>(s) * a.D + d) * a.N;
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) {
+        const bool on = n < a.N;
+        A[n] = on ? a.A[static_cast<size_t>(d) * a.N + n] : 0.0f;
+        h[n] = (on && a.h0 != nullptr) ? a.h0[hb + n] : 0.0f;
+        R[n] = (on && a.dh_final != nullptr) ? a.dh_final[hb + n] : 0.0f;
+    }
+    for (int c = 0; c < nc; ++c) {
+        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + d;
+        float4 *ph = reinterpret_cast<float4 *>(a.hck + o * kMaxState);
+        const float S = a.lsum[o];
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 H = ph[g];
+            ph[g] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+            const float Hv[4] = {H.x, H.y, H.z, H.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[4 * g + e] = __builtin_fmaf(hw_exp2(A[4 * g + e] * S), h[4 * g + e], Hv[e]);
+        }
+    }
+    for (int c = nc - 1; c >= 0; --c) {
+        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + d;
+        float4 *pe = reinterpret_cast<float4 *>(a.eck + o * kMaxState);
+        const float S = a.lsum[o];
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 E = pe[g];
+            pe[g] = make_float4(R[4 * g], R[4 * g + 1], R[4 * g + 2], R[4 * g + 3]);
+            const float Ev[4] = {E.x, E.y, E.z, E.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[4 * g + e] = __builtin_fmaf(hw_exp2(A[4 * g + e] * S), R[4 * g + e], Ev[e]);
+        }
+    }
+    if (a.dh0 != nullptr) {
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n)
+            if (n < a.N) a.dh0[hb + n] = R[n];
+    }
+}
+
+// ---------------------------------------------------------------- 3. full pass
+// grid (nwave, nchunk, nseq), 64 threads (one wave: the LDS reduction of dB / dC needs no
+// workgroup barrier beyond the wave's own).
+template <class Io, bool kFullN>
+__global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    using T = typename Io::T;
+    __shared__ float tile[kLanes * kTilePitch];
+    const int s = blockIdx.z, c = blockIdx.y, wv = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int d = wv * kLanes + lane;
+    const bool dok = d < a.D;
+    const int dc = dok ? d : a.D - 1;
+    size_t t0, t1;
+    seq_bounds(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
+    const int cs = c * kChunk;
+    if (cs >= L) return;  // uniform over the workgroup (one wave)
+    const int n_t = min(kChunk, L - cs);
+    const bool has_z = a.z != nullptr;
+    Chan ch;
+    load_chan(a, dc, ch);
+    const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + dc;
+
+    // forward sweep from the true chunk start, keeping each sub-chunk's start
+    float hsub[kNSub][kMaxState];
+    {
+        const float4 *ph = reinterpret_cast<const float4 *>(a.hck + o * kMaxState);
+        float h[kMaxState];
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 v = ph[g];
+            h[4 * g] = v.x;
+            h[4 * g + 1] = v.y;
+            h[4 * g + 2] = v.z;
+            h[4 * g + 3] = v.w;
+        }
+        float xm3 = x_at<Io>(a, s, t0, cs - 3, dc), xm2 = x_at<Io>(a, s, t0, cs - 2, dc);
+        float xm1 = x_at<Io>(a, s, t0, cs - 1, dc);
+#pragma unroll
+        for (int j = 0; j < kNSub; ++j) {
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) hsub[j][n] = h[n];
+            if (j + 1 < kNSub) {  // the last sub-chunk's end state is not needed
+#pragma unroll
+                for (int e = 0; e < kSub; ++e) {
+                    const int i = j * kSub + e;
+                    if (i < n_t) {
+                        const size_t t = t0 + static_cast<size_t>(cs + i);
+                        const float xt = Io::ld(a.x, t * a.D + dc);
+                        Front f;
+                        front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
+                        xm3 = xm2;
+                        xm2 = xm1;
+                        xm1 = xt;
+                        float b[kMaxState];
+                        row16<Io, kFullN>(a.B, t, a.N, b);
+                        const float du = (f.lg * kLn2) * f.u;
+#pragma unroll
+                        for (int n = 0; n < kMaxState; ++n)
+                            h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
+                    }
+                }
+            }
+        }
+    }
+
+    // reverse, one sub-chunk at a time
+    float R[kMaxState], dA[kMaxState];
+    {
+        const float4 *pe = reinterpret_cast<const float4 *>(a.eck + o * kMaxState);
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 v = pe[g];
+            R[4 * g] = v.x;
+            R[4 * g + 1] = v.y;
+            R[4 * g + 2] = v.z;
+            R[4 * g + 3] = v.w;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) dA[n] = 0.0f;
+    float dDacc = 0.0f, dbacc = 0.0f;
+    float *trow = tile + lane * kTilePitch;
+    const int ro = lane & 31, rp = lane >> 5;  // reduction: column ro, half rp of the lanes
+
+#pragma unroll
+    for (int j = kNSub - 1; j >= 0; --j) {
+        if (j * kSub >= n_t) continue;  // uniform
+        // recompute the sub-chunk: states after each token and the per-token front ends
+        float hs[kSub][kMaxState];
+        Front fs[kSub];
+        {
+            float h[kMaxState];
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) h[n] = hsub[j][n];
+            const int i0 = j * kSub;
+            float xm3 = x_at<Io>(a, s, t0, cs + i0 - 3, dc), xm2 = x_at<Io>(a, s, t0, cs + i0 - 2, dc);
+            float xm1 = x_at<Io>(a, s, t0, cs + i0 - 1, dc);
+#pragma unroll
+            for (int e = 0; e < kSub; ++e) {
+                const int i = i0 + e;
+                fs[e] = Front{0.0f, 0.0f, 0.0f, 0.0f};
+                if (i < n_t) {
+                    const size_t t = t0 + static_cast<size_t>(cs + i);
+                    const float xt = Io::ld(a.x, t * a.D + dc);
+                    front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), fs[e]);
+                    xm3 = xm2;
+                    xm2 = xm1;
+                    xm1 = xt;
+                    float b[kMaxState];
+                    row16<Io, kFullN>(a.B, t, a.N, b);
+                    const float du = (fs[e].lg * kLn2) * fs[e].u;
+#pragma unroll
+                    for (int n = 0; n < kMaxState; ++n)
+                        h[n] = __builtin_fmaf(hw_exp2(fs[e].lg * ch.A[n]), h[n], du * b[n]);
+                }
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
+            }
+        }
+#pragma unroll
+        for (int e = kSub - 1; e >= 0; --e) {
+            const int i = j * kSub + e;
+            if (i >= n_t) continue;  // uniform
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            const size_t ix = t * a.D + dc;
+            const Front &f = fs[e];
+            const float delta = f.lg * kLn2;
+            float br[kMaxState], cr[kMaxState];
+            row16<Io, kFullN>(a.B, t, a.N, br);
+            row16<Io, kFullN>(a.C, t, a.N, cr);
+            const float g = Io::ld(a.dout, ix);
+            float y = ch.dsk * f.u;
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) y = __builtin_fmaf(cr[n], hs[e][n], y);
+            float gy = g;
+            if (has_z) {
+                const float zv = Io::ld(a.z, ix);
+                const float sz = sigmoid(zv);
+                const float dzv = g * y * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
+                if (dok) Io::st(a.dz, ix, dzv);
+                gy = g * (zv * sz);
+            }
+            dDacc = __builtin_fmaf(gy, f.u, dDacc);
+            float S1 = 0.0f, S2 = 0.0f;
+            const float dun = delta * f.u;
+            float bc[kBC];
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) {
+                const float hp = e > 0 ? hs[e > 0 ? e - 1 : 0][n] : hsub[j][n];
+                const float abar = hw_exp2(f.lg * ch.A[n]);
+                const float G = __builtin_fmaf(gy, cr[n], R[n]);
+                const float ga = G * abar;
+                const float q = ga * hp;
+                S1 = __builtin_fmaf(q, ch.A[n], S1);
+                dA[n] = __builtin_fmaf(q, delta, dA[n]);
+                S2 = __builtin_fmaf(G, br[n], S2);
+                R[n] = ga;
+                bc[n] = G * dun;
+                bc[kMaxState + n] = gy * hs[e][n];
+            }
+            const float ddel = __builtin_fmaf(f.u, S2, S1);
+            const float du = __builtin_fmaf(delta, S2, gy * ch.dsk);
+            const float da = ddel * sigmoid(f.a);
+            dbacc += da;
+            const float sp = sigmoid(f.pre);
+            const float dpre = du * sp * __builtin_fmaf(f.pre, 1.0f - sp, 1.0f);
+            if (dok) {
+                Io::st(a.ddt, ix, da);
+                a.dpre[ix] = dpre;
+            }
+            // dB / dC: sum over the wave's 64 channels (padding channels add zeros)
+#pragma unroll
+            for (int k = 0; k < kBC; ++k) trow[k] = dok ? bc[k] : 0.0f;
+            __syncthreads();
+            float acc = 0.0f;
+#pragma unroll 8
+            for (int l = 0; l < 32; ++l) acc += tile[(rp * 32 + l) * kTilePitch + ro];
+            acc += __shfl_xor(acc, 32);
+            if (rp == 0) a.pbc[(t * a.nwave + wv) * kBC + ro] = acc;
+            __syncthreads();
+        }
+    }
+    if (dok) {
+        float *pp = a.ppar + o * kPar;
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) pp[n] = dA[n];
+        pp[kMaxState] = dDacc;
+        pp[kMaxState + 1] = dbacc;
+    }
+}
+
+// ---------------------------------------------------------------- 4. conv pass
+// grid (nrun * nseq, ceil(D / 256)), 256 threads: one thread per (sequence, run of kRun
+// tokens, channel).  dx_t = sum_k w_k dpre_{t+3-k} (+ dconv_final for the last three
+// tokens), dconv0 for the inputs before the sequence, dconv_w / dconv_b partials.
+template <class Io>
+__global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    const int s = blockIdx.x / a.nrun, r = blockIdx.x - s * a.nrun;
+    const int d = blockIdx.y * 256 + threadIdx.x;
+    if (d >= a.D) return;  // no barriers
+    size_t t0, t1;
+    seq_bounds(a, s, t0, t1);
+    const int L = static_cast<int>(t1 - t0);
+    const int tb = r * kRun;
+    if (tb >= L && r > 0) return;  // run 0 always runs (dconv0 of an empty sequence)
+    const int te = min(tb + kRun, L);
+    const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + static_cast<size_t>(d) * kConvK);
+    const float wk[kConvK] = {w.x, w.y, w.z, w.w};
+    // gradient of token tt's input from the dpre of tokens tt .. tt+3, and from dconv_final
+    auto gsrc = [&](int tt) {
+        float v = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kConvK; ++k) {
+            const int tp = tt + 3 - k;  // token whose pre-activation uses x_tt through tap k
+            if (tp >= 0 && tp < L) v = __builtin_fmaf(wk[k], a.dpre[(t0 + static_cast<size_t>(tp)) * a.D + d], v);
+        }
+        if (a.dconv_final != nullptr && tt >= L - 3)
+            v += Io::ld(a.dconv_final, (static_cast<size_t>(s) * 3 + static_cast<size_t>(tt - (L - 3))) * a.D + d);
+        return v;
+    };
+    float pw[kConvK] = {0.0f, 0.0f, 0.0f, 0.0f}, pb = 0.0f;
+    for (int t = tb; t < te; ++t) {
+        const size_t ix = (t0 + static_cast<size_t>(t)) * a.D + d;
+        Io::st(a.dx, ix, gsrc(t));
+        const float dp = a.dpre[ix];
+        pb += dp;
+#pragma unroll
+        for (int k = 0; k < kConvK; ++k) pw[k] = __builtin_fmaf(dp, x_at<Io>(a, s, t0, t - 3 + k, d), pw[k]);
+    }
+    if (r == 0 && a.dconv0 != nullptr) {
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)
+            Io::st(a.dconv0, (static_cast<size_t>(s) * 3 + jj) * a.D + d, gsrc(jj - 3));
+    }
+    float *pc = a.pconv + ((static_cast<size_t>(s) * a.nrun + r) * a.D + d) * kConvPar;
+#pragma unroll
+    for (int k = 0; k < kConvK; ++k) pc[k] = pw[k];
+    pc[kConvK] = pb;
+}
+
+// ---------------------------------------------------------------- 5. reductions
+// dB / dC: grid ceil(total * 32 / 256), one thread per (token, output).
+template <class Io>
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= static_cast<size_t>(a.total) * kBC) return;
+    const size_t t = i / kBC;
+    const int k = static_cast<int>(i - t * kBC);
+    const int n = k & (kMaxState - 1);
+    if (n >= a.N) return;
+    float acc = 0.0f;
+    for (int wv = 0; wv < a.nwave; ++wv) acc += a.pbc[(t * a.nwave + wv) * kBC + k];
+    Io::st(k < kMaxState ? a.dB : a.dC, t * a.N + n, acc);
+}
+
+// Parameters: grid ceil(D / 256), one thread per channel; sums over (sequence, chunk) and
+// (sequence, run).
+__global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs a)
+{
+    using namespace bwd;
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= a.D) return;
+    float acc[kPar];
+#pragma unroll
+    for (int k = 0; k < kPar; ++k) acc[k] = 0.0f;
+    for (int s = 0; s < a.nseq; ++s) {
+        size_t t0, t1;
+        seq_bounds(a, s, t0, t1);
+        const int nc = min((static_cast<int>(t1 - t0) + kChunk - 1) / kChunk, a.nchunk);
+        for (int c = 0; c < nc; ++c) {
+            const float *pp = a.ppar + ((static_cast<size_t>(s) * a.nchunk + c) * a.D + d) * kPar;
+#pragma unroll
+            for (int k = 0; k < kPar; ++k) acc[k] += pp[k];
+        }
+    }
+    float cw[kConvPar] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < a.nseq; ++s) {
+        size_t t0, t1;
+        seq_bounds(a, s, t0, t1);
+        const int nr = min(max(1, (static_cast<int>(t1 - t0) + kRun - 1) / kRun), a.nrun);
+        for (int r = 0; r < nr; ++r) {
+            const float *pc = a.pconv + ((static_cast<size_t>(s) * a.nrun + r) * a.D + d) * kConvPar;
+#pragma unroll
+            for (int k = 0; k < kConvPar; ++k) cw[k] += pc[k];
+        }
+    }
+    for (int n = 0; n < a.N; ++n) a.dA[static_cast<size_t>(d) * a.N + n] = acc[n];
+    a.dD[d] = acc[kMaxState];
+    a.ddt_bias[d] = acc[kMaxState + 1];
+#pragma unroll
+    for (int k = 0; k < kConvK; ++k) a.dconv_w[static_cast<size_t>(d) * kConvK + k] = cw[k];
+    a.dconv_b[d] = cw[kConvK];
+}
+
+// ---------------------------------------------------------------- host side
+// Workspace layout (offsets in floats), every part 256-byte aligned.
+struct BwdWorkspace {
+    size_t hck, eck, lsum, dpre, ppar, pbc, pconv, total_bytes;
+};
+
+inline BwdWorkspace bwd_workspace(int nseq, int seqlen, int total, int D)
+{
+    using namespace bwd;
+    auto al = [](size_t f) { return (f + 63) / 64 * 64; };
+    const size_t nchunk = (static_cast<size_t>(seqlen) + kChunk - 1) / kChunk;
+    const size_t nrun = std::max<size_t>(1, (static_cast<size_t>(seqlen) + kRun - 1) / kRun);
+    const size_t nwave = (static_cast<size_t>(D) + kLanes - 1) / kLanes;
+    const size_t sc = static_cast<size_t>(nseq) * nchunk * D;
+    BwdWorkspace w;
+    size_t off = 0;
+    w.hck = off;
+    off += al(sc * kMaxState);
+    w.eck = off;
+    off += al(sc * kMaxState);
+    w.lsum = off;
+    off += al(sc);
+    w.dpre = off;
+    off += al(static_cast<size_t>(total) * D);
+    w.ppar = off;
+    off += al(sc * kPar);
+    w.pbc = off;
+    off += al(static_cast<size_t>(total) * nwave * kBC);
+    w.pconv = off;
+    off += al(static_cast<size_t>(nseq) * nrun * D * kConvPar);
+    w.total_bytes = off * sizeof(float);
+    return w;
+}
+
+inline void launch_backward(BwdArgs a, float *ws, samba_dtype io, hipStream_t stream)
+{
+    using namespace bwd;
+    const BwdWorkspace w = bwd_workspace(a.nseq, a.seqlen, a.total, a.D);
+    a.nchunk = (a.seqlen + kChunk - 1) / kChunk;
+    a.nrun = std::max(1, (a.seqlen + kRun - 1) / kRun);
+    a.nwave = (a.D + kLanes - 1) / kLanes;
+    a.hck = ws + w.hck;
+    a.eck = ws + w.eck;
+    a.lsum = ws + w.lsum;
+    a.dpre = ws + w.dpre;
+    a.ppar = ws + w.ppar;
+    a.pbc = ws + w.pbc;
+    a.pconv = ws + w.pconv;
+    const bool full = a.N == kMaxState;
+    const dim3 g3(a.nwave, std::max(1, a.nchunk), a.nseq), b64(kLanes);
+    if (a.nchunk > 0) {
+        if (io == SAMBA_BF16) {
+            if (full) bwd_local_kernel<IoBf16, true><<<g3, b64, 0, stream>>>(a);
+            else bwd_local_kernel<IoBf16, false><<<g3, b64, 0, stream>>>(a);
+        } else {
+            if (full) bwd_local_kernel<IoF32, true><<<g3, b64, 0, stream>>>(a);
+            else bwd_local_kernel<IoF32, false><<<g3, b64, 0, stream>>>(a);
+        }
+    }
+    bwd_carry_kernel<<<dim3(a.nwave, a.nseq), b64, 0, stream>>>(a);
+    if (a.nchunk > 0) {
+        if (io == SAMBA_BF16) {
+            if (full) bwd_full_kernel<IoBf16, true><<<g3, b64, 0, stream>>>(a);
+            else bwd_full_kernel<IoBf16, false><<<g3, b64, 0, stream>>>(a);
+        } else {
+            if (full) bwd_full_kernel<IoF32, true><<<g3, b64, 0, stream>>>(a);
+            else bwd_full_kernel<IoF32, false><<<g3, b64, 0, stream>>>(a);
+        }
+    }
+    const dim3 gc(static_cast<unsigned>(a.nrun) * static_cast<unsigned>(a.nseq), (a.D + 255) / 256);
+    if (io == SAMBA_BF16) bwd_conv_kernel<IoBf16><<<gc, 256, 0, stream>>>(a);
+    else bwd_conv_kernel<IoF32><<<gc, 256, 0, stream>>>(a);
+    if (a.total > 0) {
+        const size_t nbc = static_cast<size_t>(a.total) * kBC;
+        const unsigned gb = static_cast<unsigned>((nbc + 255) / 256);
+        if (io == SAMBA_BF16) bwd_reduce_bc_kernel<IoBf16><<<gb, 256, 0, stream>>>(a);
+        else bwd_reduce_bc_kernel<IoF32><<<gb, 256, 0, stream>>>(a);
+    }
+    bwd_reduce_par_kernel<<<(a.D + 255) / 256, 256, 0, stream>>>(a);
+}
+
+}  // namespace samba
