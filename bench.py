@@ -40,6 +40,13 @@ D_INNER, D_STATE = 4096, 16
 #   per token.channel: conv 4 fma; SiLU 6 (exp 2, add, rcp 2, mul); softplus 5 (exp 2, add, log 2);
 #   dt+bias 1; Delta*u 1; D*u 1; gate 7 (SiLU(z) 6 + mul)                                          = 25
 SLOTS_PER_TC = 16 * 6 + 25
+# Algorithmic work of the gradients per token.channel: one forward recompute without the
+# readout (per state mul, exp (2 slots), mul, fma = 5; front end 17: conv 4, SiLU 6, softplus
+# 5, Delta*u 2), the reverse per state (the readout y fma, G fma, G*Abar, *h_{t-1}, the
+# dDelta, dA and dB-sum fmas, the dB and dC products = 9) and per token.channel (dz 8 with
+# its sigmoid, gy 1, dD 1, du 2, softplus' 5, SiLU' 7, conv transpose 4, dconv_w 4, dconv_b
+# 1 = 33): 16 * 14 + 17 + 33 = 274.
+BWD_SLOTS_PER_TC = 16 * 14 + 17 + 33
 # Algorithmic HBM bytes per token for bf16 I/O: read x, dt, z (2 B each per channel), write y
 # (2 B per channel), read B and C (2 B each per state).
 BYTES_PER_TOKEN = 8 * D_INNER + 4 * D_STATE
@@ -205,7 +212,19 @@ def bench_extra(dev, steps=5, warmup=2):
     res["train4k"] = dict(workload="batch 4, L=4096", ms=float(np.mean(per) * 1e3),
                           ms_median=float(np.median(per) * 1e3), mtok_s=4 * 4096 / float(np.mean(per)) / 1e6,
                           note="512 MB scratch write between timed calls")
-    del ins, out, scratch
+    # Gradients at the same training shape (dout drawn like x)
+    g = to_dev(synth.make_tokens(seed, (4, 4096), D_INNER, D_STATE, "bf16", tag="grad").x, dev)
+    ws = torch.empty(int(ss.load().samba_scan_backward_workspace_bytes(4, 4096, 4 * 4096, D_INNER, D_STATE)),
+                     dtype=torch.uint8, device=dev)
+    _, per = time_calls(lambda: ss.backward(g, *ins, *prm, want_state_grads=False, workspace=ws), steps, warmup,
+                        flush=lambda: scratch.fill_(1.0))
+    sec = float(np.median(per))
+    res["backward_train4k"] = dict(workload="gradients, batch 4, L=4096", ms=float(np.mean(per) * 1e3),
+                                   ms_median=sec * 1e3, mtok_s=4 * 4096 / sec / 1e6,
+                                   valu_frac=4 * 4096 * D_INNER * BWD_SLOTS_PER_TC / sec / 1e12 / VALU_PEAK_TSLOTS,
+                                   note="512 MB scratch write between timed calls; VALU fraction against %d "
+                                        "algorithmic slots per token.channel" % BWD_SLOTS_PER_TC)
+    del ins, out, scratch, g, ws
     # Many mid-length sequences (batch 64, L = 2048): the same 131072 tokens as the long
     # prompt, spread over enough (sequence, channel) pairs to give one lane each.
     tk = synth.make_tokens(seed, (64, 2048), D_INNER, D_STATE, "bf16")

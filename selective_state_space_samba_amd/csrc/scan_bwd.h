@@ -37,6 +37,8 @@ namespace bwd {
 constexpr int kChunk = 16;  // tokens per time chunk
 constexpr int kSub = 4;     // tokens recomputed at a time in the full pass
 constexpr int kNSub = kChunk / kSub;
+constexpr int kGroup = 4;   // consecutive chunks per lane in the full pass
+constexpr int kSplit = 32;  // row splits of the parameter reductions
 constexpr int kLanes = 64;  // one wave per workgroup: 64 consecutive channels
 constexpr int kRun = 64;    // tokens per thread in the conv pass
 constexpr int kPar = 18;    // per-chunk parameter partials: dA[16], dD, ddt_bias
@@ -57,6 +59,7 @@ struct BwdArgs {
     int nchunk;         // chunks per sequence slot = ceil(seqlen / kChunk)
     int nrun;           // conv-pass runs per sequence slot = ceil(seqlen / kRun)
     int nwave;          // channel waves = ceil(D / 64)
+    int ngroup;         // chunk groups per sequence slot = ceil(nchunk / kGroup)
     const void *x, *dt, *B, *C, *z;
     const float *A, *Dskip, *dt_bias, *conv_w, *conv_b;
     const float *h0;
@@ -72,9 +75,11 @@ struct BwdArgs {
     float *eck;   // [nseq][nchunk][D][16]  local adjoint carry -> adjoint entering from the right
     float *lsum;  // [nseq][nchunk][D]      sum of Delta log2(e) over the chunk
     float *dpre;  // [total][D]             gradient of the conv output before SiLU
-    float *ppar;  // [nseq][nchunk][D][kPar]
+    float *ppar;  // [nseq][ngroup][D][kPar]
     float *pbc;   // [total][nwave][kBC]
     float *pconv; // [nseq][nrun][D][kConvPar]
+    float *par2;  // [kSplit][D][kPar]       per-split sums of ppar
+    float *conv2; // [kSplit][D][kConvPar]   per-split sums of pconv
 };
 
 namespace bwd {
@@ -251,71 +256,93 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_local_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------- 2. carry pass
-// grid (nwave, nseq), 64 threads: one lane per (sequence, channel), sequential over chunks.
-// hck becomes the state entering each chunk, eck the adjoint entering it from the right.
-__global__ __launch_bounds__(bwd::kLanes) void bwd_carry_kernel(BwdArgs a)
+// grid (ceil(D * 16 / 256), nseq), 256 threads: one lane per (sequence, channel, state),
+// sequential over chunks, the loads kPre chunks ahead (the loop body is one exp and one
+// FMA, so it is load-latency bound).  hck becomes the state entering each chunk, eck the
+// adjoint entering it from the right; the gradient of h0 is what is left at the start.
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a)
 {
     using namespace bwd;
+    constexpr int kPre = 4;
     const int s = blockIdx.y;
-    const int d = blockIdx.x * kLanes + threadIdx.x;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int d = idx >> 4, n = idx & (kMaxState - 1);
     if (d >= a.D) return;  // no barriers: an early exit is safe
     size_t t0, t1;
     seq_bounds(a, s, t0, t1);
     const int L = static_cast<int>(t1 - t0);
-    // chunks of this sequence (clamped to the slot: offsets are caller data)
-    const int nc = min((L + kChunk - 1) / kChunk, a.nchunk);
-    float A[kMaxState], h[kMaxState], R[kMaxState];
-    const size_t hb = (static_cast<size_t>(s) * a.D + d) * a.N;
+    const int nc = min((L + kChunk - 1) / kChunk, a.nchunk);  // clamped: offsets are caller data
+    const bool on = n < a.N;
+    const float An = on ? a.A[static_cast<size_t>(d) * a.N + n] : 0.0f;
+    const size_t hb = (static_cast<size_t>(s) * a.D + d) * a.N + n;
+    float h = (on && a.h0 != nullptr) ? a.h0[hb] : 0.0f;
+    float R = (on && a.dh_final != nullptr) ? a.dh_final[hb] : 0.0f;
+    const size_t base = static_cast<size_t>(s) * a.nchunk * a.D + d;  // chunk c: base + c * D
+    auto at = [&](int c) { return base + static_cast<size_t>(c) * a.D; };
+    // forward over chunks
+    {
+        float Hq[kPre], Sq[kPre];
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) {
-        const bool on = n < a.N;
-        A[n] = on ? a.A[static_cast<size_t>(d) * a.N + n] : 0.0f;
-        h[n] = (on && a.h0 != nullptr) ? a.h0[hb + n] : 0.0f;
-        R[n] = (on && a.dh_final != nullptr) ? a.dh_final[hb + n] : 0.0f;
-    }
-    for (int c = 0; c < nc; ++c) {
-        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + d;
-        float4 *ph = reinterpret_cast<float4 *>(a.hck + o * kMaxState);
-        const float S = a.lsum[o];
+        for (int k = 0; k < kPre; ++k) {
+            const int c = min(k, max(nc - 1, 0));
+            Hq[k] = nc > 0 ? a.hck[at(c) * kMaxState + n] : 0.0f;
+            Sq[k] = nc > 0 ? a.lsum[at(c)] : 0.0f;
+        }
+        for (int c0 = 0; c0 < nc; c0 += kPre) {
 #pragma unroll
-        for (int g = 0; g < kMaxState / 4; ++g) {
-            const float4 H = ph[g];
-            ph[g] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
-            const float Hv[4] = {H.x, H.y, H.z, H.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h[4 * g + e] = __builtin_fmaf(hw_exp2(A[4 * g + e] * S), h[4 * g + e], Hv[e]);
+            for (int k = 0; k < kPre; ++k) {
+                const int c = c0 + k;
+                if (c < nc) {
+                    const float H = Hq[k], S = Sq[k];
+                    const int cn = min(c + kPre, nc - 1);  // refill (clamped re-load at the end)
+                    Hq[k] = a.hck[at(cn) * kMaxState + n];
+                    Sq[k] = a.lsum[at(cn)];
+                    a.hck[at(c) * kMaxState + n] = h;
+                    h = __builtin_fmaf(hw_exp2(An * S), h, H);
+                }
+            }
         }
     }
-    for (int c = nc - 1; c >= 0; --c) {
-        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + d;
-        float4 *pe = reinterpret_cast<float4 *>(a.eck + o * kMaxState);
-        const float S = a.lsum[o];
+    // reverse over chunks
+    {
+        float Eq[kPre], Sq[kPre];
 #pragma unroll
-        for (int g = 0; g < kMaxState / 4; ++g) {
-            const float4 E = pe[g];
-            pe[g] = make_float4(R[4 * g], R[4 * g + 1], R[4 * g + 2], R[4 * g + 3]);
-            const float Ev[4] = {E.x, E.y, E.z, E.w};
+        for (int k = 0; k < kPre; ++k) {
+            const int c = max(nc - 1 - k, 0);
+            Eq[k] = nc > 0 ? a.eck[at(c) * kMaxState + n] : 0.0f;
+            Sq[k] = nc > 0 ? a.lsum[at(c)] : 0.0f;
+        }
+        for (int c0 = nc - 1; c0 >= 0; c0 -= kPre) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) R[4 * g + e] = __builtin_fmaf(hw_exp2(A[4 * g + e] * S), R[4 * g + e], Ev[e]);
+            for (int k = 0; k < kPre; ++k) {
+                const int c = c0 - k;
+                if (c >= 0) {
+                    const float E = Eq[k], S = Sq[k];
+                    const int cn = max(c - kPre, 0);
+                    Eq[k] = a.eck[at(cn) * kMaxState + n];
+                    Sq[k] = a.lsum[at(cn)];
+                    a.eck[at(c) * kMaxState + n] = R;
+                    R = __builtin_fmaf(hw_exp2(An * S), R, E);
+                }
+            }
         }
     }
-    if (a.dh0 != nullptr) {
-#pragma unroll
-        for (int n = 0; n < kMaxState; ++n)
-            if (n < a.N) a.dh0[hb + n] = R[n];
-    }
+    if (a.dh0 != nullptr && on) a.dh0[hb] = R;
 }
 
 // ---------------------------------------------------------------- 3. full pass
-// grid (nwave, nchunk, nseq), 64 threads (one wave: the LDS reduction of dB / dC needs no
-// workgroup barrier beyond the wave's own).
+// grid (nwave, ngroup, nseq), 64 threads (one wave: the LDS reduction of dB / dC needs no
+// workgroup barrier beyond the wave's own).  A lane takes a group of kGroup consecutive
+// chunks, last to first, carrying the adjoint from one chunk into the previous one.  Within
+// a chunk, sub-chunks of kSub tokens are handled last to first, each recomputing the
+// forward from the chunk's true start (no per-sub-chunk state is kept: registers, not
+// recomputation, limit how many waves share a SIMD here).
 template <class Io, bool kFullN>
 __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
 {
     using namespace bwd;
-    using T = typename Io::T;
     __shared__ float tile[kLanes * kTilePitch];
-    const int s = blockIdx.z, c = blockIdx.y, wv = blockIdx.x;
+    const int s = blockIdx.z, cg = blockIdx.y, wv = blockIdx.x;
     const int lane = threadIdx.x;
     const int d = wv * kLanes + lane;
     const bool dok = d < a.D;
@@ -323,60 +350,24 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
     size_t t0, t1;
     seq_bounds(a, s, t0, t1);
     const int L = static_cast<int>(t1 - t0);
-    const int cs = c * kChunk;
-    if (cs >= L) return;  // uniform over the workgroup (one wave)
-    const int n_t = min(kChunk, L - cs);
+    const int nc = min((L + kChunk - 1) / kChunk, a.nchunk);
+    const int cfirst = cg * kGroup;
+    if (cfirst >= nc) {  // uniform over the workgroup (one wave): an empty slot adds zeros
+        if (dok) {
+            float *pp = a.ppar + ((static_cast<size_t>(s) * a.ngroup + cg) * a.D + d) * kPar;
+#pragma unroll
+            for (int k = 0; k < kPar; ++k) pp[k] = 0.0f;
+        }
+        return;
+    }
+    const int clast = min(cfirst + kGroup, nc) - 1;
     const bool has_z = a.z != nullptr;
     Chan ch;
     load_chan(a, dc, ch);
-    const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + dc;
 
-    // forward sweep from the true chunk start, keeping each sub-chunk's start
-    float hsub[kNSub][kMaxState];
-    {
-        const float4 *ph = reinterpret_cast<const float4 *>(a.hck + o * kMaxState);
-        float h[kMaxState];
-#pragma unroll
-        for (int g = 0; g < kMaxState / 4; ++g) {
-            const float4 v = ph[g];
-            h[4 * g] = v.x;
-            h[4 * g + 1] = v.y;
-            h[4 * g + 2] = v.z;
-            h[4 * g + 3] = v.w;
-        }
-        float xm3 = x_at<Io>(a, s, t0, cs - 3, dc), xm2 = x_at<Io>(a, s, t0, cs - 2, dc);
-        float xm1 = x_at<Io>(a, s, t0, cs - 1, dc);
-#pragma unroll
-        for (int j = 0; j < kNSub; ++j) {
-#pragma unroll
-            for (int n = 0; n < kMaxState; ++n) hsub[j][n] = h[n];
-            if (j + 1 < kNSub) {  // the last sub-chunk's end state is not needed
-#pragma unroll
-                for (int e = 0; e < kSub; ++e) {
-                    const int i = j * kSub + e;
-                    if (i < n_t) {
-                        const size_t t = t0 + static_cast<size_t>(cs + i);
-                        const float xt = Io::ld(a.x, t * a.D + dc);
-                        Front f;
-                        front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
-                        xm3 = xm2;
-                        xm2 = xm1;
-                        xm1 = xt;
-                        float b[kMaxState];
-                        row16<Io, kFullN>(a.B, t, a.N, b);
-                        const float du = (f.lg * kLn2) * f.u;
-#pragma unroll
-                        for (int n = 0; n < kMaxState; ++n)
-                            h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
-                    }
-                }
-            }
-        }
-    }
-
-    // reverse, one sub-chunk at a time
     float R[kMaxState], dA[kMaxState];
     {
+        const size_t o = (static_cast<size_t>(s) * a.nchunk + clast) * a.D + dc;
         const float4 *pe = reinterpret_cast<const float4 *>(a.eck + o * kMaxState);
 #pragma unroll
         for (int g = 0; g < kMaxState / 4; ++g) {
@@ -393,106 +384,138 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
     float *trow = tile + lane * kTilePitch;
     const int ro = lane & 31, rp = lane >> 5;  // reduction: column ro, half rp of the lanes
 
-#pragma unroll
-    for (int j = kNSub - 1; j >= 0; --j) {
-        if (j * kSub >= n_t) continue;  // uniform
-        // recompute the sub-chunk: states after each token and the per-token front ends
-        float hs[kSub][kMaxState];
-        Front fs[kSub];
+    for (int c = clast; c >= cfirst; --c) {
+        const int cs = c * kChunk;
+        const int n_t = min(kChunk, L - cs);
+        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + dc;
+        float hc[kMaxState];  // true state entering the chunk
         {
-            float h[kMaxState];
+            const float4 *ph = reinterpret_cast<const float4 *>(a.hck + o * kMaxState);
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) h[n] = hsub[j][n];
-            const int i0 = j * kSub;
-            float xm3 = x_at<Io>(a, s, t0, cs + i0 - 3, dc), xm2 = x_at<Io>(a, s, t0, cs + i0 - 2, dc);
-            float xm1 = x_at<Io>(a, s, t0, cs + i0 - 1, dc);
+            for (int g = 0; g < kMaxState / 4; ++g) {
+                const float4 v = ph[g];
+                hc[4 * g] = v.x;
+                hc[4 * g + 1] = v.y;
+                hc[4 * g + 2] = v.z;
+                hc[4 * g + 3] = v.w;
+            }
+        }
+        const float xc3 = x_at<Io>(a, s, t0, cs - 3, dc), xc2 = x_at<Io>(a, s, t0, cs - 2, dc);
+        const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
 #pragma unroll
-            for (int e = 0; e < kSub; ++e) {
-                const int i = i0 + e;
-                fs[e] = Front{0.0f, 0.0f, 0.0f, 0.0f};
-                if (i < n_t) {
+        for (int j = kNSub - 1; j >= 0; --j) {
+            if (j * kSub >= n_t) continue;  // uniform
+            // forward from the chunk start through sub-chunk j: hp = state before the
+            // sub-chunk, hs[e] = state after its token e, fs[e] = its front ends
+            float hp[kMaxState], hs[kSub][kMaxState];
+            Front fs[kSub];
+            {
+                float h[kMaxState];
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) h[n] = hc[n];
+                float xm3 = xc3, xm2 = xc2, xm1 = xc1;
+                for (int i = 0; i < j * kSub; ++i) {  // earlier sub-chunks: states only
                     const size_t t = t0 + static_cast<size_t>(cs + i);
                     const float xt = Io::ld(a.x, t * a.D + dc);
-                    front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), fs[e]);
+                    Front f;
+                    front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
                     xm3 = xm2;
                     xm2 = xm1;
                     xm1 = xt;
                     float b[kMaxState];
                     row16<Io, kFullN>(a.B, t, a.N, b);
-                    const float du = (fs[e].lg * kLn2) * fs[e].u;
+                    const float du = (f.lg * kLn2) * f.u;
 #pragma unroll
-                    for (int n = 0; n < kMaxState; ++n)
-                        h[n] = __builtin_fmaf(hw_exp2(fs[e].lg * ch.A[n]), h[n], du * b[n]);
+                    for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
                 }
 #pragma unroll
-                for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
-            }
-        }
+                for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
 #pragma unroll
-        for (int e = kSub - 1; e >= 0; --e) {
-            const int i = j * kSub + e;
-            if (i >= n_t) continue;  // uniform
-            const size_t t = t0 + static_cast<size_t>(cs + i);
-            const size_t ix = t * a.D + dc;
-            const Front &f = fs[e];
-            const float delta = f.lg * kLn2;
-            float br[kMaxState], cr[kMaxState];
-            row16<Io, kFullN>(a.B, t, a.N, br);
-            row16<Io, kFullN>(a.C, t, a.N, cr);
-            const float g = Io::ld(a.dout, ix);
-            float y = ch.dsk * f.u;
+                for (int e = 0; e < kSub; ++e) {
+                    const int i = j * kSub + e;
+                    fs[e] = Front{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (i < n_t) {
+                        const size_t t = t0 + static_cast<size_t>(cs + i);
+                        const float xt = Io::ld(a.x, t * a.D + dc);
+                        front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), fs[e]);
+                        xm3 = xm2;
+                        xm2 = xm1;
+                        xm1 = xt;
+                        float b[kMaxState];
+                        row16<Io, kFullN>(a.B, t, a.N, b);
+                        const float du = (fs[e].lg * kLn2) * fs[e].u;
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) y = __builtin_fmaf(cr[n], hs[e][n], y);
-            float gy = g;
-            if (has_z) {
-                const float zv = Io::ld(a.z, ix);
-                const float sz = sigmoid(zv);
-                const float dzv = g * y * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
-                if (dok) Io::st(a.dz, ix, dzv);
-                gy = g * (zv * sz);
-            }
-            dDacc = __builtin_fmaf(gy, f.u, dDacc);
-            float S1 = 0.0f, S2 = 0.0f;
-            const float dun = delta * f.u;
-            float bc[kBC];
+                        for (int n = 0; n < kMaxState; ++n)
+                            h[n] = __builtin_fmaf(hw_exp2(fs[e].lg * ch.A[n]), h[n], du * b[n]);
+                    }
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) {
-                const float hp = e > 0 ? hs[e > 0 ? e - 1 : 0][n] : hsub[j][n];
-                const float abar = hw_exp2(f.lg * ch.A[n]);
-                const float G = __builtin_fmaf(gy, cr[n], R[n]);
-                const float ga = G * abar;
-                const float q = ga * hp;
-                S1 = __builtin_fmaf(q, ch.A[n], S1);
-                dA[n] = __builtin_fmaf(q, delta, dA[n]);
-                S2 = __builtin_fmaf(G, br[n], S2);
-                R[n] = ga;
-                bc[n] = G * dun;
-                bc[kMaxState + n] = gy * hs[e][n];
+                    for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
+                }
             }
-            const float ddel = __builtin_fmaf(f.u, S2, S1);
-            const float du = __builtin_fmaf(delta, S2, gy * ch.dsk);
-            const float da = ddel * sigmoid(f.a);
-            dbacc += da;
-            const float sp = sigmoid(f.pre);
-            const float dpre = du * sp * __builtin_fmaf(f.pre, 1.0f - sp, 1.0f);
-            if (dok) {
-                Io::st(a.ddt, ix, da);
-                a.dpre[ix] = dpre;
-            }
-            // dB / dC: sum over the wave's 64 channels (padding channels add zeros)
 #pragma unroll
-            for (int k = 0; k < kBC; ++k) trow[k] = dok ? bc[k] : 0.0f;
-            __syncthreads();
-            float acc = 0.0f;
+            for (int e = kSub - 1; e >= 0; --e) {
+                const int i = j * kSub + e;
+                if (i >= n_t) continue;  // uniform
+                const size_t t = t0 + static_cast<size_t>(cs + i);
+                const size_t ix = t * a.D + dc;
+                const Front &f = fs[e];
+                const float delta = f.lg * kLn2;
+                float br[kMaxState], cr[kMaxState];
+                row16<Io, kFullN>(a.B, t, a.N, br);
+                row16<Io, kFullN>(a.C, t, a.N, cr);
+                const float g = Io::ld(a.dout, ix);
+                float y = ch.dsk * f.u;
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) y = __builtin_fmaf(cr[n], hs[e][n], y);
+                float gy = g;
+                if (has_z) {
+                    const float zv = Io::ld(a.z, ix);
+                    const float sz = sigmoid(zv);
+                    const float dzv = g * y * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
+                    if (dok) Io::st(a.dz, ix, dzv);
+                    gy = g * (zv * sz);
+                }
+                dDacc = __builtin_fmaf(gy, f.u, dDacc);
+                float S1 = 0.0f, S2 = 0.0f;
+                const float dun = dok ? delta * f.u : 0.0f;  // padding channels add zeros to dB / dC
+                const float gyc = dok ? gy : 0.0f;
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) {
+                    const float hprev = e > 0 ? hs[e > 0 ? e - 1 : 0][n] : hp[n];
+                    const float abar = hw_exp2(f.lg * ch.A[n]);
+                    const float G = __builtin_fmaf(gy, cr[n], R[n]);
+                    const float ga = G * abar;
+                    const float q = ga * hprev;
+                    S1 = __builtin_fmaf(q, ch.A[n], S1);
+                    dA[n] = __builtin_fmaf(q, delta, dA[n]);
+                    S2 = __builtin_fmaf(G, br[n], S2);
+                    R[n] = ga;
+                    trow[n] = G * dun;
+                    trow[kMaxState + n] = gyc * hs[e][n];
+                }
+                const float ddel = __builtin_fmaf(f.u, S2, S1);
+                const float du = __builtin_fmaf(delta, S2, gy * ch.dsk);
+                const float da = ddel * sigmoid(f.a);
+                dbacc += da;
+                const float sp = sigmoid(f.pre);
+                const float dpre = du * sp * __builtin_fmaf(f.pre, 1.0f - sp, 1.0f);
+                if (dok) {
+                    Io::st(a.ddt, ix, da);
+                    a.dpre[ix] = dpre;
+                }
+                // dB / dC: sum over the wave's 64 channels
+                __syncthreads();
+                float acc = 0.0f;
 #pragma unroll 8
-            for (int l = 0; l < 32; ++l) acc += tile[(rp * 32 + l) * kTilePitch + ro];
-            acc += __shfl_xor(acc, 32);
-            if (rp == 0) a.pbc[(t * a.nwave + wv) * kBC + ro] = acc;
-            __syncthreads();
+                for (int l = 0; l < 32; ++l) acc += tile[(rp * 32 + l) * kTilePitch + ro];
+                acc += __shfl_xor(acc, 32);
+                if (rp == 0) a.pbc[(t * a.nwave + wv) * kBC + ro] = acc;
+                __syncthreads();
+            }
         }
     }
     if (dok) {
-        float *pp = a.ppar + o * kPar;
+        float *pp = a.ppar + ((static_cast<size_t>(s) * a.ngroup + cg) * a.D + d) * kPar;
 #pragma unroll
         for (int n = 0; n < kMaxState; ++n) pp[n] = dA[n];
         pp[kMaxState] = dDacc;
@@ -515,39 +538,60 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a)
     seq_bounds(a, s, t0, t1);
     const int L = static_cast<int>(t1 - t0);
     const int tb = r * kRun;
-    if (tb >= L && r > 0) return;  // run 0 always runs (dconv0 of an empty sequence)
+    float *pc = a.pconv + ((static_cast<size_t>(s) * a.nrun + r) * a.D + d) * kConvPar;
+    if (tb >= L && r > 0) {  // run 0 always runs (dconv0 of an empty sequence); empty runs add zeros
+#pragma unroll
+        for (int k = 0; k < kConvPar; ++k) pc[k] = 0.0f;
+        return;
+    }
     const int te = min(tb + kRun, L);
     const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + static_cast<size_t>(d) * kConvK);
-    const float wk[kConvK] = {w.x, w.y, w.z, w.w};
-    // gradient of token tt's input from the dpre of tokens tt .. tt+3, and from dconv_final
-    auto gsrc = [&](int tt) {
-        float v = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kConvK; ++k) {
-            const int tp = tt + 3 - k;  // token whose pre-activation uses x_tt through tap k
-            if (tp >= 0 && tp < L) v = __builtin_fmaf(wk[k], a.dpre[(t0 + static_cast<size_t>(tp)) * a.D + d], v);
-        }
-        if (a.dconv_final != nullptr && tt >= L - 3)
-            v += Io::ld(a.dconv_final, (static_cast<size_t>(s) * 3 + static_cast<size_t>(tt - (L - 3))) * a.D + d);
-        return v;
+    auto dpre_at = [&](int tp) { return tp < L ? a.dpre[(t0 + static_cast<size_t>(tp)) * a.D + d] : 0.0f; };
+    auto dcf_at = [&](int tt) {  // gradient of the outgoing history entry holding token tt
+        return (a.dconv_final != nullptr && tt >= L - 3 && tt < L)
+                   ? Io::ld(a.dconv_final, (static_cast<size_t>(s) * 3 + static_cast<size_t>(tt - (L - 3))) * a.D + d)
+                   : 0.0f;
     };
-    float pw[kConvK] = {0.0f, 0.0f, 0.0f, 0.0f}, pb = 0.0f;
+    // windows: dp[k] = dpre of token t+k, xw[k] = x of token t-3+k
+    float dp0 = dpre_at(tb), dp1 = dpre_at(tb + 1), dp2 = dpre_at(tb + 2), dp3 = dpre_at(tb + 3);
+    float xw0 = x_at<Io>(a, s, t0, tb - 3, d), xw1 = x_at<Io>(a, s, t0, tb - 2, d), xw2 = x_at<Io>(a, s, t0, tb - 1, d);
+    float pw0 = 0.0f, pw1 = 0.0f, pw2 = 0.0f, pw3 = 0.0f, pb = 0.0f;
     for (int t = tb; t < te; ++t) {
         const size_t ix = (t0 + static_cast<size_t>(t)) * a.D + d;
-        Io::st(a.dx, ix, gsrc(t));
-        const float dp = a.dpre[ix];
-        pb += dp;
-#pragma unroll
-        for (int k = 0; k < kConvK; ++k) pw[k] = __builtin_fmaf(dp, x_at<Io>(a, s, t0, t - 3 + k, d), pw[k]);
+        const float xt = Io::ld(a.x, ix);
+        float g = __builtin_fmaf(w.w, dp0, __builtin_fmaf(w.z, dp1, __builtin_fmaf(w.y, dp2, w.x * dp3)));
+        if (t >= L - 3) g += dcf_at(t);  // uniform over the workgroup
+        Io::st(a.dx, ix, g);
+        pb += dp0;
+        pw0 = __builtin_fmaf(dp0, xw0, pw0);
+        pw1 = __builtin_fmaf(dp0, xw1, pw1);
+        pw2 = __builtin_fmaf(dp0, xw2, pw2);
+        pw3 = __builtin_fmaf(dp0, xt, pw3);
+        xw0 = xw1;
+        xw1 = xw2;
+        xw2 = xt;
+        dp0 = dp1;
+        dp1 = dp2;
+        dp2 = dp3;
+        dp3 = dpre_at(t + 4);
     }
     if (r == 0 && a.dconv0 != nullptr) {
+        // history entry jj holds token jj - 3, whose input feeds the pre-activations of
+        // tokens jj - 3 + 3 - k = jj - k through tap k
 #pragma unroll
-        for (int jj = 0; jj < 3; ++jj)
-            Io::st(a.dconv0, (static_cast<size_t>(s) * 3 + jj) * a.D + d, gsrc(jj - 3));
+        for (int jj = 0; jj < 3; ++jj) {
+            const float wk[kConvK] = {w.x, w.y, w.z, w.w};
+            float g = dcf_at(jj - 3);
+#pragma unroll
+            for (int k = 0; k < kConvK; ++k)
+                if (jj - k >= 0) g = __builtin_fmaf(wk[k], dpre_at(jj - k), g);
+            Io::st(a.dconv0, (static_cast<size_t>(s) * 3 + jj) * a.D + d, g);
+        }
     }
-    float *pc = a.pconv + ((static_cast<size_t>(s) * a.nrun + r) * a.D + d) * kConvPar;
-#pragma unroll
-    for (int k = 0; k < kConvK; ++k) pc[k] = pw[k];
+    pc[0] = pw0;
+    pc[1] = pw1;
+    pc[2] = pw2;
+    pc[3] = pw3;
     pc[kConvK] = pb;
 }
 
@@ -568,36 +612,35 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs a)
     Io::st(k < kMaxState ? a.dB : a.dC, t * a.N + n, acc);
 }
 
-// Parameters: grid ceil(D / 256), one thread per channel; sums over (sequence, chunk) and
-// (sequence, run).
+// Parameters, stage 1: column sums of a [rows][cols] partial matrix over the rows r = split
+// (mod nsplit); grid (ceil(cols / 256), nsplit).  Stage 2 adds the nsplit sums in order, so
+// the result does not depend on timing.
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(const float *__restrict__ m, int rows, int cols, int nsplit,
+                                                        float *__restrict__ out)
+{
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= cols) return;
+    float acc = 0.0f;
+    for (int r = blockIdx.y; r < rows; r += nsplit) acc += m[static_cast<size_t>(r) * cols + col];
+    out[static_cast<size_t>(blockIdx.y) * cols + col] = acc;
+}
+
+// Parameters, stage 2: one thread per channel.
 __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs a)
 {
     using namespace bwd;
     const int d = blockIdx.x * 256 + threadIdx.x;
     if (d >= a.D) return;
-    float acc[kPar];
+    float acc[kPar], cw[kConvPar];
 #pragma unroll
     for (int k = 0; k < kPar; ++k) acc[k] = 0.0f;
-    for (int s = 0; s < a.nseq; ++s) {
-        size_t t0, t1;
-        seq_bounds(a, s, t0, t1);
-        const int nc = min((static_cast<int>(t1 - t0) + kChunk - 1) / kChunk, a.nchunk);
-        for (int c = 0; c < nc; ++c) {
-            const float *pp = a.ppar + ((static_cast<size_t>(s) * a.nchunk + c) * a.D + d) * kPar;
 #pragma unroll
-            for (int k = 0; k < kPar; ++k) acc[k] += pp[k];
-        }
-    }
-    float cw[kConvPar] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < a.nseq; ++s) {
-        size_t t0, t1;
-        seq_bounds(a, s, t0, t1);
-        const int nr = min(max(1, (static_cast<int>(t1 - t0) + kRun - 1) / kRun), a.nrun);
-        for (int r = 0; r < nr; ++r) {
-            const float *pc = a.pconv + ((static_cast<size_t>(s) * a.nrun + r) * a.D + d) * kConvPar;
+    for (int k = 0; k < kConvPar; ++k) cw[k] = 0.0f;
+    for (int sp = 0; sp < kSplit; ++sp) {
 #pragma unroll
-            for (int k = 0; k < kConvPar; ++k) cw[k] += pc[k];
-        }
+        for (int k = 0; k < kPar; ++k) acc[k] += a.par2[(static_cast<size_t>(sp) * a.D + d) * kPar + k];
+#pragma unroll
+        for (int k = 0; k < kConvPar; ++k) cw[k] += a.conv2[(static_cast<size_t>(sp) * a.D + d) * kConvPar + k];
     }
     for (int n = 0; n < a.N; ++n) a.dA[static_cast<size_t>(d) * a.N + n] = acc[n];
     a.dD[d] = acc[kMaxState];
@@ -610,7 +653,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs a)
 // ---------------------------------------------------------------- host side
 // Workspace layout (offsets in floats), every part 256-byte aligned.
 struct BwdWorkspace {
-    size_t hck, eck, lsum, dpre, ppar, pbc, pconv, total_bytes;
+    size_t hck, eck, lsum, dpre, ppar, pbc, pconv, par2, conv2, total_bytes;
 };
 
 inline BwdWorkspace bwd_workspace(int nseq, int seqlen, int total, int D)
@@ -618,6 +661,7 @@ inline BwdWorkspace bwd_workspace(int nseq, int seqlen, int total, int D)
     using namespace bwd;
     auto al = [](size_t f) { return (f + 63) / 64 * 64; };
     const size_t nchunk = (static_cast<size_t>(seqlen) + kChunk - 1) / kChunk;
+    const size_t ngroup = (nchunk + kGroup - 1) / kGroup;
     const size_t nrun = std::max<size_t>(1, (static_cast<size_t>(seqlen) + kRun - 1) / kRun);
     const size_t nwave = (static_cast<size_t>(D) + kLanes - 1) / kLanes;
     const size_t sc = static_cast<size_t>(nseq) * nchunk * D;
@@ -632,11 +676,15 @@ inline BwdWorkspace bwd_workspace(int nseq, int seqlen, int total, int D)
     w.dpre = off;
     off += al(static_cast<size_t>(total) * D);
     w.ppar = off;
-    off += al(sc * kPar);
+    off += al(static_cast<size_t>(nseq) * ngroup * D * kPar);
     w.pbc = off;
     off += al(static_cast<size_t>(total) * nwave * kBC);
     w.pconv = off;
     off += al(static_cast<size_t>(nseq) * nrun * D * kConvPar);
+    w.par2 = off;
+    off += al(static_cast<size_t>(kSplit) * D * kPar);
+    w.conv2 = off;
+    off += al(static_cast<size_t>(kSplit) * D * kConvPar);
     w.total_bytes = off * sizeof(float);
     return w;
 }
@@ -655,6 +703,9 @@ inline void launch_backward(BwdArgs a, float *ws, samba_dtype io, hipStream_t st
     a.ppar = ws + w.ppar;
     a.pbc = ws + w.pbc;
     a.pconv = ws + w.pconv;
+    a.par2 = ws + w.par2;
+    a.conv2 = ws + w.conv2;
+    a.ngroup = (a.nchunk + kGroup - 1) / kGroup;
     const bool full = a.N == kMaxState;
     const dim3 g3(a.nwave, std::max(1, a.nchunk), a.nseq), b64(kLanes);
     if (a.nchunk > 0) {
@@ -666,14 +717,15 @@ inline void launch_backward(BwdArgs a, float *ws, samba_dtype io, hipStream_t st
             else bwd_local_kernel<IoF32, false><<<g3, b64, 0, stream>>>(a);
         }
     }
-    bwd_carry_kernel<<<dim3(a.nwave, a.nseq), b64, 0, stream>>>(a);
+    bwd_carry_kernel<<<dim3((a.D * kMaxState + 255) / 256, a.nseq), 256, 0, stream>>>(a);
     if (a.nchunk > 0) {
+        const dim3 gg(a.nwave, a.ngroup, a.nseq);
         if (io == SAMBA_BF16) {
-            if (full) bwd_full_kernel<IoBf16, true><<<g3, b64, 0, stream>>>(a);
-            else bwd_full_kernel<IoBf16, false><<<g3, b64, 0, stream>>>(a);
+            if (full) bwd_full_kernel<IoBf16, true><<<gg, b64, 0, stream>>>(a);
+            else bwd_full_kernel<IoBf16, false><<<gg, b64, 0, stream>>>(a);
         } else {
-            if (full) bwd_full_kernel<IoF32, true><<<g3, b64, 0, stream>>>(a);
-            else bwd_full_kernel<IoF32, false><<<g3, b64, 0, stream>>>(a);
+            if (full) bwd_full_kernel<IoF32, true><<<gg, b64, 0, stream>>>(a);
+            else bwd_full_kernel<IoF32, false><<<gg, b64, 0, stream>>>(a);
         }
     }
     const dim3 gc(static_cast<unsigned>(a.nrun) * static_cast<unsigned>(a.nseq), (a.D + 255) / 256);
@@ -684,6 +736,16 @@ inline void launch_backward(BwdArgs a, float *ws, samba_dtype io, hipStream_t st
         const unsigned gb = static_cast<unsigned>((nbc + 255) / 256);
         if (io == SAMBA_BF16) bwd_reduce_bc_kernel<IoBf16><<<gb, 256, 0, stream>>>(a);
         else bwd_reduce_bc_kernel<IoF32><<<gb, 256, 0, stream>>>(a);
+    }
+    {
+        const int pcols = a.D * kPar, ccols = a.D * kConvPar;
+        if (a.nchunk > 0)
+            bwd_colsum_kernel<<<dim3((pcols + 255) / 256, kSplit), 256, 0, stream>>>(a.ppar, a.nseq * a.ngroup, pcols,
+                                                                                     kSplit, a.par2);
+        else  // no chunk at all: the stage-2 sums read zeros
+            bwd_colsum_kernel<<<dim3((pcols + 255) / 256, kSplit), 256, 0, stream>>>(a.ppar, 0, pcols, kSplit, a.par2);
+        bwd_colsum_kernel<<<dim3((ccols + 255) / 256, kSplit), 256, 0, stream>>>(a.pconv, a.nseq * a.nrun, ccols,
+                                                                                 kSplit, a.conv2);
     }
     bwd_reduce_par_kernel<<<(a.D + 255) / 256, 256, 0, stream>>>(a);
 }

@@ -74,6 +74,22 @@ def test_long_prompt_prefill_131072():
     assert torch.isfinite(y.float()).all()
 
 
+def test_training_length_backward_4x4096():
+    """Gradients at the training shape (batch 4, L = 4096), every output against the
+    oracle's gradients over all 4096 channels (dB and dC are sums over all of them)."""
+    seed = synth.seed_for(1)
+    print("case: backward batch 4 L 4096", flush=True)
+    p = synth.make_params(seed, D, N)
+    tk = synth.make_tokens(seed, (4, 4096), D, N, "bf16")
+    g = synth.make_tokens(seed, (4, 4096), D, N, "bf16", tag="grad").x
+    got = ss.backward(bf16(g), bf16(tk.x), bf16(tk.dt), bf16(tk.B), bf16(tk.C), bf16(tk.z), *params_dev(p))
+    got = {k: None if v is None else v.float().cpu().numpy() for k, v in got.items()}
+    torch.cuda.synchronize()
+    ref = oracle.backward(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, g)
+    for k in ("dx", "ddt", "dz", "dB", "dC", "dA", "dD", "ddt_bias", "dconv_w", "dconv_b", "dh0", "dconv0"):
+        check(k, got[k], ref[k])
+
+
 def test_long_prompt_conv_silu_alone():
     """The conv-only entry point on the long prompt (the launch bench.py times)."""
     seed = synth.seed_for(2)
