@@ -287,11 +287,12 @@ def traffic_probe(dev, steps=3):
 
 
 def kernel_source_hash():
+    """Hash of the sources that define the long-prompt prefill kernel (the two-role row
+    kernel and the helpers it includes)."""
     import hashlib
-    from selective_state_space_samba_amd import build as b
     h = hashlib.sha256()
-    for f in b.sources():
-        h.update(open(f, "rb").read())
+    for f in ("scan_common.h", "scan_rows.h", "scan_split.h"):
+        h.update(open(os.path.join(ROOT, "selective_state_space_samba_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
