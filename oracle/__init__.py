@@ -63,6 +63,10 @@ def _declare(lib):
     lib.oracle_conv_silu_varlen.restype = None
     lib.oracle_backward.argtypes = [I, P, I, I] + [P] * 27
     lib.oracle_backward.restype = None
+    lib.oracle_rope.argtypes = [P, I, ctypes.c_double, ctypes.c_double]
+    lib.oracle_rope.restype = None
+    lib.oracle_swa.argtypes = [I, P, I, I, I, I, ctypes.c_double, P, P, P, P, P, I]
+    lib.oracle_swa.restype = None
     for f in (lib.oracle_scan_sequence, lib.oracle_prefill, lib.oracle_varlen, lib.oracle_decode_step):
         f.restype = None
 
@@ -281,6 +285,39 @@ def backward(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, dout, h0=None, c
         for k in ("dB", "dC"):
             out[k] = out[k].reshape(b, L, N)
     return out
+
+
+def rope(vec, pos, base=10000.0):
+    """RoPE of one head vector at position pos (pairs (2i, 2i+1), angle pos * base^(-2i/dh))."""
+    v = _f64(np.array(vec, dtype=np.float64))
+    _load().oracle_rope(_ptr(v), v.shape[0], float(pos), float(base))
+    return v
+
+
+def swa(q, k, v, window=2048, base=10000.0, cu_seqlens=None, rows=None):
+    """Sliding window attention with RoPE and grouped KV heads.  Fixed length: q [b, L, Hq, dh],
+    k, v [b, L, Hkv, dh]; packed: [T, H, dh] with cu_seqlens.  ``rows`` (flat token indices)
+    restricts the computed query tokens; other output rows are NaN.  Returns out shaped like q
+    (float64)."""
+    lib = _load()
+    q = np.asarray(q)
+    fixed = cu_seqlens is None
+    if fixed:
+        b, L = q.shape[:2]
+        cu = (np.arange(b + 1) * L).astype(np.int32)
+        flat = lambda a: np.asarray(a).reshape((b * L,) + np.asarray(a).shape[2:])
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        flat = lambda a: np.asarray(a)
+    qs, ks, vs = _f64(flat(q)), _f64(flat(k)), _f64(flat(v))
+    T, Hq, dh = qs.shape
+    Hkv = ks.shape[1]
+    assert Hq % Hkv == 0 and dh % 2 == 0
+    out = np.full((T, Hq, dh), np.nan)
+    rr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    lib.oracle_swa(cu.shape[0] - 1, _ptr(cu), Hq, Hkv, dh, int(window), float(base), _ptr(qs), _ptr(ks), _ptr(vs),
+                   _ptr(out), _ptr(rr), 0 if rr is None else rr.shape[0])
+    return out.reshape(q.shape) if fixed else out
 
 
 def timed(fn, *args, **kw):

@@ -391,6 +391,82 @@ void oracle_backward(int nseq, const int32_t *cu, int nch, int N,
     free(lC);
 }
 
+/*
+ * Sliding window attention ([P1] "The Sliding Window Attention (SWA) Layer": "Window
+ * Specification", "Positional Encoding").
+ *
+ * RoPE as in Su et al. (the formulation [P1] names): the pairs (2i, 2i+1) of a head vector at
+ * position p are rotated by the angle p * base^(-2i/dh).  The angle is formed in double
+ * precision.
+ */
+void oracle_rope(double *v, int dh, double pos, double base)
+{
+    int i;
+    for (i = 0; i < dh / 2; ++i) {
+        const double th = pos * pow(base, -2.0 * i / dh);
+        const double c = cos(th), sn = sin(th), a = v[2 * i], b = v[2 * i + 1];
+        v[2 * i] = a * c - b * sn;
+        v[2 * i + 1] = a * sn + b * c;
+    }
+}
+
+/*
+ * Causal attention restricted to a window: the query at position t of a sequence attends to
+ * the keys at positions t - window .. t of the same sequence ("for position t, the attention
+ * computation includes positions t-w through t"), after RoPE on queries and keys; scores
+ * are scaled by 1/sqrt(dh) and normalised by softmax.  Grouped-query attention: query head
+ * h reads key/value head h / (Hq / Hkv).
+ *   q [T][Hq][dh], k, v [T][Hkv][dh], out [T][Hq][dh]; sequence s covers tokens
+ *   [cu[s], cu[s+1]) and its positions start at 0.
+ *   rows (nrows entries, or NULL for all T): the query tokens to compute (out rows of the
+ *   others are left untouched).
+ */
+void oracle_swa(int nseq, const int32_t *cu, int Hq, int Hkv, int dh, int window, double base,
+                const double *q, const double *k, const double *v, double *out, const int32_t *rows,
+                int nrows)
+{
+    const int T = cu[nseq];
+    const int nr = rows ? nrows : T;
+    const int group = Hq / Hkv;
+    int it;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (it = 0; it < nr; ++it) {
+        const int t = rows ? rows[it] : it;
+        int s = 0, h, j, e;
+        double *qv = (double *)malloc(sizeof(double) * dh), *kv = (double *)malloc(sizeof(double) * dh);
+        double *sc = (double *)malloc(sizeof(double) * (window + 1));
+        while (!(cu[s] <= t && t < cu[s + 1])) ++s;
+        for (h = 0; h < Hq; ++h) {
+            const int hk = h / group;
+            const int t0 = cu[s];
+            const int lo = t - window > t0 ? t - window : t0;
+            double mx = -INFINITY, sum = 0.0;
+            for (e = 0; e < dh; ++e) qv[e] = q[((size_t)t * Hq + h) * dh + e];
+            oracle_rope(qv, dh, (double)(t - t0), base);
+            for (j = lo; j <= t; ++j) {
+                double dot = 0.0;
+                for (e = 0; e < dh; ++e) kv[e] = k[((size_t)j * Hkv + hk) * dh + e];
+                oracle_rope(kv, dh, (double)(j - t0), base);
+                for (e = 0; e < dh; ++e) dot += qv[e] * kv[e];
+                sc[j - lo] = dot / sqrt((double)dh);
+                if (sc[j - lo] > mx) mx = sc[j - lo];
+            }
+            for (j = lo; j <= t; ++j) {
+                sc[j - lo] = exp(sc[j - lo] - mx);
+                sum += sc[j - lo];
+            }
+            for (e = 0; e < dh; ++e) {
+                double acc = 0.0;
+                for (j = lo; j <= t; ++j) acc += sc[j - lo] * v[((size_t)j * Hkv + hk) * dh + e];
+                out[((size_t)t * Hq + h) * dh + e] = acc / sum;
+            }
+        }
+        free(qv);
+        free(kv);
+        free(sc);
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

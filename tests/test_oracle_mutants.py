@@ -54,6 +54,14 @@ MUTANTS = {
         "const double hp = t > 0 ? hs[(size_t)(t - 1) * N + n] : h0[(size_t)d * N + n];",
         "const double hp = hs[(size_t)t * N + n];"),
     "bwd_softplus_derivative_dropped": ("da = ddel * sigm(av[t]);", "da = ddel;"),
+    "swa_window_off_by_one": ("const int lo = t - window > t0 ? t - window : t0;",
+                              "const int lo = t - window + 1 > t0 ? t - window + 1 : t0;"),
+    "swa_rope_rotation_reversed": ("v[2 * i] = a * c - b * sn;\n        v[2 * i + 1] = a * sn + b * c;",
+                                   "v[2 * i] = a * c + b * sn;\n        v[2 * i + 1] = -a * sn + b * c;"),
+    "swa_rope_frequency_exponent": ("pow(base, -2.0 * i / dh)", "pow(base, -1.0 * i / dh)"),
+    "swa_scale_missing": ("sc[j - lo] = dot / sqrt((double)dh);", "sc[j - lo] = dot;"),
+    "swa_kv_head_interleaved": ("const int hk = h / group;", "const int hk = h % Hkv;"),
+    "swa_absolute_positions": ("oracle_rope(kv, dh, (double)(j - t0), base);", "oracle_rope(kv, dh, (double)j, base);"),
     "history_not_carried_in": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];",
                                "for (k = 0; k < ORACLE_K - 1; ++k) win[k] = 0.0;"),
 }
@@ -72,6 +80,8 @@ def _run_pins():
             variants = [{"with_h0": False}, {"with_h0": True}]
         if "gate" in params:
             variants = [{"gate": True}, {"gate": False}]
+        if "Hq" in params:
+            variants = [{"Hq": 4, "Hkv": 4}, {"Hq": 6, "Hkv": 2}]
         for kw in variants:
             try:
                 fn(**kw)

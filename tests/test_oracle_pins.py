@@ -482,3 +482,93 @@ def test_backward_packed_short_sequences_match_finite_differences():
     """Packed sequences of 0, 1, 2 and 5 tokens: gradients reach the incoming history and
     state through sequences shorter than the conv window."""
     _fd_check(_grad_case(np.random.default_rng(91), None, None, 2, 3, packed_lens=[0, 1, 2, 5]), packed_lens=True)
+
+
+# ---------------------------------------------------------------- P10: sliding window attention
+def torch_rope(x, pos, base=10000.0):
+    """RoPE as a complex product: pair (2i, 2i+1) -> (x_2i + i x_2i+1) * exp(i pos theta_i),
+    theta_i = base^(-2i/dh).  x [..., L, H, dh] (float64 numpy), pos [L]."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    dh = t.shape[-1]
+    theta = base ** (-torch.arange(0, dh, 2, dtype=torch.float64) / dh)
+    ang = torch.from_numpy(np.asarray(pos, dtype=np.float64))[:, None] * theta[None, :]   # [L, dh/2]
+    rot = torch.polar(torch.ones_like(ang), ang)[:, None, :]                              # [L, 1, dh/2]
+    z = torch.view_as_complex(t.reshape(t.shape[:-1] + (dh // 2, 2)).contiguous()) * rot
+    return torch.view_as_real(z).reshape(t.shape).numpy()
+
+
+def torch_causal_attention(q, k, v):
+    """Plain causal softmax attention (torch SDPA, float64), grouped KV heads repeated.
+    q [L, Hq, dh], k, v [L, Hkv, dh] -> [L, Hq, dh]."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_rope_closed_form_and_relative_property():
+    rng = np.random.default_rng(100)
+    a, b = rng.standard_normal(2)
+    for p in (0.0, 1.0, 7.0, 1000.0):
+        np.testing.assert_allclose(oracle.rope([a, b], p), [a * np.cos(p) - b * np.sin(p), a * np.sin(p) + b * np.cos(p)],
+                                   rtol=1e-12, atol=1e-12)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    d0 = oracle.rope(q, 130.0) @ oracle.rope(k, 100.0)
+    for shift in (1.0, 57.0, 4096.0):
+        np.testing.assert_allclose(oracle.rope(q, 130.0 + shift) @ oracle.rope(k, 100.0 + shift), d0, rtol=1e-10)
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, 123.0)), np.linalg.norm(q), rtol=1e-13)
+    np.testing.assert_allclose(oracle.rope(q, 37.0), torch_rope(q[None, None, :], [37.0])[0, 0], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 1), (6, 2)])
+def test_swa_full_window_is_causal_attention(Hq, Hkv):
+    """A window longer than the sequence is plain causal attention (torch SDPA in float64
+    on queries and keys rotated by the complex-product RoPE)."""
+    rng = np.random.default_rng(101)
+    L, dh = 40, 16
+    q, k, v = rng.standard_normal((L, Hq, dh)), rng.standard_normal((L, Hkv, dh)), rng.standard_normal((L, Hkv, dh))
+    out = oracle.swa(q, k, v, window=L + 5, cu_seqlens=np.array([0, L]))
+    pos = np.arange(L)
+    ref = torch_causal_attention(torch_rope(q, pos), torch_rope(k, pos), v)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_swa_window_brute_force_and_locality():
+    """Window 5 against explicit per-query softmax over keys t-5..t; keys outside the window
+    have no effect, a key inside it does."""
+    rng = np.random.default_rng(102)
+    L, Hq, Hkv, dh, w = 23, 2, 1, 8, 5
+    q, k, v = rng.standard_normal((L, Hq, dh)), rng.standard_normal((L, Hkv, dh)), rng.standard_normal((L, Hkv, dh))
+    cu = np.array([0, L])
+    out = oracle.swa(q, k, v, window=w, cu_seqlens=cu)
+    qr, kr = torch_rope(q, np.arange(L)), torch_rope(k, np.arange(L))
+    for t in range(L):
+        keys = np.arange(max(0, t - w), t + 1)
+        for h in range(Hq):
+            sc = kr[keys, 0] @ qr[t, h] / np.sqrt(dh)
+            p = np.exp(sc - sc.max())
+            np.testing.assert_allclose(out[t, h], (p / p.sum()) @ v[keys, 0], rtol=1e-12, atol=1e-12)
+    t = 15
+    k2, v2 = k.copy(), v.copy()
+    k2[t - w - 1] += 5.0
+    v2[t - w - 1] += 5.0
+    np.testing.assert_array_equal(oracle.swa(q, k2, v2, window=w, cu_seqlens=cu)[t], out[t])
+    k2[t - w] += 5.0
+    assert np.abs(oracle.swa(q, k2, v2, window=w, cu_seqlens=cu)[t] - out[t]).max() > 1e-3
+
+
+def test_swa_packed_equals_separate_sequences():
+    """Positions restart at every sequence and no key crosses a sequence boundary."""
+    rng = np.random.default_rng(103)
+    lens = [7, 1, 12, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, Hq, Hkv, dh = int(cu[-1]), 4, 2, 8
+    q, k, v = rng.standard_normal((T, Hq, dh)), rng.standard_normal((T, Hkv, dh)), rng.standard_normal((T, Hkv, dh))
+    out = oracle.swa(q, k, v, window=4, cu_seqlens=cu)
+    for i, n in enumerate(lens):
+        sl = slice(cu[i], cu[i + 1])
+        if n:
+            ref = oracle.swa(q[sl], k[sl], v[sl], window=4, cu_seqlens=np.array([0, n]))
+            np.testing.assert_array_equal(out[sl], ref)
