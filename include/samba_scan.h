@@ -193,6 +193,30 @@ samba_status samba_scan_backward(int nseq, const int32_t *cu_seqlens, int seqlen
                                  float *dA, float *dD, float *ddt_bias, float *dconv_w, float *dconv_b,
                                  float *dh0, void *dconv0, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size in bytes of the device workspace samba_swa_prefill needs (the rotated keys). */
+size_t samba_swa_workspace_bytes(int total_tokens, int n_kv_heads, int head_dim);
+
+/* Sliding window attention, the other sequence mixer of the Samba layer stack (page 1,
+ * "The Sliding Window Attention (SWA) Layer"): the query at position t of a sequence
+ * attends to the keys at positions t - window .. t of the same sequence ("Window
+ * Specification"), queries and keys rotated by RoPE with base rope_base ("Positional
+ * Encoding"; pairs (2i, 2i+1) turn by position * base^(-2i/head_dim), positions counting
+ * from each sequence start), softmax of the scores scaled by 1/sqrt(head_dim).  Query
+ * head h reads key/value head h / (n_heads / n_kv_heads) (grouped-query attention, as in
+ * the pages' 1.7B and 3.8B configurations).
+ *   cu_seqlens NULL: nseq sequences of seqlen tokens, q, out [nseq][seqlen][n_heads][head_dim],
+ *              k, v [nseq][seqlen][n_kv_heads][head_dim]; total_tokens is ignored.
+ *              Non-NULL: packed as for samba_scan_varlen ([total_tokens][heads][head_dim]),
+ *              seqlen = the longest sequence.
+ *   io must be SAMBA_BF16 (the matrix-core operand type; SAMBA_ERR_UNSUPPORTED otherwise);
+ *   head_dim 64 or 128 (SAMBA_ERR_UNSUPPORTED otherwise); window >= 0; rope_base > 1.
+ *   workspace: at least samba_swa_workspace_bytes() bytes, 16-byte aligned.
+ * out must not overlap the inputs or the workspace. */
+samba_status samba_swa_prefill(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int n_heads,
+                               int n_kv_heads, int head_dim, int window, float rope_base, samba_dtype io,
+                               const void *q, const void *k, const void *v, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char *samba_last_error(void);

@@ -5,8 +5,8 @@ A thin ctypes layer over ``libsamba_scan.so`` (C ABI declared in
 and the current HIP stream; every step of the computation runs in the library's HIP
 kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
 
-Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``, ``conv_silu`` and
-``backward``.
+Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``, ``conv_silu``,
+``backward`` and ``swa`` (sliding window attention).
 """
 from __future__ import annotations
 
@@ -16,8 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "workspace_bytes", "lib_path", "SambaError",
-           "version"]
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "workspace_bytes", "lib_path",
+           "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
@@ -67,6 +67,10 @@ def load():
         lib.samba_scan_backward.restype = I
         lib.samba_scan_backward.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P,
                                             P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.samba_swa_workspace_bytes.restype = Z
+        lib.samba_swa_workspace_bytes.argtypes = [I, I, I]
+        lib.samba_swa_prefill.restype = I
+        lib.samba_swa_prefill.argtypes = [I, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, Z, P]
         lib.samba_conv_silu.restype = I
         lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
         _lib = lib
@@ -340,3 +344,38 @@ def backward(dout, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, c
         _ptr(workspace, "workspace"), wsb, _stream(dev))
     _check(st)
     return g
+
+
+def swa(q, k, v, *, window=2048, rope_base=10000.0, cu_seqlens=None, max_seqlen=None, out=None, workspace=None):
+    """Sliding window attention with RoPE and grouped KV heads (bfloat16).  Fixed length:
+    q [b, L, Hq, dh], k, v [b, L, Hkv, dh]; packed: [T, H, dh] with cu_seqlens (int32
+    [nseq+1] on the GPU) and max_seqlen.  Returns out shaped like q."""
+    dev = _gpu_device(q)
+    io = _io(q)
+    if cu_seqlens is None:
+        b, L, Hq, dh = q.shape
+        nseq, total = b, b * L
+    else:
+        T, Hq, dh = q.shape
+        nseq = cu_seqlens.numel() - 1
+        total = T
+        _shape(cu_seqlens, (nseq + 1,), "cu_seqlens")
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+        L = int(max_seqlen)
+    Hkv = k.shape[-2]
+    _shape(k, tuple(q.shape[:-2]) + (Hkv, dh), "k")
+    _shape(v, tuple(k.shape), "v")
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, tuple(q.shape), "out")
+    need = int(load().samba_swa_workspace_bytes(total, Hkv, dh))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().samba_swa_prefill(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), L, total, Hq, Hkv, dh, int(window), float(rope_base),
+        io, _ptr(q, "q", q.dtype, dev), _ptr(k, "k", q.dtype, dev), _ptr(v, "v", q.dtype, dev),
+        _ptr(out, "out", q.dtype, dev), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(dev))
+    _check(st)
+    return out

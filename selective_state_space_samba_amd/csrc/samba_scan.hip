@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
@@ -26,6 +27,7 @@
 #include "scan_decode.h"
 #include "scan_conv.h"
 #include "scan_bwd.h"
+#include "scan_swa.h"
 
 
 namespace {
@@ -454,6 +456,79 @@ samba_status samba_scan_backward(int nseq, const int32_t *cu_seqlens, int seqlen
     a.dh0 = dh0;
     a.dconv0 = dconv0;
     samba::launch_backward(a, static_cast<float *>(workspace), io, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+size_t samba_swa_workspace_bytes(int total_tokens, int n_kv_heads, int head_dim)
+{
+    if (total_tokens <= 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
+    return samba::swa_workspace_bytes(total_tokens, n_kv_heads, head_dim);
+}
+
+samba_status samba_swa_prefill(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int n_heads,
+                               int n_kv_heads, int head_dim, int window, float rope_base, samba_dtype io,
+                               const void *q, const void *k, const void *v, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    const char *fn = "samba_swa_prefill";
+    if (nseq < 0 || seqlen < 0 || (cu_seqlens != nullptr && total_tokens < 0) || window < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d seqlen=%d total_tokens=%d window=%d must be >= 0", fn, nseq,
+                    seqlen, total_tokens, window);
+    if (io != SAMBA_BF16)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: io dtype %d: attention takes bfloat16 (the matrix-core operand type)",
+                    fn, (int)io);
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: n_heads=%d must be a positive multiple of n_kv_heads=%d", fn, n_heads,
+                    n_kv_heads);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: head_dim=%d (64 and 128 are built)", fn, head_dim);
+    if (!(rope_base > 1.0f)) return fail(SAMBA_ERR_INVALID_ARG, "%s: rope_base must be > 1", fn);
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    size_t tokens;
+    if (cu_seqlens != nullptr) {
+        if (seqlen > total_tokens)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total_tokens=%d", fn, seqlen, total_tokens);
+        tokens = static_cast<size_t>(total_tokens);
+    } else {
+        tokens = static_cast<size_t>(nseq) * static_cast<size_t>(seqlen);
+        if (tokens > static_cast<size_t>(INT32_MAX))
+            return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq*seqlen=%zu exceeds 2^31-1 tokens", fn, tokens);
+    }
+    if (static_cast<double>(nseq) * n_heads * ((seqlen + 63) / 64) > 2147483647.0)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq x n_heads x row blocks exceeds 2^31-1 workgroups", fn);
+    if (tokens == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(out, "out");
+    const size_t need = samba::swa_workspace_bytes(static_cast<int>(tokens), n_kv_heads, head_dim);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    REQUIRE_PTR(workspace, "workspace");
+    samba::SwaArgs a{};
+    a.nseq = nseq;
+    a.seqlen = seqlen;
+    a.cu = cu_seqlens;
+    a.total = static_cast<int>(tokens);
+    a.Hq = n_heads;
+    a.Hkv = n_kv_heads;
+    a.dh = head_dim;
+    a.window = window;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.krot = static_cast<uint16_t *>(workspace);
+    samba::swa_set_theta(a, static_cast<double>(rope_base));
+    samba::launch_swa(a, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 

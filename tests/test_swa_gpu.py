@@ -1,0 +1,121 @@
+"""GPU parity of sliding window attention (RoPE, grouped KV heads, bfloat16 matrix-core
+operands) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_samba_amd as ss
+from selective_state_space_samba_amd import synth
+from tests.helpers import TOL, host, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def bf16_round(a):
+    """The values the GPU sees: float32 -> bfloat16 (round to nearest even) -> float64."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def make_qkv(seed, lead, Hq, Hkv, dh):
+    rng = np.random.default_rng(seed)
+    q = bf16_round(rng.standard_normal(lead + (Hq, dh)))
+    k = bf16_round(rng.standard_normal(lead + (Hkv, dh)))
+    v = bf16_round(rng.standard_normal(lead + (Hkv, dh)))
+    return q, k, v
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def run(q, k, v, window, cu=None, max_seqlen=None, rows=None):
+    print("case: swa q", q.shape, "kv heads", k.shape[-2], "window", window, "packed", cu is not None, flush=True)
+    o = ss.swa(dev(q), dev(k), dev(v), window=window,
+               cu_seqlens=None if cu is None else torch.from_numpy(cu).to(DEV), max_seqlen=max_seqlen)
+    got = host(o)
+    torch.cuda.synchronize()
+    ref = oracle.swa(q, k, v, window=window, cu_seqlens=cu, rows=rows)
+    return got, ref
+
+
+def check(got, ref, rows=None):
+    if rows is not None:
+        got = got.reshape((-1,) + got.shape[-2:])[rows]
+        ref = ref.reshape((-1,) + ref.shape[-2:])[rows]
+    e = rel_err(got, ref)
+    print("  out err %.3e (tol %.0e)" % (e, TOL["bf16"]), flush=True)
+    assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("window", [0, 1, 70, 128, 500])
+def test_swa_fixed_length(dh, window):
+    """L = 200: three full 64-row blocks and a ragged one; windows shorter than a tile, at a
+    tile multiple, and longer than the sequence."""
+    q, k, v = make_qkv(3000 + dh + window, (2, 200), 4, 2, dh)
+    check(*run(q, k, v, window))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (6, 3), (4, 4)])
+def test_swa_grouped_heads(Hq, Hkv):
+    q, k, v = make_qkv(3100 + Hq * 10 + Hkv, (1, 150), Hq, Hkv, 64)
+    check(*run(q, k, v, 96))
+
+
+def test_swa_packed():
+    lens = [0, 1, 5, 64, 65, 130, 0, 200]
+    cu = synth.cu_from_lengths(lens)
+    q, k, v = make_qkv(3200, (int(cu[-1]),), 4, 2, 64)
+    check(*run(q, k, v, 100, cu=cu, max_seqlen=max(lens)))
+
+
+def test_swa_large_positions():
+    """Positions past 100K (RoPE angles reduced exactly on the GPU): a 66-token packed
+    sequence after a 131072-token one, checked on the second sequence and the first one's
+    last rows."""
+    lens = [131072, 66]
+    cu = synth.cu_from_lengths(lens)
+    T = int(cu[-1])
+    q, k, v = make_qkv(3300, (T,), 2, 1, 64)
+    rows = np.concatenate([np.arange(131072 - 70, 131072), np.arange(131072, T)])
+    got, ref = run(q, k, v, 2048, cu=cu, max_seqlen=max(lens), rows=rows)
+    check(got, ref, rows=rows)
+
+
+def test_swa_training_shape_sampled_rows():
+    """The 1.7B configuration (32 query heads, 4 KV heads, head_dim 64, window 2048) at the
+    training length: batch 2 x 4096, sampled rows (first, last, window and tile edges)."""
+    q, k, v = make_qkv(3400, (2, 4096), 32, 4, 64)
+    rng = np.random.default_rng(1)
+    per = np.unique(np.concatenate([[0, 1, 63, 64, 2047, 2048, 2049, 2111, 2112, 4095], rng.integers(0, 4096, 20)]))
+    rows = np.concatenate([per, 4096 + per])
+    got, ref = run(q, k, v, 2048, rows=rows)
+    check(got, ref, rows=rows)
+
+
+def test_swa_keys_outside_the_window_have_no_effect():
+    """Changing the keys and values just outside row t's window (position t - w - 1)
+    leaves row t bitwise unchanged; changing the oldest key inside it does not."""
+    w = 100
+    q, k, v = make_qkv(3500, (1, 400), 4, 2, 64)
+    o1 = host(ss.swa(dev(q), dev(k), dev(v), window=w))
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 150], v2[0, 150] = k2[0, 150] * -3.0, v2[0, 150] + 7.0
+    o2 = host(ss.swa(dev(q), dev(k2), dev(v2), window=w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o2[0, 251:], o1[0, 251:])  # rows whose windows start after 150
+    np.testing.assert_array_equal(o2[0, :150], o1[0, :150])  # rows before the key (causal)
+    assert np.abs(o2[0, 250] - o1[0, 250]).max() > 1e-2      # row 250's window starts at 150
+
+
+def test_swa_argument_errors():
+    q = torch.zeros((1, 8, 4, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(ss.SambaError, match="UNSUPPORTED"):
+        ss.swa(q, q[:, :, :2].contiguous(), q[:, :, :2].contiguous())
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(ss.SambaError, match="UNSUPPORTED"):
+        ss.swa(qb[..., :32].contiguous(), qb[:, :, :2, :32].contiguous(), qb[:, :, :2, :32].contiguous())
+    with pytest.raises(ss.SambaError, match="INVALID_ARG"):
+        ss.swa(qb[:, :, :3].contiguous(), qb[:, :, :2].contiguous(), qb[:, :, :2].contiguous())
