@@ -198,6 +198,7 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
             rotate8(a, d, rowc, f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                f[e] *= a.scale_log2;  // scores come out in log2 units
                 qf[kk][e] = static_cast<__bf16>(f[e]);
                 ql[kk][e] = static_cast<__bf16>(f[e] - static_cast<float>(qf[kk][e]));
             }
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
     f32x4 o[kDS];
 #pragma unroll
     for (int i = 0; i < kDS; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -1e30f, l_run = 0.0f;  // running max (log2 units) and this lane's share of the sum
+    float m_run = -1e30f, l_run = 0.0f;  // exponent offset (log2 units) and this lane's share of the sum
 
     fetch(kt0);
     stage(0);
@@ -299,30 +300,38 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
             }
             sc[st] = acc;
         }
-        // scale, mask (only tiles that cross a window edge, the diagonal or the sequence end)
-        const bool edge = kt < row - a.window || kt + kKeys - 1 > row || kt + kKeys > L;
-        float mt = -1e30f;
+        // mask: only tiles that cross a window edge, the diagonal or the sequence end for
+        // some row of the wave (a wave-uniform test), then element selects
+        const int rw0 = R0 + wave * 16;
+        if (kt < rw0 + 15 - a.window || kt + kKeys - 1 > rw0 || kt + kKeys > L) {
 #pragma unroll
-        for (int st = 0; st < kKeys / 16; ++st) {
+            for (int st = 0; st < kKeys / 16; ++st) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = sc[st][e] * a.scale_log2;
-                if (edge) {
+                for (int e = 0; e < 4; ++e) {
                     const int key = kt + 16 * st + 4 * g + e;
-                    if (key > row || key < row - a.window || key >= L) v = -__builtin_inff();
+                    sc[st][e] = (key > row || key < row - a.window || key >= L) ? -__builtin_inff() : sc[st][e];
                 }
-                sc[st][e] = v;
-                mt = __builtin_fmaxf(mt, v);
             }
         }
+        float mt = -1e30f;
+#pragma unroll
+        for (int st = 0; st < kKeys / 16; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mt = __builtin_fmaxf(mt, sc[st][e]);
         mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
         mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = __builtin_fmaxf(m_run, mt);
-        const float alpha = hw_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+        // The exponent offset m_run only moves when some row of the wave would otherwise see
+        // probabilities above 2^8 (the output and sum are then rescaled); between moves the
+        // probabilities stay in (0, 256], which bfloat16 and the fp32 sums carry exactly as well.
+        if (__any(mt > m_run + 8.0f)) {
+            const float m_new = __builtin_fmaxf(m_run, mt);
+            const float alpha = hw_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < kDS; ++i) o[i] *= alpha;
+            for (int i = 0; i < kDS; ++i) o[i] *= alpha;
+        }
+        const float m_new = m_run;
         // probabilities, as the B operand of O^T = V^T P^T (k-step kk = sub-tiles 2kk, 2kk+1)
         bf16x8 pb[kKeys / 32];
 #pragma unroll
