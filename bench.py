@@ -258,6 +258,9 @@ def bench_extra(dev, steps=5, warmup=2):
                                           bytes_per_launch=nbytes),
                             copy_same_bytes_gbs=round(copy_gbs, 1), frac_of_copy=round(nbytes / sec / 1e9 / copy_gbs, 4))
     del x, u
+    # Sliding window attention of the 1.7B configuration (32 query heads, 4 KV heads,
+    # head_dim 64, window 2048, RoPE base 10000) on the long prompt and the training shape.
+    res["swa"] = bench_swa(dev, steps, warmup)
     seed = synth.seed_for(4)
     p = synth.make_params(seed, D_INNER, D_STATE)
     prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
@@ -272,6 +275,37 @@ def bench_extra(dev, steps=5, warmup=2):
     res["varlen8"] = dict(workload="8 sequences, lengths %s, %d tokens" % (lens.tolist(), T),
                           ms=float(np.mean(per) * 1e3), ms_median=float(np.median(per) * 1e3),
                           mtok_s=T / float(np.mean(per)) / 1e6)
+    return res
+
+
+def swa_flops(b, L, Hq, dh, w):
+    """Algorithmic FLOPs of windowed attention: per query row and head, 2 * dh for each
+    score and 2 * dh for each probability-weighted value, over min(t, w) + 1 keys."""
+    keys = sum(min(t, w) + 1 for t in range(min(L, w + 1))) + max(0, L - (w + 1)) * (w + 1)
+    return 4.0 * b * keys * Hq * dh
+
+
+def bench_swa(dev, steps, warmup):
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+    res = {}
+    Hq, Hkv, dh, w = 32, 4, 64, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed_for(5))
+    for name, (b, L) in (("prompt128k", (1, 131072)), ("train4k", (4, 4096))):
+        mk = lambda H: torch.randn((b, L, H, dh), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        q, k, v = mk(Hq), mk(Hkv), mk(Hkv)
+        out = torch.empty_like(q)
+        ws = torch.empty(int(ss.load().samba_swa_workspace_bytes(b * L, Hkv, dh)), dtype=torch.uint8, device=dev)
+        _, per = time_calls(lambda: ss.swa(q, k, v, window=w, out=out, workspace=ws), steps, warmup)
+        sec = float(np.median(per))
+        fl = swa_flops(b, L, Hq, dh, w)
+        res[name] = dict(workload="batch %d, L=%d, 32 query heads, 4 KV heads, head_dim 64, window 2048" % (b, L),
+                         ms=float(np.mean(per) * 1e3), ms_median=sec * 1e3,
+                         roofline=dict(bound="mfma", achieved=round(fl / sec / 1e12, 1), peak=2500.0,
+                                       unit="TFLOP/s", frac=round(fl / sec / 1e12 / 2500.0, 4), flops_per_launch=fl))
+        del q, k, v, out, ws
     return res
 
 
