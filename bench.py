@@ -306,6 +306,31 @@ def bench_swa(dev, steps, warmup):
                          roofline=dict(bound="mfma", achieved=round(fl / sec / 1e12, 1), peak=2500.0,
                                        unit="TFLOP/s", frac=round(fl / sec / 1e12 / 2500.0, 4), flops_per_launch=fl))
         del q, k, v, out, ws
+    # decode: 256 sequences with full rings (positions 4096..), one token per step; the
+    # rings of the 4 KV heads (2049 keys and values) are read once per step
+    S, P = 256, 64
+    kc = torch.randn((S, Hkv, w + 1, dh), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.randn((S, Hkv, w + 1, dh), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    mk = lambda H: torch.randn((P, S, H, dh), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v = mk(Hq), mk(Hkv), mk(Hkv)
+    out = torch.empty((S, Hq, dh), dtype=torch.bfloat16, device=dev)
+    pos = [torch.full((S,), 4096 + i, dtype=torch.int32, device=dev) for i in range(P)]
+    ws = torch.empty(int(ss.load().samba_swa_decode_workspace_bytes(S, Hq, dh)), dtype=torch.uint8, device=dev)
+    it = iter(range(10 ** 9))
+
+    def step():
+        i = next(it) % P
+        ss.swa_decode(q[i], k[i], v[i], pos[i], kc, vc, window=w, out=out, workspace=ws)
+
+    _, per = time_calls(step, 50, 5)
+    sec = float(np.median(per))
+    nbytes = S * Hkv * (w + 1) * dh * 2 * 2 + S * (Hq + 2 * Hkv + Hq) * dh * 2
+    res["decode_256"] = dict(workload="256 sequences, full 2049-entry rings, 32 query heads, 4 KV heads, head_dim 64",
+                             us_per_step=sec * 1e6, tok_s=S / sec,
+                             roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1), peak=HBM_PEAK_GBS,
+                                           unit="GB/s", frac=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                           bytes_per_step=nbytes),
+                             note="per-step launches timed one by one (three kernels: store, attention, combine)")
     return res
 
 

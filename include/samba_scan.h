@@ -217,6 +217,34 @@ samba_status samba_swa_prefill(int nseq, const int32_t *cu_seqlens, int seqlen, 
                                const void *q, const void *k, const void *v, void *out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Size in bytes of the workspace samba_swa_decode needs (per-split partial results). */
+size_t samba_swa_decode_workspace_bytes(int nseq, int n_heads, int head_dim);
+
+/* One decode step of sliding window attention for nseq sequences over ring-buffer KV caches
+ * (a query at position t reads the keys t - window .. t: "Window Specification" on page 1,
+ * so each sequence keeps only window + 1 keys and values, whatever its length).
+ *   q [nseq][n_heads][head_dim], k, v [nseq][n_kv_heads][head_dim]: the new token (bf16)
+ *   pos      DEVICE int32 [nseq]: the new token's position (tokens before it); a sequence
+ *            with pos < 0 is skipped (its out rows are set to 0). Not modified.
+ *   k_cache, v_cache [nseq][n_kv_heads][window + 1][head_dim] bf16, IN/OUT: position p is
+ *            kept in entry p mod (window + 1), keys rotated by RoPE at p; the step writes the
+ *            new token's entry, then attends over the window.
+ *   out [nseq][n_heads][head_dim] bf16.
+ *   n_heads / n_kv_heads <= 16; head_dim 64 or 128; io must be SAMBA_BF16.
+ *   workspace: at least samba_swa_decode_workspace_bytes() bytes, 16-byte aligned. */
+samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
+                              samba_dtype io, const void *q, const void *k, const void *v, const int32_t *pos,
+                              void *k_cache, void *v_cache, void *out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Fills the ring-buffer caches from a prefill's keys and values (fixed length when
+ * cu_seqlens is NULL, else packed as for samba_scan_varlen): each sequence's last
+ * min(L, window + 1) tokens go to entry position mod (window + 1), keys rotated, so that a
+ * following samba_swa_decode with pos = L continues the sequence. */
+samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int n_kv_heads,
+                               int head_dim, int window, float rope_base, samba_dtype io, const void *k,
+                               const void *v, void *k_cache, void *v_cache, void *stream);
+
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char *samba_last_error(void);

@@ -6,7 +6,7 @@ and the current HIP stream; every step of the computation runs in the library's 
 kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
 
 Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``, ``conv_silu``,
-``backward`` and ``swa`` (sliding window attention).
+``backward``, ``swa`` (sliding window attention), ``swa_decode`` and ``swa_kv_fill``.
 """
 from __future__ import annotations
 
@@ -16,8 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "workspace_bytes", "lib_path",
-           "SambaError", "version"]
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill",
+           "workspace_bytes", "lib_path", "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
@@ -71,6 +71,12 @@ def load():
         lib.samba_swa_workspace_bytes.argtypes = [I, I, I]
         lib.samba_swa_prefill.restype = I
         lib.samba_swa_prefill.argtypes = [I, P, I, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, Z, P]
+        lib.samba_swa_decode_workspace_bytes.restype = Z
+        lib.samba_swa_decode_workspace_bytes.argtypes = [I, I, I]
+        lib.samba_swa_decode.restype = I
+        lib.samba_swa_decode.argtypes = [I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, Z, P]
+        lib.samba_swa_kv_fill.restype = I
+        lib.samba_swa_kv_fill.argtypes = [I, P, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
         lib.samba_conv_silu.restype = I
         lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
         _lib = lib
@@ -379,3 +385,52 @@ def swa(q, k, v, *, window=2048, rope_base=10000.0, cu_seqlens=None, max_seqlen=
         _stream(dev))
     _check(st)
     return out
+
+
+def swa_decode(q, k, v, pos, k_cache, v_cache, *, window=2048, rope_base=10000.0, out=None, workspace=None):
+    """One decode step of sliding window attention: q [S, Hq, dh], k, v [S, Hkv, dh] (bf16),
+    pos int32 [S] on the GPU (the new token's position), k_cache / v_cache
+    [S, Hkv, window + 1, dh] ring buffers updated in place.  Returns out [S, Hq, dh]."""
+    dev = _gpu_device(q)
+    S, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    _shape(k, (S, Hkv, dh), "k")
+    _shape(v, (S, Hkv, dh), "v")
+    _shape(pos, (S,), "pos")
+    _shape(k_cache, (S, Hkv, int(window) + 1, dh), "k_cache")
+    _shape(v_cache, (S, Hkv, int(window) + 1, dh), "v_cache")
+    if out is None:
+        out = torch.empty_like(q)
+    need = int(load().samba_swa_decode_workspace_bytes(S, Hq, dh))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().samba_swa_decode(
+        S, Hq, Hkv, dh, int(window), float(rope_base), _io(q), _ptr(q, "q", q.dtype, dev), _ptr(k, "k", q.dtype, dev),
+        _ptr(v, "v", q.dtype, dev), _ptr(pos, "pos", torch.int32, dev), _ptr(k_cache, "k_cache", q.dtype, dev),
+        _ptr(v_cache, "v_cache", q.dtype, dev), _ptr(out, "out", q.dtype, dev), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return out
+
+
+def swa_kv_fill(k, v, k_cache, v_cache, *, window=2048, rope_base=10000.0, cu_seqlens=None, max_seqlen=None):
+    """Writes a prefill's keys (rotated) and values into the ring-buffer caches: k, v
+    [b, L, Hkv, dh] or packed [T, Hkv, dh] with cu_seqlens; caches [nseq, Hkv, window + 1, dh]."""
+    dev = _gpu_device(k)
+    if cu_seqlens is None:
+        b, L, Hkv, dh = k.shape
+        nseq, total = b, b * L
+    else:
+        T, Hkv, dh = k.shape
+        nseq, total = cu_seqlens.numel() - 1, T
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+        L = int(max_seqlen)
+    _shape(v, tuple(k.shape), "v")
+    _shape(k_cache, (nseq, Hkv, int(window) + 1, dh), "k_cache")
+    _shape(v_cache, (nseq, Hkv, int(window) + 1, dh), "v_cache")
+    st = load().samba_swa_kv_fill(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), L, total, Hkv, dh, int(window), float(rope_base),
+        _io(k), _ptr(k, "k", k.dtype, dev), _ptr(v, "v", k.dtype, dev), _ptr(k_cache, "k_cache", k.dtype, dev),
+        _ptr(v_cache, "v_cache", k.dtype, dev), _stream(dev))
+    _check(st)

@@ -28,6 +28,7 @@
 #include "scan_conv.h"
 #include "scan_bwd.h"
 #include "scan_swa.h"
+#include "scan_swa_decode.h"
 
 
 namespace {
@@ -529,6 +530,123 @@ samba_status samba_swa_prefill(int nseq, const int32_t *cu_seqlens, int seqlen, 
     a.krot = static_cast<uint16_t *>(workspace);
     samba::swa_set_theta(a, static_cast<double>(rope_base));
     samba::launch_swa(a, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+size_t samba_swa_decode_workspace_bytes(int nseq, int n_heads, int head_dim)
+{
+    if (nseq <= 0 || n_heads <= 0 || head_dim <= 0) return 0;
+    return samba::swa_decode_workspace_bytes(nseq, n_heads, head_dim);
+}
+
+namespace {
+samba_status swa_dec_common(const char *fn, int nseq, int n_heads, int n_kv_heads, int head_dim, int window,
+                            float rope_base, samba_dtype io, bool decode)
+{
+    if (nseq < 0 || window < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d window=%d must be >= 0", fn, nseq, window);
+    if (io != SAMBA_BF16)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: io dtype %d: attention takes bfloat16", fn, (int)io);
+    if (n_heads < 1 || n_kv_heads < 1 || n_heads % n_kv_heads != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: n_heads=%d must be a positive multiple of n_kv_heads=%d", fn, n_heads,
+                    n_kv_heads);
+    if (decode && n_heads / n_kv_heads > samba::swadec::kMaxGroup)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most %d are built)", fn,
+                    n_heads / n_kv_heads, samba::swadec::kMaxGroup);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: head_dim=%d (64 and 128 are built)", fn, head_dim);
+    if (!(rope_base > 1.0f)) return fail(SAMBA_ERR_INVALID_ARG, "%s: rope_base must be > 1", fn);
+    if (window >= 65535 * 64)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: window=%d exceeds the launch limit", fn, window);
+    if (nseq > 65535) return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d exceeds 65535", fn, nseq);
+    return SAMBA_OK;
+}
+}  // namespace
+
+samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
+                              samba_dtype io, const void *q, const void *k, const void *v, const int32_t *pos,
+                              void *k_cache, void *v_cache, void *out, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    const char *fn = "samba_swa_decode";
+    samba_status st = swa_dec_common(fn, nseq, n_heads, n_kv_heads, head_dim, window, rope_base, io, true);
+    if (st != SAMBA_OK) return st;
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
+    const size_t need = samba::swa_decode_workspace_bytes(nseq, n_heads, head_dim);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    REQUIRE_PTR(workspace, "workspace");
+    samba::SwaDecArgs a{};
+    a.S = nseq;
+    a.Hq = n_heads;
+    a.Hkv = n_kv_heads;
+    a.dh = head_dim;
+    a.window = window;
+    a.cap = window + 1;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.pos = pos;
+    a.kc = static_cast<uint16_t *>(k_cache);
+    a.vc = static_cast<uint16_t *>(v_cache);
+    a.out = out;
+    a.part = static_cast<float *>(workspace);
+    samba::swa_dec_set_theta(a, static_cast<double>(rope_base));
+    samba::launch_swa_decode(a, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int n_kv_heads,
+                               int head_dim, int window, float rope_base, samba_dtype io, const void *k,
+                               const void *v, void *k_cache, void *v_cache, void *stream)
+{
+    const char *fn = "samba_swa_kv_fill";
+    samba_status st = swa_dec_common(fn, nseq, n_kv_heads, n_kv_heads, head_dim, window, rope_base, io, false);
+    if (st != SAMBA_OK) return st;
+    if (seqlen < 0 || (cu_seqlens != nullptr && total_tokens < 0))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: seqlen=%d total_tokens=%d must be >= 0", fn, seqlen, total_tokens);
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    size_t tokens = cu_seqlens != nullptr ? static_cast<size_t>(total_tokens)
+                                          : static_cast<size_t>(nseq) * static_cast<size_t>(seqlen);
+    if (tokens > static_cast<size_t>(INT32_MAX))
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: %zu tokens exceed 2^31-1", fn, tokens);
+    if (tokens > 0) {
+        REQUIRE_PTR(k, "k");
+        REQUIRE_PTR(v, "v");
+    }
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    samba::SwaDecArgs a{};
+    a.S = nseq;
+    a.Hq = n_kv_heads;
+    a.Hkv = n_kv_heads;
+    a.dh = head_dim;
+    a.window = window;
+    a.cap = window + 1;
+    a.k = k;
+    a.v = v;
+    a.kc = static_cast<uint16_t *>(k_cache);
+    a.vc = static_cast<uint16_t *>(v_cache);
+    a.cu = cu_seqlens;
+    a.seqlen = seqlen;
+    a.total = static_cast<int>(tokens);
+    samba::swa_dec_set_theta(a, static_cast<double>(rope_base));
+    samba::launch_swa_kv_fill(a, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 

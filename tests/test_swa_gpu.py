@@ -119,3 +119,49 @@ def test_swa_argument_errors():
         ss.swa(qb[..., :32].contiguous(), qb[:, :, :2, :32].contiguous(), qb[:, :, :2, :32].contiguous())
     with pytest.raises(ss.SambaError, match="INVALID_ARG"):
         ss.swa(qb[:, :, :3].contiguous(), qb[:, :, :2].contiguous(), qb[:, :, :2].contiguous())
+
+
+def _decode_all(q, k, v, window):
+    """Runs every position of fixed-length sequences through the decode step from empty
+    caches; returns the outputs [S, L, Hq, dh]."""
+    S, L, Hq, dh = q.shape
+    Hkv = k.shape[2]
+    kc = torch.zeros((S, Hkv, window + 1, dh), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    outs = []
+    for t in range(L):
+        pos = torch.full((S,), t, dtype=torch.int32, device=DEV)
+        outs.append(ss.swa_decode(qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), pos, kc, vc,
+                                  window=window).clone())
+    return host(torch.stack(outs, dim=1))
+
+
+@pytest.mark.parametrize("Hq,Hkv,dh", [(8, 2, 64), (11, 1, 128)])
+def test_swa_decode_steps_from_empty_cache(Hq, Hkv, dh):
+    """300 decode steps with window 100 (the 101-entry rings wrap twice) equal the oracle's
+    prefill rows."""
+    print("case: swa decode", Hq, Hkv, dh, flush=True)
+    q, k, v = make_qkv(3600 + Hq + dh, (3, 300), Hq, Hkv, dh)
+    got = _decode_all(q, k, v, 100)
+    torch.cuda.synchronize()
+    check(got, oracle.swa(q, k, v, window=100))
+
+
+def test_swa_decode_after_fill():
+    """The 1.7B configuration: rings filled from a 2200-token prefill (window 2048), then three
+    decode steps, against the oracle's rows for those positions."""
+    S, L, Hq, Hkv, dh, w = 2, 2203, 32, 4, 64, 2048
+    print("case: swa fill + decode", flush=True)
+    q, k, v = make_qkv(3700, (S, L), Hq, Hkv, dh)
+    kc = torch.zeros((S, Hkv, w + 1, dh), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    ss.swa_kv_fill(dev(k[:, :2200]), dev(v[:, :2200]), kc, vc, window=w)
+    outs = []
+    for t in range(2200, L):
+        pos = torch.full((S,), t, dtype=torch.int32, device=DEV)
+        outs.append(host(ss.swa_decode(dev(q[:, t]), dev(k[:, t]), dev(v[:, t]), pos, kc, vc, window=w)))
+    torch.cuda.synchronize()
+    rows = np.concatenate([s * L + np.arange(2200, L) for s in range(S)])
+    ref = oracle.swa(q, k, v, window=w, rows=rows).reshape(S * L, Hq, dh)[rows].reshape(S, 3, Hq, dh)
+    check(np.stack(outs, axis=1), ref)
