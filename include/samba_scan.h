@@ -18,8 +18,9 @@
  * (zeros at a fresh sequence start), tap k multiplying x_{t-3+k}; A is used as given
  * (normally negative, A = -exp(A_log)); the gate is SiLU(z) -- these follow "Samba Guide:
  * Hybrid Mamba & Sliding Window Architecture", "Step 1: The Selective State Space (Mamba)
- * Layer".  The input projection, x_proj/dt_proj and out_proj GEMMs are not part of this
- * library: x, dt, B, C and z are its inputs.
+ * Layer".  The scan entry points take x, dt, B, C and z as inputs; the projections that
+ * make them (and the layer's output projection, the attention and MLP projections) are
+ * bf16 matrix-core GEMMs of their own, samba_gemm below.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -244,6 +245,36 @@ samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_di
 samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, int total_tokens, int n_kv_heads,
                                int head_dim, int window, float rope_base, samba_dtype io, const void *k,
                                const void *v, void *k_cache, void *v_cache, void *stream);
+
+/* Epilogue of samba_gemm. */
+typedef enum {
+    SAMBA_GEMM_STORE = 0,  /* out bf16 = A . W^T */
+    SAMBA_GEMM_ADD_F32 = 1, /* out fp32 = residual fp32 + A . W^T (the residual stream) */
+    SAMBA_GEMM_SWIGLU = 2  /* W = [W1; W2] (2N rows): out bf16 = (A . W1^T) * SiLU(A . W2^T) */
+} samba_gemm_epilogue;
+
+/* Size in bytes of the workspace samba_gemm needs for this shape (0 when the K range is
+ * not split; then workspace may be NULL). */
+size_t samba_gemm_workspace_bytes(int M, int N, int K, samba_gemm_epilogue epilogue);
+
+/* out[m][n] = epilogue(sum_k A[m][k] * W[n][k]): the linear projections of the Samba layers
+ * (page "Samba: Simple Hybrid State Space Models ...": "Input Projection and Short
+ * Convolution" H = X W_in, the low-rank Delta projection U W_r W_q, B = U W_b, C = U W_c,
+ * the gate X W_g and output projection W_out of "Gated Output", the attention projections,
+ * and "SwiGLU Formulation" (X W1) * SiLU(X W2) followed by W3), with fp32 accumulation.
+ *   A   bf16 [M][lda] (rows of K used; lda >= K, lda % 8 == 0)
+ *   W   bf16 [N][K] (one row per output feature: the transpose of a d_in x d_out matrix);
+ *       SWIGLU: [2N][K], rows 0..N-1 = W1^T, rows N..2N-1 = W2^T
+ *   out bf16 [M][ldo] (STORE, SWIGLU) or fp32 [M][ldo] (ADD_F32), ldo >= N
+ *   residual fp32 [M][ldr] (ADD_F32 only; may be exactly out with ldr == ldo -- the
+ *       residual stream updated in place -- but must not partially overlap it)
+ *   K % 8 == 0 (16-byte rows; SAMBA_ERR_UNSUPPORTED otherwise); M, N, K >= 0;
+ *   A and W 16-byte aligned, out and residual aligned to their element size.  workspace: samba_gemm_workspace_bytes() bytes, 256-byte
+ *   aligned.  out must not overlap A, W or the workspace.  Deterministic: a split K range
+ *   is summed in a fixed order. */
+samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
+                        void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */

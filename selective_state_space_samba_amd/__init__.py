@@ -16,7 +16,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill",
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill", "gemm",
            "workspace_bytes", "lib_path", "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
 _lib = None
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
+GEMM_EPILOGUES = {"store": 0, "add": 1, "swiglu": 2}
 _STATUS = {0: "OK", 1: "SAMBA_ERR_INVALID_ARG", 2: "SAMBA_ERR_UNSUPPORTED", 3: "SAMBA_ERR_WORKSPACE", 4: "SAMBA_ERR_HIP"}
 
 
@@ -79,6 +80,10 @@ def load():
         lib.samba_swa_kv_fill.argtypes = [I, P, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
         lib.samba_conv_silu.restype = I
         lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
+        lib.samba_gemm_workspace_bytes.restype = Z
+        lib.samba_gemm_workspace_bytes.argtypes = [I, I, I, I]
+        lib.samba_gemm.restype = I
+        lib.samba_gemm.argtypes = [I, I, I, I, P, I, P, P, I, P, I, P, Z, P]
         _lib = lib
     return _lib
 
@@ -434,3 +439,55 @@ def swa_kv_fill(k, v, k_cache, v_cache, *, window=2048, rope_base=10000.0, cu_se
         _io(k), _ptr(k, "k", k.dtype, dev), _ptr(v, "v", k.dtype, dev), _ptr(k_cache, "k_cache", k.dtype, dev),
         _ptr(v_cache, "v_cache", k.dtype, dev), _stream(dev))
     _check(st)
+
+
+def _rows(t, name, dtype, dev):
+    """Pointer and row pitch of a 2-D tensor whose rows are contiguous (stride(1) == 1)."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError("%s must be a 2-D tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != dev:
+        raise ValueError("%s must be on %s, got %s" % (name, dev, t.device))
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have contiguous rows" % name)
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return (t.data_ptr() if t.numel() > 0 else None), int(ld)
+
+
+def gemm(a, w, *, epilogue="store", out=None, residual=None, workspace=None):
+    """out = epilogue(a @ w.T) on the matrix cores (fp32 accumulation).
+    a bf16 [M, K] (rows may be a strided view), w bf16 [N, K] ([2N, K] = [W1; W2] for
+    "swiglu").  epilogue "store": out bf16 [M, N]; "add": out fp32 = residual + a @ w.T
+    (residual fp32 [M, N], may be out itself); "swiglu": out bf16 = (a W1^T) * SiLU(a W2^T)."""
+    dev = _gpu_device(a)
+    if epilogue not in GEMM_EPILOGUES:
+        raise ValueError("epilogue must be one of %s" % sorted(GEMM_EPILOGUES))
+    epi = GEMM_EPILOGUES[epilogue]
+    M, K = a.shape
+    N = w.shape[0] // 2 if epilogue == "swiglu" else w.shape[0]
+    if epilogue == "swiglu" and w.shape[0] % 2:
+        raise ValueError("swiglu weight must have an even number of rows ([W1; W2])")
+    _shape(w, (w.shape[0], K), "w")
+    pa, lda = _rows(a, "a", torch.bfloat16, dev)
+    pw = _ptr(w, "w", torch.bfloat16, dev)
+    odt = torch.float32 if epilogue == "add" else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=dev)
+    _shape(out, (M, N), "out")
+    po, ldo = _rows(out, "out", odt, dev)
+    pr, ldr = None, 0
+    if epilogue == "add":
+        if residual is None:
+            raise ValueError("epilogue 'add' needs residual")
+        _shape(residual, (M, N), "residual")
+        pr, ldr = _rows(residual, "residual", torch.float32, dev)
+    need = int(load().samba_gemm_workspace_bytes(M, N, K, epi))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    pws = _ptr(workspace, "workspace") if workspace is not None else None
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().samba_gemm(M, N, K, epi, pa, max(lda, K), pw, po, max(ldo, N), pr, max(ldr, N), pws, nws,
+                           _stream(dev))
+    _check(st)
+    return out

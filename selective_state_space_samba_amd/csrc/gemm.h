@@ -1,0 +1,341 @@
+// gemm.h -- bfloat16 matrix-core GEMM for the projections of a Samba layer (gfx950).
+//
+// out = A . W^T with A [M, K] (token rows) and W [N, K] (one row per output feature, the
+// transpose of the pages' d_in x d_out projection matrices), fp32 accumulation on
+// v_mfma_f32_16x16x32_bf16.  Epilogues fused into the store:
+//   store   out bf16 [M, ldo]                 (in_proj, gate, x_proj, dt, q/k/v)
+//   add     out fp32 = residual fp32 + A.W^T  (the residual stream after W_out, W_o, W_3)
+//   swiglu  W = [W1; W2] (2N rows), out bf16 = (A.W1^T) * SiLU(A.W2^T)
+//           (page "Samba: Simple Hybrid State Space Models ...", "SwiGLU Formulation")
+//
+// Tiling.  A workgroup of 4 waves (2 x 2) computes a TM x TN tile, TM = 32 FM, TN = 32 FN;
+// each wave a 16FM x 16FN block of 16 x 16 MFMA tiles.  K advances 64 at a time through
+// double-buffered LDS tiles (row pitch 72 elements = 144 bytes, so the 16 rows a fragment
+// read touches start on 16 different 4-bank groups); the next K tile's global loads are
+// in flight while the current one is multiplied.  MFMA operand layouts (16x16x32 bf16):
+// lane l supplies A[i = l % 16][k = 8 (l / 16) + e] and B[k = 8 (l / 16) + e][j = l % 16],
+// e = 0..7, and receives D[i = 4 (l / 16) + e][j = l % 16], e = 0..3.  Both operands are
+// K-contiguous rows (A rows, W rows), so both fragments are one 16-byte LDS read.
+//
+// Split K.  When the tiles alone cannot fill the chip (decode: M = a few hundred rows),
+// the K range is cut into splits that write fp32 partial tiles to a workspace; a second
+// kernel sums the splits in a fixed order (deterministic) and applies the epilogue.
+#pragma once
+
+#include "scan_common.h"
+
+#include <algorithm>
+
+namespace samba {
+namespace gemm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kTK = 64;          // K per LDS stage
+constexpr int kPitch = kTK + 8;  // LDS row pitch in elements
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every extent: loads 0
+
+enum Epi { kStore = 0, kAdd = 1, kSwiglu = 2, kPartial = 3 };
+
+struct GemmArgs {
+    int M, N, K;      // out is M x N; swiglu: W has 2N rows
+    const uint16_t *A;
+    int lda;          // A row pitch (elements)
+    const uint16_t *W;
+    void *out;
+    int ldo;          // out row pitch (elements)
+    const float *R;   // residual (add)
+    int ldr;
+    float *part;      // split-K partials [splits][M][Nw]
+    int Nw;           // W rows = partial columns (N, or 2N for swiglu)
+    int ksplit;       // K per split, a multiple of kTK
+    int splits;
+    int tiles_m, tiles_n;
+    int group_m;      // M tiles per group of the tile order
+};
+
+__device__ inline float silu_f(float v) { return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
+
+// Logical tile order.  The hardware deals consecutive workgroup ids to the 8 XCDs in turn;
+// the remap gives each XCD a contiguous range of logical ids, and within it tiles run in
+// groups of group_m M tiles x all N tiles, column by column, so the workgroups resident on
+// one XCD at a time share a few A row blocks and W row blocks in that XCD's L2.
+__device__ inline void tile_of(const GemmArgs &a, int &tm, int &tn, int &split)
+{
+    const int total = a.tiles_m * a.tiles_n * a.splits;
+    const int b = blockIdx.x;
+    const int q = total / 8, r = total % 8, x = b % 8;
+    const int L = x * q + min(x, r) + b / 8;
+    const int ntiles = a.tiles_m * a.tiles_n;
+    split = L / ntiles;
+    const int t = L % ntiles;
+    const int gsz = a.group_m * a.tiles_n;
+    const int g = t / gsz, first = g * a.group_m;
+    const int gm = min(a.group_m, a.tiles_m - first);
+    tm = first + (t % gsz) % gm;
+    tn = (t % gsz) / gm;
+}
+
+template <int FM, int FN, int kEpi>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+{
+    constexpr int TM = 32 * FM, TN = 32 * FN;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][TM * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN * kPitch];
+
+    int tm, tn, split;
+    tile_of(a, tm, tn, split);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int m0 = tm * TM;
+    // Output columns of this tile: TN of them, or TN / 2 for the fused SwiGLU (the W tile
+    // then holds TN / 2 rows of W1 and the same TN / 2 rows of W2, in alternating
+    // 16-row blocks, so a wave's MFMA tiles 2p and 2p + 1 hold the two factors of the
+    // same outputs in the same lanes).
+    constexpr int kOutCols = kEpi == kSwiglu ? TN / 2 : TN;
+    const int n0 = tn * kOutCols;
+    const int kbeg = split * a.ksplit;
+    const int kend = min(a.K, kbeg + a.ksplit);
+    const int nk = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+
+    // Global -> register loaders: thread t moves 16-byte chunk c = t % 8 of rows
+    // t / 8 + 32 j of the A tile (j < FM) and of the W tile (j < FN); the row offsets below
+    // exclude the chunk, which enters through the K index of load_tile.
+    const int c = tid & 7, r0 = tid >> 3;
+    const int rows_a = min(TM, a.M - m0);
+    const Rsrc ra = make_rsrc(a.A + static_cast<size_t>(m0) * a.lda,
+                              rows_a > 0 ? static_cast<uint32_t>(((rows_a - 1) * a.lda + a.K) * 2) : 0u);
+    Rsrc rw, rw2;
+    if constexpr (kEpi == kSwiglu) {
+        const int rows = max(0, min(kOutCols, a.N - n0));
+        const uint32_t ext = rows > 0 ? static_cast<uint32_t>(((rows - 1) * a.K + a.K) * 2) : 0u;
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, ext);
+        rw2 = make_rsrc(a.W + static_cast<size_t>(a.N + n0) * a.K, ext);
+    } else {
+        const int rows = max(0, min(TN, a.Nw - n0));
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, rows > 0 ? static_cast<uint32_t>(rows * a.K * 2) : 0u);
+        rw2 = rw;
+    }
+    uint32_t aoff[FM], woff[FN];
+    bool wsecond[FN];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) aoff[j] = static_cast<uint32_t>((r0 + 32 * j) * a.lda * 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int r = r0 + 32 * j;
+        int wrow = r;
+        wsecond[j] = false;
+        if constexpr (kEpi == kSwiglu) {
+            const int blk = r >> 4;
+            wsecond[j] = (blk & 1) != 0;
+            wrow = (blk >> 1) * 16 + (r & 15);
+        }
+        woff[j] = static_cast<uint32_t>(wrow * a.K * 2);
+    }
+
+    uint4 ra_v[FM], rw_v[FN];
+    auto load_tile = [&](int kt) {
+        const int k = kbeg + kt * kTK + c * 8;
+        const bool in = k < kend;
+        const uint32_t kb = static_cast<uint32_t>(k) * 2u;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) ra_v[j] = buf_ld128(ra, in ? aoff[j] + kb : kOob);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) rw_v[j] = buf_ld128(wsecond[j] ? rw2 : rw, in ? woff[j] + kb : kOob);
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            *reinterpret_cast<uint4 *>(&As[buf][(r0 + 32 * j) * kPitch + c * 8]) = ra_v[j];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            *reinterpret_cast<uint4 *>(&Bs[buf][(r0 + 32 * j) * kPitch + c * 8]) = rw_v[j];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nk > 0) {
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+    }
+    const int frow = lane & 15, fk = 8 * (lane >> 4);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load_tile(kt + 1);
+        const uint16_t *as = &As[buf][(wm * 16 * FM + frow) * kPitch + fk];
+        const uint16_t *bs = &Bs[buf][(wn * 16 * FN + frow) * kPitch + fk];
+#pragma unroll
+        for (int ks = 0; ks < kTK / 32; ++ks) {
+            bf16x8 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(as + i * 16 * kPitch + ks * 32);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const bf16x8 *>(bs + j * 16 * kPitch + ks * 32);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane holds rows 4 (l / 16) + e, column l % 16 of every 16 x 16 tile.
+    const int erow = m0 + wm * 16 * FM + 4 * (lane >> 4);
+    const int ecol = lane & 15;
+    if constexpr (kEpi == kSwiglu) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p) {
+                const int col = n0 + (wn * FN / 2 + p) * 16 + ecol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = erow + i * 16 + e;
+                    if (row < a.M && col < a.N)
+                        static_cast<uint16_t *>(a.out)[static_cast<size_t>(row) * a.ldo + col] = __builtin_bit_cast(
+                            uint16_t, static_cast<__bf16>(acc[i][2 * p][e] * silu_f(acc[i][2 * p + 1][e])));
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * 16 * FN + j * 16 + ecol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = erow + i * 16 + e;
+                    if constexpr (kEpi == kPartial) {
+                        if (row < a.M && col < a.Nw)
+                            a.part[(static_cast<size_t>(split) * a.M + row) * a.Nw + col] = acc[i][j][e];
+                    } else {
+                        if (row >= a.M || col >= a.N) continue;
+                        const size_t o = static_cast<size_t>(row) * a.ldo + col;
+                        if constexpr (kEpi == kStore) {
+                            static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][e]));
+                        } else {
+                            static_cast<float *>(a.out)[o] = a.R[static_cast<size_t>(row) * a.ldr + col] + acc[i][j][e];
+                        }
+                    }
+                }
+            }
+    }
+}
+
+// Sums the split partials in split order and applies the epilogue; one thread per output.
+template <int kEpi>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
+{
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= static_cast<size_t>(a.M) * a.N) return;
+    const int row = static_cast<int>(i / a.N), col = static_cast<int>(i % a.N);
+    const size_t stride = static_cast<size_t>(a.M) * a.Nw;
+    const float *p = a.part + static_cast<size_t>(row) * a.Nw + col;
+    float s = 0.f, g = 0.f;
+    for (int k = 0; k < a.splits; ++k) {
+        s += p[k * stride];
+        if constexpr (kEpi == kSwiglu) g += p[k * stride + a.N];
+    }
+    const size_t o = static_cast<size_t>(row) * a.ldo + col;
+    if constexpr (kEpi == kStore) {
+        static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
+    } else if constexpr (kEpi == kAdd) {
+        static_cast<float *>(a.out)[o] = a.R[static_cast<size_t>(row) * a.ldr + col] + s;
+    } else {
+        static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s * silu_f(g)));
+    }
+}
+
+// ---------------------------------------------------------------- host side
+struct Plan {
+    int fm, fn;       // tile config
+    int splits, ksplit;
+    int tiles_m, tiles_n;
+    size_t part_bytes;
+};
+
+// Tile shape and split count for a problem.  Large problems take 256 x 256 tiles (one
+// workgroup per CU, 144 KB of LDS); problems with fewer than 256 such tiles take
+// 128 x 128 tiles (two per CU), and if those still leave CUs idle, the K range is split
+// (each split keeps at least 4 K tiles) until about 512 workgroups exist.
+inline Plan plan(int M, int N, int K, int epi)
+{
+    Plan p{};
+    const int Nw = epi == kSwiglu ? 2 * N : N;
+    auto tiles = [&](int tm, int tn) {
+        const long long outc = epi == kSwiglu ? tn / 2 : tn;
+        return static_cast<long long>((M + tm - 1) / tm) * ((N + outc - 1) / outc);
+    };
+    if (tiles(256, 256) >= 256) {
+        p.fm = 8;
+        p.fn = 8;
+    } else {
+        p.fm = 4;
+        p.fn = 4;
+    }
+    const int TM = 32 * p.fm, TN = 32 * p.fn;
+    const int outc = epi == kSwiglu ? TN / 2 : TN;
+    p.tiles_m = (M + TM - 1) / TM;
+    p.tiles_n = (N + outc - 1) / outc;
+    const long long t = static_cast<long long>(p.tiles_m) * p.tiles_n;
+    const int nk = (K + kTK - 1) / kTK;
+    int s = 1;
+    if (p.fm == 4 && t < 512 && nk >= 8) s = static_cast<int>(std::min<long long>((512 + t - 1) / t, nk / 4));
+    s = std::max(1, s);
+    const int kt_per = (nk + s - 1) / s;
+    p.ksplit = std::max(1, kt_per) * kTK;
+    p.splits = nk > 0 ? (nk + kt_per - 1) / kt_per : 1;
+    // the partial layout of a split SwiGLU is the plain [M, 2N] product
+    if (p.splits > 1 && epi == kSwiglu) p.tiles_n = (Nw + TN - 1) / TN;
+    p.part_bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
+    return p;
+}
+
+inline void launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
+{
+    a.splits = p.splits;
+    a.ksplit = p.ksplit;
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
+    a.Nw = epi == kSwiglu ? 2 * a.N : a.N;
+    a.group_m = 4;
+    const int grid = p.tiles_m * p.tiles_n * p.splits;
+    if (grid == 0) return;
+    const int kern_epi = p.splits > 1 ? kPartial : epi;
+#define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
+    if (p.fm == 8) {
+        switch (kern_epi) {
+        case kStore: SAMBA_GEMM_LAUNCH(8, 8, kStore); break;
+        case kAdd: SAMBA_GEMM_LAUNCH(8, 8, kAdd); break;
+        default: SAMBA_GEMM_LAUNCH(8, 8, kSwiglu); break;  // the plan never splits 256 x 256 tiles
+        }
+    } else {
+        switch (kern_epi) {
+        case kStore: SAMBA_GEMM_LAUNCH(4, 4, kStore); break;
+        case kAdd: SAMBA_GEMM_LAUNCH(4, 4, kAdd); break;
+        case kSwiglu: SAMBA_GEMM_LAUNCH(4, 4, kSwiglu); break;
+        default: SAMBA_GEMM_LAUNCH(4, 4, kPartial); break;
+        }
+    }
+#undef SAMBA_GEMM_LAUNCH
+    if (p.splits > 1) {
+        const size_t n = static_cast<size_t>(a.M) * a.N;
+        const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+        switch (epi) {
+        case kStore: hipLaunchKernelGGL(gemm_reduce_kernel<kStore>, dim3(blocks), dim3(256), 0, s, a); break;
+        case kAdd: hipLaunchKernelGGL(gemm_reduce_kernel<kAdd>, dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(gemm_reduce_kernel<kSwiglu>, dim3(blocks), dim3(256), 0, s, a); break;
+        }
+    }
+}
+
+}  // namespace gemm
+}  // namespace samba

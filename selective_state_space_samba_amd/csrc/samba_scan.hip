@@ -29,6 +29,7 @@
 #include "scan_bwd.h"
 #include "scan_swa.h"
 #include "scan_swa_decode.h"
+#include "gemm.h"
 
 
 namespace {
@@ -647,6 +648,88 @@ samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, 
     a.total = static_cast<int>(tokens);
     samba::swa_dec_set_theta(a, static_cast<double>(rope_base));
     samba::launch_swa_kv_fill(a, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+size_t samba_gemm_workspace_bytes(int M, int N, int K, samba_gemm_epilogue epilogue)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || epilogue < SAMBA_GEMM_STORE || epilogue > SAMBA_GEMM_SWIGLU) return 0;
+    return samba::gemm::plan(M, N, K, static_cast<int>(epilogue)).part_bytes;
+}
+
+samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
+                        void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    const char *fn = "samba_gemm";
+    if (M < 0 || N < 0 || K < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: M=%d N=%d K=%d must be >= 0", fn, M, N, K);
+    if (epilogue < SAMBA_GEMM_STORE || epilogue > SAMBA_GEMM_SWIGLU)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: unknown epilogue %d", fn, (int)epilogue);
+    if (K % 8 != 0) return fail(SAMBA_ERR_UNSUPPORTED, "%s: K=%d is not a multiple of 8", fn, K);
+    if (M == 0 || N == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    if (lda < K || lda % 8 != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: lda=%d must be >= K=%d and a multiple of 8", fn, lda, K);
+    if (ldo < N) return fail(SAMBA_ERR_INVALID_ARG, "%s: ldo=%d must be >= N=%d", fn, ldo, N);
+    const bool add = epilogue == SAMBA_GEMM_ADD_F32;
+    const size_t esz = add ? 4 : 2;
+    const int Nw = epilogue == SAMBA_GEMM_SWIGLU ? 2 * N : N;
+    // every row and tile offset is a 32-bit byte offset from a tile base
+    if (static_cast<size_t>(lda) * 2 * 256 > 0x7fffffffull || static_cast<size_t>(K) * 2 * 256 > 0x7fffffffull ||
+        static_cast<size_t>(Nw) > 0x7fffffffull)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: K=%d or lda=%d too large", fn, K, lda);
+    if (K > 0) {
+        REQUIRE_PTR(A, "A");
+        REQUIRE_PTR(W, "W");
+    }
+    // the epilogue stores single elements: out and residual need only element alignment
+    if (out == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(out) & (esz - 1)) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: out is not %zu-byte aligned", fn, esz);
+    if (add) {
+        if (residual == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: residual is NULL", fn);
+        if ((reinterpret_cast<uintptr_t>(residual) & 3u) != 0)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: residual is not 4-byte aligned", fn);
+        if (ldr < N) return fail(SAMBA_ERR_INVALID_ARG, "%s: ldr=%d must be >= N=%d", fn, ldr, N);
+    }
+    const size_t a_bytes = (static_cast<size_t>(M - 1) * lda + K) * 2;
+    const size_t w_bytes = static_cast<size_t>(Nw) * K * 2;
+    const size_t o_bytes = (static_cast<size_t>(M - 1) * ldo + N) * esz;
+    if (overlaps(out, o_bytes, A, K > 0 ? a_bytes : 0) || overlaps(out, o_bytes, W, w_bytes))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: out overlaps an input", fn);
+    if (add && static_cast<const void *>(residual) != out &&
+        overlaps(out, o_bytes, residual, (static_cast<size_t>(M - 1) * ldr + N) * 4))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: residual partially overlaps out", fn);
+    if (add && static_cast<const void *>(residual) == out && ldr != ldo)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: residual is out with ldr != ldo", fn);
+    const samba::gemm::Plan pl = samba::gemm::plan(M, N, K, static_cast<int>(epilogue));
+    if (pl.part_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < pl.part_bytes)
+            return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.part_bytes,
+                        workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+        if (overlaps(out, o_bytes, workspace, pl.part_bytes))
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: out overlaps the workspace", fn);
+    }
+    if (static_cast<long long>(pl.tiles_m) * pl.tiles_n * pl.splits > 0x7fffffffll)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    samba::gemm::GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = static_cast<const uint16_t *>(A);
+    a.lda = lda;
+    a.W = static_cast<const uint16_t *>(W);
+    a.out = out;
+    a.ldo = ldo;
+    a.R = residual;
+    a.ldr = ldr;
+    a.part = static_cast<float *>(workspace);
+    samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
 
