@@ -276,6 +276,79 @@ samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const
                         void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
                         void *stream);
 
+/* RMSNorm of the rows of a float32 matrix (page 1, "The layer arrangement pattern": each
+ * layer is preceded by RMSNorm): out[r][i] = x[r][i] / sqrt(mean_i(x[r][i]^2) + eps) * weight[i].
+ *   x fp32 [rows][d], weight fp32 [d], out bf16 [rows][d]; eps >= 0.  out must not overlap x. */
+samba_status samba_rmsnorm(int rows, int d, const float *x, const float *weight, float eps, void *out, void *stream);
+
+/* Shape of a Samba model (page 1, "The Mamba Layer" parameter summary, "The Sliding Window
+ * Attention (SWA) Layer", "The SwiGLU MLP Layer"; the 1.7B configuration is d_model 2048,
+ * d_inner 4096, dt_rank 128, d_state 16, d_ff 8196 (stored as 8200), 32 query heads,
+ * 4 KV heads, head_dim 64, window 2048, RoPE base 10000). */
+typedef struct {
+    int d_model;     /* d_m */
+    int d_inner;     /* d_e = 2 d_m */
+    int d_state;     /* d_s = 16 */
+    int dt_rank;     /* d_r = d_m / 16, rank of the Delta projection */
+    int d_ff;        /* MLP width as stored: d_p rounded up to a multiple of 8; the extra W1/W2
+                      * rows and W3 columns must be zero (the result is then exactly that of d_p) */
+    int n_heads;     /* query heads */
+    int n_kv_heads;
+    int head_dim;    /* 64 or 128 */
+    int window;      /* sliding window w */
+    float rope_base;
+    float norm_eps;  /* RMSNorm epsilon */
+} samba_model_config;
+
+typedef enum { SAMBA_LAYER_MAMBA = 0, SAMBA_LAYER_SWA = 1, SAMBA_LAYER_MLP = 2 } samba_layer_kind;
+
+/* One layer of the stack: its kind, its RMSNorm weight, its weights (bf16, one row per output
+ * feature) and its decode state (device memory updated in place by samba_decode_step).
+ * Only the fields of the layer's kind are read.
+ * MAMBA ("The Mamba Layer"): H = X W_in, gate X W_g, U = SiLU(conv(H)), Delta from U W_r W_q
+ *   + b, B = U W_b, C = U W_c, output (Y * SiLU(X W_g)) W_out:
+ *   w_in, w_gate [d_inner][d_model]; w_dt_down (W_r) [dt_rank][d_inner];
+ *   w_dt_up (W_q) [d_inner][dt_rank]; w_b, w_c [d_state][d_inner]; w_out [d_model][d_inner];
+ *   ssm: A, D, dt_bias (b), conv_w, conv_b as for samba_scan_prefill;
+ *   h [nseq][d_inner][d_state] fp32 and conv_state [nseq][3][d_inner] bf16 (as for
+ *   samba_scan_decode).
+ * SWA: w_query [n_heads*head_dim][d_model]; w_key, w_value [n_kv_heads*head_dim][d_model];
+ *   w_o [d_model][n_heads*head_dim]; k_cache, v_cache [nseq][n_kv_heads][window+1][head_dim]
+ *   ring buffers as for samba_swa_decode.
+ * MLP ("SwiGLU Formulation"): w12 [2 d_ff][d_model] = [W1^T; W2^T]; w3 [d_model][d_ff]. */
+typedef struct {
+    int kind;
+    const float *norm_w;
+    const void *w_in, *w_gate, *w_dt_down, *w_dt_up, *w_b, *w_c, *w_out;
+    samba_params ssm;
+    float *h;
+    void *conv_state;
+    const void *w_query, *w_key, *w_value, *w_o;
+    void *k_cache, *v_cache;
+    const void *w12, *w3;
+} samba_layer;
+
+/* Workspace samba_decode_step needs for nseq sequences (intermediate activations and the
+ * partial sums of the projections). */
+size_t samba_decode_step_workspace_bytes(const samba_model_config *cfg, int nseq);
+
+/* One generation step of a whole Samba stack for nseq sequences (one new token each):
+ * for every layer, hidden += Layer(RMSNorm(hidden)) ("The layer arrangement pattern", with
+ * the Mamba, SWA and MLP layers as defined on page 1), then out = RMSNorm(hidden) with
+ * final_norm_w, and pos += 1 for every pos >= 0.
+ *   layers     HOST array [n_layers] (the pointers in it are device pointers)
+ *   hidden     fp32 [nseq][d_model] IN: the new tokens' embeddings; OUT: the residual stream
+ *              after the last layer
+ *   out        bf16 [nseq][d_model] or NULL (then final_norm_w is not read)
+ *   pos        DEVICE int32 [nseq] IN/OUT: the new tokens' positions (SWA layers); a
+ *              sequence with pos < 0 gets no attention output and keeps its position
+ *   workspace  samba_decode_step_workspace_bytes(cfg, nseq) bytes, 256-byte aligned
+ * d_model, d_inner, dt_rank and d_ff must be multiples of 8.  Every launch goes to `stream`
+ * and the call allocates nothing, so the whole step can be captured into a HIP graph. */
+samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, const samba_layer *layers,
+                               const float *final_norm_w, int nseq, float *hidden, void *out, int32_t *pos,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char *samba_last_error(void);

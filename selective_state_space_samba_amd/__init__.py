@@ -14,9 +14,11 @@ import ctypes
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill", "gemm",
+__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill", "gemm", "rmsnorm",
+           "decode_step", "decode_step_workspace_bytes",
            "workspace_bytes", "lib_path", "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +39,23 @@ class SambaError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
                 ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
+
+
+class ModelConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int), ("d_inner", ctypes.c_int), ("d_state", ctypes.c_int),
+                ("dt_rank", ctypes.c_int), ("d_ff", ctypes.c_int), ("n_heads", ctypes.c_int),
+                ("n_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int), ("window", ctypes.c_int),
+                ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+LAYER_KINDS = {"mamba": 0, "swa": 1, "mlp": 2}
+_LAYER_PTRS = ("norm_w", "w_in", "w_gate", "w_dt_down", "w_dt_up", "w_b", "w_c", "w_out")
+_LAYER_PTRS2 = ("h", "conv_state", "w_query", "w_key", "w_value", "w_o", "k_cache", "v_cache", "w12", "w3")
+
+
+class Layer(ctypes.Structure):
+    _fields_ = ([("kind", ctypes.c_int)] + [(n, ctypes.c_void_p) for n in _LAYER_PTRS] + [("ssm", Params)] +
+                [(n, ctypes.c_void_p) for n in _LAYER_PTRS2])
 
 
 def lib_path() -> str:
@@ -80,6 +99,13 @@ def load():
         lib.samba_swa_kv_fill.argtypes = [I, P, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
         lib.samba_conv_silu.restype = I
         lib.samba_conv_silu.argtypes = [I, P, I, I, I, I, P, P, P, P, P, P, P]
+        lib.samba_rmsnorm.restype = I
+        lib.samba_rmsnorm.argtypes = [I, I, P, P, ctypes.c_float, P, P]
+        lib.samba_decode_step_workspace_bytes.restype = Z
+        lib.samba_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(ModelConfig), I]
+        lib.samba_decode_step.restype = I
+        lib.samba_decode_step.argtypes = [ctypes.POINTER(ModelConfig), I, ctypes.POINTER(Layer), P, I, P, P, P, P, Z,
+                                          P]
         lib.samba_gemm_workspace_bytes.restype = Z
         lib.samba_gemm_workspace_bytes.argtypes = [I, I, I, I]
         lib.samba_gemm.restype = I
@@ -490,4 +516,101 @@ def gemm(a, w, *, epilogue="store", out=None, residual=None, workspace=None):
     st = load().samba_gemm(M, N, K, epi, pa, max(lda, K), pw, po, max(ldo, N), pr, max(ldr, N), pws, nws,
                            _stream(dev))
     _check(st)
+    return out
+
+
+def rmsnorm(x, weight, *, eps=1e-5, out=None):
+    """out bf16 [rows, d] = x / sqrt(mean(x^2) + eps) * weight for fp32 x [rows, d]."""
+    dev = _gpu_device(x)
+    rows, d = x.shape
+    _shape(weight, (d,), "weight")
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+    _shape(out, (rows, d), "out")
+    _check(load().samba_rmsnorm(rows, d, _ptr(x, "x", torch.float32, dev), _ptr(weight, "weight", torch.float32, dev),
+                                float(eps), _ptr(out, "out", torch.bfloat16, dev), _stream(dev)))
+    return out
+
+
+def _model_config(cfg):
+    return ModelConfig(*(int(cfg[k]) for k in ("d_model", "d_inner", "d_state", "dt_rank", "d_ff", "n_heads",
+                                                "n_kv_heads", "head_dim", "window")),
+                       float(cfg.get("rope_base", 10000.0)), float(cfg.get("norm_eps", 1e-5)))
+
+
+def decode_step_workspace_bytes(cfg, nseq):
+    return int(load().samba_decode_step_workspace_bytes(ctypes.byref(_model_config(cfg)), int(nseq)))
+
+
+class DecodeStep:
+    """Marshals a Samba stack once (config, per-layer weights and decode state: dicts of GPU
+    tensors keyed like the fields of samba_layer, plus "kind") and runs samba_decode_step.
+    The tensors must stay alive as long as this object is used."""
+
+    def __init__(self, cfg, layers, final_norm_w, nseq):
+        self.cfg = _model_config(cfg)
+        self.nseq = int(nseq)
+        self.dev = _gpu_device(final_norm_w)
+        arr = (Layer * max(1, len(layers)))()
+        for i, ly in enumerate(layers):
+            L = arr[i]
+            L.kind = LAYER_KINDS[ly["kind"]]
+            for n in _LAYER_PTRS + _LAYER_PTRS2:
+                t = ly.get(n)
+                setattr(L, n, _ptr(t, n, None, self.dev) if t is not None else None)
+            if ly["kind"] == "mamba":
+                L.ssm = _params(ly["A"], ly.get("D"), ly.get("dt_bias"), ly["conv_w"], ly.get("conv_b"), self.dev,
+                                int(cfg["d_inner"]), int(cfg["d_state"]))
+        self.layers = arr
+        self.n_layers = len(layers)
+        self.final_norm_w = final_norm_w
+        self.ws_bytes = decode_step_workspace_bytes(cfg, nseq)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.dev)
+
+    def __call__(self, hidden, pos, out=None):
+        """hidden fp32 [nseq, d_model] (updated in place), pos int32 [nseq] (advanced by one);
+        returns out bf16 [nseq, d_model] = the final RMSNorm of hidden, or None if out is False."""
+        S, dm = self.nseq, self.cfg.d_model
+        _shape(hidden, (S, dm), "hidden")
+        _shape(pos, (S,), "pos")
+        if out is None:
+            out = torch.empty((S, dm), dtype=torch.bfloat16, device=self.dev)
+        po = None if out is False else _ptr(out, "out", torch.bfloat16, self.dev)
+        _check(load().samba_decode_step(
+            ctypes.byref(self.cfg), self.n_layers, self.layers, _ptr(self.final_norm_w, "final_norm_w", torch.float32,
+                                                                     self.dev),
+            S, _ptr(hidden, "hidden", torch.float32, self.dev), po, _ptr(pos, "pos", torch.int32, self.dev),
+            _ptr(self.workspace, "workspace"), self.ws_bytes, _stream(self.dev)))
+        return None if out is False else out
+
+
+def decode_step(cfg, layers, final_norm_w, hidden, pos, out=None):
+    """One-shot form of DecodeStep (marshals the stack on every call)."""
+    return DecodeStep(cfg, layers, final_norm_w, hidden.shape[0])(hidden, pos, out)
+
+
+_F32_KEYS = ("norm_w", "A", "D", "dt_bias", "conv_w", "conv_b")
+
+
+def upload_stack(cfg, layers, nseq, device):
+    """Device copies of a stack given as numpy arrays (weights bf16, RMSNorm and Mamba
+    parameters fp32) plus a zero decode state for nseq sequences: per Mamba layer h
+    [nseq, d_inner, d_state] fp32 and conv_state [nseq, 3, d_inner] bf16, per SWA layer
+    k_cache / v_cache [nseq, n_kv_heads, window + 1, head_dim] bf16."""
+    out = []
+    for ly in layers:
+        d = {"kind": ly["kind"]}
+        for k, a in ly.items():
+            if k == "kind":
+                continue
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+            d[k] = t if k in _F32_KEYS else t.to(torch.bfloat16)
+        if ly["kind"] == "mamba":
+            d["h"] = torch.zeros((nseq, cfg["d_inner"], cfg["d_state"]), dtype=torch.float32, device=device)
+            d["conv_state"] = torch.zeros((nseq, 3, cfg["d_inner"]), dtype=torch.bfloat16, device=device)
+        elif ly["kind"] == "swa":
+            shape = (nseq, cfg["n_kv_heads"], cfg["window"] + 1, cfg["head_dim"])
+            d["k_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+            d["v_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        out.append(d)
     return out

@@ -25,6 +25,8 @@
 #include "scan_common.h"
 
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 namespace samba {
 namespace gemm {
@@ -159,12 +161,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Per K tile: the next tile's global loads are issued first and stay in flight while
+    // the two 32-wide MFMA steps run on this tile's LDS buffer; then they are written to the
+    // other buffer and one barrier ends the tile.  (Interleaving the LDS reads and writes with
+    // the MFMAs through scheduling group barriers measured slower on 128 x 128 tiles, and
+    // 256 x 256 tiles have no registers left for a second fragment set.)
+    const int frow = lane & 15, fk = 8 * (lane >> 4);
     if (nk > 0) {
         load_tile(0);
         store_tile(0);
         __syncthreads();
     }
-    const int frow = lane & 15, fk = 8 * (lane >> 4);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_tile(kt + 1);
@@ -274,7 +281,10 @@ inline Plan plan(int M, int N, int K, int epi)
         const long long outc = epi == kSwiglu ? tn / 2 : tn;
         return static_cast<long long>((M + tm - 1) / tm) * ((N + outc - 1) / outc);
     };
-    if (tiles(256, 256) >= 256) {
+    const char *force = getenv("SAMBA_GEMM_TILE");  // "128" / "256": tile choice for tests and timing
+    const bool f128 = force != nullptr && strcmp(force, "128") == 0;
+    const bool f256 = force != nullptr && strcmp(force, "256") == 0;
+    if (f256 || (!f128 && tiles(256, 256) >= 256)) {
         p.fm = 8;
         p.fn = 8;
     } else {

@@ -30,6 +30,7 @@
 #include "scan_swa.h"
 #include "scan_swa_decode.h"
 #include "gemm.h"
+#include "model_step.h"
 
 
 namespace {
@@ -730,6 +731,188 @@ samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const
     a.ldr = ldr;
     a.part = static_cast<float *>(workspace);
     samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+samba_status samba_rmsnorm(int rows, int d, const float *x, const float *weight, float eps, void *out, void *stream)
+{
+    const char *fn = "samba_rmsnorm";
+    if (rows < 0 || d < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: rows=%d must be >= 0 and d=%d >= 1", fn, rows, d);
+    if (!(eps >= 0.0f)) return fail(SAMBA_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+    if (rows == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(weight, "weight");
+    if (out == nullptr || (reinterpret_cast<uintptr_t>(out) & 1u) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: out is NULL or not 2-byte aligned", fn);
+    const size_t n = static_cast<size_t>(rows) * d;
+    if (overlaps(out, n * 2, x, n * 4)) return fail(SAMBA_ERR_INVALID_ARG, "%s: out overlaps x", fn);
+    samba::step::launch_rmsnorm(rows, d, x, weight, eps, static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the decode step's intermediate activations in the caller's workspace.
+struct StepLayout {
+    size_t hn, x, z, u, dtl, B, C, dt, y, q, k, v, o, m, part, swa, total;
+    size_t part_bytes, swa_bytes;
+};
+
+StepLayout step_layout(const samba_model_config &c, int S)
+{
+    StepLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~static_cast<size_t>(255);
+        return o;
+    };
+    const size_t s = static_cast<size_t>(S), hq = static_cast<size_t>(c.n_heads) * c.head_dim,
+                 hk = static_cast<size_t>(c.n_kv_heads) * c.head_dim;
+    L.hn = take(s * c.d_model * 2);
+    L.x = take(s * c.d_inner * 2);
+    L.z = take(s * c.d_inner * 2);
+    L.u = take(s * c.d_inner * 2);
+    L.dt = take(s * c.d_inner * 2);
+    L.y = take(s * c.d_inner * 2);
+    L.dtl = take(s * c.dt_rank * 2);
+    L.B = take(s * c.d_state * 2);
+    L.C = take(s * c.d_state * 2);
+    L.q = take(s * hq * 2);
+    L.k = take(s * hk * 2);
+    L.v = take(s * hk * 2);
+    L.o = take(s * hq * 2);
+    L.m = take(s * c.d_ff * 2);
+    using samba::gemm::plan;
+    const int shapes[][4] = {
+        {c.d_inner, c.d_model, 0, 0},         {c.dt_rank, c.d_inner, 0, 0},
+        {c.d_state, c.d_inner, 0, 0},         {c.d_inner, c.dt_rank, 0, 0},
+        {c.d_model, c.d_inner, 1, 0},         {static_cast<int>(hq), c.d_model, 0, 0},
+        {static_cast<int>(hk), c.d_model, 0, 0}, {c.d_model, static_cast<int>(hq), 1, 0},
+        {c.d_ff, c.d_model, 2, 0},            {c.d_model, c.d_ff, 1, 0}};
+    L.part_bytes = 0;
+    for (const auto &sh : shapes) L.part_bytes = std::max(L.part_bytes, plan(S, sh[0], sh[1], sh[2]).part_bytes);
+    L.part = take(L.part_bytes);
+    L.swa_bytes = samba::swa_decode_workspace_bytes(S, c.n_heads, c.head_dim);
+    L.swa = take(L.swa_bytes);
+    L.total = off;
+    return L;
+}
+
+samba_status check_model_config(const char *fn, const samba_model_config *c)
+{
+    if (c == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: config is NULL", fn);
+    if (c->d_model < 8 || c->d_inner < 8 || c->dt_rank < 8 || c->d_ff < 8 || c->d_model % 8 || c->d_inner % 8 ||
+        c->dt_rank % 8 || c->d_ff % 8)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: d_model=%d d_inner=%d dt_rank=%d d_ff=%d must be positive multiples of 8",
+                    fn, c->d_model, c->d_inner, c->dt_rank, c->d_ff);
+    if (c->d_state < 1 || c->d_state > samba::kMaxState)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: d_state=%d (1..%d)", fn, c->d_state, samba::kMaxState);
+    if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0 || c->window < 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: heads %d / %d or window %d invalid", fn, c->n_heads, c->n_kv_heads,
+                    c->window);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: head_dim=%d (64 and 128 are built)", fn, c->head_dim);
+    if (!(c->norm_eps >= 0.0f) || !(c->rope_base > 1.0f))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: norm_eps must be >= 0 and rope_base > 1", fn);
+    return SAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t samba_decode_step_workspace_bytes(const samba_model_config *cfg, int nseq)
+{
+    if (nseq <= 0 || check_model_config("samba_decode_step_workspace_bytes", cfg) != SAMBA_OK) return 0;
+    return step_layout(*cfg, nseq).total;
+}
+
+samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, const samba_layer *layers,
+                               const float *final_norm_w, int nseq, float *hidden, void *out, int32_t *pos,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *fn = "samba_decode_step";
+    samba_status st = check_model_config(fn, cfg);
+    if (st != SAMBA_OK) return st;
+    if (n_layers < 0 || nseq < 0) return fail(SAMBA_ERR_INVALID_ARG, "%s: n_layers=%d nseq=%d must be >= 0", fn, n_layers, nseq);
+    if (n_layers > 0 && layers == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: layers is NULL", fn);
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    REQUIRE_PTR(hidden, "hidden");
+    if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
+    if (out != nullptr) REQUIRE_PTR(final_norm_w, "final_norm_w");
+    for (int l = 0; l < n_layers; ++l)
+        if (layers[l].kind < SAMBA_LAYER_MAMBA || layers[l].kind > SAMBA_LAYER_MLP)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: layer %d has unknown kind %d", fn, l, layers[l].kind);
+    const samba_model_config &c = *cfg;
+    const StepLayout L = step_layout(c, nseq);
+    if (workspace == nullptr || workspace_bytes < L.total)
+        return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, L.total,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    char *ws = static_cast<char *>(workspace);
+    void *hn = ws + L.hn, *x = ws + L.x, *z = ws + L.z, *u = ws + L.u, *dtl = ws + L.dtl, *Bm = ws + L.B,
+         *Cm = ws + L.C, *dt = ws + L.dt, *y = ws + L.y, *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *o = ws + L.o,
+         *m = ws + L.m, *part = ws + L.part, *swa = ws + L.swa;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int S = nseq, dm = c.d_model, de = c.d_inner, hq = c.n_heads * c.head_dim, hk = c.n_kv_heads * c.head_dim;
+    int layer = -1;
+    const char *what = "";
+    // Runs one sub-call; a failure is reported with the layer and the step that failed.
+#define STEP(name, call)                                                                               \
+    do {                                                                                               \
+        what = name;                                                                                   \
+        const samba_status s_ = (call);                                                                \
+        if (s_ != SAMBA_OK) {                                                                          \
+            const std::string msg = g_err;                                                             \
+            return fail(s_, "%s: layer %d (%s): %s", fn, layer, what, msg.c_str());                    \
+        }                                                                                              \
+    } while (0)
+    auto gemm = [&](int N, int K, samba_gemm_epilogue e, const void *A, const void *W, void *dst, int ld) {
+        return samba_gemm(S, N, K, e, A, K, W, dst, ld, e == SAMBA_GEMM_ADD_F32 ? hidden : nullptr, ld, part,
+                          L.part_bytes, stream);
+    };
+    for (layer = 0; layer < n_layers; ++layer) {
+        const samba_layer &ly = layers[layer];
+        STEP("rmsnorm", samba_rmsnorm(S, dm, hidden, ly.norm_w, c.norm_eps, hn, stream));
+        if (ly.kind == SAMBA_LAYER_MAMBA) {
+            STEP("x = X W_in", gemm(de, dm, SAMBA_GEMM_STORE, hn, ly.w_in, x, de));
+            STEP("z = X W_g", gemm(de, dm, SAMBA_GEMM_STORE, hn, ly.w_gate, z, de));
+            STEP("u = SiLU(conv(x))", samba_conv_silu(S, nullptr, 1, 0, de, SAMBA_BF16, x, ly.ssm.conv_w,
+                                                      ly.ssm.conv_b, ly.conv_state, u, nullptr, stream));
+            STEP("U W_r", gemm(c.dt_rank, de, SAMBA_GEMM_STORE, u, ly.w_dt_down, dtl, c.dt_rank));
+            STEP("B = U W_b", gemm(c.d_state, de, SAMBA_GEMM_STORE, u, ly.w_b, Bm, c.d_state));
+            STEP("C = U W_c", gemm(c.d_state, de, SAMBA_GEMM_STORE, u, ly.w_c, Cm, c.d_state));
+            STEP("dt = U W_r W_q", gemm(de, c.dt_rank, SAMBA_GEMM_STORE, dtl, ly.w_dt_up, dt, de));
+            STEP("scan decode", samba_scan_decode(S, de, c.d_state, SAMBA_BF16, x, dt, Bm, Cm, z, &ly.ssm, ly.h,
+                                                  ly.conv_state, y, stream));
+            STEP("hidden += Y W_out", gemm(dm, de, SAMBA_GEMM_ADD_F32, y, ly.w_out, hidden, dm));
+        } else if (ly.kind == SAMBA_LAYER_SWA) {
+            STEP("q", gemm(hq, dm, SAMBA_GEMM_STORE, hn, ly.w_query, q, hq));
+            STEP("k", gemm(hk, dm, SAMBA_GEMM_STORE, hn, ly.w_key, k, hk));
+            STEP("v", gemm(hk, dm, SAMBA_GEMM_STORE, hn, ly.w_value, v, hk));
+            STEP("attention decode", samba_swa_decode(S, c.n_heads, c.n_kv_heads, c.head_dim, c.window, c.rope_base,
+                                                      SAMBA_BF16, q, k, v, pos, ly.k_cache, ly.v_cache, o, swa,
+                                                      L.swa_bytes, stream));
+            STEP("hidden += O W_o", gemm(dm, hq, SAMBA_GEMM_ADD_F32, o, ly.w_o, hidden, dm));
+        } else {
+            STEP("SwiGLU", gemm(c.d_ff, dm, SAMBA_GEMM_SWIGLU, hn, ly.w12, m, c.d_ff));
+            STEP("hidden += M W_3", gemm(dm, c.d_ff, SAMBA_GEMM_ADD_F32, m, ly.w3, hidden, dm));
+        }
+    }
+    layer = n_layers;
+    if (out != nullptr) STEP("final rmsnorm", samba_rmsnorm(S, dm, hidden, final_norm_w, c.norm_eps, out, stream));
+#undef STEP
+    samba::step::launch_advance(S, pos, hs);
     return launched(fn);
 }
 

@@ -163,3 +163,58 @@ def cu_from_lengths(lens) -> np.ndarray:
 
 def seed_for(config_index: int) -> int:
     return 20260000 + config_index
+
+
+# ---------------------------------------------------------------- whole-model stacks
+# Shapes of the page's 1.7B configuration ("Samba 1.7B": 48 layers, d_m = 2048, d_p = 8196,
+# 32 query heads, 4 KV heads; d_e = 2 d_m, d_r = d_m / 16, d_s = 16, w = 2048, RoPE base
+# 10000).  d_ff is the stored MLP width: d_p rounded up to a multiple of 8, the extra W1/W2
+# rows and W3 columns zero.
+MODEL_1P7B = dict(d_model=2048, d_inner=4096, d_state=16, dt_rank=128, d_p=8196, d_ff=8200, n_heads=32,
+                  n_kv_heads=4, head_dim=64, window=2048, rope_base=10000.0, norm_eps=1e-5, n_layers=48)
+PATTERN = ("mamba", "mlp", "mamba", "mlp", "swa", "mlp")  # the repeating unit of the layer stack
+
+
+def layer_kinds(n_layers: int):
+    return [PATTERN[i % len(PATTERN)] for i in range(n_layers)]
+
+
+def make_model(seed: int, cfg: dict, n_layers: int):
+    """Random-initialised weights of a Samba stack (no trained weights exist here): every
+    projection W^T [d_out, d_in] ~ N(0, 1/d_in), rounded to bfloat16 (the values the device
+    receives); RMSNorm weights ~ N(1, 0.1); Mamba parameters as make_params.  Returns
+    (layers: list of dicts of float32 arrays, final_norm_w)."""
+    dm, de, N, dr = cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg["dt_rank"]
+    dp, dff = cfg.get("d_p", cfg["d_ff"]), cfg["d_ff"]
+    hq, hk = cfg["n_heads"] * cfg["head_dim"], cfg["n_kv_heads"] * cfg["head_dim"]
+
+    def w(name, dout, din):
+        return _normal(seed, name, (dout, din), std=din ** -0.5, io="bf16")
+
+    layers = []
+    for i, kind in enumerate(layer_kinds(n_layers)):
+        p = "L%d." % i
+        ly = dict(kind=kind, norm_w=_normal(seed, p + "norm", (dm,), mean=1.0, std=0.1))
+        if kind == "mamba":
+            prm = make_params(seed + 7919 * (i + 1), de, N)
+            ly.update(w_in=w(p + "w_in", de, dm), w_gate=w(p + "w_gate", de, dm), w_dt_down=w(p + "w_r", dr, de),
+                      w_dt_up=w(p + "w_q", de, dr), w_b=w(p + "w_b", N, de), w_c=w(p + "w_c", N, de),
+                      w_out=w(p + "w_out", dm, de), A=prm.A, D=prm.Dskip, dt_bias=prm.dt_bias, conv_w=prm.conv_w,
+                      conv_b=prm.conv_b)
+        elif kind == "swa":
+            ly.update(w_query=w(p + "wq", hq, dm), w_key=w(p + "wk", hk, dm), w_value=w(p + "wv", hk, dm),
+                      w_o=w(p + "wo", dm, hq))
+        else:
+            w12 = np.zeros((2 * dff, dm), dtype=np.float32)
+            w12[:dp] = w(p + "w1", dp, dm)
+            w12[dff:dff + dp] = w(p + "w2", dp, dm)
+            w3 = np.zeros((dm, dff), dtype=np.float32)
+            w3[:, :dp] = w(p + "w3", dm, dp)
+            ly.update(w12=w12, w3=w3)
+        layers.append(ly)
+    return layers, _normal(seed, "final_norm", (dm,), mean=1.0, std=0.1)
+
+
+def make_hidden(seed: int, step: int, nseq: int, d_model: int):
+    """The new tokens' embeddings for one step, N(0, 1)."""
+    return _normal(seed, "emb%d" % step, (nseq, d_model))

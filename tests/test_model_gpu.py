@@ -1,0 +1,185 @@
+"""GPU parity of the whole Samba decode step (samba_decode_step: RMSNorm, projections on the
+matrix cores, the Mamba decode core, ring-buffer attention, SwiGLU MLP, residual stream)
+against the fp64 model oracle, through the C ABI.  The oracle's decode form is pinned to
+its sequence form in test_oracle_model_pins."""
+import numpy as np
+import pytest
+import torch
+
+import selective_state_space_samba_amd as ss
+from oracle import model
+from selective_state_space_samba_amd import synth
+from tests.helpers import TOL, host, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def tol_stack(n_layers):
+    """Tolerance against the plain fp64 oracle: 2e-2 (bf16 I/O) for one repeat of the layer
+    pattern (6 layers); the activations a layer stores in bf16 (2^-9 relative rounding at
+    ~10 points per layer) give each layer an independent error, and the residual stream adds
+    them like a random walk, so the bound grows as sqrt(repeats)."""
+    return TOL["bf16"] * max(1.0, (n_layers / 6.0) ** 0.5)
+
+
+# Against the oracle evaluated with bf16 activations (rounded where the GPU stores them),
+# what remains is float32 vs float64 arithmetic (~1e-7: many steps match to that), the
+# attention's own float32 softmax (~2e-3 over a 2049-key window) and values within float32
+# error of a bf16 rounding boundary, which the two sides round one bf16 ulp (2^-8 relative)
+# apart.  A layer alone stays within 5e-3 (TOL_LAYER); in a stack each flip moves a full
+# 2048-wide normed input of the next layers, flips add up over layers and steps (the Mamba
+# state carries them), and the bound becomes that of the plain comparison.
+TOL_LAYER = 5e-3
+
+
+def tol_matched(n_layers):
+    return tol_stack(n_layers)
+
+
+def bf16_act(a):
+    return synth.round_bf16(np.asarray(a, dtype=np.float32)).astype(np.float64)
+
+SMALL = dict(d_model=64, d_inner=128, d_state=16, dt_rank=8, d_ff=96, n_heads=4, n_kv_heads=2, head_dim=64,
+             window=5, rope_base=10000.0, norm_eps=1e-5)
+
+
+def rounded_history(k, base):
+    """Keys [P, H, dh] as a rotated bf16 cache holds them (see model.cached_key)."""
+    return np.stack([model.cached_key(k[p], p, base, bf16_act) for p in range(k.shape[0])])
+
+
+def run_steps(cfg, n_layers, S, steps, seed, pos0=None, prep=None, kinds=None, matched_tol=None):
+    """Runs `steps` decode steps on the GPU and in both oracles and checks every step: the
+    hidden state and the output against the plain oracle within tol_stack, and the layers'
+    increment (hidden - embedding, what the layers add) against the bf16-activation oracle
+    within matched_tol (default tol_matched).  `kinds` keeps one layer of each listed kind."""
+    layers, fn = synth.make_model(seed, cfg, n_layers)
+    if kinds is not None:  # the first layer of each listed kind, in that order
+        layers = [next(ly for ly in layers if ly["kind"] == k) for k in kinds]
+    n_layers = len(layers)
+    mtol = tol_matched(n_layers) if matched_tol is None else matched_tol
+    dev_layers = ss.upload_stack(cfg, layers, S, DEV)
+    st = model.DecodeState(cfg, layers, S)
+    stm = model.DecodeState(cfg, layers, S)
+    pos_np = np.zeros(S, dtype=np.int32) if pos0 is None else np.asarray(pos0, dtype=np.int32).copy()
+    if prep is not None:
+        prep(layers, dev_layers, st, pos_np)
+        prep(layers, None, stm, pos_np, matched=True)
+    fnw = torch.from_numpy(fn).to(DEV)
+    step = ss.DecodeStep(cfg, dev_layers, fnw, S)
+    pos = torch.from_numpy(pos_np.copy()).to(DEV)
+    worst = 0.0
+    for t in range(steps):
+        emb = synth.make_hidden(seed, t, S, cfg["d_model"])
+        hid = torch.from_numpy(emb).to(DEV)
+        out = step(hid, pos)
+        torch.cuda.synchronize()
+        rh, ro = model.decode_step(cfg, layers, fn, emb, st, pos_np)
+        mh, mo = model.decode_step(cfg, layers, fn, emb, stm, pos_np, act=bf16_act)
+        pos_np = np.where(pos_np >= 0, pos_np + 1, pos_np)
+        gh, go = host(hid), host(out)
+        eh, eo = rel_err(gh, rh), rel_err(go, ro)
+        fi = rel_err(gh - emb, mh - emb)
+        worst = max(worst, eh, eo)
+        print("  step %d hidden err %.3e out err %.3e (tol %.1e) | increment vs bf16-activation oracle %.3e "
+              "(tol %.1e)" % (t, eh, eo, tol_stack(n_layers), fi, mtol), flush=True)
+        assert eh <= tol_stack(n_layers) and eo <= tol_stack(n_layers)
+        assert fi <= mtol
+        np.testing.assert_array_equal(host(pos), pos_np)
+    return worst
+
+
+def test_decode_step_small_stack_from_empty_state():
+    """One repeat of the pattern (Mamba, MLP, Mamba, MLP, SWA, MLP), 3 sequences, 12 steps
+    from an empty state: the 6-entry rings wrap twice."""
+    print("case: small stack 6 layers", flush=True)
+    run_steps(SMALL, 6, 3, 12, 21)
+
+
+def test_decode_step_deep_stack_and_inactive_sequence():
+    """Eight repeats (48 layers, 16 Mamba / 8 SWA / 24 MLP), one sequence inactive (pos < 0:
+    no attention output, position kept)."""
+    print("case: small stack 48 layers", flush=True)
+    run_steps(SMALL, 48, 3, 4, 22, pos0=[0, -1, 0])
+
+
+def _prep_1p7b(S, P):
+    """State set-up for the 1.7B-width tests: random Mamba states and conv histories, rings
+    filled from a random P-token key/value history, every sequence at position P."""
+    cfg = synth.MODEL_1P7B
+
+    def prep(layers, dev_layers, st, pos_np, matched=False):
+        for i, ly in enumerate(layers):
+            if ly["kind"] == "mamba":
+                h, hist = synth.make_state(500 + i, S, cfg["d_inner"], cfg["d_state"], "bf16", scale=0.5)
+                st.h[i][...] = h
+                st.hist[i][...] = hist
+                if dev_layers is not None:
+                    dev_layers[i]["h"].copy_(torch.from_numpy(h))
+                    dev_layers[i]["conv_state"].copy_(torch.from_numpy(hist).to(torch.bfloat16))
+            elif ly["kind"] == "swa":
+                shape = (S, P, cfg["n_kv_heads"], cfg["head_dim"])
+                k = synth._normal(600 + i, "k", shape, io="bf16")
+                v = synth._normal(600 + i, "v", shape, io="bf16")
+                st.k[i] = [rounded_history(k[s], cfg["rope_base"]) if matched else k[s].astype(np.float64)
+                           for s in range(S)]
+                st.v[i] = [v[s].astype(np.float64) for s in range(S)]
+                if dev_layers is not None:
+                    ss.swa_kv_fill(torch.from_numpy(k).to(DEV).to(torch.bfloat16),
+                                   torch.from_numpy(v).to(DEV).to(torch.bfloat16), dev_layers[i]["k_cache"],
+                                   dev_layers[i]["v_cache"], window=cfg["window"])
+        pos_np[:] = P
+
+    return prep
+
+
+def test_decode_step_1p7b_widths_with_resident_state():
+    """The 1.7B widths (d_model 2048, d_inner 4096, dt_rank 128, d_ff 8200 with d_p = 8196,
+    32 / 4 heads, window 2048), one repeat of the pattern, 2 sequences resuming at position
+    2100 from random Mamba states and rings filled from a random 2100-token key/value history."""
+    print("case: 1.7B widths, 6 layers", flush=True)
+    run_steps(dict(synth.MODEL_1P7B), 6, 2, 3, 23, prep=_prep_1p7b(2, 2100))
+
+
+@pytest.mark.parametrize("kind", ["mamba", "swa", "mlp"])
+def test_decode_step_single_layer_1p7b_widths(kind):
+    """One layer of each kind at the 1.7B widths (resident Mamba state, rings filled from a
+    2100-token history): the layer's increment within TOL_LAYER of the bf16-activation oracle."""
+    print("case: one %s layer, 1.7B widths" % kind, flush=True)
+    run_steps(dict(synth.MODEL_1P7B), 6, 2, 2, 24, prep=_prep_1p7b(2, 2100), kinds=(kind,), matched_tol=TOL_LAYER)
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The step captured in a HIP graph and replayed three times gives bitwise the results of
+    three eager steps from the same state (the call allocates nothing and every launch is on
+    the capturing stream)."""
+    print("case: graph replay", flush=True)
+    cfg, S = SMALL, 3
+    layers, fn = synth.make_model(31, cfg, 6)
+    fnw = torch.from_numpy(fn).to(DEV)
+    runs = []
+    for mode in ("eager", "graph"):
+        dl = ss.upload_stack(cfg, layers, S, DEV)
+        step = ss.DecodeStep(cfg, dl, fnw, S)
+        pos = torch.zeros(S, dtype=torch.int32, device=DEV)
+        hid = torch.zeros((S, cfg["d_model"]), device=DEV)
+        out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=DEV)
+        res = []
+        if mode == "graph":  # every kernel has been launched once by the eager run
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(hid, pos, out)
+        for t in range(3):
+            hid.copy_(torch.from_numpy(synth.make_hidden(31, t, S, cfg["d_model"])))
+            if mode == "graph":
+                g.replay()
+            else:
+                step(hid, pos, out)
+            torch.cuda.synchronize()
+            res.append((host(hid), host(out), host(pos)))
+        runs.append(res)
+    for (h1, o1, p1), (h2, o2, p2) in zip(*runs):
+        np.testing.assert_array_equal(h1, h2)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(p1, p2)
