@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--cpu-channels", type=int, default=2048)
     ap.add_argument("--prefill-only", action="store_true", help="time only the long-prompt prefill (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="time only the streaming decode (profiling)")
+    ap.add_argument("--model-only", action="store_true", help="time only the GEMMs and the whole-model decode step")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the prefill and a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -334,6 +335,127 @@ def bench_swa(dev, steps, warmup):
     return res
 
 
+def bench_gemm(dev, steps, warmup):
+    """The layer projections on the matrix cores at the 1.7B widths (bf16 operands, fp32
+    accumulation): prefill shapes (4 x 4096 tokens) against the bf16 MFMA peak, and the
+    decode shapes (256 tokens) against HBM for their weights."""
+    import torch
+    import selective_state_space_samba_amd as ss
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    res = {}
+    shapes = [("in_proj_16k", 16384, 4096, 2048, "store"), ("out_proj_16k", 16384, 2048, 4096, "add"),
+              ("mlp_w12_swiglu_16k", 16384, 8200, 2048, "swiglu"), ("mlp_w3_16k", 16384, 2048, 8200, "add"),
+              ("in_proj_decode256", 256, 4096, 2048, "store"), ("mlp_w12_swiglu_decode256", 256, 8200, 2048, "swiglu")]
+    for name, M, N, K, epi in shapes:
+        Nw = 2 * N if epi == "swiglu" else N
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        w = (torch.randn((Nw, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16)
+        r = torch.randn((M, N), generator=g, device=dev) if epi == "add" else None
+        out = torch.empty((M, N), device=dev, dtype=torch.float32 if epi == "add" else torch.bfloat16)
+        need = int(ss.load().samba_gemm_workspace_bytes(M, N, K, ss.GEMM_EPILOGUES[epi]))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _, per = time_calls(lambda: ss.gemm(a, w, epilogue=epi, out=out, residual=r, workspace=ws), steps, warmup)
+        sec = float(np.median(per))
+        fl = 2.0 * M * K * Nw
+        d = dict(workload="M=%d N=%d K=%d %s" % (M, N, K, epi), us=sec * 1e6,
+                 roofline=dict(bound="mfma", achieved=round(fl / sec / 1e12, 1), peak=2500.0, unit="TFLOP/s",
+                               frac=round(fl / sec / 1e12 / 2500.0, 4), flops_per_launch=fl))
+        if M <= 256:
+            wb = Nw * K * 2
+            d["weights_gbs"] = round(wb / sec / 1e9, 1)
+        res[name] = d
+        del a, w, r, out, ws
+    return res
+
+
+def device_stack(cfg, n_layers, S, dev, seed=11):
+    """A random-initialised 1.7B-shaped stack on the device (weights ~ N(0, 1/d_in) in bf16,
+    Mamba parameters as the synthetic recipe) with a full decode state: random Mamba states
+    and conv histories, full random rings.  Returns (layers, final_norm_w, bytes moved per
+    decode step by an ideal implementation: every weight, state and ring read once, states
+    written once)."""
+    import torch
+    from selective_state_space_samba_amd import synth
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    dm, de, N, dr, dff = cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg["dt_rank"], cfg["d_ff"]
+    dp = cfg.get("d_p", dff)
+    hq, hk = cfg["n_heads"] * cfg["head_dim"], cfg["n_kv_heads"] * cfg["head_dim"]
+
+    def w(dout, din):
+        return (torch.randn((dout, din), generator=g, device=dev) * din ** -0.5).to(torch.bfloat16)
+
+    layers, nbytes = [], 0
+    for i, kind in enumerate(synth.layer_kinds(n_layers)):
+        ly = dict(kind=kind, norm_w=1.0 + 0.1 * torch.randn(dm, generator=g, device=dev))
+        if kind == "mamba":
+            prm = synth.make_params(seed + i, de, N)
+            ly.update(w_in=w(de, dm), w_gate=w(de, dm), w_dt_down=w(dr, de), w_dt_up=w(de, dr), w_b=w(N, de),
+                      w_c=w(N, de), w_out=w(dm, de), A=to_dev(prm.A, dev, False), D=to_dev(prm.Dskip, dev, False),
+                      dt_bias=to_dev(prm.dt_bias, dev, False), conv_w=to_dev(prm.conv_w, dev, False),
+                      conv_b=to_dev(prm.conv_b, dev, False),
+                      h=0.5 * torch.randn((S, de, N), generator=g, device=dev),
+                      conv_state=torch.randn((S, 3, de), generator=g, device=dev).to(torch.bfloat16))
+            nbytes += 2 * S * de * N * 4 + 2 * S * 3 * de * 2
+        elif kind == "swa":
+            shape = (S, cfg["n_kv_heads"], cfg["window"] + 1, cfg["head_dim"])
+            ly.update(w_query=w(hq, dm), w_key=w(hk, dm), w_value=w(hk, dm), w_o=w(dm, hq),
+                      k_cache=torch.randn(shape, generator=g, device=dev).to(torch.bfloat16),
+                      v_cache=torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+            nbytes += 2 * S * hk * (cfg["window"] + 1) * 2
+        else:
+            w12 = torch.zeros((2 * dff, dm), dtype=torch.bfloat16, device=dev)
+            w12[:dp] = w(dp, dm)
+            w12[dff:dff + dp] = w(dp, dm)
+            w3 = torch.zeros((dm, dff), dtype=torch.bfloat16, device=dev)
+            w3[:, :dp] = w(dm, dp)
+            ly.update(w12=w12, w3=w3)
+        for k, t in ly.items():
+            if k.startswith("w") and k != "kind":
+                nbytes += t.numel() * t.element_size()
+        layers.append(ly)
+    return layers, 1.0 + 0.1 * torch.randn(dm, generator=g, device=dev), nbytes
+
+
+def bench_model_decode(dev, steps, warmup, S=256):
+    """A whole Samba decode step (48 layers of the 1.7B configuration, 256 sequences with full
+    rings at position 4096): eager launches and a HIP-graph replay of the same step."""
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+    cfg = dict(synth.MODEL_1P7B)
+    layers, fnw, nbytes = device_stack(cfg, cfg["n_layers"], S, dev)
+    step = ss.DecodeStep(cfg, layers, fnw, S)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    emb = torch.randn((S, cfg["d_model"]), generator=g, device=dev)
+    hid = emb.clone()
+    pos = torch.full((S,), 4096, dtype=torch.int32, device=dev)
+    out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=dev)
+
+    def eager():
+        hid.copy_(emb)
+        step(hid, pos, out)
+
+    _, per_e = time_calls(eager, steps, warmup)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hid.copy_(emb)
+        step(hid, pos, out)
+    _, per_g = time_calls(graph.replay, steps, warmup)
+    sec = float(np.median(per_g))
+    res = dict(workload="48 layers (16 Mamba, 8 SWA, 24 MLP; d_model 2048, d_inner 4096, d_ff 8196, 32/4 heads, "
+                        "window 2048), 256 sequences, full rings",
+               ms_per_step=sec * 1e3, ms_per_step_eager=float(np.median(per_e)) * 1e3, tok_s=S / sec,
+               roofline=dict(bound="hbm", achieved=round(nbytes / sec / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), bytes_per_step=nbytes),
+               note="HIP-graph replay of one step (the eager figure launches the same kernels one by one); "
+                    "bytes = weights + Mamba states read and written + rings read")
+    del layers, step
+    return res
+
+
 def traffic_probe(dev, steps=3):
     """A plain device-to-device copy of exactly 2^30 bytes (bf16), the reference that scales
     the FETCH_SIZE / WRITE_SIZE counters into bytes."""
@@ -434,6 +556,10 @@ def main():
     ss.load()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
 
+    if args.model_only:
+        print(json.dumps({"gemm": bench_gemm(dev, args.steps, args.warmup),
+                          "model_decode_1p7b": bench_model_decode(dev, args.steps, args.warmup)}), flush=True)
+        return
     if args.decode_only:
         dec = bench_decode(args, dev)
         print(json.dumps({"decode_only": decode_summary(dec)}), flush=True)
@@ -484,6 +610,8 @@ def main():
         line["decode_s1024"] = ctl
     if not args.prefill_only and not args.no_extra:
         line["extra"] = bench_extra(dev)
+        line["extra"]["gemm"] = bench_gemm(dev, 10, 3)
+        line["extra"]["model_decode_1p7b"] = bench_model_decode(dev, 10, 3)
     if not args.prefill_only and not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(pre["host"], args.cpu_channels)
     print(json.dumps(line), flush=True)

@@ -309,8 +309,10 @@ inline Plan plan(int M, int N, int K, int epi)
     return p;
 }
 
-inline void launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
+// Returns false (launching nothing) for a plan no kernel is built for.
+inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
 {
+    if (p.fm == 8 && p.splits > 1) return false;
     a.splits = p.splits;
     a.ksplit = p.ksplit;
     a.tiles_m = p.tiles_m;
@@ -318,14 +320,15 @@ inline void launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
     a.Nw = epi == kSwiglu ? 2 * a.N : a.N;
     a.group_m = 4;
     const int grid = p.tiles_m * p.tiles_n * p.splits;
-    if (grid == 0) return;
+    if (grid == 0) return true;
     const int kern_epi = p.splits > 1 ? kPartial : epi;
 #define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
     if (p.fm == 8) {
         switch (kern_epi) {
         case kStore: SAMBA_GEMM_LAUNCH(8, 8, kStore); break;
         case kAdd: SAMBA_GEMM_LAUNCH(8, 8, kAdd); break;
-        default: SAMBA_GEMM_LAUNCH(8, 8, kSwiglu); break;  // the plan never splits 256 x 256 tiles
+        case kSwiglu: SAMBA_GEMM_LAUNCH(8, 8, kSwiglu); break;
+        default: return false;  // no split-K kernel for 256 x 256 tiles: plan() never asks for one
         }
     } else {
         switch (kern_epi) {
@@ -345,6 +348,7 @@ inline void launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
         default: hipLaunchKernelGGL(gemm_reduce_kernel<kSwiglu>, dim3(blocks), dim3(256), 0, s, a); break;
         }
     }
+    return true;
 }
 
 }  // namespace gemm

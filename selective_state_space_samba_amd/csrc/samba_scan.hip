@@ -730,7 +730,8 @@ samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const
     a.R = residual;
     a.ldr = ldr;
     a.part = static_cast<float *>(workspace);
-    samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream));
+    if (!samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream)))
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: no kernel for this tile plan", fn);
     return launched(fn);
 }
 
