@@ -391,8 +391,8 @@ def device_stack(cfg, n_layers, S, dev, seed=11):
         ly = dict(kind=kind, norm_w=1.0 + 0.1 * torch.randn(dm, generator=g, device=dev))
         if kind == "mamba":
             prm = synth.make_params(seed + i, de, N)
-            ly.update(w_in=w(de, dm), w_gate=w(de, dm), w_dt_down=w(dr, de), w_dt_up=w(de, dr), w_b=w(N, de),
-                      w_c=w(N, de), w_out=w(dm, de), A=to_dev(prm.A, dev, False), D=to_dev(prm.Dskip, dev, False),
+            ly.update(w_in_gate=w(2 * de, dm), w_xproj=w(dr + 2 * N, de), w_dt_up=w(de, dr),
+                      w_out=w(dm, de), A=to_dev(prm.A, dev, False), D=to_dev(prm.Dskip, dev, False),
                       dt_bias=to_dev(prm.dt_bias, dev, False), conv_w=to_dev(prm.conv_w, dev, False),
                       conv_b=to_dev(prm.conv_b, dev, False),
                       h=0.5 * torch.randn((S, de, N), generator=g, device=dev),
@@ -400,7 +400,7 @@ def device_stack(cfg, n_layers, S, dev, seed=11):
             nbytes += 2 * S * de * N * 4 + 2 * S * 3 * de * 2
         elif kind == "swa":
             shape = (S, cfg["n_kv_heads"], cfg["window"] + 1, cfg["head_dim"])
-            ly.update(w_query=w(hq, dm), w_key=w(hk, dm), w_value=w(hk, dm), w_o=w(dm, hq),
+            ly.update(w_qkv=w(hq + 2 * hk, dm), w_o=w(dm, hq),
                       k_cache=torch.randn(shape, generator=g, device=dev).to(torch.bfloat16),
                       v_cache=torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
             nbytes += 2 * S * hk * (cfg["window"] + 1) * 2

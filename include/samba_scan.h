@@ -303,27 +303,29 @@ typedef struct {
 typedef enum { SAMBA_LAYER_MAMBA = 0, SAMBA_LAYER_SWA = 1, SAMBA_LAYER_MLP = 2 } samba_layer_kind;
 
 /* One layer of the stack: its kind, its RMSNorm weight, its weights (bf16, one row per output
- * feature) and its decode state (device memory updated in place by samba_decode_step).
- * Only the fields of the layer's kind are read.
+ * feature, the projections that read the same input stacked into one matrix) and its decode
+ * state (device memory updated in place by samba_decode_step).  Only the fields of the
+ * layer's kind are read.
  * MAMBA ("The Mamba Layer"): H = X W_in, gate X W_g, U = SiLU(conv(H)), Delta from U W_r W_q
  *   + b, B = U W_b, C = U W_c, output (Y * SiLU(X W_g)) W_out:
- *   w_in, w_gate [d_inner][d_model]; w_dt_down (W_r) [dt_rank][d_inner];
- *   w_dt_up (W_q) [d_inner][dt_rank]; w_b, w_c [d_state][d_inner]; w_out [d_model][d_inner];
+ *   w_in_gate [2 d_inner][d_model] = [W_in^T; W_g^T];
+ *   w_xproj [dt_rank + 2 d_state][d_inner] = [W_r^T; W_b^T; W_c^T];
+ *   w_dt_up (W_q^T) [d_inner][dt_rank]; w_out [d_model][d_inner];
  *   ssm: A, D, dt_bias (b), conv_w, conv_b as for samba_scan_prefill;
  *   h [nseq][d_inner][d_state] fp32 and conv_state [nseq][3][d_inner] bf16 (as for
  *   samba_scan_decode).
- * SWA: w_query [n_heads*head_dim][d_model]; w_key, w_value [n_kv_heads*head_dim][d_model];
- *   w_o [d_model][n_heads*head_dim]; k_cache, v_cache [nseq][n_kv_heads][window+1][head_dim]
- *   ring buffers as for samba_swa_decode.
+ * SWA ("The Sliding Window Attention (SWA) Layer"): w_qkv [(n_heads + 2 n_kv_heads) head_dim]
+ *   [d_model] = [W_q^T; W_k^T; W_v^T]; w_o [d_model][n_heads head_dim]; k_cache, v_cache
+ *   [nseq][n_kv_heads][window + 1][head_dim] ring buffers as for samba_swa_decode.
  * MLP ("SwiGLU Formulation"): w12 [2 d_ff][d_model] = [W1^T; W2^T]; w3 [d_model][d_ff]. */
 typedef struct {
     int kind;
     const float *norm_w;
-    const void *w_in, *w_gate, *w_dt_down, *w_dt_up, *w_b, *w_c, *w_out;
+    const void *w_in_gate, *w_xproj, *w_dt_up, *w_out;
     samba_params ssm;
     float *h;
     void *conv_state;
-    const void *w_query, *w_key, *w_value, *w_o;
+    const void *w_qkv, *w_o;
     void *k_cache, *v_cache;
     const void *w12, *w3;
 } samba_layer;
@@ -343,7 +345,8 @@ size_t samba_decode_step_workspace_bytes(const samba_model_config *cfg, int nseq
  *   pos        DEVICE int32 [nseq] IN/OUT: the new tokens' positions (SWA layers); a
  *              sequence with pos < 0 gets no attention output and keeps its position
  *   workspace  samba_decode_step_workspace_bytes(cfg, nseq) bytes, 256-byte aligned
- * d_model, d_inner, dt_rank and d_ff must be multiples of 8.  Every launch goes to `stream`
+ * d_model, d_inner, dt_rank and d_ff must be multiples of 8, d_state 16, nseq <= 65535.  Every
+ * launch goes to `stream`
  * and the call allocates nothing, so the whole step can be captured into a HIP graph. */
 samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, const samba_layer *layers,
                                const float *final_norm_w, int nseq, float *hidden, void *out, int32_t *pos,

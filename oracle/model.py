@@ -45,6 +45,20 @@ def _split_heads(a, heads, dh):
     return a.reshape(a.shape[:-1] + (heads, dh))
 
 
+def mamba_weights(cfg, ly):
+    """W_in^T, W_g^T, W_r^T, W_b^T, W_c^T from the stacked matrices of a Mamba layer."""
+    de, dr, N = cfg["d_inner"], cfg["dt_rank"], cfg["d_state"]
+    wig, wx = ly["w_in_gate"], ly["w_xproj"]
+    return wig[:de], wig[de:], wx[:dr], wx[dr:dr + N], wx[dr + N:]
+
+
+def qkv_weights(cfg, ly):
+    """W_q^T, W_k^T, W_v^T from the stacked matrix of an attention layer."""
+    hq, hk = cfg["n_heads"] * cfg["head_dim"], cfg["n_kv_heads"] * cfg["head_dim"]
+    w = ly["w_qkv"]
+    return w[:hq], w[hq:hq + hk], w[hq + hk:]
+
+
 class DecodeState:
     """Decode state of a stack, float64: per Mamba layer h [S, d_inner, N] and the conv
     history [S, 3, d_inner] (oldest first); per SWA layer every key and value of every
@@ -98,18 +112,20 @@ def decode_step(cfg, layers, final_norm_w, hidden, state, pos, act=None):
     for i, ly in enumerate(layers):
         hn = act(rmsnorm(hidden, ly["norm_w"], eps))
         if ly["kind"] == "mamba":
-            x, z = act(linear(hn, ly["w_in"])), act(linear(hn, ly["w_gate"]))
+            w_in, w_g, w_r, w_b, w_c = mamba_weights(cfg, ly)
+            x, z = act(linear(hn, w_in)), act(linear(hn, w_g))
             u, _ = oracle.conv_silu(x[:, None, :], ly["conv_w"], ly["conv_b"], conv0=state.hist[i])
             u = act(u[:, 0, :])
-            dt = act(linear(act(linear(u, ly["w_dt_down"])), ly["w_dt_up"]))
-            Bm, Cm = act(linear(u, ly["w_b"])), act(linear(u, ly["w_c"]))
+            dt = act(linear(act(linear(u, w_r)), ly["w_dt_up"]))
+            Bm, Cm = act(linear(u, w_b)), act(linear(u, w_c))
             y = act(oracle.decode_step(x, dt, Bm, Cm, z, ly["A"], ly["D"], ly["dt_bias"], ly["conv_w"],
                                        ly["conv_b"], state.h[i], state.hist[i]))
             hidden += linear(y, ly["w_out"])
         elif ly["kind"] == "swa":
-            q = _split_heads(act(linear(hn, ly["w_query"])), H, dh)
-            k = _split_heads(act(linear(hn, ly["w_key"])), Hk, dh)
-            v = _split_heads(act(linear(hn, ly["w_value"])), Hk, dh)
+            w_q, w_k, w_v = qkv_weights(cfg, ly)
+            q = _split_heads(act(linear(hn, w_q)), H, dh)
+            k = _split_heads(act(linear(hn, w_k)), Hk, dh)
+            v = _split_heads(act(linear(hn, w_v)), Hk, dh)
             o = np.zeros((S, H, dh))
             for s in range(S):
                 p = int(pos[s])
@@ -144,19 +160,21 @@ def prefill(cfg, layers, final_norm_w, emb):
         hn = rmsnorm(hidden, ly["norm_w"], eps).reshape(S * L, dm)
         if ly["kind"] == "mamba":
             de = cfg["d_inner"]
-            x = linear(hn, ly["w_in"]).reshape(S, L, de)
-            z = linear(hn, ly["w_gate"]).reshape(S, L, de)
+            w_in, w_g, w_r, w_b, w_c = mamba_weights(cfg, ly)
+            x = linear(hn, w_in).reshape(S, L, de)
+            z = linear(hn, w_g).reshape(S, L, de)
             u, _ = oracle.conv_silu(x, ly["conv_w"], ly["conv_b"])
             u2 = u.reshape(S * L, de)
-            dt = linear(linear(u2, ly["w_dt_down"]), ly["w_dt_up"]).reshape(S, L, de)
-            Bm = linear(u2, ly["w_b"]).reshape(S, L, -1)
-            Cm = linear(u2, ly["w_c"]).reshape(S, L, -1)
+            dt = linear(linear(u2, w_r), ly["w_dt_up"]).reshape(S, L, de)
+            Bm = linear(u2, w_b).reshape(S, L, -1)
+            Cm = linear(u2, w_c).reshape(S, L, -1)
             y, _, _ = oracle.prefill(x, dt, Bm, Cm, z, ly["A"], ly["D"], ly["dt_bias"], ly["conv_w"], ly["conv_b"])
             hidden += linear(y.reshape(S * L, de), ly["w_out"]).reshape(S, L, dm)
         elif ly["kind"] == "swa":
-            q = linear(hn, ly["w_query"]).reshape(S, L, H, dh)
-            k = linear(hn, ly["w_key"]).reshape(S, L, Hk, dh)
-            v = linear(hn, ly["w_value"]).reshape(S, L, Hk, dh)
+            w_q, w_k, w_v = qkv_weights(cfg, ly)
+            q = linear(hn, w_q).reshape(S, L, H, dh)
+            k = linear(hn, w_k).reshape(S, L, Hk, dh)
+            v = linear(hn, w_v).reshape(S, L, Hk, dh)
             o = oracle.swa(q, k, v, window=cfg["window"], base=cfg["rope_base"])
             hidden += linear(o.reshape(S * L, H * dh), ly["w_o"]).reshape(S, L, dm)
         else:

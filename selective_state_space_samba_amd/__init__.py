@@ -49,8 +49,8 @@ class ModelConfig(ctypes.Structure):
 
 
 LAYER_KINDS = {"mamba": 0, "swa": 1, "mlp": 2}
-_LAYER_PTRS = ("norm_w", "w_in", "w_gate", "w_dt_down", "w_dt_up", "w_b", "w_c", "w_out")
-_LAYER_PTRS2 = ("h", "conv_state", "w_query", "w_key", "w_value", "w_o", "k_cache", "v_cache", "w12", "w3")
+_LAYER_PTRS = ("norm_w", "w_in_gate", "w_xproj", "w_dt_up", "w_out")
+_LAYER_PTRS2 = ("h", "conv_state", "w_qkv", "w_o", "k_cache", "v_cache", "w12", "w3")
 
 
 class Layer(ctypes.Structure):

@@ -142,7 +142,7 @@ samba::ScanArgs make_args(int nseq, int seqlen, const int32_t *cu, int d_inner, 
                           const samba_params *p, const float *h0, const void *conv0, void *out,
                           float *h_final, void *conv_final)
 {
-    samba::ScanArgs a;
+    samba::ScanArgs a{};
     a.nseq = nseq;
     a.seqlen = seqlen;
     a.cu = cu;
@@ -542,6 +542,30 @@ size_t samba_swa_decode_workspace_bytes(int nseq, int n_heads, int head_dim)
 }
 
 namespace {
+samba::SwaDecArgs swa_dec_args(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
+                               const void *q, const void *k, const void *v, const int32_t *pos, void *k_cache,
+                               void *v_cache, void *out, void *workspace)
+{
+    samba::SwaDecArgs a{};
+    a.S = nseq;
+    a.Hq = n_heads;
+    a.Hkv = n_kv_heads;
+    a.dh = head_dim;
+    a.window = window;
+    a.cap = window + 1;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.pos = pos;
+    a.kc = static_cast<uint16_t *>(k_cache);
+    a.vc = static_cast<uint16_t *>(v_cache);
+    a.out = out;
+    a.part = static_cast<float *>(workspace);
+    samba::swa_dec_set_theta(a, static_cast<double>(rope_base));
+    return a;
+}
+
 samba_status swa_dec_common(const char *fn, int nseq, int n_heads, int n_kv_heads, int head_dim, int window,
                             float rope_base, samba_dtype io, bool decode)
 {
@@ -589,23 +613,8 @@ samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_di
         return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace == nullptr ? (size_t)0 : workspace_bytes);
     REQUIRE_PTR(workspace, "workspace");
-    samba::SwaDecArgs a{};
-    a.S = nseq;
-    a.Hq = n_heads;
-    a.Hkv = n_kv_heads;
-    a.dh = head_dim;
-    a.window = window;
-    a.cap = window + 1;
-    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(head_dim)));
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.pos = pos;
-    a.kc = static_cast<uint16_t *>(k_cache);
-    a.vc = static_cast<uint16_t *>(v_cache);
-    a.out = out;
-    a.part = static_cast<float *>(workspace);
-    samba::swa_dec_set_theta(a, static_cast<double>(rope_base));
+    samba::SwaDecArgs a = swa_dec_args(nseq, n_heads, n_kv_heads, head_dim, window, rope_base, q, k, v, pos, k_cache,
+                                       v_cache, out, workspace);
     samba::launch_swa_decode(a, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
@@ -759,10 +768,15 @@ samba_status samba_rmsnorm(int rows, int d, const float *x, const float *weight,
 namespace {
 
 // Byte offsets of the decode step's intermediate activations in the caller's workspace.
+// Projections that read the same input are one GEMM over concatenated weights: x and z are the
+// two column halves of xz, (U W_r, B, C) the column blocks of xp, q / k / v those of qkv.
 struct StepLayout {
-    size_t hn, x, z, u, dtl, B, C, dt, y, q, k, v, o, m, part, swa, total;
+    size_t hn, xz, u, xp, dt, y, qkv, o, m, part, swa, total;
     size_t part_bytes, swa_bytes;
 };
+
+int xproj_width(const samba_model_config &c) { return c.dt_rank + 2 * c.d_state; }
+int qkv_width(const samba_model_config &c) { return (c.n_heads + 2 * c.n_kv_heads) * c.head_dim; }
 
 StepLayout step_layout(const samba_model_config &c, int S)
 {
@@ -773,29 +787,20 @@ StepLayout step_layout(const samba_model_config &c, int S)
         off += (bytes + 255) & ~static_cast<size_t>(255);
         return o;
     };
-    const size_t s = static_cast<size_t>(S), hq = static_cast<size_t>(c.n_heads) * c.head_dim,
-                 hk = static_cast<size_t>(c.n_kv_heads) * c.head_dim;
+    const size_t s = static_cast<size_t>(S), hq = static_cast<size_t>(c.n_heads) * c.head_dim;
     L.hn = take(s * c.d_model * 2);
-    L.x = take(s * c.d_inner * 2);
-    L.z = take(s * c.d_inner * 2);
+    L.xz = take(s * 2 * c.d_inner * 2);
     L.u = take(s * c.d_inner * 2);
+    L.xp = take(s * xproj_width(c) * 2);
     L.dt = take(s * c.d_inner * 2);
     L.y = take(s * c.d_inner * 2);
-    L.dtl = take(s * c.dt_rank * 2);
-    L.B = take(s * c.d_state * 2);
-    L.C = take(s * c.d_state * 2);
-    L.q = take(s * hq * 2);
-    L.k = take(s * hk * 2);
-    L.v = take(s * hk * 2);
+    L.qkv = take(s * qkv_width(c) * 2);
     L.o = take(s * hq * 2);
     L.m = take(s * c.d_ff * 2);
     using samba::gemm::plan;
-    const int shapes[][4] = {
-        {c.d_inner, c.d_model, 0, 0},         {c.dt_rank, c.d_inner, 0, 0},
-        {c.d_state, c.d_inner, 0, 0},         {c.d_inner, c.dt_rank, 0, 0},
-        {c.d_model, c.d_inner, 1, 0},         {static_cast<int>(hq), c.d_model, 0, 0},
-        {static_cast<int>(hk), c.d_model, 0, 0}, {c.d_model, static_cast<int>(hq), 1, 0},
-        {c.d_ff, c.d_model, 2, 0},            {c.d_model, c.d_ff, 1, 0}};
+    const int shapes[][3] = {{2 * c.d_inner, c.d_model, 0}, {xproj_width(c), c.d_inner, 0}, {c.d_inner, c.dt_rank, 0},
+                             {c.d_model, c.d_inner, 1},     {qkv_width(c), c.d_model, 0},   {c.d_model, static_cast<int>(hq), 1},
+                             {c.d_ff, c.d_model, 2},        {c.d_model, c.d_ff, 1}};
     L.part_bytes = 0;
     for (const auto &sh : shapes) L.part_bytes = std::max(L.part_bytes, plan(S, sh[0], sh[1], sh[2]).part_bytes);
     L.part = take(L.part_bytes);
@@ -812,13 +817,17 @@ samba_status check_model_config(const char *fn, const samba_model_config *c)
         c->dt_rank % 8 || c->d_ff % 8)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: d_model=%d d_inner=%d dt_rank=%d d_ff=%d must be positive multiples of 8",
                     fn, c->d_model, c->d_inner, c->dt_rank, c->d_ff);
-    if (c->d_state < 1 || c->d_state > samba::kMaxState)
-        return fail(SAMBA_ERR_UNSUPPORTED, "%s: d_state=%d (1..%d)", fn, c->d_state, samba::kMaxState);
+    if (c->d_state != samba::kMaxState)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: d_state=%d (the decode step is built for %d)", fn, c->d_state,
+                    samba::kMaxState);
     if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads != 0 || c->window < 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: heads %d / %d or window %d invalid", fn, c->n_heads, c->n_kv_heads,
                     c->window);
     if (c->head_dim != 64 && c->head_dim != 128)
         return fail(SAMBA_ERR_UNSUPPORTED, "%s: head_dim=%d (64 and 128 are built)", fn, c->head_dim);
+    if (c->n_heads / c->n_kv_heads > samba::swadec::kMaxGroup || c->window >= 65535 * 64)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: %d query heads per KV head or window %d beyond the built limits", fn,
+                    c->n_heads / c->n_kv_heads, c->window);
     if (!(c->norm_eps >= 0.0f) || !(c->rope_base > 1.0f))
         return fail(SAMBA_ERR_INVALID_ARG, "%s: norm_eps must be >= 0 and rope_base > 1", fn);
     return SAMBA_OK;
@@ -847,6 +856,7 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
         g_err.clear();
         return SAMBA_OK;
     }
+    if (nseq > 65535) return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d exceeds 65535", fn, nseq);
     REQUIRE_PTR(hidden, "hidden");
     if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
     if (out != nullptr) REQUIRE_PTR(final_norm_w, "final_norm_w");
@@ -861,11 +871,15 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
     char *ws = static_cast<char *>(workspace);
-    void *hn = ws + L.hn, *x = ws + L.x, *z = ws + L.z, *u = ws + L.u, *dtl = ws + L.dtl, *Bm = ws + L.B,
-         *Cm = ws + L.C, *dt = ws + L.dt, *y = ws + L.y, *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *o = ws + L.o,
-         *m = ws + L.m, *part = ws + L.part, *swa = ws + L.swa;
+    uint16_t *hn = reinterpret_cast<uint16_t *>(ws + L.hn), *xz = reinterpret_cast<uint16_t *>(ws + L.xz),
+             *u = reinterpret_cast<uint16_t *>(ws + L.u), *xp = reinterpret_cast<uint16_t *>(ws + L.xp),
+             *dt = reinterpret_cast<uint16_t *>(ws + L.dt), *y = reinterpret_cast<uint16_t *>(ws + L.y),
+             *qkv = reinterpret_cast<uint16_t *>(ws + L.qkv), *o = reinterpret_cast<uint16_t *>(ws + L.o),
+             *m = reinterpret_cast<uint16_t *>(ws + L.m);
+    void *part = ws + L.part, *swa = ws + L.swa;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int S = nseq, dm = c.d_model, de = c.d_inner, hq = c.n_heads * c.head_dim, hk = c.n_kv_heads * c.head_dim;
+    const int S = nseq, dm = c.d_model, de = c.d_inner, dr = c.dt_rank, N = c.d_state;
+    const int hq = c.n_heads * c.head_dim, hk = c.n_kv_heads * c.head_dim, wx = xproj_width(c), wq = qkv_width(c);
     int layer = -1;
     const char *what = "";
     // Runs one sub-call; a failure is reported with the layer and the step that failed.
@@ -878,38 +892,65 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             return fail(s_, "%s: layer %d (%s): %s", fn, layer, what, msg.c_str());                    \
         }                                                                                              \
     } while (0)
-    auto gemm = [&](int N, int K, samba_gemm_epilogue e, const void *A, const void *W, void *dst, int ld) {
-        return samba_gemm(S, N, K, e, A, K, W, dst, ld, e == SAMBA_GEMM_ADD_F32 ? hidden : nullptr, ld, part,
+#define NEED(p, name)                                                                                  \
+    do {                                                                                               \
+        if ((p) == nullptr || !aligned16(p))                                                           \
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: layer %d: %s is NULL or not 16-byte aligned", fn, layer, name); \
+    } while (0)
+    auto gemm = [&](int Nn, int K, samba_gemm_epilogue e, const void *A, int lda, const void *W, void *dst, int ld) {
+        return samba_gemm(S, Nn, K, e, A, lda, W, dst, ld, e == SAMBA_GEMM_ADD_F32 ? hidden : nullptr, ld, part,
                           L.part_bytes, stream);
     };
     for (layer = 0; layer < n_layers; ++layer) {
         const samba_layer &ly = layers[layer];
         STEP("rmsnorm", samba_rmsnorm(S, dm, hidden, ly.norm_w, c.norm_eps, hn, stream));
         if (ly.kind == SAMBA_LAYER_MAMBA) {
-            STEP("x = X W_in", gemm(de, dm, SAMBA_GEMM_STORE, hn, ly.w_in, x, de));
-            STEP("z = X W_g", gemm(de, dm, SAMBA_GEMM_STORE, hn, ly.w_gate, z, de));
-            STEP("u = SiLU(conv(x))", samba_conv_silu(S, nullptr, 1, 0, de, SAMBA_BF16, x, ly.ssm.conv_w,
-                                                      ly.ssm.conv_b, ly.conv_state, u, nullptr, stream));
-            STEP("U W_r", gemm(c.dt_rank, de, SAMBA_GEMM_STORE, u, ly.w_dt_down, dtl, c.dt_rank));
-            STEP("B = U W_b", gemm(c.d_state, de, SAMBA_GEMM_STORE, u, ly.w_b, Bm, c.d_state));
-            STEP("C = U W_c", gemm(c.d_state, de, SAMBA_GEMM_STORE, u, ly.w_c, Cm, c.d_state));
-            STEP("dt = U W_r W_q", gemm(de, c.dt_rank, SAMBA_GEMM_STORE, dtl, ly.w_dt_up, dt, de));
-            STEP("scan decode", samba_scan_decode(S, de, c.d_state, SAMBA_BF16, x, dt, Bm, Cm, z, &ly.ssm, ly.h,
-                                                  ly.conv_state, y, stream));
-            STEP("hidden += Y W_out", gemm(dm, de, SAMBA_GEMM_ADD_F32, y, ly.w_out, hidden, dm));
+            NEED(ly.ssm.A, "ssm.A");
+            NEED(ly.ssm.conv_w, "ssm.conv_w");
+            NEED(ly.h, "h");
+            NEED(ly.conv_state, "conv_state");
+            // [x | z] = X [W_in ; W_g]
+            STEP("[x | z] = X [W_in; W_g]", gemm(2 * de, dm, SAMBA_GEMM_STORE, hn, dm, ly.w_in_gate, xz, 2 * de));
+            // u = SiLU(conv(x)) for the Delta / B / C projections; the conv state is not advanced
+            samba::ConvArgs ca{};
+            ca.nseq = S;
+            ca.seqlen = 1;
+            ca.D = de;
+            ca.x = xz;
+            ca.ldx = 2 * de;
+            ca.conv_w = ly.ssm.conv_w;
+            ca.conv_b = ly.ssm.conv_b;
+            ca.conv0 = ly.conv_state;
+            ca.u = u;
+            samba::launch_conv_silu(ca, SAMBA_BF16, hs);
+            STEP("u = SiLU(conv(x))", launched(fn));
+            // [U W_r | B | C] = U [W_r; W_b; W_c], then Delta's input (U W_r) W_q
+            STEP("U [W_r; W_b; W_c]", gemm(wx, de, SAMBA_GEMM_STORE, u, de, ly.w_xproj, xp, wx));
+            STEP("dt = (U W_r) W_q", gemm(de, dr, SAMBA_GEMM_STORE, xp, wx, ly.w_dt_up, dt, de));
+            samba::ScanArgs sa = make_args(S, 1, nullptr, de, N, xz, dt, xp + dr, xp + dr + N, xz + de, &ly.ssm,
+                                           ly.h, ly.conv_state, y, ly.h, ly.conv_state);
+            sa.ldx = 2 * de;
+            sa.ldbc = wx;
+            samba::launch_decode16(sa, SAMBA_BF16, hs);
+            STEP("scan decode", launched(fn));
+            STEP("hidden += Y W_out", gemm(dm, de, SAMBA_GEMM_ADD_F32, y, de, ly.w_out, hidden, dm));
         } else if (ly.kind == SAMBA_LAYER_SWA) {
-            STEP("q", gemm(hq, dm, SAMBA_GEMM_STORE, hn, ly.w_query, q, hq));
-            STEP("k", gemm(hk, dm, SAMBA_GEMM_STORE, hn, ly.w_key, k, hk));
-            STEP("v", gemm(hk, dm, SAMBA_GEMM_STORE, hn, ly.w_value, v, hk));
-            STEP("attention decode", samba_swa_decode(S, c.n_heads, c.n_kv_heads, c.head_dim, c.window, c.rope_base,
-                                                      SAMBA_BF16, q, k, v, pos, ly.k_cache, ly.v_cache, o, swa,
-                                                      L.swa_bytes, stream));
-            STEP("hidden += O W_o", gemm(dm, hq, SAMBA_GEMM_ADD_F32, o, ly.w_o, hidden, dm));
+            NEED(ly.k_cache, "k_cache");
+            NEED(ly.v_cache, "v_cache");
+            STEP("[q | k | v] = X [W_q; W_k; W_v]", gemm(wq, dm, SAMBA_GEMM_STORE, hn, dm, ly.w_qkv, qkv, wq));
+            samba::SwaDecArgs aa = swa_dec_args(S, c.n_heads, c.n_kv_heads, c.head_dim, c.window, c.rope_base, qkv,
+                                                qkv + hq, qkv + hq + hk, pos, ly.k_cache, ly.v_cache, o, swa);
+            aa.ldq = wq;
+            aa.ldkv = wq;
+            samba::launch_swa_decode(aa, hs);
+            STEP("attention decode", launched(fn));
+            STEP("hidden += O W_o", gemm(dm, hq, SAMBA_GEMM_ADD_F32, o, hq, ly.w_o, hidden, dm));
         } else {
-            STEP("SwiGLU", gemm(c.d_ff, dm, SAMBA_GEMM_SWIGLU, hn, ly.w12, m, c.d_ff));
-            STEP("hidden += M W_3", gemm(dm, c.d_ff, SAMBA_GEMM_ADD_F32, m, ly.w3, hidden, dm));
+            STEP("SwiGLU", gemm(c.d_ff, dm, SAMBA_GEMM_SWIGLU, hn, dm, ly.w12, m, c.d_ff));
+            STEP("hidden += M W_3", gemm(dm, c.d_ff, SAMBA_GEMM_ADD_F32, m, c.d_ff, ly.w3, hidden, dm));
         }
     }
+#undef NEED
     layer = n_layers;
     if (out != nullptr) STEP("final rmsnorm", samba_rmsnorm(S, dm, hidden, final_norm_w, c.norm_eps, out, stream));
 #undef STEP

@@ -27,6 +27,7 @@ struct ScanArgs {
     int D;               // d_inner
     int N;               // d_state (<= kMaxState)
     const void *x, *dt, *B, *C, *z;
+    int ldx, ldbc;       // decode only: row pitch of x and z, of B and C (0: contiguous)
     const float *A, *Dskip, *dt_bias, *conv_w, *conv_b;
     const float *h0;
     const void *conv0;

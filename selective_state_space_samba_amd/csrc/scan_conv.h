@@ -34,6 +34,7 @@ struct ConvArgs {
     int run;             // tokens per thread
     int nruns;           // runs per sequence (= ceil(seqlen / run), at least 1)
     const void *x;
+    int ldx;             // x row pitch in elements (0: D, the contiguous layout)
     const float *conv_w, *conv_b;
     const void *conv0;
     void *u;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(conv::kThreads) void conv_silu_kernel(ConvArgs a)
     if (g >= nvec) return;  // no barriers: an early exit is safe
     const int c = g * kVec;
     const int D = a.D;
+    const size_t ldx = a.ldx > 0 ? static_cast<size_t>(a.ldx) : static_cast<size_t>(D);
 
     size_t t0, t1;
     {
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(conv::kThreads) void conv_silu_kernel(ConvArgs a)
     for (int k = 0; k < 3; ++k) {
         const int tt = tb - 3 + k;
         if (tt >= 0) {
-            load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(tt)) * D + c, win[k]);
+            load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(tt)) * ldx + c, win[k]);
         } else if (a.conv0 != nullptr) {
             load_vec<Io, kVec>(static_cast<const T *>(a.conv0) + (static_cast<size_t>(s) * 3 + (3 + tt)) * D + c, win[k]);
         } else {
@@ -167,13 +169,13 @@ __global__ __launch_bounds__(conv::kThreads) void conv_silu_kernel(ConvArgs a)
         float xv[kGroup][kVec];
 #pragma unroll
         for (int k = 0; k < kGroup; ++k)
-            load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(t + k)) * D + c, xv[k]);
+            load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(t + k)) * ldx + c, xv[k]);
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) token((t0 + static_cast<size_t>(t + k)) * D + c, xv[k]);
     }
     for (; t < te; ++t) {
         float xv[kVec];
-        load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(t)) * D + c, xv);
+        load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(t)) * ldx + c, xv);
         token((t0 + static_cast<size_t>(t)) * D + c, xv);
     }
     if (te == L && a.conv_final != nullptr) {  // this run holds the sequence end

@@ -57,7 +57,7 @@ __device__ inline void widen4(const float *p, float *f)
 }  // namespace dec
 
 template <class Io>
-__global__ __launch_bounds__(256) void decode16_kernel(int D, const typename Io::T *__restrict__ x,
+__global__ __launch_bounds__(256) void decode16_kernel(int D, int ldx, int ldbc, const typename Io::T *__restrict__ x,
                                                        const typename Io::T *__restrict__ dt,
                                                        const typename Io::T *__restrict__ Bm,
                                                        const typename Io::T *__restrict__ Cm,
@@ -81,11 +81,12 @@ __global__ __launch_bounds__(256) void decode16_kernel(int D, const typename Io:
     const bool fok = cf < D;
     const int cfc = fok ? cf : D - 1;  // clamped for loads
     const size_t sdf = static_cast<size_t>(s) * D + cfc;
+    const size_t sxf = static_cast<size_t>(s) * ldx + cfc;  // x and z may be column blocks of wider rows
     const size_t cbase = static_cast<size_t>(s) * 3 * D + cfc;
     const T h0 = conv[cbase], h1 = conv[cbase + D], h2 = conv[cbase + 2 * static_cast<size_t>(D)];
-    const T xr = x[sdf];
+    const T xr = x[sxf];
     const float dtv = to_f32(dt[sdf]);
-    const float zv = z ? to_f32(z[sdf]) : 0.0f;
+    const float zv = z ? to_f32(z[sxf]) : 0.0f;
     const float4 w = *reinterpret_cast<const float4 *>(conv_w + static_cast<size_t>(cfc) * kConvK);
     const float cb = conv_b ? conv_b[cfc] : 0.0f;
     const float dsk = Dskip ? Dskip[cfc] : 0.0f;
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(256) void decode16_kernel(int D, const typename Io:
         Av[k][0] = av.x; Av[k][1] = av.y; Av[k][2] = av.z; Av[k][3] = av.w;
     }
     float Bv[4], Cv[4];
-    widen4(Bm + static_cast<size_t>(s) * N + n0, Bv);
-    widen4(Cm + static_cast<size_t>(s) * N + n0, Cv);
+    widen4(Bm + static_cast<size_t>(s) * ldbc + n0, Bv);
+    widen4(Cm + static_cast<size_t>(s) * ldbc + n0, Cv);
 
     // conv (tap k multiplies x_{t-3+k}) + SiLU, Delta (log2 units), skip and gate terms
     float pre = __builtin_fmaf(w.x, to_f32(h0), cb);
@@ -170,13 +171,13 @@ inline void launch_decode16(const ScanArgs &a, samba_dtype io, hipStream_t strea
     if (io == SAMBA_BF16) {
         using T = uint16_t;
         decode16_kernel<IoBf16><<<grid, block, 0, stream>>>(
-            a.D, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
+            a.D, a.ldx > 0 ? a.ldx : a.D, a.ldbc > 0 ? a.ldbc : kMaxState, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
             static_cast<const T *>(a.C), static_cast<const T *>(a.z), a.A, a.Dskip, a.dt_bias, a.conv_w, a.conv_b,
             a.h_final, static_cast<T *>(a.conv_final), static_cast<T *>(a.out));
     } else {
         using T = float;
         decode16_kernel<IoF32><<<grid, block, 0, stream>>>(
-            a.D, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
+            a.D, a.ldx > 0 ? a.ldx : a.D, a.ldbc > 0 ? a.ldbc : kMaxState, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
             static_cast<const T *>(a.C), static_cast<const T *>(a.z), a.A, a.Dskip, a.dt_bias, a.conv_w, a.conv_b,
             a.h_final, static_cast<T *>(a.conv_final), static_cast<T *>(a.out));
     }

@@ -29,6 +29,7 @@ struct SwaDecArgs {
     int S, Hq, Hkv, dh, window, cap;
     float scale_log2;
     const void *q, *k, *v;  // new token: q [S][Hq][dh], k, v [S][Hkv][dh]
+    int ldq, ldkv;          // row pitch of q and of k, v per sequence (0: contiguous)
     const int32_t *pos;     // [S] position of the new token (tokens before it in the sequence)
     uint16_t *kc, *vc;      // rings [S][Hkv][cap][dh], bfloat16, keys rotated
     void *out;              // [S][Hq][dh]
@@ -86,7 +87,8 @@ __global__ __launch_bounds__(256) void swa_dec_store_kernel(SwaDecArgs a)
     const int nvec = a.Hkv * a.dh / 8;
     for (int i = threadIdx.x; i < nvec; i += 256) {
         const int hk = i / (a.dh / 8), d = (i % (a.dh / 8)) * 8;
-        const size_t src = (static_cast<size_t>(s) * a.Hkv + hk) * a.dh + d;
+        const size_t ldkv = a.ldkv > 0 ? static_cast<size_t>(a.ldkv) : static_cast<size_t>(a.Hkv) * a.dh;
+        const size_t src = static_cast<size_t>(s) * ldkv + static_cast<size_t>(hk) * a.dh + d;
         const size_t dst = ((static_cast<size_t>(s) * a.Hkv + hk) * a.cap + slot) * a.dh + d;
         float f[8];
         load8bf(static_cast<const uint16_t *>(a.k) + src, f);
@@ -125,7 +127,9 @@ __global__ __launch_bounds__(64) void swa_dec_attn_kernel(SwaDecArgs a)
         float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         const int d = 32 * kk + 8 * g;
         if (c16 < G && pos >= 0) {
-            load8bf(static_cast<const uint16_t *>(a.q) + (static_cast<size_t>(s) * a.Hq + hk * G + c16) * kDh + d, f);
+            const size_t ldq = a.ldq > 0 ? static_cast<size_t>(a.ldq) : static_cast<size_t>(a.Hq) * kDh;
+            load8bf(static_cast<const uint16_t *>(a.q) + static_cast<size_t>(s) * ldq +
+                        static_cast<size_t>(hk * G + c16) * kDh + d, f);
             rotate8(a, d, pos, f);
         }
 #pragma unroll

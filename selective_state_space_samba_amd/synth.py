@@ -182,7 +182,9 @@ def layer_kinds(n_layers: int):
 def make_model(seed: int, cfg: dict, n_layers: int):
     """Random-initialised weights of a Samba stack (no trained weights exist here): every
     projection W^T [d_out, d_in] ~ N(0, 1/d_in), rounded to bfloat16 (the values the device
-    receives); RMSNorm weights ~ N(1, 0.1); Mamba parameters as make_params.  Returns
+    receives); RMSNorm weights ~ N(1, 0.1); Mamba parameters as make_params.  Projections that
+    read the same input are stacked: w_in_gate = [W_in; W_g], w_xproj = [W_r; W_b; W_c],
+    w_qkv = [W_q; W_k; W_v], w12 = [W1; W2] (each W given as W^T, one row per output).  Returns
     (layers: list of dicts of float32 arrays, final_norm_w)."""
     dm, de, N, dr = cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg["dt_rank"]
     dp, dff = cfg.get("d_p", cfg["d_ff"]), cfg["d_ff"]
@@ -197,12 +199,12 @@ def make_model(seed: int, cfg: dict, n_layers: int):
         ly = dict(kind=kind, norm_w=_normal(seed, p + "norm", (dm,), mean=1.0, std=0.1))
         if kind == "mamba":
             prm = make_params(seed + 7919 * (i + 1), de, N)
-            ly.update(w_in=w(p + "w_in", de, dm), w_gate=w(p + "w_gate", de, dm), w_dt_down=w(p + "w_r", dr, de),
-                      w_dt_up=w(p + "w_q", de, dr), w_b=w(p + "w_b", N, de), w_c=w(p + "w_c", N, de),
-                      w_out=w(p + "w_out", dm, de), A=prm.A, D=prm.Dskip, dt_bias=prm.dt_bias, conv_w=prm.conv_w,
-                      conv_b=prm.conv_b)
+            ly.update(w_in_gate=np.concatenate([w(p + "w_in", de, dm), w(p + "w_gate", de, dm)]),
+                      w_xproj=np.concatenate([w(p + "w_r", dr, de), w(p + "w_b", N, de), w(p + "w_c", N, de)]),
+                      w_dt_up=w(p + "w_q", de, dr), w_out=w(p + "w_out", dm, de), A=prm.A, D=prm.Dskip,
+                      dt_bias=prm.dt_bias, conv_w=prm.conv_w, conv_b=prm.conv_b)
         elif kind == "swa":
-            ly.update(w_query=w(p + "wq", hq, dm), w_key=w(p + "wk", hk, dm), w_value=w(p + "wv", hk, dm),
+            ly.update(w_qkv=np.concatenate([w(p + "wq", hq, dm), w(p + "wk", hk, dm), w(p + "wv", hk, dm)]),
                       w_o=w(p + "wo", dm, hq))
         else:
             w12 = np.zeros((2 * dff, dm), dtype=np.float32)
