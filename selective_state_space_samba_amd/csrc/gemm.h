@@ -237,28 +237,62 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
 }
 
-// Sums the split partials in split order and applies the epilogue; one thread per output.
-template <int kEpi>
+// Sums the split partials in split order and applies the epilogue; one thread per kVec
+// consecutive outputs of a row (kVec = 4: 16-byte partial loads, when N, the row pitches and
+// the output are aligned for them; see vec_ok).
+template <int kEpi, int kVec>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
 {
+    const int nvec = a.N / kVec;
     const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= static_cast<size_t>(a.M) * a.N) return;
-    const int row = static_cast<int>(i / a.N), col = static_cast<int>(i % a.N);
+    if (i >= static_cast<size_t>(a.M) * nvec) return;
+    const int row = static_cast<int>(i / nvec), col = static_cast<int>(i % nvec) * kVec;
     const size_t stride = static_cast<size_t>(a.M) * a.Nw;
     const float *p = a.part + static_cast<size_t>(row) * a.Nw + col;
-    float s = 0.f, g = 0.f;
+    float s[kVec] = {}, g[kVec] = {};
     for (int k = 0; k < a.splits; ++k) {
-        s += p[k * stride];
-        if constexpr (kEpi == kSwiglu) g += p[k * stride + a.N];
+        if constexpr (kVec == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(p + k * stride);
+            s[0] += v.x, s[1] += v.y, s[2] += v.z, s[3] += v.w;
+            if constexpr (kEpi == kSwiglu) {
+                const float4 w = *reinterpret_cast<const float4 *>(p + k * stride + a.N);
+                g[0] += w.x, g[1] += w.y, g[2] += w.z, g[3] += w.w;
+            }
+        } else {
+            s[0] += p[k * stride];
+            if constexpr (kEpi == kSwiglu) g[0] += p[k * stride + a.N];
+        }
     }
     const size_t o = static_cast<size_t>(row) * a.ldo + col;
-    if constexpr (kEpi == kStore) {
-        static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
-    } else if constexpr (kEpi == kAdd) {
-        static_cast<float *>(a.out)[o] = a.R[static_cast<size_t>(row) * a.ldr + col] + s;
+    if constexpr (kEpi == kAdd) {
+        const float *r = a.R + static_cast<size_t>(row) * a.ldr + col;
+        if constexpr (kVec == 4) {
+            const float4 rv = *reinterpret_cast<const float4 *>(r);
+            *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + o) =
+                make_float4(rv.x + s[0], rv.y + s[1], rv.z + s[2], rv.w + s[3]);
+        } else {
+            static_cast<float *>(a.out)[o] = r[0] + s[0];
+        }
     } else {
-        static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s * silu_f(g)));
+        float v[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) v[e] = kEpi == kSwiglu ? s[e] * silu_f(g[e]) : s[e];
+        uint16_t *dst = static_cast<uint16_t *>(a.out) + o;
+        if constexpr (kVec == 4)
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+        else
+            dst[0] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0]));
     }
+}
+
+// Whether the reduce may move 4 outputs per thread: N and the row pitches multiples of 4,
+// the output 8-byte (bf16) or 16-byte (fp32) aligned, the residual 16-byte aligned.
+inline bool vec_ok(const GemmArgs &a, int epi)
+{
+    const uintptr_t o = reinterpret_cast<uintptr_t>(a.out);
+    if (a.N % 4 || a.ldo % 4) return false;
+    if (epi == kAdd) return (o & 15u) == 0 && a.ldr % 4 == 0 && (reinterpret_cast<uintptr_t>(a.R) & 15u) == 0;
+    return (o & 7u) == 0;
 }
 
 // ---------------------------------------------------------------- host side
@@ -340,13 +374,22 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
     }
 #undef SAMBA_GEMM_LAUNCH
     if (p.splits > 1) {
-        const size_t n = static_cast<size_t>(a.M) * a.N;
+        const bool v4 = vec_ok(a, epi);
+        const size_t n = static_cast<size_t>(a.M) * (v4 ? a.N / 4 : a.N);
         const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+#define SAMBA_GEMM_REDUCE(E)                                                                        \
+    do {                                                                                            \
+        if (v4)                                                                                     \
+            hipLaunchKernelGGL((gemm_reduce_kernel<E, 4>), dim3(blocks), dim3(256), 0, s, a);       \
+        else                                                                                        \
+            hipLaunchKernelGGL((gemm_reduce_kernel<E, 1>), dim3(blocks), dim3(256), 0, s, a);       \
+    } while (0)
         switch (epi) {
-        case kStore: hipLaunchKernelGGL(gemm_reduce_kernel<kStore>, dim3(blocks), dim3(256), 0, s, a); break;
-        case kAdd: hipLaunchKernelGGL(gemm_reduce_kernel<kAdd>, dim3(blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(gemm_reduce_kernel<kSwiglu>, dim3(blocks), dim3(256), 0, s, a); break;
+        case kStore: SAMBA_GEMM_REDUCE(kStore); break;
+        case kAdd: SAMBA_GEMM_REDUCE(kAdd); break;
+        default: SAMBA_GEMM_REDUCE(kSwiglu); break;
         }
+#undef SAMBA_GEMM_REDUCE
     }
     return true;
 }
