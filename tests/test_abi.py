@@ -116,3 +116,28 @@ def test_conv_silu_argument_errors():
     with pytest.raises(ValueError, match="on a GPU"):
         import torch
         ss.conv_silu(torch.zeros((1, 4, 8)), torch.zeros((8, 4)))
+
+
+def test_struct_layouts_match_the_binding(tmp_path):
+    """samba_params, samba_model_config and samba_layer as the C compiler lays them out (gcc
+    on the header) equal the ctypes structures the binding passes: size and every offset."""
+    import ctypes
+    import subprocess
+    import selective_state_space_samba_amd as ss
+    structs = {"samba_params": ss.Params, "samba_model_config": ss.ModelConfig, "samba_layer": ss.Layer}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines += ['return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.rsplit(" ", 1) for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                         text=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got["%s size" % cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got["%s %s" % (cname, f)]) == getattr(py, f).offset, (cname, f)
