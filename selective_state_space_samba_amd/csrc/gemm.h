@@ -8,8 +8,11 @@
 //   swiglu  W = [W1; W2] (2N rows), out bf16 = (A.W1^T) * SiLU(A.W2^T)
 //           (page "Samba: Simple Hybrid State Space Models ...", "SwiGLU Formulation")
 //
-// Tiling.  A workgroup of 4 waves (2 x 2) computes a TM x TN tile, TM = 32 FM, TN = 32 FN;
-// each wave a 16FM x 16FN block of 16 x 16 MFMA tiles.  K advances 64 at a time through
+// Tiling.  A workgroup of WGM x WGN waves computes a TM x TN tile, TM = 16 FM WGM,
+// TN = 16 FN WGN; each wave a 16FM x 16FN block of 16 x 16 MFMA tiles.  256 x 256 tiles run
+// on 8 waves (4 x 2, 64 x 128 per wave: two waves per SIMD, one computing while the other
+// waits; measured 0.35-0.43 of peak against 0.30-0.36 for 4 waves of 128 x 128), 128 x 128
+// tiles on 4 waves (2 x 2).  K advances 64 at a time through
 // double-buffered LDS tiles (row pitch 72 elements = 144 bytes, so the 16 rows a fragment
 // read touches start on 16 different 4-bank groups); the next K tile's global loads are
 // in flight while the current one is multiplied.  MFMA operand layouts (16x16x32 bf16):
@@ -79,17 +82,21 @@ __device__ inline void tile_of(const GemmArgs &a, int &tm, int &tn, int &split)
     tn = (t % gsz) / gm;
 }
 
-template <int FM, int FN, int kEpi>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+template <int WGM, int WGN, int FM, int FN, int kEpi>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a)
 {
-    constexpr int TM = 32 * FM, TN = 32 * FN;
+    // WGM x WGN waves, each a 16 FM x 16 FN block of 16 x 16 MFMA tiles
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int TM = 16 * FM * WGM, TN = 16 * FN * WGN;
+    constexpr int RP = NT / 8;                 // tile rows per loader pass (8 threads per row)
+    constexpr int LA = TM / RP, LW = TN / RP;  // 16-byte vectors per thread per K tile
     __shared__ __attribute__((aligned(16))) uint16_t As[2][TM * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TN * kPitch];
 
     int tm, tn, split;
     tile_of(a, tm, tn, split);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WGN, wn = w % WGN;
     const int m0 = tm * TM;
     // Output columns of this tile: TN of them, or TN / 2 for the fused SwiGLU (the W tile
     // then holds TN / 2 rows of W1 and the same TN / 2 rows of W2, in alternating
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int nk = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
 
     // Global -> register loaders: thread t moves 16-byte chunk c = t % 8 of rows
-    // t / 8 + 32 j of the A tile (j < FM) and of the W tile (j < FN); the row offsets below
+    // t / 8 + RP j of the A tile (j < LA) and of the W tile (j < LW); the row offsets below
     // exclude the chunk, which enters through the K index of load_tile.
     const int c = tid & 7, r0 = tid >> 3;
     const int rows_a = min(TM, a.M - m0);
@@ -119,13 +126,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, rows > 0 ? static_cast<uint32_t>(rows * a.K * 2) : 0u);
         rw2 = rw;
     }
-    uint32_t aoff[FM], woff[FN];
-    bool wsecond[FN];
+    uint32_t aoff[LA], woff[LW];
+    bool wsecond[LW];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) aoff[j] = static_cast<uint32_t>((r0 + 32 * j) * a.lda * 2);
+    for (int j = 0; j < LA; ++j) aoff[j] = static_cast<uint32_t>((r0 + RP * j) * a.lda * 2);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int r = r0 + 32 * j;
+    for (int j = 0; j < LW; ++j) {
+        const int r = r0 + RP * j;
         int wrow = r;
         wsecond[j] = false;
         if constexpr (kEpi == kSwiglu) {
@@ -136,23 +143,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         woff[j] = static_cast<uint32_t>(wrow * a.K * 2);
     }
 
-    uint4 ra_v[FM], rw_v[FN];
+    uint4 ra_v[LA], rw_v[LW];
     auto load_tile = [&](int kt) {
         const int k = kbeg + kt * kTK + c * 8;
         const bool in = k < kend;
         const uint32_t kb = static_cast<uint32_t>(k) * 2u;
 #pragma unroll
-        for (int j = 0; j < FM; ++j) ra_v[j] = buf_ld128(ra, in ? aoff[j] + kb : kOob);
+        for (int j = 0; j < LA; ++j) ra_v[j] = buf_ld128(ra, in ? aoff[j] + kb : kOob);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) rw_v[j] = buf_ld128(wsecond[j] ? rw2 : rw, in ? woff[j] + kb : kOob);
+        for (int j = 0; j < LW; ++j) rw_v[j] = buf_ld128(wsecond[j] ? rw2 : rw, in ? woff[j] + kb : kOob);
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-            *reinterpret_cast<uint4 *>(&As[buf][(r0 + 32 * j) * kPitch + c * 8]) = ra_v[j];
+        for (int j = 0; j < LA; ++j)
+            *reinterpret_cast<uint4 *>(&As[buf][(r0 + RP * j) * kPitch + c * 8]) = ra_v[j];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            *reinterpret_cast<uint4 *>(&Bs[buf][(r0 + 32 * j) * kPitch + c * 8]) = rw_v[j];
+        for (int j = 0; j < LW; ++j)
+            *reinterpret_cast<uint4 *>(&Bs[buf][(r0 + RP * j) * kPitch + c * 8]) = rw_v[j];
     };
 
     f32x4 acc[FM][FN];
@@ -298,6 +305,7 @@ inline bool vec_ok(const GemmArgs &a, int epi)
 // ---------------------------------------------------------------- host side
 struct Plan {
     int fm, fn;       // tile config
+    bool w8;          // 256 x 256 tiles on 8 waves (4 along M x 2 along N)
     int splits, ksplit;
     int tiles_m, tiles_n;
     size_t part_bytes;
@@ -321,6 +329,7 @@ inline Plan plan(int M, int N, int K, int epi)
     if (f256 || (!f128 && tiles(256, 256) >= 256)) {
         p.fm = 8;
         p.fn = 8;
+        p.w8 = true;
     } else {
         p.fm = 4;
         p.fn = 4;
@@ -356,14 +365,17 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
     const int grid = p.tiles_m * p.tiles_n * p.splits;
     if (grid == 0) return true;
     const int kern_epi = p.splits > 1 ? kPartial : epi;
-#define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
-    if (p.fm == 8) {
+#define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
+#define SAMBA_GEMM_LAUNCH8(E) hipLaunchKernelGGL((gemm_kernel<4, 2, 4, 8, E>), dim3(grid), dim3(512), 0, s, a)
+    if (p.fm == 8 && p.w8) {
         switch (kern_epi) {
-        case kStore: SAMBA_GEMM_LAUNCH(8, 8, kStore); break;
-        case kAdd: SAMBA_GEMM_LAUNCH(8, 8, kAdd); break;
-        case kSwiglu: SAMBA_GEMM_LAUNCH(8, 8, kSwiglu); break;
-        default: return false;  // no split-K kernel for 256 x 256 tiles: plan() never asks for one
+        case kStore: SAMBA_GEMM_LAUNCH8(kStore); break;
+        case kAdd: SAMBA_GEMM_LAUNCH8(kAdd); break;
+        case kSwiglu: SAMBA_GEMM_LAUNCH8(kSwiglu); break;
+        default: return false;
         }
+    } else if (p.fm == 8) {
+        return false;
     } else {
         switch (kern_epi) {
         case kStore: SAMBA_GEMM_LAUNCH(4, 4, kStore); break;
@@ -373,6 +385,7 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
         }
     }
 #undef SAMBA_GEMM_LAUNCH
+#undef SAMBA_GEMM_LAUNCH8
     if (p.splits > 1) {
         const bool v4 = vec_ok(a, epi);
         const size_t n = static_cast<size_t>(a.M) * (v4 ? a.N / 4 : a.N);
