@@ -312,7 +312,7 @@ struct Plan {
 };
 
 // Tile shape and split count for a problem.  Large problems take 256 x 256 tiles (one
-// workgroup per CU, 144 KB of LDS); problems with fewer than 256 such tiles take
+// 8-wave workgroup per CU, 144 KB of LDS); problems with fewer than 256 such tiles take
 // 128 x 128 tiles (two per CU), and if those still leave CUs idle, the K range is split
 // (each split keeps at least 4 K tiles) until about 512 workgroups exist.
 inline Plan plan(int M, int N, int K, int epi)
