@@ -213,7 +213,10 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
 
     // staging: threads 0..127 move the V tile, transposing it to V^T in registers (a thread
     // reads 4 keys x 8 elements and writes 8 rows of 4 keys); threads 128..255 move the K
-    // tile (rotated keys) as 16-byte pieces
+    // tile (rotated keys) as 16-byte pieces.  Consecutive V-staging lanes take consecutive
+    // 4-key groups (key group = lane % 16): their 8-byte V^T writes then fall on distinct
+    // banks of the 144-byte-pitch rows (with the element group as the fast index, four lanes
+    // of a half-wave shared a bank pair: 60 % of the kernel's LDS cycles were conflicts).
     constexpr int kKPieces = kKeys * kDh / 8;          // 16-byte pieces of the K tile
     constexpr int kKPer = kKPieces / 128;              // per K-staging thread
     constexpr int kVBlocks = (kKeys / 4) * (kDh / 8);  // 4-key x 8-element blocks of V
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
 #pragma unroll
             for (int i = 0; i < kVPer; ++i) {
                 const int bi = i * 128 + st_id;
-                const int kg = bi / (kDh / 8), d = (bi % (kDh / 8)) * 8;
+                const int kg = bi % (kKeys / 4), d = (bi / (kKeys / 4)) * 8;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int kk = min(kt + 4 * kg + r, L - 1);  // keys past the end: clamped, masked later
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
 #pragma unroll
             for (int i = 0; i < kVPer; ++i) {
                 const int bi = i * 128 + st_id;
-                const int kg = bi / (kDh / 8), d = (bi % (kDh / 8)) * 8;
+                const int kg = bi % (kKeys / 4), d = (bi / (kKeys / 4)) * 8;
                 const uint32_t w0[4] = {sreg[i * 4].x, sreg[i * 4].y, sreg[i * 4].z, sreg[i * 4].w};
                 const uint32_t w1[4] = {sreg[i * 4 + 1].x, sreg[i * 4 + 1].y, sreg[i * 4 + 1].z, sreg[i * 4 + 1].w};
                 const uint32_t w2[4] = {sreg[i * 4 + 2].x, sreg[i * 4 + 2].y, sreg[i * 4 + 2].z, sreg[i * 4 + 2].w};
