@@ -149,7 +149,11 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
     using T = typename Io::T;
     constexpr int kKS = kDh / 32;         // k-steps of S^T = K Q^T
     constexpr int kDS = kDh / 16;         // d sub-tiles of O^T
-    constexpr int kKPitch = kDh + 8;      // LDS pitch of a K row (bf16): staggers the banks
+    // K rows are unpadded (kDh elements); 16-byte chunk q of key row r sits at chunk
+    // q ^ kswz(r), so that the 16 rows a fragment read touches (and the two rows a 16-lane
+    // group of the staging writes fills) fall on distinct banks
+    constexpr int kKPitch = kDh;
+    auto kswz = [](int r) { return kDh == 64 ? ((r >> 1) & 7) : (r & 15); };
     constexpr int kVPitch = kKeys + 8;    // LDS pitch of a V^T row (bf16)
     __shared__ __align__(16) uint16_t ks[2][kKeys * kKPitch];
     __shared__ __align__(16) uint16_t vs[2][kDh * kVPitch];
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
             for (int i = 0; i < kKPer; ++i) {
                 const int pi = i * 128 + st_id;
                 const int key = pi / (kDh / 8), d = (pi % (kDh / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&ks[buf][key * kKPitch + d]) = sreg[i];
+                *reinterpret_cast<uint4 *>(&ks[buf][key * kKPitch + (((d >> 3) ^ kswz(key)) << 3)]) = sreg[i];
             }
         }
     };
@@ -297,7 +301,8 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < kKS; ++kk) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&ks[buf][(16 * st + c16) * kKPitch + 32 * kk + 8 * g]);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+                    &ks[buf][(16 * st + c16) * kKPitch + (((4 * kk + g) ^ kswz(16 * st + c16)) << 3)]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[kk], acc, 0, 0, 0);
             }
