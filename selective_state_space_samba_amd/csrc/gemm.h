@@ -13,8 +13,7 @@
 // on 8 waves (4 x 2, 64 x 128 per wave: two waves per SIMD, one computing while the other
 // waits; measured 0.35-0.43 of peak against 0.30-0.36 for 4 waves of 128 x 128), 128 x 128
 // tiles on 4 waves (2 x 2).  K advances 64 at a time through
-// double-buffered LDS tiles (row pitch 72 elements = 144 bytes, so the 16 rows a fragment
-// read touches start on 16 different 4-bank groups); the next K tile's global loads are
+// double-buffered LDS tiles (swizzled 128-byte rows, see kPitch); the next K tile's global loads are
 // in flight while the current one is multiplied.  MFMA operand layouts (16x16x32 bf16):
 // lane l supplies A[i = l % 16][k = 8 (l / 16) + e] and B[k = 8 (l / 16) + e][j = l % 16],
 // e = 0..7, and receives D[i = 4 (l / 16) + e][j = l % 16], e = 0..3.  Both operands are
@@ -38,7 +37,12 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kTK = 64;          // K per LDS stage
-constexpr int kPitch = kTK + 8;  // LDS row pitch in elements
+// LDS tiles: 128-byte rows (kTK elements, unpadded), 16-byte chunk q of row r stored at chunk
+// q ^ ((r >> 1) & 7).  Measured with rocprofv3 on gfx950: 16-byte reads of 16 rows at one
+// chunk spend half their LDS cycles in bank conflicts with a padded 144-byte pitch and none
+// with this swizzle; the staging writes (8 lanes per row) are conflict-free either way.
+constexpr int kPitch = kTK;
+__device__ inline int swz(int r) { return (r >> 1) & 7; }
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every extent: loads 0
 
 enum Epi { kStore = 0, kAdd = 1, kSwiglu = 2, kPartial = 3 };
@@ -156,10 +160,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a)
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < LA; ++j)
-            *reinterpret_cast<uint4 *>(&As[buf][(r0 + RP * j) * kPitch + c * 8]) = ra_v[j];
+            *reinterpret_cast<uint4 *>(&As[buf][(r0 + RP * j) * kPitch + ((c ^ swz(r0)) << 3)]) = ra_v[j];
 #pragma unroll
         for (int j = 0; j < LW; ++j)
-            *reinterpret_cast<uint4 *>(&Bs[buf][(r0 + RP * j) * kPitch + c * 8]) = rw_v[j];
+            *reinterpret_cast<uint4 *>(&Bs[buf][(r0 + RP * j) * kPitch + ((c ^ swz(r0)) << 3)]) = rw_v[j];
     };
 
     f32x4 acc[FM][FN];
@@ -182,15 +186,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a)
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_tile(kt + 1);
-        const uint16_t *as = &As[buf][(wm * 16 * FM + frow) * kPitch + fk];
-        const uint16_t *bs = &Bs[buf][(wn * 16 * FN + frow) * kPitch + fk];
+        // rows 16 m + frow: the swizzle depends on frow only (RP and 16 are multiples of 16)
+        const uint16_t *as = &As[buf][(wm * 16 * FM + frow) * kPitch];
+        const uint16_t *bs = &Bs[buf][(wn * 16 * FN + frow) * kPitch];
 #pragma unroll
         for (int ks = 0; ks < kTK / 32; ++ks) {
             bf16x8 af[FM], bf[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(as + i * 16 * kPitch + ks * 32);
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(as + i * 16 * kPitch + (((ks * 4 + (fk >> 3)) ^ swz(frow)) << 3));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const bf16x8 *>(bs + j * 16 * kPitch + ks * 32);
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8 *>(bs + j * 16 * kPitch + (((ks * 4 + (fk >> 3)) ^ swz(frow)) << 3));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -312,7 +319,7 @@ struct Plan {
 };
 
 // Tile shape and split count for a problem.  Large problems take 256 x 256 tiles (one
-// 8-wave workgroup per CU, 144 KB of LDS); problems with fewer than 256 such tiles take
+// 8-wave workgroup per CU, 128 KB of LDS); problems with fewer than 256 such tiles take
 // 128 x 128 tiles (two per CU), and if those still leave CUs idle, the K range is split
 // (each split keeps at least 4 K tiles) until about 512 workgroups exist.
 inline Plan plan(int M, int N, int K, int epi)
