@@ -151,6 +151,10 @@ __global__ __launch_bounds__(64) void swa_dec_attn_kernel(SwaDecArgs a)
             constexpr int kBlocks = (kKeys / 4) * (kDh / 8);
 #pragma unroll
             for (int bi = 0; bi < kBlocks / 64; ++bi) {
+                // element groups are the fast index so that a lane group reads 128 contiguous
+                // bytes of a ring entry; the transposed map (key groups fast) removes the V^T
+                // write bank conflicts but halves the read segments and measured 9 % slower:
+                // this kernel is bound by reading the rings
                 const int blk = bi * 64 + l;
                 const int kg = blk / (kDh / 8), d = (blk % (kDh / 8)) * 8;
                 uint32_t w[4][4];
