@@ -39,10 +39,17 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kRowsPerWave = 4;           // channels per wave (4 rows of 16 lanes)
 constexpr int kChannels = kWaves * kRowsPerWave;  // channels per workgroup
 constexpr int kBlock = 16;                // tokens per block (one per lane of a row)
-constexpr int kPPitch = kBlock + 4;       // LDS pitch of one token's 16 partial products
-// LDS pitch of one row's 16x16 product tile: 16*20 + 16 floats puts the 4 rows of a
-// wave 16 banks apart, so a wave-wide store of one token's products does not conflict.
+// Single-role kernel's state tiles and C rows: one token's 16 values are a 64-byte row whose 16-byte chunk q sits
+// at chunk q ^ tswz(t); a channel's 16 x 16 tile is followed by 16 floats of padding.
+// Measured with rocprofv3 on gfx950 (probe kernels of these exact access patterns): the
+// token lanes' 16-byte reads of 16 rows spent half their LDS cycles in bank conflicts with
+// the earlier 80-byte padded rows and none with this layout, and the state lanes' 4-byte
+// writes (one token, 16 states x 4 channels per wave) stay conflict-free.
+constexpr int kPPitch = kBlock;
 constexpr int kRowPitch = kBlock * kPPitch + 16;
+__device__ constexpr int tswz(int t) { return (t >> 2) & 3; }
+// float offset, within a token row, of value n (chunk n / 4 swizzled by the token's tswz = k)
+__device__ inline int row_elem(int n, int k) { return (((n >> 2) ^ k) << 2) + (n & 3); }
 constexpr int kStagerThreads = 256;       // threads that move one stage (B/C or token words)
 
 // Logical workgroup index (sequence-major, then 16-channel block) of hardware workgroup h.
@@ -118,6 +125,7 @@ template <class T, int kStage>
 struct Smem {
     static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
     static constexpr int kTokPitch = tok_pitch_bytes<T>();
+    static constexpr bool kCSwizzle = true;      // C rows in the swizzled token-row layout
     float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
     float crow[2][kStage][kPPitch];              // [buffer][token][state]: C rows
     float p[kWaves][kRowsPerWave * kRowPitch];   // [wave][row][token][state]: states h_t (padded)
@@ -175,7 +183,7 @@ struct Stager {
         }
     }
 
-    template <class S>  // LDS layout with bcol[2][kMaxState][>= kStage] and crow[2][kStage][kPPitch]
+    template <class S>  // LDS layout with bcol[2][kMaxState][>= kStage], crow[2][kStage][>= 16] (swizzled if S::kCSwizzle)
     __device__ inline void store(S &sm, int buf, int rtid) const
     {
         const int pair = rtid / kParts;
@@ -208,7 +216,8 @@ struct Stager {
             // C: token rows (read by the lane that finishes the token's readout)
 #pragma unroll
             for (int k = 0; k < kPer / 4; ++k)
-                *reinterpret_cast<float4 *>(&sm.crow[buf][tt][n0 + 4 * k]) =
+                *reinterpret_cast<float4 *>(
+                    &sm.crow[buf][tt][S::kCSwizzle ? ((((n0 >> 2) + k) ^ tswz(tt)) << 2) : n0 + 4 * k]) =
                     make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
         }
     }
@@ -409,8 +418,9 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         const float *cr = &sm.crow[cb_][(max(pblk, 0) % kStage) + j][0];
 #pragma unroll
         for (int g = 0; g < kBlock / 4; ++g) {
-            py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
-            pc[g] = *reinterpret_cast<const float4 *>(cr + 4 * g);
+            const int q = (g ^ tswz(j)) << 2;  // token j's chunk g
+            py[g] = *reinterpret_cast<const float4 *>(pr + q);
+            pc[g] = *reinterpret_cast<const float4 *>(cr + q);
         }
     };
     // Raw token words of one block for this lane (read from the LDS tile one block ahead).
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
             // ---- publish this block's states (the tile was read above, in order)
             wave_order();
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) pw[t * kPPitch + j] = p[t];
+            for (int t = 0; t < kBlock; ++t) pw[t * kPPitch + row_elem(j, tswz(t))] = p[t];
             wave_order();
 
             pu = fe.u;

@@ -44,14 +44,21 @@ constexpr int kExSlots = 4;                                    // Delta hand-ove
 constexpr int kMaxSplitGrid = 256;                             // workgroups: one per CU
 static_assert(kRoleWaves * rows::kRowsPerWave == rows::kChannels && kRoleThreads == rows::kStagerThreads,
               "roles cover the 16 channels of a workgroup");
+// State tiles and C rows here keep 80-byte token rows (16 states + 4 floats of padding) and
+// 336-float channel tiles: the token lanes' 16-byte reads conflict (half their LDS cycles),
+// but the swizzled layout of the single-role kernel costs the scan waves address work on
+// their critical path and measured 4 % slower here.
+constexpr int kSPPitch = rows::kBlock + 4;
+constexpr int kSRowPitch = rows::kBlock * kSPPitch + 16;
 
 template <class T, int kStage, int kHsSlots>
 struct SplitSmem {
     static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
     static constexpr int kTokPitch = rows::tok_pitch_bytes<T>();
     float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
-    float crow[2][kStage][rows::kPPitch];        // [buffer][token][state]: C rows
-    float hs[kHsSlots][rows::kChannels * rows::kRowPitch];  // [block slot][channel][token][state]: h_t
+    static constexpr bool kCSwizzle = false;     // C rows unswizzled (see kSPPitch)
+    float crow[2][kStage][kSPPitch];             // [buffer][token][state]: C rows
+    float hs[kHsSlots][rows::kChannels * kSRowPitch];  // [block slot][channel][token][state]: h_t
     float lg[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * log2(e)
     float du[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * u
     alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         const float An = state_ok ? a.A[static_cast<size_t>(cc) * N + j] : 0.0f;
         const size_t hidx = (static_cast<size_t>(s) * D + cc) * N + j;
         float h = (a.h0 != nullptr && state_ok) ? a.h0[hidx] : 0.0f;
-        float *hw = &sm.hs[0][ch * kRowPitch + j];  // this lane's state column of the tile
+        float *hw = &sm.hs[0][ch * kSRowPitch + j];  // this lane's state column of the tile
 
         struct Cols {
             float4 b[kBlock / 4];
@@ -152,9 +159,9 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
             for (int bk = 0; bk < kSB; ++bk) {
                 // ---- publish block k-1 (its slot; zeros before block 0)
                 {
-                    float *hp = hw + ((bk + kHsSlots - 1) % kHsSlots) * (kChannels * kRowPitch);
+                    float *hp = hw + ((bk + kHsSlots - 1) % kHsSlots) * (kChannels * kSRowPitch);
 #pragma unroll
-                    for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
+                    for (int t = 0; t < kBlock; ++t) hp[t * kSPPitch] = pp[t];
                 }
                 // ---- next block's inputs (published by the token role kDist steps ago)
                 const int nslot = (bk + 1) % kExSlots;
@@ -207,9 +214,9 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         }
         // Publish the last block.
         if (nstages > 0) {
-            float *hp = hw + ((nstages * kSB - 1) % kHsSlots) * (kChannels * kRowPitch);
+            float *hp = hw + ((nstages * kSB - 1) % kHsSlots) * (kChannels * kSRowPitch);
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) hp[t * kPPitch] = pp[t];
+            for (int t = 0; t < kBlock; ++t) hp[t * kSPPitch] = pp[t];
         }
         __syncthreads();
         if (a.h_final != nullptr && chan_ok && state_ok) a.h_final[hidx] = h;
@@ -319,9 +326,9 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     };
     // A finished block's states for this lane's token (tile slot hslot) and the token's C
     // row (block cbk of stage buffer cbuf).
-    const float *hr = &sm.hs[0][ch * kRowPitch + j * kPPitch];
+    const float *hr = &sm.hs[0][ch * kSRowPitch + j * kSPPitch];
     auto read_states = [&](int hslot, int cbuf, int cbk, float4 *py, float4 *pc) {
-        const float *pr = hr + hslot * (kChannels * kRowPitch);
+        const float *pr = hr + hslot * (kChannels * kSRowPitch);
         const float *cr = &sm.crow[cbuf][cbk * kBlock + j][0];
 #pragma unroll
         for (int g = 0; g < kBlock / 4; ++g) {
