@@ -320,8 +320,11 @@ struct Plan {
 
 // Tile shape and split count for a problem.  Large problems take 256 x 256 tiles (one
 // 8-wave workgroup per CU, 128 KB of LDS); problems with fewer than 256 such tiles take
-// 128 x 128 tiles (two per CU), and if those still leave CUs idle, the K range is split
-// (each split keeps at least 4 K tiles) until about 512 workgroups exist.
+// 128 x 128 tiles (two per CU), and if there are fewer than 256 of those, the K range is
+// split (each split keeps at least 4 K tiles) until about 256 workgroups exist.  Measured on
+// the decode step's projections (256 rows): aiming at 512 workgroups instead doubles the
+// fp32 partial bytes (each split writes as many as the weights it reads) and made the step
+// 3 % slower; 1024, 6-12 % slower.
 inline Plan plan(int M, int N, int K, int epi)
 {
     Plan p{};
@@ -348,7 +351,7 @@ inline Plan plan(int M, int N, int K, int epi)
     const long long t = static_cast<long long>(p.tiles_m) * p.tiles_n;
     const int nk = (K + kTK - 1) / kTK;
     int s = 1;
-    if (p.fm == 4 && t < 512 && nk >= 8) s = static_cast<int>(std::min<long long>((512 + t - 1) / t, nk / 4));
+    if (p.fm == 4 && t < 256 && nk >= 8) s = static_cast<int>(std::min<long long>((256 + t - 1) / t, nk / 4));
     s = std::max(1, s);
     const int kt_per = (nk + s - 1) / s;
     p.ksplit = std::max(1, kt_per) * kTK;

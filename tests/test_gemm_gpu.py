@@ -36,7 +36,9 @@ def check(got, ref, tol):
 
 SHAPES = [(1, 1, 8), (5, 3, 16), (37, 50, 72), (128, 128, 64), (300, 260, 200), (256, 160, 4096),
           (256, 16, 4096), (256, 4096, 128), (256, 2048, 8200), (700, 900, 1000), (1100, 2304, 512),
-          (2048, 2048, 256)]
+          (2048, 2048, 256),
+          # 512 tiles of 128 x 128: one 64-wide K chunk per stage (two workgroups per CU)
+          (4096, 2048, 200)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
