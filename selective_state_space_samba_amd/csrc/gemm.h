@@ -9,12 +9,12 @@
 //           (page "Samba: Simple Hybrid State Space Models ...", "SwiGLU Formulation")
 //
 // Tiling.  A workgroup of WGM x WGN waves computes a TM x TN tile, TM = 16 FM WGM,
-// TN = 16 FN WGN; each wave a 16FM x 16FN block of 16 x 16 MFMA tiles.  256 x 256 tiles run
-// on 8 waves (4 x 2, 64 x 128 per wave: two waves per SIMD, one computing while the other
-// waits; measured 0.35-0.43 of peak against 0.30-0.36 for 4 waves of 128 x 128), 128 x 128
-// tiles on 4 waves (2 x 2).  K advances 64 at a time through
-// double-buffered LDS tiles (swizzled 128-byte rows, see kPitch); the next K tile's global loads are
-// in flight while the current one is multiplied.  MFMA operand layouts (16x16x32 bf16):
+// TN = 16 FN WGN; each wave a 16FM x 16FN block of 16 x 16 MFMA tiles.  K advances 64 at a
+// time through double-buffered LDS tiles (swizzled 128-byte rows, see kPitch); the next K
+// tile's global loads are in flight while the current one is multiplied.  256 x 256 tiles
+// run on 8 waves (4 x 2, 64 x 128 per wave, two waves per SIMD) with the operands loaded
+// straight into LDS (gemm_ring_kernel); 128 x 128 tiles on 4 waves (2 x 2, two workgroups
+// per CU) with loads staged through registers (gemm_kernel).  MFMA operand layouts (16x16x32 bf16):
 // lane l supplies A[i = l % 16][k = 8 (l / 16) + e] and B[k = 8 (l / 16) + e][j = l % 16],
 // e = 0..7, and receives D[i = 4 (l / 16) + e][j = l % 16], e = 0..3.  Both operands are
 // K-contiguous rows (A rows, W rows), so both fragments are one 16-byte LDS read.
@@ -84,6 +84,54 @@ __device__ inline void tile_of(const GemmArgs &a, int &tm, int &tn, int &split)
     const int gm = min(a.group_m, a.tiles_m - first);
     tm = first + (t % gsz) % gm;
     tn = (t % gsz) / gm;
+}
+
+// Epilogue of a TM x TN tile: lane holds rows 4 (l / 16) + e, column l % 16 of every
+// 16 x 16 MFMA tile of its wave's 16 FM x 16 FN block.
+template <int FM, int FN, int kOutCols, int kEpi>
+__device__ inline void store_tile_out(const GemmArgs &a, const f32x4 (&acc)[FM][FN], int m0, int n0, int wm, int wn,
+                                      int lane, int split)
+{
+    const int erow = m0 + wm * 16 * FM + 4 * (lane >> 4);
+    const int ecol = lane & 15;
+    if constexpr (kEpi == kSwiglu) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p) {
+                const int col = n0 + (wn * FN / 2 + p) * 16 + ecol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = erow + i * 16 + e;
+                    if (row < a.M && col < a.N)
+                        static_cast<uint16_t *>(a.out)[static_cast<size_t>(row) * a.ldo + col] = __builtin_bit_cast(
+                            uint16_t, static_cast<__bf16>(acc[i][2 * p][e] * silu_f(acc[i][2 * p + 1][e])));
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = n0 + wn * 16 * FN + j * 16 + ecol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = erow + i * 16 + e;
+                    if constexpr (kEpi == kPartial) {
+                        if (row < a.M && col < a.Nw)
+                            a.part[(static_cast<size_t>(split) * a.M + row) * a.Nw + col] = acc[i][j][e];
+                    } else {
+                        if (row >= a.M || col >= a.N) continue;
+                        const size_t o = static_cast<size_t>(row) * a.ldo + col;
+                        if constexpr (kEpi == kStore) {
+                            static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][e]));
+                        } else {
+                            static_cast<float *>(a.out)[o] = a.R[static_cast<size_t>(row) * a.ldr + col] + acc[i][j][e];
+                        }
+                    }
+                }
+            }
+    }
 }
 
 template <int WGM, int WGN, int FM, int FN, int kEpi>
@@ -208,47 +256,153 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a)
         __syncthreads();
     }
 
-    // Epilogue: lane holds rows 4 (l / 16) + e, column l % 16 of every 16 x 16 tile.
-    const int erow = m0 + wm * 16 * FM + 4 * (lane >> 4);
-    const int ecol = lane & 15;
+    store_tile_out<FM, FN, kOutCols, kEpi>(a, acc, m0, n0, wm, wn, lane, split);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A workgroup barrier with no memory fence: the compiler keeps every memory access on its
+// side of it (the empty asm statements clobber memory) but adds no wait of its own, so loads
+// into LDS issued before it stay in flight.  (__syncthreads() carries a workgroup fence that
+// waits for all of them.)
+__device__ inline void barrier_no_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The same tile product with the operands loaded straight into LDS (buffer_load_dwordx4 ...
+// lds: no register staging and no LDS-store phase in the instruction stream) through a ring
+// of S stages, S - 1 of them in flight while one is multiplied.  A load-to-LDS instruction
+// writes 64 lanes x 16 bytes contiguously (lane l at byte 16 l), i.e. 8 rows of a tile; lane l
+// fetches the global chunk that the swizzle puts at its position, so the LDS layout is the
+// one the fragment reads of gemm_kernel expect.  Lanes past a resource's extent (rows past M
+// or N, K past the split) write zeros.  Used for 256 x 256 tiles on 8 waves with S = 2 (128 KB,
+// one stage in flight while one is multiplied, as in gemm_kernel): measured 9-16 % faster than
+// register staging on the 1.7B prefill projections.  For 128 x 128 tiles a 4-stage ring (one
+// workgroup per CU, three stages in flight) measured slower than two register-staged
+// workgroups per CU, on prefill and decode shapes alike.
+template <int WGM, int WGN, int FM, int FN, int kEpi, int S>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_ring_kernel(GemmArgs a)
+{
+    constexpr int NW = WGM * WGN;
+    constexpr int TM = 16 * FM * WGM, TN = 16 * FN * WGN;
+    constexpr int kRowsPerLd = 8;                                // rows of one load-to-LDS instruction
+    constexpr int kLdPerWave = (TM + TN) / (kRowsPerLd * NW);    // per wave and stage
+    static_assert((TM + TN) % (kRowsPerLd * NW) == 0 && TM % (kRowsPerLd * kLdPerWave) == 0,
+                  "every load instruction of a wave must fall in one operand");
+    static_assert(S >= 2 && S <= 4, "the stage waits below cover at most two stages in flight after the current one");
+    // SwiGLU tiles alternate 16-row blocks of W1 and W2 rows; with these the block of the
+    // wave's instruction j is W2 exactly when bit 1 of j is set (a compile-time choice)
+    static_assert(kLdPerWave % 4 == 0 && (TM / kRowsPerLd) % 4 == 0, "W1 / W2 block parity must follow j");
+    constexpr int kStageElems = (TM + TN) * kPitch;
+    __shared__ __attribute__((aligned(16))) uint16_t ring[S][kStageElems];
+
+    int tm, tn, split;
+    tile_of(a, tm, tn, split);
+    // the wave index in a scalar register: the operand, resource and LDS destination of every
+    // load instruction derive from it, and must be wave-uniform
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w / WGN, wn = w % WGN;
+    const int m0 = tm * TM;
+    constexpr int kOutCols = kEpi == kSwiglu ? TN / 2 : TN;
+    const int n0 = tn * kOutCols;
+    const int kbeg = split * a.ksplit;
+    const int kend = min(a.K, kbeg + a.ksplit);
+    const int nk = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+
+    const int rows_a = min(TM, a.M - m0);
+    const Rsrc ra = make_rsrc(a.A + static_cast<size_t>(m0) * a.lda,
+                              rows_a > 0 ? static_cast<uint32_t>(((rows_a - 1) * a.lda + a.K) * 2) : 0u);
+    Rsrc rw, rw2;
     if constexpr (kEpi == kSwiglu) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int p = 0; p < FN / 2; ++p) {
-                const int col = n0 + (wn * FN / 2 + p) * 16 + ecol;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = erow + i * 16 + e;
-                    if (row < a.M && col < a.N)
-                        static_cast<uint16_t *>(a.out)[static_cast<size_t>(row) * a.ldo + col] = __builtin_bit_cast(
-                            uint16_t, static_cast<__bf16>(acc[i][2 * p][e] * silu_f(acc[i][2 * p + 1][e])));
-                }
-            }
+        const int rows = max(0, min(kOutCols, a.N - n0));
+        const uint32_t ext = static_cast<uint32_t>(rows * a.K * 2);
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, ext);
+        rw2 = make_rsrc(a.W + static_cast<size_t>(a.N + n0) * a.K, ext);
     } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wn * 16 * FN + j * 16 + ecol;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = erow + i * 16 + e;
-                    if constexpr (kEpi == kPartial) {
-                        if (row < a.M && col < a.Nw)
-                            a.part[(static_cast<size_t>(split) * a.M + row) * a.Nw + col] = acc[i][j][e];
-                    } else {
-                        if (row >= a.M || col >= a.N) continue;
-                        const size_t o = static_cast<size_t>(row) * a.ldo + col;
-                        if constexpr (kEpi == kStore) {
-                            static_cast<uint16_t *>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][e]));
-                        } else {
-                            static_cast<float *>(a.out)[o] = a.R[static_cast<size_t>(row) * a.ldr + col] + acc[i][j][e];
-                        }
-                    }
-                }
-            }
+        const int rows = max(0, min(TN, a.Nw - n0));
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, static_cast<uint32_t>(rows * a.K * 2));
+        rw2 = rw;
     }
+
+    // The wave's load instructions: instruction j covers rows 8 g .. 8 g + 7 of the stage
+    // (A rows first, then W rows), g = w kLdPerWave + j; lane l loads row 8 g + l / 8 at the
+    // chunk that the swizzle stores at position l % 8.
+    const bool is_a = w * kLdPerWave * kRowsPerLd < TM;          // wave-uniform
+    uint32_t off[kLdPerWave];
+    int qk[kLdPerWave];                                          // the lane's K offset in a stage
+#pragma unroll
+    for (int j = 0; j < kLdPerWave; ++j) {
+        const int g = w * kLdPerWave + j;
+        const int gop = is_a ? g : g - TM / kRowsPerLd;            // instruction within its operand
+        const int r = gop * kRowsPerLd + (lane >> 3);              // row in its operand tile
+        const int q = (lane & 7) ^ swz(r);
+        qk[j] = q * 8;
+        if (is_a) {
+            off[j] = static_cast<uint32_t>(r * a.lda * 2);
+        } else {
+            int wrow = r;
+            if constexpr (kEpi == kSwiglu) wrow = ((r >> 4) >> 1) * 16 + (r & 15);
+            off[j] = static_cast<uint32_t>(wrow * a.K * 2);
+        }
+    }
+    auto issue = [&](int kt, int slot) {
+#pragma unroll
+        for (int j = 0; j < kLdPerWave; ++j) {
+            const int k = kbeg + kt * kTK + qk[j];
+            const uint32_t o = k < kend ? off[j] + static_cast<uint32_t>(k) * 2u : kOob;
+            uint16_t *dst = &ring[slot][(w * kLdPerWave + j) * kRowsPerLd * kPitch];
+            const Rsrc rs = is_a ? ra : ((kEpi == kSwiglu && ((j >> 1) & 1)) ? rw2 : rw);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst,
+                                                     16, o, 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15, fk = 8 * (lane >> 4);
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+        if (p < nk) issue(p, p);
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed for this wave once only the stages issued after it are
+        // outstanding; the barrier then covers every wave's loads of it, and every wave has
+        // finished reading the slot that the next issue overwrites (stage kt - 1's).
+        const int after = min(S - 2, nk - 1 - kt);
+        if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLdPerWave));
+        else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLdPerWave));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        barrier_no_fence();
+        if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+        const uint16_t *st = ring[kt % S];
+        const uint16_t *as = st + (wm * 16 * FM + frow) * kPitch;
+        const uint16_t *bs = st + (TM + wn * 16 * FN + frow) * kPitch;
+#pragma unroll
+        for (int ks = 0; ks < kTK / 32; ++ks) {
+            bf16x8 af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(as + i * 16 * kPitch + (((ks * 4 + (fk >> 3)) ^ swz(frow)) << 3));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8 *>(bs + j * 16 * kPitch + (((ks * 4 + (fk >> 3)) ^ swz(frow)) << 3));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    store_tile_out<FM, FN, kOutCols, kEpi>(a, acc, m0, n0, wm, wn, lane, split);
 }
 
 // Sums the split partials in split order and applies the epilogue; one thread per kVec
@@ -312,7 +466,7 @@ inline bool vec_ok(const GemmArgs &a, int epi)
 // ---------------------------------------------------------------- host side
 struct Plan {
     int fm, fn;       // tile config
-    bool w8;          // 256 x 256 tiles on 8 waves (4 along M x 2 along N)
+    bool w8;          // 256 x 256 tiles on 8 waves (4 along M x 2 along N), gemm_ring_kernel
     int splits, ksplit;
     int tiles_m, tiles_n;
     size_t part_bytes;
@@ -376,7 +530,7 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
     if (grid == 0) return true;
     const int kern_epi = p.splits > 1 ? kPartial : epi;
 #define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
-#define SAMBA_GEMM_LAUNCH8(E) hipLaunchKernelGGL((gemm_kernel<4, 2, 4, 8, E>), dim3(grid), dim3(512), 0, s, a)
+#define SAMBA_GEMM_LAUNCH8(E) hipLaunchKernelGGL((gemm_ring_kernel<4, 2, 4, 8, E, 2>), dim3(grid), dim3(512), 0, s, a)
     if (p.fm == 8 && p.w8) {
         switch (kern_epi) {
         case kStore: SAMBA_GEMM_LAUNCH8(kStore); break;

@@ -37,7 +37,7 @@ def check(got, ref, tol):
 SHAPES = [(1, 1, 8), (5, 3, 16), (37, 50, 72), (128, 128, 64), (300, 260, 200), (256, 160, 4096),
           (256, 16, 4096), (256, 4096, 128), (256, 2048, 8200), (700, 900, 1000), (1100, 2304, 512),
           (2048, 2048, 256),
-          # 512 tiles of 128 x 128: one 64-wide K chunk per stage (two workgroups per CU)
+          # 512 tiles of 128 x 128: no split, two workgroups per CU
           (4096, 2048, 200)]
 
 
@@ -66,6 +66,47 @@ def test_gemm_residual_add_in_place(M, N, K):
 def test_gemm_swiglu(M, N, K):
     print("case: gemm swiglu", M, N, K, "workspace", ss.load().samba_gemm_workspace_bytes(M, N, K, 2), flush=True)
     a, w = operands(300 + M + N + K, M, N, K, wrows=2 * N)
+    out = ss.gemm(a, w, epilogue="swiglu")
+    torch.cuda.synchronize()
+    wh = host(w)
+    check(out, model.swiglu(host(a), wh[:N], wh[N:]), TOL_BF16_OUT)
+
+
+# Problems with at least 256 tiles of 256 x 256 take the 8-wave tiles with loads straight into
+# LDS; ragged in M, N and K.
+@pytest.mark.parametrize("M,N,K,epi", [(4100, 4110, 72, "store"), (4097, 4100, 200, "add"),
+                                       (4100, 8196, 40, "swiglu")])
+def test_gemm_large_tiles(M, N, K, epi):
+    print("case: gemm large tiles", epi, M, N, K, flush=True)
+    a, w = operands(400 + M + N + K, M, N, K, wrows=2 * N if epi == "swiglu" else None)
+    ah, wh = host(a), host(w)
+    if epi == "swiglu":
+        out = ss.gemm(a, w, epilogue="swiglu")
+        ref = model.swiglu(ah, wh[:N], wh[N:])
+        tol = TOL_BF16_OUT
+    elif epi == "add":
+        r = torch.from_numpy(np.random.default_rng(8).standard_normal((M, N)).astype(np.float32)).to(DEV)
+        ref = host(r) + model.linear(ah, wh)
+        out = ss.gemm(a, w, epilogue="add", residual=r, out=r)
+        tol = TOL_F32_OUT
+    else:
+        out = ss.gemm(a, w)
+        ref = model.linear(ah, wh)
+        tol = TOL_BF16_OUT
+    torch.cuda.synchronize()
+    check(out, ref, tol)
+
+
+# The same tiles forced onto small ragged problems (single partial tiles, K tails).
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (37, 50, 72), (300, 260, 200), (257, 129, 1000)])
+def test_gemm_large_tiles_on_ragged_shapes(M, N, K, monkeypatch):
+    monkeypatch.setenv("SAMBA_GEMM_TILE", "256")
+    print("case: gemm 256 tiles forced", M, N, K, flush=True)
+    a, w = operands(500 + M + N + K, M, N, K)
+    out = ss.gemm(a, w)
+    torch.cuda.synchronize()
+    check(out, model.linear(host(a), host(w)), TOL_BF16_OUT)
+    a, w = operands(600 + M + N + K, M, N, K, wrows=2 * N)
     out = ss.gemm(a, w, epilogue="swiglu")
     torch.cuda.synchronize()
     wh = host(w)
