@@ -24,7 +24,13 @@ namespace samba {
 
 namespace swa {
 
-constexpr int kRows = 64;   // query rows per workgroup
+constexpr int kRows = 64;   // query rows per workgroup and row block of its waves (16 per wave)
+// Row blocks per wave: a wave takes kRB blocks of 16 query rows, so every K and V^T fragment
+// it reads from LDS feeds kRB sets of MFMAs and a staged key tile serves 64 kRB rows.
+// head_dim 64: two; head_dim 128: one (no registers left for a second).
+template <int kDh>
+constexpr int row_blocks() { return kDh == 64 ? 2 : 1; }
+inline int rows_per_workgroup(int dh) { return kRows * (dh == 64 ? row_blocks<64>() : row_blocks<128>()); }
 constexpr int kKeys = 64;   // keys per tile
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -40,7 +46,7 @@ struct SwaArgs {
     const int32_t *cu;  // packed offsets or nullptr
     int total;
     int Hq, Hkv, dh, window;
-    int nrb;            // row blocks per sequence slot = ceil(seqlen / 64)
+    int nrb;            // row blocks per sequence slot = ceil(seqlen / rows_per_workgroup(dh))
     float scale_log2;   // log2(e) / sqrt(dh)
     const void *q, *k, *v;
     void *out;
@@ -179,21 +185,27 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
     int t0, t1;
     seq_bounds(a, s, t0, t1);
     const int L = t1 - t0;
-    const int R0 = rb * kRows;
+    constexpr int kRB = row_blocks<kDh>();
+    const int R0 = rb * kRows * kRB;
     if (R0 >= L) return;  // uniform over the workgroup
     const int hk = h / (a.Hq / a.Hkv);
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
     const int g = l >> 4, c16 = l & 15;
-    const int row = R0 + wave * 16 + c16;  // this lane's query row (position in the sequence)
+    // this lane's query rows (positions in the sequence): row c16 of the wave's blocks
+    const int rw0 = R0 + wave * 16 * kRB;
+    int row[kRB];
+#pragma unroll
+    for (int b = 0; b < kRB; ++b) row[b] = rw0 + 16 * b + c16;
 
     // queries of the wave's 16 rows as the B operand of S^T = K Q^T: lane (g, c16) holds
     // row c16, elements 32 ks + 8 g .. +7, rotated
     // (high and low bfloat16 parts: the scores are formed as K Qhi + K Qlo, so rounding the
     // rotated queries to bfloat16 does not move them; the keys are rounded once, as
     // FlashAttention-2's bfloat16 operands are)
-    bf16x8 qf[kKS], ql[kKS];
-    {
-        const int rowc = min(row, L - 1);
+    bf16x8 qf[kRB][kKS], ql[kRB][kKS];
+#pragma unroll
+    for (int b = 0; b < kRB; ++b) {
+        const int rowc = min(row[b], L - 1);
 #pragma unroll
         for (int kk = 0; kk < kKS; ++kk) {
             const int d = 32 * kk + 8 * g;
@@ -203,16 +215,16 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f[e] *= a.scale_log2;  // scores come out in log2 units
-                qf[kk][e] = static_cast<__bf16>(f[e]);
-                ql[kk][e] = static_cast<__bf16>(f[e] - static_cast<float>(qf[kk][e]));
+                qf[b][kk][e] = static_cast<__bf16>(f[e]);
+                ql[b][kk][e] = static_cast<__bf16>(f[e] - static_cast<float>(qf[b][kk][e]));
             }
         }
     }
 
-    // key tiles covering [R0 - window, R0 + 63] within the sequence
+    // key tiles covering [R0 - window, R0 + 64 kRB - 1] within the sequence
     const int klo = max(0, R0 - a.window);
     const int kt0 = klo / kKeys * kKeys;
-    const int khi = min(L, R0 + kRows);  // exclusive
+    const int khi = min(L, R0 + kRows * kRB);  // exclusive
     const int ntiles = (khi - kt0 + kKeys - 1) / kKeys;
 
     // staging: threads 0..127 move the V tile, transposing it to V^T in registers (a thread
@@ -282,10 +294,15 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
         }
     };
 
-    f32x4 o[kDS];
+    f32x4 o[kRB][kDS];
+    float m_run[kRB], l_run[kRB];  // exponent offset (log2 units) and this lane's share of the sum
 #pragma unroll
-    for (int i = 0; i < kDS; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -1e30f, l_run = 0.0f;  // exponent offset (log2 units) and this lane's share of the sum
+    for (int b = 0; b < kRB; ++b) {
+#pragma unroll
+        for (int i = 0; i < kDS; ++i) o[b][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        m_run[b] = -1e30f;
+        l_run[b] = 0.0f;
+    }
 
     fetch(kt0);
     stage(0);
@@ -294,61 +311,73 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
         const int buf = it & 1;
         const int kt = kt0 + it * kKeys;
         if (it + 1 < ntiles) fetch(kt + kKeys);
-        // S^T for the 4 sub-tiles of 16 keys: lane holds keys kt + 16 st + 4 g + e of row c16
-        f32x4 sc[kKeys / 16];
+        // S^T for the 4 sub-tiles of 16 keys: lane holds keys kt + 16 st + 4 g + e of row c16 of
+        // each of its blocks; one K fragment read serves every block
+        f32x4 sc[kRB][kKeys / 16];
 #pragma unroll
         for (int st = 0; st < kKeys / 16; ++st) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 acc[kRB];
+#pragma unroll
+            for (int b = 0; b < kRB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < kKS; ++kk) {
                 const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
                     &ks[buf][(16 * st + c16) * kKPitch + (((4 * kk + g) ^ kswz(16 * st + c16)) << 3)]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[kk], acc, 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < kRB; ++b) {
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[b][kk], acc[b], 0, 0, 0);
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[b][kk], acc[b], 0, 0, 0);
+                }
             }
-            sc[st] = acc;
+#pragma unroll
+            for (int b = 0; b < kRB; ++b) sc[b][st] = acc[b];
         }
         // mask: only tiles that cross a window edge, the diagonal or the sequence end for
         // some row of the wave (a wave-uniform test), then element selects
-        const int rw0 = R0 + wave * 16;
-        if (kt < rw0 + 15 - a.window || kt + kKeys - 1 > rw0 || kt + kKeys > L) {
+        if (kt < rw0 + 16 * kRB - 1 - a.window || kt + kKeys - 1 > rw0 || kt + kKeys > L) {
+#pragma unroll
+            for (int b = 0; b < kRB; ++b)
+#pragma unroll
+                for (int st = 0; st < kKeys / 16; ++st) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = kt + 16 * st + 4 * g + e;
+                        sc[b][st][e] = (key > row[b] || key < row[b] - a.window || key >= L) ? -__builtin_inff() : sc[b][st][e];
+                    }
+                }
+        }
+        // probabilities, as the B operand of O^T = V^T P^T (k-step kk = sub-tiles 2kk, 2kk+1)
+        bf16x8 pb[kRB][kKeys / 32];
+#pragma unroll
+        for (int b = 0; b < kRB; ++b) {
+            float mt = -1e30f;
+#pragma unroll
+            for (int st = 0; st < kKeys / 16; ++st)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mt = __builtin_fmaxf(mt, sc[b][st][e]);
+            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
+            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+            // The exponent offset m_run only moves when some row of the block would otherwise
+            // see probabilities above 2^8 (the output and sum are then rescaled); between moves
+            // the probabilities stay in (0, 256], which bfloat16 and the fp32 sums carry
+            // exactly as well.
+            if (__any(mt > m_run[b] + 8.0f)) {
+                const float m_new = __builtin_fmaxf(m_run[b], mt);
+                const float alpha = hw_exp2(m_run[b] - m_new);
+                m_run[b] = m_new;
+                l_run[b] *= alpha;
+#pragma unroll
+                for (int i = 0; i < kDS; ++i) o[b][i] *= alpha;
+            }
+            const float m_new = m_run[b];
 #pragma unroll
             for (int st = 0; st < kKeys / 16; ++st) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int key = kt + 16 * st + 4 * g + e;
-                    sc[st][e] = (key > row || key < row - a.window || key >= L) ? -__builtin_inff() : sc[st][e];
+                    const float p = hw_exp2(sc[b][st][e] - m_new);
+                    l_run[b] += p;
+                    pb[b][st / 2][(st & 1) * 4 + e] = static_cast<__bf16>(p);
                 }
-            }
-        }
-        float mt = -1e30f;
-#pragma unroll
-        for (int st = 0; st < kKeys / 16; ++st)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mt = __builtin_fmaxf(mt, sc[st][e]);
-        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
-        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-        // The exponent offset m_run only moves when some row of the wave would otherwise see
-        // probabilities above 2^8 (the output and sum are then rescaled); between moves the
-        // probabilities stay in (0, 256], which bfloat16 and the fp32 sums carry exactly as well.
-        if (__any(mt > m_run + 8.0f)) {
-            const float m_new = __builtin_fmaxf(m_run, mt);
-            const float alpha = hw_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < kDS; ++i) o[i] *= alpha;
-        }
-        const float m_new = m_run;
-        // probabilities, as the B operand of O^T = V^T P^T (k-step kk = sub-tiles 2kk, 2kk+1)
-        bf16x8 pb[kKeys / 32];
-#pragma unroll
-        for (int st = 0; st < kKeys / 16; ++st) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p = hw_exp2(sc[st][e] - m_new);
-                l_run += p;
-                pb[st / 2][(st & 1) * 4 + e] = static_cast<__bf16>(p);
             }
         }
 #pragma unroll
@@ -359,8 +388,10 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
                 // keys 32 kk + 4 g .. +3 and 32 kk + 16 + 4 g .. +3, in the order of pb
                 const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 32 * kk + 4 * g);
                 const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 32 * kk + 16 + 4 * g);
-                const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                o[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], o[ds], 0, 0, 0);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+                for (int b = 0; b < kRB; ++b)
+                    o[b][ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[b][kk], o[b][ds], 0, 0, 0);
             }
         }
         if (it + 1 < ntiles) {
@@ -368,21 +399,25 @@ __global__ __launch_bounds__(swa::kThreads) void swa_attention_kernel(SwaArgs a)
         }
         __syncthreads();
     }
-    // normalise and store: lane holds O[row c16][16 ds + 4 g + e]
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (row < L) {
-        const float inv = 1.0f / l_run;
-        T *op = static_cast<T *>(a.out) + (static_cast<size_t>(t0 + row) * a.Hq + h) * kDh;
+    // normalise and store: lane holds O[row c16][16 ds + 4 g + e] of each block
 #pragma unroll
-        for (int ds = 0; ds < kDS; ++ds) {
-            const int d = 16 * ds + 4 * g;
-            if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<uint2 *>(op + d) =
-                    make_uint2(pack_bf16(o[ds][0] * inv, o[ds][1] * inv), pack_bf16(o[ds][2] * inv, o[ds][3] * inv));
-            } else {
-                *reinterpret_cast<float4 *>(op + d) =
-                    make_float4(o[ds][0] * inv, o[ds][1] * inv, o[ds][2] * inv, o[ds][3] * inv);
+    for (int b = 0; b < kRB; ++b) {
+        float lsum = l_run[b];
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        if (row[b] < L) {
+            const float inv = 1.0f / lsum;
+            T *op = static_cast<T *>(a.out) + (static_cast<size_t>(t0 + row[b]) * a.Hq + h) * kDh;
+#pragma unroll
+            for (int ds = 0; ds < kDS; ++ds) {
+                const int d = 16 * ds + 4 * g;
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<uint2 *>(op + d) = make_uint2(pack_bf16(o[b][ds][0] * inv, o[b][ds][1] * inv),
+                                                                    pack_bf16(o[b][ds][2] * inv, o[b][ds][3] * inv));
+                } else {
+                    *reinterpret_cast<float4 *>(op + d) = make_float4(o[b][ds][0] * inv, o[b][ds][1] * inv,
+                                                                      o[b][ds][2] * inv, o[b][ds][3] * inv);
+                }
             }
         }
     }
@@ -412,7 +447,8 @@ inline void launch_swa(SwaArgs a, hipStream_t stream)
     const int nruns = std::max(1, (a.seqlen + 63) / 64);
     const dim3 gr(static_cast<unsigned>(a.nseq) * nruns);
     swa_rotate_keys_kernel<IoBf16><<<gr, 256, 0, stream>>>(a, nruns);
-    a.nrb = (a.seqlen + kRows - 1) / kRows;
+    const int rows = rows_per_workgroup(a.dh);
+    a.nrb = (a.seqlen + rows - 1) / rows;
     const size_t W = static_cast<size_t>(a.nrb) * a.Hq * a.nseq;
     if (W == 0) return;
     const dim3 ga(static_cast<unsigned>(W));
