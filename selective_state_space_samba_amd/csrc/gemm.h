@@ -259,22 +259,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a)
     store_tile_out<FM, FN, kOutCols, kEpi>(a, acc, m0, n0, wm, wn, lane, split);
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
-// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
-// maxima, i.e. not waited for).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// A workgroup barrier with no memory fence: the compiler keeps every memory access on its
-// side of it (the empty asm statements clobber memory) but adds no wait of its own, so loads
-// into LDS issued before it stay in flight.  (__syncthreads() carries a workgroup fence that
-// waits for all of them.)
-__device__ inline void barrier_no_fence()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // The same tile product with the operands loaded straight into LDS (buffer_load_dwordx4 ...
 // lds: no register staging and no LDS-store phase in the instruction stream) through a ring
 // of S stages, S - 1 of them in flight while one is multiplied.  A load-to-LDS instruction

@@ -72,6 +72,22 @@ struct IoBf16 {
     }
 };
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A workgroup barrier with no memory fence: the compiler keeps every memory access on its
+// side of it (the empty asm statements clobber memory) but adds no wait of its own, so loads
+// into LDS issued before it stay in flight.  (__syncthreads() carries a workgroup fence that
+// waits for all of them.)
+__device__ inline void barrier_no_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Raw buffer access: a wave-uniform 128-bit resource (base, byte range) in SGPRs plus a
 // 32-bit per-lane byte offset.  The hardware returns 0 for loads and drops stores whose
 // offset falls outside the range, so a resource built from the exact extent of an
