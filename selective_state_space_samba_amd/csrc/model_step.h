@@ -35,6 +35,55 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int rows, int d, const flo
         orow[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(xr[i] * inv * w[i]));
 }
 
+// The same with 16-byte accesses: thread t holds elements 8 (256 c + t) .. + 7 of the row for
+// c < NCH in registers between the sum of squares and the scaling, so the row is read once
+// (d a multiple of 8, at most 2048 NCH; x, w and out 16-byte aligned).  The per-thread sum
+// runs over its elements in order, then the same wave and LDS steps: deterministic.
+template <int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(int rows, int d, const float *__restrict__ x,
+                                                          const float *__restrict__ w, float eps,
+                                                          uint16_t *__restrict__ out)
+{
+    const int r = blockIdx.x;
+    if (r >= rows) return;
+    const float *xr = x + static_cast<size_t>(r) * d;
+    float v[NCH][8];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int i = (c * 256 + threadIdx.x) * 8;
+        if (i < d) {
+            const float4 a = *reinterpret_cast<const float4 *>(xr + i);
+            const float4 b = *reinterpret_cast<const float4 *>(xr + i + 4);
+            v[c][0] = a.x, v[c][1] = a.y, v[c][2] = a.z, v[c][3] = a.w;
+            v[c][4] = b.x, v[c][5] = b.y, v[c][6] = b.z, v[c][7] = b.w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[c][e], v[c][e], s);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = __builtin_amdgcn_rsqf(tot / static_cast<float>(d) + eps);
+    uint16_t *orow = out + static_cast<size_t>(r) * d;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int i = (c * 256 + threadIdx.x) * 8;
+        if (i < d) {
+            const float4 a = *reinterpret_cast<const float4 *>(w + i);
+            const float4 b = *reinterpret_cast<const float4 *>(w + i + 4);
+            const float ws[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = pack_bf16(v[c][2 * e] * inv * ws[2 * e], v[c][2 * e + 1] * inv * ws[2 * e + 1]);
+            *reinterpret_cast<uint4 *>(orow + i) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+    }
+}
+
 // Positions of the sequences advance by one token after a step (negative = inactive, kept).
 __global__ __launch_bounds__(256) void advance_pos_kernel(int n, int32_t *pos)
 {
@@ -45,7 +94,18 @@ __global__ __launch_bounds__(256) void advance_pos_kernel(int n, int32_t *pos)
 inline void launch_rmsnorm(int rows, int d, const float *x, const float *w, float eps, uint16_t *out,
                            hipStream_t s)
 {
-    if (rows > 0) hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out);
+    if (rows <= 0) return;
+    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const int nch = (d + 2047) / 2048;
+    if (d % 8 == 0 && nch <= 4 && a16(x) && a16(w) && a16(out)) {
+        switch (nch) {
+        case 1: hipLaunchKernelGGL(rmsnorm_vec_kernel<1>, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out); return;
+        case 2: hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out); return;
+        case 3: hipLaunchKernelGGL(rmsnorm_vec_kernel<3>, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out); return;
+        default: hipLaunchKernelGGL(rmsnorm_vec_kernel<4>, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out); return;
+        }
+    }
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out);
 }
 
 inline void launch_advance(int n, int32_t *pos, hipStream_t s)
