@@ -62,6 +62,11 @@ struct GemmArgs {
     int splits;
     int tiles_m, tiles_n;
     int group_m;      // M tiles per group of the tile order
+    // optional, add epilogue with a split K range: the reduce also writes RMSNorm of each new
+    // out row with weight nw to nout (bf16 [M][N]) -- the next layer's normed input
+    const float *nw;
+    float neps;
+    uint16_t *nout;
 };
 
 __device__ inline float silu_f(float v) { return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
@@ -447,6 +452,70 @@ inline bool vec_ok(const GemmArgs &a, int epi)
     return (o & 7u) == 0;
 }
 
+// The reduce of a split add epilogue fused with the RMSNorm that follows it: one workgroup
+// per row; thread t sums, for elements 8 (256 c + t) .. + 7 (c < NCH), the splits in split
+// order and adds the residual -- the arithmetic of gemm_reduce_kernel<kAdd, 4> -- writes the
+// new row, then normalises it with the arithmetic of the 16-byte RMSNorm (sum of squares per
+// thread in element order, then across the wave and the 4 waves), so that the result is
+// bitwise that of the two kernels run one after the other.  N % 8 == 0, N <= 2048 NCH,
+// ldo == ldr == N, out, R, nw and nout 16-byte aligned.
+template <int NCH>
+__global__ __launch_bounds__(256) void gemm_reduce_add_norm_kernel(GemmArgs a)
+{
+    const int r = blockIdx.x;
+    if (r >= a.M) return;
+    const int d = a.N;
+    const size_t stride = static_cast<size_t>(a.M) * a.Nw;
+    const float *prow = a.part + static_cast<size_t>(r) * a.Nw;
+    float *orow = static_cast<float *>(a.out) + static_cast<size_t>(r) * d;
+    const float *rrow = a.R + static_cast<size_t>(r) * d;
+    float v[NCH][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int i = (c * 256 + threadIdx.x) * 8;
+        if (i < d) {
+            float acc[8] = {};
+            for (int k = 0; k < a.splits; ++k) {
+                const float4 p0 = *reinterpret_cast<const float4 *>(prow + k * stride + i);
+                const float4 p1 = *reinterpret_cast<const float4 *>(prow + k * stride + i + 4);
+                acc[0] += p0.x, acc[1] += p0.y, acc[2] += p0.z, acc[3] += p0.w;
+                acc[4] += p1.x, acc[5] += p1.y, acc[6] += p1.z, acc[7] += p1.w;
+            }
+            const float4 r0 = *reinterpret_cast<const float4 *>(rrow + i);
+            const float4 r1 = *reinterpret_cast<const float4 *>(rrow + i + 4);
+            const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = rv[e] + acc[e];
+            *reinterpret_cast<float4 *>(orow + i) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
+            *reinterpret_cast<float4 *>(orow + i + 4) = make_float4(v[c][4], v[c][5], v[c][6], v[c][7]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[c][e], v[c][e], ss);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = __builtin_amdgcn_rsqf(tot / static_cast<float>(d) + a.neps);
+    uint16_t *nrow = a.nout + static_cast<size_t>(r) * d;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int i = (c * 256 + threadIdx.x) * 8;
+        if (i < d) {
+            const float4 w0 = *reinterpret_cast<const float4 *>(a.nw + i);
+            const float4 w1 = *reinterpret_cast<const float4 *>(a.nw + i + 4);
+            const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = pack_bf16(v[c][2 * e] * inv * ws[2 * e], v[c][2 * e + 1] * inv * ws[2 * e + 1]);
+            *reinterpret_cast<uint4 *>(nrow + i) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 struct Plan {
     int fm, fn;       // tile config
@@ -500,9 +569,19 @@ inline Plan plan(int M, int N, int K, int epi)
     return p;
 }
 
-// Returns false (launching nothing) for a plan no kernel is built for.
-inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
+// Whether the reduce of this launch can also write the RMSNorm of the new rows (a.nw set).
+inline bool norm_fusable(const GemmArgs &a, int epi, const Plan &p)
 {
+    const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+    return a.nw != nullptr && a.nout != nullptr && epi == kAdd && p.splits > 1 && a.N % 8 == 0 && a.N <= 8192 &&
+           a.ldo == a.N && a.ldr == a.N && a16(a.out) && a16(a.R) && a16(a.nw) && a16(a.nout);
+}
+
+// Returns false (launching nothing) for a plan no kernel is built for.  *normed (if given)
+// tells whether the RMSNorm requested through a.nw was written (see norm_fusable).
+inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool *normed = nullptr)
+{
+    if (normed != nullptr) *normed = false;
     if (p.fm == 8 && p.splits > 1) return false;
     a.splits = p.splits;
     a.ksplit = p.ksplit;
@@ -534,7 +613,15 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s)
     }
 #undef SAMBA_GEMM_LAUNCH
 #undef SAMBA_GEMM_LAUNCH8
-    if (p.splits > 1) {
+    if (p.splits > 1 && norm_fusable(a, epi, p)) {
+        switch ((a.N + 2047) / 2048) {
+        case 1: hipLaunchKernelGGL(gemm_reduce_add_norm_kernel<1>, dim3(a.M), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(gemm_reduce_add_norm_kernel<2>, dim3(a.M), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL(gemm_reduce_add_norm_kernel<3>, dim3(a.M), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(gemm_reduce_add_norm_kernel<4>, dim3(a.M), dim3(256), 0, s, a); break;
+        }
+        if (normed != nullptr) *normed = true;
+    } else if (p.splits > 1) {
         const bool v4 = vec_ok(a, epi);
         const size_t n = static_cast<size_t>(a.M) * (v4 ? a.N / 4 : a.N);
         const unsigned blocks = static_cast<unsigned>((n + 255) / 256);

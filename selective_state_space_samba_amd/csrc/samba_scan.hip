@@ -667,10 +667,16 @@ size_t samba_gemm_workspace_bytes(int M, int N, int K, samba_gemm_epilogue epilo
     return samba::gemm::plan(M, N, K, static_cast<int>(epilogue)).part_bytes;
 }
 
-samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
-                        void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
-                        void *stream)
+namespace {
+// samba_gemm, optionally with the RMSNorm of the new rows fused into the split-K reduce of an
+// add epilogue (norm_w != nullptr; *normed tells whether norm_out was written, see
+// samba::gemm::norm_fusable -- if not, the caller normalises separately).
+samba_status gemm_impl(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
+                       void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
+                       void *stream, const float *norm_w = nullptr, float norm_eps = 0.f, uint16_t *norm_out = nullptr,
+                       bool *normed = nullptr)
 {
+    if (normed != nullptr) *normed = false;
     const char *fn = "samba_gemm";
     if (M < 0 || N < 0 || K < 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: M=%d N=%d K=%d must be >= 0", fn, M, N, K);
@@ -739,9 +745,20 @@ samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const
     a.R = residual;
     a.ldr = ldr;
     a.part = static_cast<float *>(workspace);
-    if (!samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream)))
+    a.nw = norm_w;
+    a.neps = norm_eps;
+    a.nout = norm_out;
+    if (!samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream), normed))
         return fail(SAMBA_ERR_UNSUPPORTED, "%s: no kernel for this tile plan", fn);
     return launched(fn);
+}
+}  // namespace
+
+samba_status samba_gemm(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
+                        void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    return gemm_impl(M, N, K, epilogue, A, lda, W, out, ldo, residual, ldr, workspace, workspace_bytes, stream);
 }
 
 samba_status samba_rmsnorm(int rows, int d, const float *x, const float *weight, float eps, void *out, void *stream)
@@ -901,9 +918,27 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
         return samba_gemm(S, Nn, K, e, A, lda, W, dst, ld, e == SAMBA_GEMM_ADD_F32 ? hidden : nullptr, ld, part,
                           L.part_bytes, stream);
     };
+    // The add that ends a layer also writes the RMSNorm of the new hidden rows that the next
+    // layer (or the final norm) reads, when its K range is split (the reduce then does both);
+    // normed_next records whether it did.
+    bool normed_next = false;
+    auto gemm_add = [&](int K, const void *A, int lda, const void *W) {
+        const float *nw = nullptr;
+        uint16_t *nout = nullptr;
+        if (layer + 1 < n_layers) {
+            nw = layers[layer + 1].norm_w;
+            nout = hn;
+        } else if (out != nullptr) {
+            nw = final_norm_w;
+            nout = static_cast<uint16_t *>(out);
+        }
+        return gemm_impl(S, dm, K, SAMBA_GEMM_ADD_F32, A, lda, W, hidden, dm, hidden, dm, part, L.part_bytes, stream,
+                         nw, c.norm_eps, nout, &normed_next);
+    };
     for (layer = 0; layer < n_layers; ++layer) {
         const samba_layer &ly = layers[layer];
-        STEP("rmsnorm", samba_rmsnorm(S, dm, hidden, ly.norm_w, c.norm_eps, hn, stream));
+        if (!normed_next) STEP("rmsnorm", samba_rmsnorm(S, dm, hidden, ly.norm_w, c.norm_eps, hn, stream));
+        normed_next = false;
         if (ly.kind == SAMBA_LAYER_MAMBA) {
             NEED(ly.ssm.A, "ssm.A");
             NEED(ly.ssm.conv_w, "ssm.conv_w");
@@ -933,7 +968,7 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             sa.ldbc = wx;
             samba::launch_decode16(sa, SAMBA_BF16, hs);
             STEP("scan decode", launched(fn));
-            STEP("hidden += Y W_out", gemm(dm, de, SAMBA_GEMM_ADD_F32, y, de, ly.w_out, hidden, dm));
+            STEP("hidden += Y W_out", gemm_add(de, y, de, ly.w_out));
         } else if (ly.kind == SAMBA_LAYER_SWA) {
             NEED(ly.k_cache, "k_cache");
             NEED(ly.v_cache, "v_cache");
@@ -944,15 +979,16 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             aa.ldkv = wq;
             samba::launch_swa_decode(aa, hs);
             STEP("attention decode", launched(fn));
-            STEP("hidden += O W_o", gemm(dm, hq, SAMBA_GEMM_ADD_F32, o, hq, ly.w_o, hidden, dm));
+            STEP("hidden += O W_o", gemm_add(hq, o, hq, ly.w_o));
         } else {
             STEP("SwiGLU", gemm(c.d_ff, dm, SAMBA_GEMM_SWIGLU, hn, dm, ly.w12, m, c.d_ff));
-            STEP("hidden += M W_3", gemm(dm, c.d_ff, SAMBA_GEMM_ADD_F32, m, c.d_ff, ly.w3, hidden, dm));
+            STEP("hidden += M W_3", gemm_add(c.d_ff, m, c.d_ff, ly.w3));
         }
     }
 #undef NEED
     layer = n_layers;
-    if (out != nullptr) STEP("final rmsnorm", samba_rmsnorm(S, dm, hidden, final_norm_w, c.norm_eps, out, stream));
+    if (out != nullptr && !normed_next)
+        STEP("final rmsnorm", samba_rmsnorm(S, dm, hidden, final_norm_w, c.norm_eps, out, stream));
 #undef STEP
     samba::step::launch_advance(S, pos, hs);
     return launched(fn);

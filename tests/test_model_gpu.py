@@ -42,6 +42,10 @@ def bf16_act(a):
 
 SMALL = dict(d_model=64, d_inner=128, d_state=16, dt_rank=8, d_ff=96, n_heads=4, n_kv_heads=2, head_dim=64,
              window=5, rope_base=10000.0, norm_eps=1e-5)
+# wide enough that the adds ending the Mamba and MLP layers split their K range, so that their
+# reduce also writes the next layer's RMSNorm
+MEDIUM = dict(d_model=256, d_inner=512, d_state=16, dt_rank=16, d_ff=520, n_heads=4, n_kv_heads=2, head_dim=64,
+              window=5, rope_base=10000.0, norm_eps=1e-5)
 
 
 def rounded_history(k, base):
@@ -150,12 +154,13 @@ def test_decode_step_single_layer_1p7b_widths(kind):
     run_steps(dict(synth.MODEL_1P7B), 6, 2, 2, 24, prep=_prep_1p7b(2, 2100), kinds=(kind,), matched_tol=TOL_LAYER)
 
 
-def test_decode_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("cfg", [SMALL, MEDIUM], ids=["small", "split_adds"])
+def test_decode_step_graph_replay_matches_eager(cfg):
     """The step captured in a HIP graph and replayed three times gives bitwise the results of
     three eager steps from the same state (the call allocates nothing and every launch is on
     the capturing stream)."""
-    print("case: graph replay", flush=True)
-    cfg, S = SMALL, 3
+    print("case: graph replay", cfg["d_model"], flush=True)
+    S = 3
     layers, fn = synth.make_model(31, cfg, 6)
     fnw = torch.from_numpy(fn).to(DEV)
     runs = []
@@ -183,3 +188,27 @@ def test_decode_step_graph_replay_matches_eager():
         np.testing.assert_array_equal(h1, h2)
         np.testing.assert_array_equal(o1, o2)
         np.testing.assert_array_equal(p1, p2)
+
+
+def test_decode_step_fused_add_norm_is_bitwise_the_separate_kernels():
+    """With a split K range, the reduce of the add that ends a layer also writes the RMSNorm of
+    the new rows.  An output buffer that is not 16-byte aligned makes the last layer take the
+    plain reduce and the separate RMSNorm instead: hidden and out must be bitwise the same."""
+    print("case: fused add + norm", flush=True)
+    cfg, S = MEDIUM, 3
+    layers, fn = synth.make_model(37, cfg, 6)  # ends with an MLP layer, whose add splits
+    fnw = torch.from_numpy(fn).to(DEV)
+    res = []
+    for aligned in (True, False):
+        dl = ss.upload_stack(cfg, layers, S, DEV)
+        step = ss.DecodeStep(cfg, dl, fnw, S)
+        pos = torch.zeros(S, dtype=torch.int32, device=DEV)
+        hid = torch.from_numpy(synth.make_hidden(37, 0, S, cfg["d_model"])).to(DEV)
+        buf = torch.zeros(S * cfg["d_model"] + 8, dtype=torch.bfloat16, device=DEV)
+        out = (buf[:S * cfg["d_model"]] if aligned else buf[1:1 + S * cfg["d_model"]]).view(S, cfg["d_model"])
+        step(hid, pos, out)
+        torch.cuda.synchronize()
+        res.append((host(hid), host(out)))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    assert np.isfinite(res[0][1]).all() and np.abs(res[0][1]).max() > 0
