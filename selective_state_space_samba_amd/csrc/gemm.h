@@ -67,6 +67,13 @@ struct GemmArgs {
     const float *nw;
     float neps;
     uint16_t *nout;
+    // optional, store epilogue with a split K range: the reduce also writes, for the columns
+    // below cD (the x half of [x | z]), u = SiLU(conv(x)) of this one new token from the conv
+    // history c0 (bf16 [M][3][cD], oldest first), weights cw [cD][4] and bias cb (nullable)
+    const float *cw, *cb;
+    const uint16_t *c0;
+    uint16_t *cu;
+    int cD;
 };
 
 __device__ inline float silu_f(float v) { return v * hw_rcp(1.0f + hw_exp2(-v * kLog2e)); }
@@ -435,10 +442,38 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
 #pragma unroll
         for (int e = 0; e < kVec; ++e) v[e] = kEpi == kSwiglu ? s[e] * silu_f(g[e]) : s[e];
         uint16_t *dst = static_cast<uint16_t *>(a.out) + o;
-        if constexpr (kVec == 4)
-            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
-        else
+        if constexpr (kVec == 4) {
+            const uint2 pk = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+            *reinterpret_cast<uint2 *>(dst) = pk;
+            if constexpr (kEpi == kStore) {
+                if (a.cu != nullptr && col < a.cD) {
+                    // the conv of the one new token, in the order and precision of
+                    // conv_silu_kernel: x as stored (bf16), the history as stored
+                    const float xs[4] = {bf16lo(pk.x), bf16hi(pk.x), bf16lo(pk.y), bf16hi(pk.y)};
+                    const uint16_t *h = a.c0 + static_cast<size_t>(row) * 3 * a.cD + col;
+                    const uint2 h0 = *reinterpret_cast<const uint2 *>(h);
+                    const uint2 h1 = *reinterpret_cast<const uint2 *>(h + a.cD);
+                    const uint2 h2 = *reinterpret_cast<const uint2 *>(h + 2 * a.cD);
+                    const float w0[4] = {bf16lo(h0.x), bf16hi(h0.x), bf16lo(h0.y), bf16hi(h0.y)};
+                    const float w1[4] = {bf16lo(h1.x), bf16hi(h1.x), bf16lo(h1.y), bf16hi(h1.y)};
+                    const float w2[4] = {bf16lo(h2.x), bf16hi(h2.x), bf16lo(h2.y), bf16hi(h2.y)};
+                    float u[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float4 cwv = *reinterpret_cast<const float4 *>(a.cw + static_cast<size_t>(col + e) * 4);
+                        float pre = __builtin_fmaf(cwv.x, w0[e], a.cb ? a.cb[col + e] : 0.0f);
+                        pre = __builtin_fmaf(cwv.y, w1[e], pre);
+                        pre = __builtin_fmaf(cwv.z, w2[e], pre);
+                        pre = __builtin_fmaf(cwv.w, xs[e], pre);
+                        u[e] = silu_f(pre);
+                    }
+                    *reinterpret_cast<uint2 *>(a.cu + static_cast<size_t>(row) * a.cD + col) =
+                        make_uint2(pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3]));
+                }
+            }
+        } else {
             dst[0] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0]));
+        }
     }
 }
 
@@ -577,11 +612,23 @@ inline bool norm_fusable(const GemmArgs &a, int epi, const Plan &p)
            a.ldo == a.N && a.ldr == a.N && a16(a.out) && a16(a.R) && a16(a.nw) && a16(a.nout);
 }
 
-// Returns false (launching nothing) for a plan no kernel is built for.  *normed (if given)
-// tells whether the RMSNorm requested through a.nw was written (see norm_fusable).
-inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool *normed = nullptr)
+// Whether the reduce of this launch can also write the conv requested through a.cu.
+inline bool conv_fusable(const GemmArgs &a, int epi, const Plan &p)
+{
+    const auto a_n = [](const void *q, unsigned n) { return (reinterpret_cast<uintptr_t>(q) & (n - 1u)) == 0; };
+    return a.cu != nullptr && a.cw != nullptr && a.c0 != nullptr && epi == kStore && p.splits > 1 && vec_ok(a, epi) &&
+           a.cD > 0 && a.cD % 4 == 0 && a.cD <= a.N && a_n(a.cw, 16) && a_n(a.c0, 8) && a_n(a.cu, 8);
+}
+
+// Returns false (launching nothing) for a plan no kernel is built for.  *normed / *conved (if
+// given) tell whether the RMSNorm requested through a.nw / the conv requested through a.cu
+// were written (see norm_fusable, conv_fusable).
+inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool *normed = nullptr,
+                        bool *conved = nullptr)
 {
     if (normed != nullptr) *normed = false;
+    if (conved != nullptr) *conved = false;
+    if (!conv_fusable(a, epi, p)) a.cu = nullptr;
     if (p.fm == 8 && p.splits > 1) return false;
     a.splits = p.splits;
     a.ksplit = p.ksplit;
@@ -623,6 +670,7 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool 
         if (normed != nullptr) *normed = true;
     } else if (p.splits > 1) {
         const bool v4 = vec_ok(a, epi);
+        if (conved != nullptr) *conved = a.cu != nullptr;
         const size_t n = static_cast<size_t>(a.M) * (v4 ? a.N / 4 : a.N);
         const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
 #define SAMBA_GEMM_REDUCE(E)                                                                        \

@@ -668,15 +668,25 @@ size_t samba_gemm_workspace_bytes(int M, int N, int K, samba_gemm_epilogue epilo
 }
 
 namespace {
-// samba_gemm, optionally with the RMSNorm of the new rows fused into the split-K reduce of an
-// add epilogue (norm_w != nullptr; *normed tells whether norm_out was written, see
-// samba::gemm::norm_fusable -- if not, the caller normalises separately).
+// Work the split-K reduce of a decode-step projection can do on the way (see
+// samba::gemm::norm_fusable / conv_fusable); the flags tell the caller what was done.
+struct GemmFuse {
+    const float *norm_w = nullptr;  // add: RMSNorm of the new rows into norm_out
+    float norm_eps = 0.f;
+    uint16_t *norm_out = nullptr;
+    const float *conv_w = nullptr, *conv_b = nullptr;  // store: u = SiLU(conv(x)) of the x half
+    const uint16_t *conv0 = nullptr;
+    uint16_t *conv_u = nullptr;
+    int conv_D = 0;
+    bool normed = false, conved = false;
+};
+
+// samba_gemm, optionally with the work of a GemmFuse done by its split-K reduce.
 samba_status gemm_impl(int M, int N, int K, samba_gemm_epilogue epilogue, const void *A, int lda, const void *W,
                        void *out, int ldo, const float *residual, int ldr, void *workspace, size_t workspace_bytes,
-                       void *stream, const float *norm_w = nullptr, float norm_eps = 0.f, uint16_t *norm_out = nullptr,
-                       bool *normed = nullptr)
+                       void *stream, GemmFuse *fz = nullptr)
 {
-    if (normed != nullptr) *normed = false;
+    if (fz != nullptr) fz->normed = fz->conved = false;
     const char *fn = "samba_gemm";
     if (M < 0 || N < 0 || K < 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: M=%d N=%d K=%d must be >= 0", fn, M, N, K);
@@ -745,10 +755,18 @@ samba_status gemm_impl(int M, int N, int K, samba_gemm_epilogue epilogue, const 
     a.R = residual;
     a.ldr = ldr;
     a.part = static_cast<float *>(workspace);
-    a.nw = norm_w;
-    a.neps = norm_eps;
-    a.nout = norm_out;
-    if (!samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream), normed))
+    if (fz != nullptr) {
+        a.nw = fz->norm_w;
+        a.neps = fz->norm_eps;
+        a.nout = fz->norm_out;
+        a.cw = fz->conv_w;
+        a.cb = fz->conv_b;
+        a.c0 = fz->conv0;
+        a.cu = fz->conv_u;
+        a.cD = fz->conv_D;
+    }
+    if (!samba::gemm::launch_gemm(a, static_cast<int>(epilogue), pl, static_cast<hipStream_t>(stream),
+                                  fz != nullptr ? &fz->normed : nullptr, fz != nullptr ? &fz->conved : nullptr))
         return fail(SAMBA_ERR_UNSUPPORTED, "%s: no kernel for this tile plan", fn);
     return launched(fn);
 }
@@ -921,19 +939,23 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
     // The add that ends a layer also writes the RMSNorm of the new hidden rows that the next
     // layer (or the final norm) reads, when its K range is split (the reduce then does both);
     // normed_next records whether it did.
+    // SAMBA_DECODE_NOFUSE set: every reduce does only its own work (the same results, for tests)
+    const bool fuse = getenv("SAMBA_DECODE_NOFUSE") == nullptr;
     bool normed_next = false;
     auto gemm_add = [&](int K, const void *A, int lda, const void *W) {
-        const float *nw = nullptr;
-        uint16_t *nout = nullptr;
+        GemmFuse fz;
+        fz.norm_eps = c.norm_eps;
         if (layer + 1 < n_layers) {
-            nw = layers[layer + 1].norm_w;
-            nout = hn;
+            fz.norm_w = layers[layer + 1].norm_w;
+            fz.norm_out = hn;
         } else if (out != nullptr) {
-            nw = final_norm_w;
-            nout = static_cast<uint16_t *>(out);
+            fz.norm_w = final_norm_w;
+            fz.norm_out = static_cast<uint16_t *>(out);
         }
-        return gemm_impl(S, dm, K, SAMBA_GEMM_ADD_F32, A, lda, W, hidden, dm, hidden, dm, part, L.part_bytes, stream,
-                         nw, c.norm_eps, nout, &normed_next);
+        const samba_status st = gemm_impl(S, dm, K, SAMBA_GEMM_ADD_F32, A, lda, W, hidden, dm, hidden, dm, part,
+                                          L.part_bytes, stream, fuse ? &fz : nullptr);
+        normed_next = fz.normed;
+        return st;
     };
     for (layer = 0; layer < n_layers; ++layer) {
         const samba_layer &ly = layers[layer];
@@ -944,9 +966,16 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             NEED(ly.ssm.conv_w, "ssm.conv_w");
             NEED(ly.h, "h");
             NEED(ly.conv_state, "conv_state");
-            // [x | z] = X [W_in ; W_g]
-            STEP("[x | z] = X [W_in; W_g]", gemm(2 * de, dm, SAMBA_GEMM_STORE, hn, dm, ly.w_in_gate, xz, 2 * de));
-            // u = SiLU(conv(x)) for the Delta / B / C projections; the conv state is not advanced
+            // [x | z] = X [W_in ; W_g], and (by the split-K reduce, when it can) u = SiLU(conv(x))
+            // for the Delta / B / C projections; the conv state is not advanced
+            GemmFuse fz;
+            fz.conv_w = ly.ssm.conv_w;
+            fz.conv_b = ly.ssm.conv_b;
+            fz.conv0 = static_cast<const uint16_t *>(ly.conv_state);
+            fz.conv_u = u;
+            fz.conv_D = de;
+            STEP("[x | z] = X [W_in; W_g]", gemm_impl(S, 2 * de, dm, SAMBA_GEMM_STORE, hn, dm, ly.w_in_gate, xz, 2 * de,
+                                                       nullptr, 2 * de, part, L.part_bytes, stream, fuse ? &fz : nullptr));
             samba::ConvArgs ca{};
             ca.nseq = S;
             ca.seqlen = 1;
@@ -957,8 +986,10 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             ca.conv_b = ly.ssm.conv_b;
             ca.conv0 = ly.conv_state;
             ca.u = u;
-            samba::launch_conv_silu(ca, SAMBA_BF16, hs);
-            STEP("u = SiLU(conv(x))", launched(fn));
+            if (!fz.conved) {
+                samba::launch_conv_silu(ca, SAMBA_BF16, hs);
+                STEP("u = SiLU(conv(x))", launched(fn));
+            }
             // [U W_r | B | C] = U [W_r; W_b; W_c], then Delta's input (U W_r) W_q
             STEP("U [W_r; W_b; W_c]", gemm(wx, de, SAMBA_GEMM_STORE, u, de, ly.w_xproj, xp, wx));
             STEP("dt = (U W_r) W_q", gemm(de, dr, SAMBA_GEMM_STORE, xp, wx, ly.w_dt_up, dt, de));

@@ -42,9 +42,9 @@ def bf16_act(a):
 
 SMALL = dict(d_model=64, d_inner=128, d_state=16, dt_rank=8, d_ff=96, n_heads=4, n_kv_heads=2, head_dim=64,
              window=5, rope_base=10000.0, norm_eps=1e-5)
-# wide enough that the adds ending the Mamba and MLP layers split their K range, so that their
-# reduce also writes the next layer's RMSNorm
-MEDIUM = dict(d_model=256, d_inner=512, d_state=16, dt_rank=16, d_ff=520, n_heads=4, n_kv_heads=2, head_dim=64,
+# wide enough that in_proj and the adds ending each layer split their K range, so that their
+# reduces also write u = SiLU(conv(x)) and the next layer's RMSNorm
+MEDIUM = dict(d_model=512, d_inner=1024, d_state=16, dt_rank=32, d_ff=1032, n_heads=8, n_kv_heads=2, head_dim=64,
               window=5, rope_base=10000.0, norm_eps=1e-5)
 
 
@@ -190,25 +190,30 @@ def test_decode_step_graph_replay_matches_eager(cfg):
         np.testing.assert_array_equal(p1, p2)
 
 
-def test_decode_step_fused_add_norm_is_bitwise_the_separate_kernels():
-    """With a split K range, the reduce of the add that ends a layer also writes the RMSNorm of
-    the new rows.  An output buffer that is not 16-byte aligned makes the last layer take the
-    plain reduce and the separate RMSNorm instead: hidden and out must be bitwise the same."""
-    print("case: fused add + norm", flush=True)
+def test_decode_step_fused_reduces_are_bitwise_the_separate_kernels(monkeypatch):
+    """The split-K reduces of the decode step also compute u = SiLU(conv(x)) (in_proj) and the
+    next RMSNorm (the add ending each layer).  Run once fused and once with every kernel
+    separate (SAMBA_DECODE_NOFUSE): hidden, out, the Mamba state and the conv history must be
+    bitwise the same after two steps."""
+    print("case: fused reduces", flush=True)
     cfg, S = MEDIUM, 3
-    layers, fn = synth.make_model(37, cfg, 6)  # ends with an MLP layer, whose add splits
+    layers, fn = synth.make_model(37, cfg, 6)  # mamba, mlp, mamba, mlp, swa, mlp
     fnw = torch.from_numpy(fn).to(DEV)
     res = []
-    for aligned in (True, False):
+    for fused in (True, False):
+        if not fused:
+            monkeypatch.setenv("SAMBA_DECODE_NOFUSE", "1")
         dl = ss.upload_stack(cfg, layers, S, DEV)
         step = ss.DecodeStep(cfg, dl, fnw, S)
         pos = torch.zeros(S, dtype=torch.int32, device=DEV)
-        hid = torch.from_numpy(synth.make_hidden(37, 0, S, cfg["d_model"])).to(DEV)
-        buf = torch.zeros(S * cfg["d_model"] + 8, dtype=torch.bfloat16, device=DEV)
-        out = (buf[:S * cfg["d_model"]] if aligned else buf[1:1 + S * cfg["d_model"]]).view(S, cfg["d_model"])
-        step(hid, pos, out)
+        hid = torch.zeros((S, cfg["d_model"]), device=DEV)
+        out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=DEV)
+        for t in range(2):  # the second step reads the conv state and rings the first one wrote
+            hid.copy_(torch.from_numpy(synth.make_hidden(37, t, S, cfg["d_model"])))
+            step(hid, pos, out)
         torch.cuda.synchronize()
-        res.append((host(hid), host(out)))
-    np.testing.assert_array_equal(res[0][0], res[1][0])
-    np.testing.assert_array_equal(res[0][1], res[1][1])
+        res.append((host(hid), host(out), host(dl[0]["h"]), host(dl[0]["conv_state"])))
+        monkeypatch.delenv("SAMBA_DECODE_NOFUSE", raising=False)
+    for a, b in zip(*res):
+        np.testing.assert_array_equal(a, b)
     assert np.isfinite(res[0][1]).all() and np.abs(res[0][1]).max() > 0
