@@ -46,6 +46,12 @@
  *   message readable with samba_last_error().  A launch failure returns SAMBA_ERR_HIP.
  *   Faults inside a kernel surface at the caller's next synchronisation.  The library
  *   never aborts the process.
+ * - Environment, read at every call, for tests and timing (each computes the same function;
+ *   results may differ by rounding where the kernel changes):
+ *   SAMBA_SCAN_PATH=lane|single|split forces the prefill kernel family (otherwise chosen by
+ *   shape); SAMBA_GEMM_TILE=128|256 forces the GEMM tile size; SAMBA_DECODE_NOFUSE set makes
+ *   samba_decode_step run every kernel separately instead of folding the conv and the next
+ *   RMSNorm into the split-K reduces (bitwise the same results).
  */
 #ifndef SAMBA_SCAN_H
 #define SAMBA_SCAN_H
