@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true", help="time only the long-prompt prefill (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="time only the streaming decode (profiling)")
     ap.add_argument("--model-only", action="store_true", help="time only the GEMMs and the whole-model decode step")
+    ap.add_argument("--valu-probe", action="store_true", help="run only the vector-ALU issue-rate probe")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the prefill and a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -456,6 +457,45 @@ def bench_model_decode(dev, steps, warmup, S=256):
     return res
 
 
+def valu_probe():
+    """Issue rates of the vector ALU measured on this GPU (libsamba_probe.so): independent
+    v_fma_f32 / v_fmac_f32 / v_exp_f32 chains, a 1:4 exp:FMA mix in one wave and split between
+    waves, dependent-chain latencies, and the shader clock during each run.  Reported beside
+    the roofline so that its peak (unit counts x 2.4 GHz) can be checked against the chip."""
+    import ctypes
+    path = os.path.join(ROOT, "selective_state_space_samba_amd", "libsamba_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.samba_probe_rates.restype = ctypes.c_int
+    lib.samba_probe_rates.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    simds = 256 * 4
+    res = {}
+    for kind, name, iters in ((0, "v_fma_f32", 20000), (3, "v_fmac_f32", 20000), (1, "v_exp_f32", 8000),
+                              (2, "exp_plus_4fma_one_wave", 4000), (4, "exp_plus_4fma_split_waves", 4000),
+                              (5, "v_fma_f32_dependent", 20000), (6, "v_exp_f32_dependent", 8000)):
+        out = (ctypes.c_double * 4)()
+        # rate probes: 2048 x 256 threads (1024 x 512 for the split mix): 8 waves per SIMD;
+        # latency probes: one wave per SIMD
+        rc = lib.samba_probe_rates(kind, 1024 if kind in (4, 5, 6) else 2048, iters, out)
+        if rc != 0:
+            raise RuntimeError("samba_probe_rates(%d) failed: %d" % (kind, rc))
+        sec, ops, exps, ghz = out[0], out[1], out[2], out[3]
+        rate = ops / sec
+        # cycles one SIMD spends per wave64 instruction at the measured clock
+        cyc = simds * ghz * 1e9 / (rate / 64) if ghz > 0 else None
+        res[name] = {"t_lane_ops_s": round(rate / 1e12, 3), "ms": round(sec * 1e3, 3), "clock_ghz": round(ghz, 3),
+                     "cycles_per_wave_instr": None if cyc is None else round(cyc, 3)}
+    fma = res["v_fma_f32"]["t_lane_ops_s"]
+    ex = res["v_exp_f32"]["t_lane_ops_s"]
+    # the mix costs the sum of its parts when the exponential does not overlap the FMAs
+    mix_sum = 5.0 / (4.0 / fma + 1.0 / ex)
+    res["exp_over_fma_rate"] = round(ex / fma, 4)
+    res["mix_if_serial_t_lane_ops_s"] = round(mix_sum, 3)
+    res["note"] = ("cycles_per_wave_instr: SIMD cycles per wave64 instruction at the measured clock (rate probes: "
+                   "throughput with 8 waves per SIMD; *_dependent: issue-to-issue latency of one chain, 1 wave "
+                   "per SIMD)")
+    return res
+
+
 def traffic_probe(dev, steps=3):
     """A plain device-to-device copy of exactly 2^30 bytes (bf16), the reference that scales
     the FETCH_SIZE / WRITE_SIZE counters into bytes."""
@@ -556,6 +596,9 @@ def main():
     ss.load()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda:0")
 
+    if args.valu_probe:
+        print(json.dumps({"valu_probe": valu_probe()}), flush=True)
+        return
     if args.model_only:
         print(json.dumps({"gemm": bench_gemm(dev, args.steps, args.warmup),
                           "model_decode_1p7b": bench_model_decode(dev, args.steps, args.warmup)}), flush=True)

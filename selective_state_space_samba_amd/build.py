@@ -9,6 +9,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsamba_scan.so")
 MAIN = os.path.join(CSRC, "samba_scan.hip")
+# the benchmark's measurement of the vector-ALU issue rates (not part of the scan's C ABI)
+PROBE_LIB = os.path.join(PKG, "libsamba_probe.so")
+PROBE = os.path.join(CSRC, "peak_probe.hip")
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-shared", "-fPIC",
@@ -23,16 +26,21 @@ def sources():
                   glob.glob(os.path.join(PKG, "..", "include", "*.h")))
 
 
-def build_library(verbose: bool = False) -> str:
+def _hipcc(src: str, lib: str, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp, MAIN]
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False) -> str:
+    _hipcc(MAIN, LIB, verbose)
+    _hipcc(PROBE, PROBE_LIB, verbose)
     return LIB
 
 

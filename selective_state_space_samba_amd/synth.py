@@ -103,9 +103,11 @@ class Params:
     conv_b: np.ndarray   # [D]
 
 
-def make_params(seed: int, D: int, N: int, random_A: bool = False) -> Params:
+def make_params(seed: int, D: int, N: int, random_A: bool = False, conv_bias: bool = False) -> Params:
+    """Layer parameters drawn as in the workloads' recipe (conv bias 0).  conv_bias=True
+    draws the conv bias ~ N(0, 0.5) instead, so that tests exercise the bias term."""
     conv_w = _normal(seed, "conv_w", (D, CONV_K), std=0.5)
-    conv_b = np.zeros(D, dtype=np.float32)
+    conv_b = _normal(seed, "conv_b", (D,), std=0.5) if conv_bias else np.zeros(D, dtype=np.float32)
     g = _rng(seed, "dt_bias")
     delta0 = np.exp(g.uniform(np.log(1e-3), np.log(1e-1), size=D))
     dt_bias = np.log(np.expm1(delta0)).astype(np.float32)
@@ -198,7 +200,7 @@ def make_model(seed: int, cfg: dict, n_layers: int):
         p = "L%d." % i
         ly = dict(kind=kind, norm_w=_normal(seed, p + "norm", (dm,), mean=1.0, std=0.1))
         if kind == "mamba":
-            prm = make_params(seed + 7919 * (i + 1), de, N)
+            prm = make_params(seed + 7919 * (i + 1), de, N, conv_bias=True)
             ly.update(w_in_gate=np.concatenate([w(p + "w_in", de, dm), w(p + "w_gate", de, dm)]),
                       w_xproj=np.concatenate([w(p + "w_r", dr, de), w(p + "w_b", N, de), w(p + "w_c", N, de)]),
                       w_dt_up=w(p + "w_q", de, dr), w_out=w(p + "w_out", dm, de), A=prm.A, D=prm.Dskip,

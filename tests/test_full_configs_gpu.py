@@ -40,10 +40,10 @@ def check(name, g, r, io="bf16"):
     assert e <= TOL[io], name
 
 
-def run_prefill_case(cfg_index, b, L):
+def run_prefill_case(cfg_index, b, L, conv_bias=False):
     seed = synth.seed_for(cfg_index)
-    print("case: config %d batch %d L %d" % (cfg_index, b, L), flush=True)
-    p = synth.make_params(seed, D, N)
+    print("case: config %d batch %d L %d conv_bias %s" % (cfg_index, b, L, conv_bias), flush=True)
+    p = synth.make_params(seed, D, N, conv_bias=conv_bias)
     tk = synth.make_tokens(seed, (b, L), D, N, "bf16")
     y, hf, cf = ss.prefill(bf16(tk.x), bf16(tk.dt), bf16(tk.B), bf16(tk.C), bf16(tk.z), *params_dev(p))
     chans = sample_channels(seed)
@@ -62,6 +62,16 @@ def run_prefill_case(cfg_index, b, L):
 
 def test_training_length_prefill_4x4096():
     run_prefill_case(1, 4, 4096)
+
+
+def test_training_length_prefill_4x4096_conv_bias():
+    """The same shape with a nonzero conv bias (the workload recipe has bias 0)."""
+    run_prefill_case(1, 4, 4096, conv_bias=True)
+
+
+def test_long_prompt_prefill_131072_conv_bias():
+    """The long prompt with a nonzero conv bias, in the launch configuration the benchmark times."""
+    run_prefill_case(2, 1, 131072, conv_bias=True)
 
 
 def test_batch64_prefill_2048():

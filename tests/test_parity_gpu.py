@@ -28,7 +28,8 @@ def scan_path(request, monkeypatch):
 
 
 def make_case(seed, b, L, D, N, io, random_A=False, with_state=False, gate=True):
-    p = synth.make_params(seed, D, N, random_A=random_A)
+    # nonzero conv bias throughout: every prefill path must add it
+    p = synth.make_params(seed, D, N, random_A=random_A, conv_bias=True)
     tk = synth.make_tokens(seed, (b, L), D, N, io)
     h0 = conv0 = None
     if with_state:
@@ -126,7 +127,7 @@ def test_varlen_ragged(io):
     cu = synth.cu_from_lengths(lens)
     T, D, N = int(cu[-1]), 192, 16
     seed = 500
-    p = synth.make_params(seed, D, N, random_A=True)
+    p = synth.make_params(seed, D, N, random_A=True, conv_bias=True)
     tk = synth.make_tokens(seed, (T,), D, N, io)
     h0, c0 = synth.make_state(seed, len(lens), D, N, io, scale=0.5)
     print("case: varlen", lens, io, flush=True)
@@ -144,7 +145,7 @@ def test_varlen_fresh_sequences():
     lens = [17, 3, 40]
     cu = synth.cu_from_lengths(lens)
     T, D, N, io = int(cu[-1]), 64, 16, "bf16"
-    p = synth.make_params(510, D, N)
+    p = synth.make_params(510, D, N, conv_bias=True)
     tk = synth.make_tokens(510, (T,), D, N, io)
     y, hf, cf = ss.varlen(torch.from_numpy(cu).to(DEV), tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV),
                           tdev(tk.B, io, DEV), tdev(tk.C, io, DEV), tdev(tk.z, io, DEV), tf32(p.A, DEV),
@@ -161,7 +162,7 @@ def test_decode_steps(io, D, gate):
     channels, and z = None exercises the ungated output."""
     S, N, steps = 5, 16, 24
     seed = 600
-    p = synth.make_params(seed, D, N, random_A=True)
+    p = synth.make_params(seed, D, N, random_A=True, conv_bias=True)
     h0, c0 = synth.make_state(seed, S, D, N, io, scale=0.5)
     h = tf32(h0, DEV)
     cs = tdev(c0, io, DEV)
@@ -186,7 +187,7 @@ def test_decode_continues_prefill():
     io = "bf16"
     b, L, D, N = 3, 300, 128, 16
     seed = 700
-    p = synth.make_params(seed, D, N)
+    p = synth.make_params(seed, D, N, conv_bias=True)
     tk = synth.make_tokens(seed, (b, L), D, N, io)
     args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
     _, h, cs = ss.prefill(tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
