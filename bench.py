@@ -51,9 +51,10 @@ BWD_SLOTS_PER_TC = 16 * 14 + 17 + 33
 # (2 B per channel), read B and C (2 B each per state).
 BYTES_PER_TOKEN = 8 * D_INNER + 4 * D_STATE
 # Algorithmic bytes of one decode step: per (sequence, channel) the fp32 state read and
-# written (2 x 64 B), the 3-token conv history read and shifted (3 x 2 B read, 3 x 2 B
-# written), x, dt, z read and y written (4 x 2 B); per sequence B and C (2 x 32 B).
-DECODE_BYTES_PER_SC = 2 * 4 * D_STATE + 12 + 8
+# written (2 x 64 B), the conv ring's three slots read and the oldest one overwritten
+# (3 x 2 B + 2 B), x, dt, z read and y written (4 x 2 B): 144 B; per sequence B and C
+# (2 x 32 B).
+DECODE_BYTES_PER_SC = 2 * 4 * D_STATE + 4 * 2 + 4 * 2
 DECODE_BYTES_PER_SEQ = 2 * 2 * D_STATE
 
 
@@ -165,10 +166,15 @@ def bench_decode(args, dev, S=256, P=256, warm_prefill=True, steps=None):
     pool = dict(x=randn((P, S, D_INNER)), dt=randn((P, S, D_INNER), 0.5), z=randn((P, S, D_INNER)),
                 B=randn((P, S, D_STATE)), C=randn((P, S, D_STATE)))
     y = torch.empty((S, D_INNER), dtype=torch.bfloat16, device=dev)
+    # ring heads, double-buffered: step k reads heads[k % 2] and writes heads[(k + 1) % 2]
+    # (P is even, so every graph replay starts from heads[0]); a prefill's history is the
+    # ring with head 0
+    heads = [torch.zeros(S, dtype=torch.int32, device=dev), torch.zeros(S, dtype=torch.int32, device=dev)]
     torch.cuda.synchronize()
 
     def one(k):
-        ss.decode(pool["x"][k], pool["dt"][k], pool["B"][k], pool["C"][k], pool["z"][k], *prm, h, cs, out=y)
+        ss.decode(pool["x"][k], pool["dt"][k], pool["B"][k], pool["C"][k], pool["z"][k], *prm, h, cs,
+                  heads[k % 2], heads[(k + 1) % 2], out=y)
 
     # eager per-step timing (a few steps) for the kernel duration
     _, per = time_calls(lambda: one(0), 20, 5)
@@ -398,7 +404,8 @@ def device_stack(cfg, n_layers, S, dev, seed=11):
                       conv_b=to_dev(prm.conv_b, dev, False),
                       h=0.5 * torch.randn((S, de, N), generator=g, device=dev),
                       conv_state=torch.randn((S, 3, de), generator=g, device=dev).to(torch.bfloat16))
-            nbytes += 2 * S * de * N * 4 + 2 * S * 3 * de * 2
+            # state read and written; conv ring: three slots read, one written
+            nbytes += 2 * S * de * N * 4 + S * de * (3 + 1) * 2
         elif kind == "swa":
             shape = (S, cfg["n_kv_heads"], cfg["window"] + 1, cfg["head_dim"])
             ly.update(w_qkv=w(hq + 2 * hk, dm), w_o=w(dm, hq),
@@ -433,17 +440,18 @@ def bench_model_decode(dev, steps, warmup, S=256):
     emb = torch.randn((S, cfg["d_model"]), generator=g, device=dev)
     hid = emb.clone()
     pos = torch.full((S,), 4096, dtype=torch.int32, device=dev)
+    head = torch.zeros(S, dtype=torch.int32, device=dev)
     out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=dev)
 
     def eager():
         hid.copy_(emb)
-        step(hid, pos, out)
+        step(hid, pos, head, out)
 
     _, per_e = time_calls(eager, steps, warmup)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         hid.copy_(emb)
-        step(hid, pos, out)
+        step(hid, pos, head, out)
     _, per_g = time_calls(graph.replay, steps, warmup)
     sec = float(np.median(per_g))
     res = dict(workload="48 layers (16 Mamba, 8 SWA, 24 MLP; d_model 2048, d_inner 4096, d_ff 8196, 32/4 heads, "

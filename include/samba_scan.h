@@ -34,9 +34,11 @@
  *   rounded to nearest even.  Parameters and the state h are always float32; all
  *   arithmetic is float32.
  * - The recurrent state is [seq][d_inner][d_state] float32 (state index fastest).
- * - The conv history is [seq][3][d_inner] in the I/O dtype, oldest token first.  A
- *   prefill's conv_final can be passed unchanged as the next prefill's conv0 or as the
- *   decode conv_state.
+ * - The conv history is [seq][3][d_inner] in the I/O dtype.  Prefill takes and returns it
+ *   oldest token first; decode keeps it as a ring of three slots with a head index per
+ *   sequence (the slot of the oldest token), so that a step writes one slot.  A prefill's
+ *   conv_final can be passed unchanged as the next prefill's conv0, or as the decode ring
+ *   with head 0.
  * - d_state must be in [1, 16]; d_inner >= 1; every pointer must be aligned to 16 bytes.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
  *   return once the work is enqueued.  Outputs must not overlap inputs, except the
@@ -132,15 +134,26 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
 
 /* One decode step: one new token for each of nseq resident sequences (the constant
  * per-token cost of the fixed-size state, page 1 section 5 "Experimental Analysis",
- * generation throughput).
+ * generation throughput; the recurrence of section 3.4 with L = 1).
  *   x, dt, z, out [nseq][d_inner]; B, C [nseq][d_state]   (io dtype); z may be NULL
  *   h          [nseq][d_inner][d_state] float32, IN/OUT: updated in place
- *   conv_state [nseq][3][d_inner] (io dtype), IN/OUT: the last three pre-conv inputs,
- *              oldest first; shifted by one token in place */
+ *   conv_ring  [nseq][3][d_inner] (io dtype), IN/OUT: the last three pre-conv inputs as a
+ *              ring: with hd = ring_head_in[s] mod 3, slot (hd + k) mod 3 holds x_{t-3+k}
+ *              (k = 0 oldest).  The step reads the three slots and writes the new input x_t
+ *              into slot hd only.
+ *   ring_head_in  DEVICE int32 [nseq], required: each sequence's head (any value; taken
+ *              mod 3).  Not modified.  A prefill's conv_final is a ring with head 0.
+ *   ring_head_out DEVICE int32 [nseq] or NULL: receives (hd + 1) mod 3, the head of the
+ *              next step.  Must not overlap ring_head_in (every workgroup of a sequence
+ *              reads its head during the step, so the heads are double-buffered).
+ * Limits: nseq <= 65535 (SAMBA_ERR_UNSUPPORTED beyond).  Bytes moved per sequence and
+ * channel: the state read and written (2 x 64 B at d_state 16), three ring slots read and
+ * one written, x, dt, z read and out written. */
 samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype io,
                                const void *x, const void *dt, const void *B, const void *C,
                                const void *z, const samba_params *params,
-                               float *h, void *conv_state, void *out, void *stream);
+                               float *h, void *conv_ring, const int32_t *ring_head_in, int32_t *ring_head_out,
+                               void *out, void *stream);
 
 /* The short causal convolution and its SiLU alone (page 1 section 3.4, "Input Projection
  * and Short Convolution"): u_t = SiLU(conv_b + sum_k conv_w[k] x_{t-3+k}), the activation a
@@ -318,8 +331,8 @@ typedef enum { SAMBA_LAYER_MAMBA = 0, SAMBA_LAYER_SWA = 1, SAMBA_LAYER_MLP = 2 }
  *   w_xproj [dt_rank + 2 d_state][d_inner] = [W_r^T; W_b^T; W_c^T];
  *   w_dt_up (W_q^T) [d_inner][dt_rank]; w_out [d_model][d_inner];
  *   ssm: A, D, dt_bias (b), conv_w, conv_b as for samba_scan_prefill;
- *   h [nseq][d_inner][d_state] fp32 and conv_state [nseq][3][d_inner] bf16 (as for
- *   samba_scan_decode).
+ *   h [nseq][d_inner][d_state] fp32 and conv_state [nseq][3][d_inner] bf16, a ring whose
+ *   head is samba_decode_step's conv_head (as conv_ring / ring_head_in of samba_scan_decode).
  * SWA ("The Sliding Window Attention (SWA) Layer"): w_qkv [(n_heads + 2 n_kv_heads) head_dim]
  *   [d_model] = [W_q^T; W_k^T; W_v^T]; w_o [d_model][n_heads head_dim]; k_cache, v_cache
  *   [nseq][n_kv_heads][window + 1][head_dim] ring buffers as for samba_swa_decode.
@@ -350,13 +363,16 @@ size_t samba_decode_step_workspace_bytes(const samba_model_config *cfg, int nseq
  *   out        bf16 [nseq][d_model] or NULL (then final_norm_w is not read)
  *   pos        DEVICE int32 [nseq] IN/OUT: the new tokens' positions (SWA layers); a
  *              sequence with pos < 0 gets no attention output and keeps its position
+ *   conv_head  DEVICE int32 [nseq] IN/OUT: the head of every Mamba layer's conv ring (the
+ *              layers advance together); set to (head + 1) mod 3 for every sequence after the
+ *              last layer.  May be NULL only when no layer is a Mamba layer.
  *   workspace  samba_decode_step_workspace_bytes(cfg, nseq) bytes, 256-byte aligned
  * d_model, d_inner, dt_rank and d_ff must be multiples of 8, d_state 16, nseq <= 65535.  Every
  * launch goes to `stream`
  * and the call allocates nothing, so the whole step can be captured into a HIP graph. */
 samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, const samba_layer *layers,
                                const float *final_norm_w, int nseq, float *hidden, void *out, int32_t *pos,
-                               void *workspace, size_t workspace_bytes, void *stream);
+                               int32_t *conv_head, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Message describing the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */

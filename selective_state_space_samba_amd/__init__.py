@@ -81,7 +81,7 @@ def load():
         lib.samba_scan_varlen.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P,
                                           P, Z, P]
         lib.samba_scan_decode.restype = I
-        lib.samba_scan_decode.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P]
+        lib.samba_scan_decode.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P, P]
         lib.samba_scan_backward_workspace_bytes.restype = Z
         lib.samba_scan_backward_workspace_bytes.argtypes = [I, I, I, I, I]
         lib.samba_scan_backward.restype = I
@@ -104,8 +104,8 @@ def load():
         lib.samba_decode_step_workspace_bytes.restype = Z
         lib.samba_decode_step_workspace_bytes.argtypes = [ctypes.POINTER(ModelConfig), I]
         lib.samba_decode_step.restype = I
-        lib.samba_decode_step.argtypes = [ctypes.POINTER(ModelConfig), I, ctypes.POINTER(Layer), P, I, P, P, P, P, Z,
-                                          P]
+        lib.samba_decode_step.argtypes = [ctypes.POINTER(ModelConfig), I, ctypes.POINTER(Layer), P, I, P, P, P, P, P,
+                                          Z, P]
         lib.samba_gemm_workspace_bytes.restype = Z
         lib.samba_gemm_workspace_bytes.argtypes = [I, I, I, I]
         lib.samba_gemm.restype = I
@@ -263,9 +263,12 @@ def varlen(cu_seqlens, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=Non
     return out, h_final, conv_final
 
 
-def decode(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, conv_state, *, out=None):
+def decode(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, conv_ring, ring_head_in, ring_head_out=None, *,
+           out=None):
     """One decode step for S sequences: x, dt, z [S, D]; B, C [S, N]; h [S, D, N] float32
-    and conv_state [S, 3, D] (I/O dtype) are updated in place.  Returns out [S, D]."""
+    and the conv ring [S, 3, D] (I/O dtype) are updated in place; ring_head_in int32 [S] (the
+    slot of each sequence's oldest input) is read, and ring_head_out int32 [S] (optional, a
+    different tensor) receives the next heads.  Returns out [S, D]."""
     dev = _gpu_device(x)
     S, D = x.shape
     N = B.shape[-1]
@@ -277,12 +280,15 @@ def decode(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, conv_state, *, 
     _shape(B, (S, N), "B")
     _shape(C, (S, N), "C")
     _shape(h, (S, D, N), "h")
-    _shape(conv_state, (S, 3, D), "conv_state")
+    _shape(conv_ring, (S, 3, D), "conv_ring")
+    _shape(ring_head_in, (S,), "ring_head_in")
+    _shape(ring_head_out, (S,), "ring_head_out")
     p = _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N)
     st = load().samba_scan_decode(
         S, D, N, io, _ptr(x, "x", x.dtype, dev), _ptr(dt, "dt", x.dtype, dev), _ptr(B, "B", x.dtype, dev),
         _ptr(C, "C", x.dtype, dev), _ptr(z, "z", x.dtype, dev), ctypes.byref(p),
-        _ptr(h, "h", torch.float32, dev), _ptr(conv_state, "conv_state", x.dtype, dev),
+        _ptr(h, "h", torch.float32, dev), _ptr(conv_ring, "conv_ring", x.dtype, dev),
+        _ptr(ring_head_in, "ring_head_in", torch.int32, dev), _ptr(ring_head_out, "ring_head_out", torch.int32, dev),
         _ptr(out, "out", x.dtype, dev), _stream(dev))
     _check(st)
     return out
@@ -567,12 +573,15 @@ class DecodeStep:
         self.ws_bytes = decode_step_workspace_bytes(cfg, nseq)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.dev)
 
-    def __call__(self, hidden, pos, out=None):
-        """hidden fp32 [nseq, d_model] (updated in place), pos int32 [nseq] (advanced by one);
-        returns out bf16 [nseq, d_model] = the final RMSNorm of hidden, or None if out is False."""
+    def __call__(self, hidden, pos, conv_head, out=None):
+        """hidden fp32 [nseq, d_model] (updated in place), pos int32 [nseq] (advanced by one),
+        conv_head int32 [nseq] (the Mamba layers' conv-ring head, advanced mod 3; None for a
+        stack without Mamba layers); returns out bf16 [nseq, d_model] = the final RMSNorm of
+        hidden, or None if out is False."""
         S, dm = self.nseq, self.cfg.d_model
         _shape(hidden, (S, dm), "hidden")
         _shape(pos, (S,), "pos")
+        _shape(conv_head, (S,), "conv_head")
         if out is None:
             out = torch.empty((S, dm), dtype=torch.bfloat16, device=self.dev)
         po = None if out is False else _ptr(out, "out", torch.bfloat16, self.dev)
@@ -580,13 +589,14 @@ class DecodeStep:
             ctypes.byref(self.cfg), self.n_layers, self.layers, _ptr(self.final_norm_w, "final_norm_w", torch.float32,
                                                                      self.dev),
             S, _ptr(hidden, "hidden", torch.float32, self.dev), po, _ptr(pos, "pos", torch.int32, self.dev),
+            _ptr(conv_head, "conv_head", torch.int32, self.dev),
             _ptr(self.workspace, "workspace"), self.ws_bytes, _stream(self.dev)))
         return None if out is False else out
 
 
-def decode_step(cfg, layers, final_norm_w, hidden, pos, out=None):
+def decode_step(cfg, layers, final_norm_w, hidden, pos, conv_head, out=None):
     """One-shot form of DecodeStep (marshals the stack on every call)."""
-    return DecodeStep(cfg, layers, final_norm_w, hidden.shape[0])(hidden, pos, out)
+    return DecodeStep(cfg, layers, final_norm_w, hidden.shape[0])(hidden, pos, conv_head, out)
 
 
 _F32_KEYS = ("norm_w", "A", "D", "dt_bias", "conv_w", "conv_b")

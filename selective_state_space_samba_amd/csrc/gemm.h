@@ -72,6 +72,7 @@ struct GemmArgs {
     // history c0 (bf16 [M][3][cD], oldest first), weights cw [cD][4] and bias cb (nullable)
     const float *cw, *cb;
     const uint16_t *c0;
+    const int32_t *chead;  // nullable: c0 is a ring, entry k in slot (chead[row] + k) mod 3
     uint16_t *cu;
     int cD;
 };
@@ -451,9 +452,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a)
                     // conv_silu_kernel: x as stored (bf16), the history as stored
                     const float xs[4] = {bf16lo(pk.x), bf16hi(pk.x), bf16lo(pk.y), bf16hi(pk.y)};
                     const uint16_t *h = a.c0 + static_cast<size_t>(row) * 3 * a.cD + col;
-                    const uint2 h0 = *reinterpret_cast<const uint2 *>(h);
-                    const uint2 h1 = *reinterpret_cast<const uint2 *>(h + a.cD);
-                    const uint2 h2 = *reinterpret_cast<const uint2 *>(h + 2 * a.cD);
+                    const int hd = a.chead != nullptr ? a.chead[row] : 0;
+                    const uint2 h0 = *reinterpret_cast<const uint2 *>(h + ring_slot(hd, 0) * a.cD);
+                    const uint2 h1 = *reinterpret_cast<const uint2 *>(h + ring_slot(hd, 1) * a.cD);
+                    const uint2 h2 = *reinterpret_cast<const uint2 *>(h + ring_slot(hd, 2) * a.cD);
                     const float w0[4] = {bf16lo(h0.x), bf16hi(h0.x), bf16lo(h0.y), bf16hi(h0.y)};
                     const float w1[4] = {bf16lo(h1.x), bf16hi(h1.x), bf16lo(h1.y), bf16hi(h1.y)};
                     const float w2[4] = {bf16lo(h2.x), bf16hi(h2.x), bf16lo(h2.y), bf16hi(h2.y)};

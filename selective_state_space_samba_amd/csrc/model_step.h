@@ -84,11 +84,15 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(int rows, int d, const
     }
 }
 
-// Positions of the sequences advance by one token after a step (negative = inactive, kept).
-__global__ __launch_bounds__(256) void advance_pos_kernel(int n, int32_t *pos)
+// After a step the positions advance by one token (negative = inactive, kept) and the
+// Mamba layers' conv-ring head moves to the next slot (every sequence: the Mamba layers
+// advance inactive sequences too).  conv_head may be nullptr (a stack without Mamba layers).
+__global__ __launch_bounds__(256) void advance_pos_kernel(int n, int32_t *pos, int32_t *conv_head)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n && pos[i] >= 0) pos[i] += 1;
+    if (i >= n) return;
+    if (pos[i] >= 0) pos[i] += 1;
+    if (conv_head != nullptr) conv_head[i] = ring_slot(conv_head[i], 1);
 }
 
 inline void launch_rmsnorm(int rows, int d, const float *x, const float *w, float eps, uint16_t *out,
@@ -108,9 +112,9 @@ inline void launch_rmsnorm(int rows, int d, const float *x, const float *w, floa
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, rows, d, x, w, eps, out);
 }
 
-inline void launch_advance(int n, int32_t *pos, hipStream_t s)
+inline void launch_advance(int n, int32_t *pos, int32_t *conv_head, hipStream_t s)
 {
-    if (n > 0) hipLaunchKernelGGL(advance_pos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, pos);
+    if (n > 0) hipLaunchKernelGGL(advance_pos_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, pos, conv_head);
 }
 
 }  // namespace step

@@ -268,7 +268,8 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
 samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype io,
                                const void *x, const void *dt, const void *B, const void *C,
                                const void *z, const samba_params *params,
-                               float *h, void *conv_state, void *out, void *stream)
+                               float *h, void *conv_ring, const int32_t *ring_head_in, int32_t *ring_head_out,
+                               void *out, void *stream)
 {
     const char *fn = "samba_scan_decode";
     if (nseq < 0) return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d must be >= 0", fn, nseq);
@@ -278,18 +279,29 @@ samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype i
         g_err.clear();
         return SAMBA_OK;
     }
+    // one grid row per sequence
+    if (nseq > 65535) return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d exceeds 65535", fn, nseq);
     REQUIRE_PTR(x, "x");
     REQUIRE_PTR(dt, "dt");
     REQUIRE_PTR(B, "B");
     REQUIRE_PTR(C, "C");
     REQUIRE_PTR(out, "out");
     REQUIRE_PTR(h, "h");
-    REQUIRE_PTR(conv_state, "conv_state");
+    REQUIRE_PTR(conv_ring, "conv_ring");
+    if (ring_head_in == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: ring_head_in is NULL", fn);
+    if ((reinterpret_cast<uintptr_t>(ring_head_in) & 3u) != 0 || (reinterpret_cast<uintptr_t>(ring_head_out) & 3u) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: ring heads must be 4-byte aligned", fn);
+    const size_t head_bytes = static_cast<size_t>(nseq) * sizeof(int32_t);
+    if (overlaps(ring_head_out, head_bytes, ring_head_in, head_bytes))
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: ring_head_out overlaps ring_head_in (the heads are double-buffered: "
+                    "every workgroup of a sequence reads its head)", fn);
     OPTIONAL_PTR(z, "z");
     // A decode step is the recurrence over a single token whose state and history are
     // read and written in place.
-    samba::ScanArgs a = make_args(nseq, 1, nullptr, d_inner, d_state, x, dt, B, C, z, params, h, conv_state,
-                                  out, h, conv_state);
+    samba::ScanArgs a = make_args(nseq, 1, nullptr, d_inner, d_state, x, dt, B, C, z, params, h, conv_ring,
+                                  out, h, conv_ring);
+    a.head_in = ring_head_in;
+    a.head_out = ring_head_out;
     if (d_state == samba::kMaxState)
         samba::launch_decode16(a, io, static_cast<hipStream_t>(stream));
     else
@@ -676,6 +688,7 @@ struct GemmFuse {
     uint16_t *norm_out = nullptr;
     const float *conv_w = nullptr, *conv_b = nullptr;  // store: u = SiLU(conv(x)) of the x half
     const uint16_t *conv0 = nullptr;
+    const int32_t *conv_head = nullptr;  // conv0 is a ring with these heads (nullptr: oldest first)
     uint16_t *conv_u = nullptr;
     int conv_D = 0;
     bool normed = false, conved = false;
@@ -762,6 +775,7 @@ samba_status gemm_impl(int M, int N, int K, samba_gemm_epilogue epilogue, const 
         a.cw = fz->conv_w;
         a.cb = fz->conv_b;
         a.c0 = fz->conv0;
+        a.chead = fz->conv_head;
         a.cu = fz->conv_u;
         a.cD = fz->conv_D;
     }
@@ -880,7 +894,7 @@ size_t samba_decode_step_workspace_bytes(const samba_model_config *cfg, int nseq
 
 samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, const samba_layer *layers,
                                const float *final_norm_w, int nseq, float *hidden, void *out, int32_t *pos,
-                               void *workspace, size_t workspace_bytes, void *stream)
+                               int32_t *conv_head, void *workspace, size_t workspace_bytes, void *stream)
 {
     const char *fn = "samba_decode_step";
     samba_status st = check_model_config(fn, cfg);
@@ -895,9 +909,14 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
     REQUIRE_PTR(hidden, "hidden");
     if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
     if (out != nullptr) REQUIRE_PTR(final_norm_w, "final_norm_w");
-    for (int l = 0; l < n_layers; ++l)
+    for (int l = 0; l < n_layers; ++l) {
         if (layers[l].kind < SAMBA_LAYER_MAMBA || layers[l].kind > SAMBA_LAYER_MLP)
             return fail(SAMBA_ERR_INVALID_ARG, "%s: layer %d has unknown kind %d", fn, l, layers[l].kind);
+        if (layers[l].kind == SAMBA_LAYER_MAMBA && conv_head == nullptr)
+            return fail(SAMBA_ERR_INVALID_ARG, "%s: conv_head is NULL but layer %d is a Mamba layer", fn, l);
+    }
+    if ((reinterpret_cast<uintptr_t>(conv_head) & 3u) != 0)
+        return fail(SAMBA_ERR_INVALID_ARG, "%s: conv_head is not 4-byte aligned", fn);
     const samba_model_config &c = *cfg;
     const StepLayout L = step_layout(c, nseq);
     if (workspace == nullptr || workspace_bytes < L.total)
@@ -972,6 +991,7 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             fz.conv_w = ly.ssm.conv_w;
             fz.conv_b = ly.ssm.conv_b;
             fz.conv0 = static_cast<const uint16_t *>(ly.conv_state);
+            fz.conv_head = conv_head;
             fz.conv_u = u;
             fz.conv_D = de;
             STEP("[x | z] = X [W_in; W_g]", gemm_impl(S, 2 * de, dm, SAMBA_GEMM_STORE, hn, dm, ly.w_in_gate, xz, 2 * de,
@@ -985,6 +1005,7 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
             ca.conv_w = ly.ssm.conv_w;
             ca.conv_b = ly.ssm.conv_b;
             ca.conv0 = ly.conv_state;
+            ca.conv_head = conv_head;
             ca.u = u;
             if (!fz.conved) {
                 samba::launch_conv_silu(ca, SAMBA_BF16, hs);
@@ -997,6 +1018,8 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
                                            ly.h, ly.conv_state, y, ly.h, ly.conv_state);
             sa.ldx = 2 * de;
             sa.ldbc = wx;
+            sa.head_in = conv_head;  // advanced once for all layers at the end of the step
+            sa.head_out = nullptr;
             samba::launch_decode16(sa, SAMBA_BF16, hs);
             STEP("scan decode", launched(fn));
             STEP("hidden += Y W_out", gemm_add(de, y, de, ly.w_out));
@@ -1021,7 +1044,7 @@ samba_status samba_decode_step(const samba_model_config *cfg, int n_layers, cons
     if (out != nullptr && !normed_next)
         STEP("final rmsnorm", samba_rmsnorm(S, dm, hidden, final_norm_w, c.norm_eps, out, stream));
 #undef STEP
-    samba::step::launch_advance(S, pos, hs);
+    samba::step::launch_advance(S, pos, conv_head, hs);
     return launched(fn);
 }
 

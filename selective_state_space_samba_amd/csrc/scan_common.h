@@ -34,7 +34,20 @@ struct ScanArgs {
     void *out;
     float *h_final;
     void *conv_final;
+    // Decode only: the conv history is a ring [seq][3][d_inner] whose slot (head + k) mod 3
+    // holds x_{t-3+k}, head = head_in[seq] (any int; taken mod 3).  A step reads the three
+    // slots and writes the new input into slot head (the oldest); head_out[seq] (nullable)
+    // receives (head + 1) mod 3.  head_in == nullptr: the history is stored oldest first.
+    const int32_t *head_in;
+    int32_t *head_out;
 };
+
+// Ring slot of the history entry k (0 = oldest) for a head value from device memory.
+__device__ inline int ring_slot(int head, int k)
+{
+    const int h = head % 3;
+    return (h + (h < 0 ? 3 : 0) + k) % 3;
+}
 
 // Token range [t0, t1) of sequence s.  Varlen offsets are device data supplied by the
 // caller; they are clamped into [0, total] so that malformed offsets can never address

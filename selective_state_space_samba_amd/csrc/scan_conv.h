@@ -37,6 +37,9 @@ struct ConvArgs {
     int ldx;             // x row pitch in elements (0: D, the contiguous layout)
     const float *conv_w, *conv_b;
     const void *conv0;
+    // nullable: conv0 is a ring [nseq][3][D] whose slot (conv_head[s] + k) mod 3 holds
+    // history entry k (oldest first); nullptr: entry k is in slot k
+    const int32_t *conv_head;
     void *u;
     void *conv_final;
 };
@@ -141,7 +144,8 @@ __global__ __launch_bounds__(conv::kThreads) void conv_silu_kernel(ConvArgs a)
         if (tt >= 0) {
             load_vec<Io, kVec>(xs + (t0 + static_cast<size_t>(tt)) * ldx + c, win[k]);
         } else if (a.conv0 != nullptr) {
-            load_vec<Io, kVec>(static_cast<const T *>(a.conv0) + (static_cast<size_t>(s) * 3 + (3 + tt)) * D + c, win[k]);
+            const int slot = a.conv_head != nullptr ? ring_slot(a.conv_head[s], 3 + tt) : 3 + tt;
+            load_vec<Io, kVec>(static_cast<const T *>(a.conv0) + (static_cast<size_t>(s) * 3 + slot) * D + c, win[k]);
         } else {
 #pragma unroll
             for (int i = 0; i < kVec; ++i) win[k][i] = 0.0f;

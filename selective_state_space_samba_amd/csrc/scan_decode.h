@@ -13,7 +13,10 @@
 //    channel on coalesced 2-byte rows; Delta and Delta*u reach the four lanes that hold a
 //    channel's states by a cross-lane permute, the readout's partial sums are added across
 //    those four lanes by DPP, and skip and gate terms return by a permute;
-//  * the conv history is shifted in place (oldest first).
+//  * the conv history is a ring of three slots per sequence: the step reads the three
+//    slots from the head (the oldest) on and overwrites only the head slot with the new
+//    input (144 bytes per sequence and channel per step in all); the next head goes to
+//    head_out.
 #pragma once
 
 #include "scan_common.h"
@@ -66,7 +69,9 @@ __global__ __launch_bounds__(256) void decode16_kernel(int D, int ldx, int ldbc,
                                                        const float *__restrict__ dt_bias,
                                                        const float *__restrict__ conv_w,
                                                        const float *__restrict__ conv_b, float *__restrict__ h,
-                                                       typename Io::T *__restrict__ conv, typename Io::T *__restrict__ out)
+                                                       typename Io::T *__restrict__ conv,
+                                                       const int32_t *__restrict__ head_in,
+                                                       int32_t *__restrict__ head_out, typename Io::T *__restrict__ out)
 {
     using namespace dec;
     using T = typename Io::T;
@@ -82,8 +87,12 @@ __global__ __launch_bounds__(256) void decode16_kernel(int D, int ldx, int ldbc,
     const int cfc = fok ? cf : D - 1;  // clamped for loads
     const size_t sdf = static_cast<size_t>(s) * D + cfc;
     const size_t sxf = static_cast<size_t>(s) * ldx + cfc;  // x and z may be column blocks of wider rows
+    // ring slots of x_{t-3}, x_{t-2}, x_{t-1} (the head is the same for the whole wave)
+    const int hd = __builtin_amdgcn_readfirstlane(head_in[s]);
     const size_t cbase = static_cast<size_t>(s) * 3 * D + cfc;
-    const T h0 = conv[cbase], h1 = conv[cbase + D], h2 = conv[cbase + 2 * static_cast<size_t>(D)];
+    const int k0 = ring_slot(hd, 0), k1 = ring_slot(hd, 1), k2 = ring_slot(hd, 2);
+    const T h0 = conv[cbase + static_cast<size_t>(k0) * D], h1 = conv[cbase + static_cast<size_t>(k1) * D];
+    const T h2 = conv[cbase + static_cast<size_t>(k2) * D];
     const T xr = x[sxf];
     const float dtv = to_f32(dt[sdf]);
     const float zv = z ? to_f32(z[sxf]) : 0.0f;
@@ -120,11 +129,8 @@ __global__ __launch_bounds__(256) void decode16_kernel(int D, int ldx, int ldbc,
     const float du = (lg * kLn2) * u;
     const float dskip = dsk * u;
     const float gate = z ? silu(zv) : 1.0f;
-    if (fok) {
-        conv[cbase] = h1;
-        conv[cbase + D] = h2;
-        conv[cbase + 2 * static_cast<size_t>(D)] = xr;
-    }
+    if (fok) conv[cbase + static_cast<size_t>(k0) * D] = xr;  // the new input replaces the oldest
+    if (head_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) head_out[s] = ring_slot(hd, 1);
 
     // ---- recurrence and partial readout over this lane's 4 states of 4 channels
     float part[4];
@@ -173,13 +179,13 @@ inline void launch_decode16(const ScanArgs &a, samba_dtype io, hipStream_t strea
         decode16_kernel<IoBf16><<<grid, block, 0, stream>>>(
             a.D, a.ldx > 0 ? a.ldx : a.D, a.ldbc > 0 ? a.ldbc : kMaxState, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
             static_cast<const T *>(a.C), static_cast<const T *>(a.z), a.A, a.Dskip, a.dt_bias, a.conv_w, a.conv_b,
-            a.h_final, static_cast<T *>(a.conv_final), static_cast<T *>(a.out));
+            a.h_final, static_cast<T *>(a.conv_final), a.head_in, a.head_out, static_cast<T *>(a.out));
     } else {
         using T = float;
         decode16_kernel<IoF32><<<grid, block, 0, stream>>>(
             a.D, a.ldx > 0 ? a.ldx : a.D, a.ldbc > 0 ? a.ldbc : kMaxState, static_cast<const T *>(a.x), static_cast<const T *>(a.dt), static_cast<const T *>(a.B),
             static_cast<const T *>(a.C), static_cast<const T *>(a.z), a.A, a.Dskip, a.dt_bias, a.conv_w, a.conv_b,
-            a.h_final, static_cast<T *>(a.conv_final), static_cast<T *>(a.out));
+            a.h_final, static_cast<T *>(a.conv_final), a.head_in, a.head_out, static_cast<T *>(a.out));
     }
 }
 

@@ -101,11 +101,17 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
     const size_t cbase = static_cast<size_t>(s) * 3 * D + d;
+    // History entry k (oldest first) lives in slot k, or in ring slot (head + k) mod 3 when
+    // the decode passes a ring head.
+    const int hd = a.head_in != nullptr ? a.head_in[s] : 0;
+    const size_t e0 = cbase + static_cast<size_t>(ring_slot(hd, 0)) * D;
+    const size_t e1 = cbase + static_cast<size_t>(ring_slot(hd, 1)) * D;
+    const size_t e2 = cbase + static_cast<size_t>(ring_slot(hd, 2)) * D;
     float x0 = 0.0f, x1 = 0.0f, x2 = 0.0f;  // x_{t-3}, x_{t-2}, x_{t-1}
     if (a.conv0 != nullptr) {
-        x0 = Io::ld(a.conv0, cbase);
-        x1 = Io::ld(a.conv0, cbase + D);
-        x2 = Io::ld(a.conv0, cbase + 2 * static_cast<size_t>(D));
+        x0 = Io::ld(a.conv0, e0);
+        x1 = Io::ld(a.conv0, e1);
+        x2 = Io::ld(a.conv0, e2);
     }
     const bool has_z = a.z != nullptr;
     const T *xs = static_cast<const T *>(a.x);
@@ -221,9 +227,18 @@ done:
             if (kFullN || n < N) a.h_final[hbase + n] = h[n];
     }
     if (a.conv_final != nullptr) {
-        Io::st(a.conv_final, cbase, x0);
-        Io::st(a.conv_final, cbase + D, x1);
-        Io::st(a.conv_final, cbase + 2 * static_cast<size_t>(D), x2);
+        if (a.head_in != nullptr) {
+            // ring after one token: the new head is the old head + 1, so the entries
+            // (oldest first) go to slots head + 1, head + 2 and head
+            Io::st(a.conv_final, e1, x0);
+            Io::st(a.conv_final, e2, x1);
+            Io::st(a.conv_final, e0, x2);
+            if (a.head_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) a.head_out[s] = ring_slot(hd, 1);
+        } else {
+            Io::st(a.conv_final, cbase, x0);
+            Io::st(a.conv_final, cbase + D, x1);
+            Io::st(a.conv_final, cbase + 2 * static_cast<size_t>(D), x2);
+        }
     }
 }
 

@@ -41,3 +41,24 @@ def tf32(a, dev):
 
 def host(t):
     return t.float().cpu().numpy()
+
+
+def ring_from_ordered(hist, heads):
+    """A conv ring [S, 3, D] holding the ordered history hist [S, 3, D] (oldest first) with
+    each sequence's oldest entry in slot heads[s] mod 3."""
+    hist = np.asarray(hist)
+    ring = np.empty_like(hist)
+    for s, hd in enumerate(np.asarray(heads)):
+        for k in range(3):
+            ring[s, (int(hd) + k) % 3] = hist[s, k]
+    return ring
+
+
+def ordered_from_ring(ring, heads):
+    """The history oldest first from a ring and its heads (the inverse of ring_from_ordered)."""
+    ring = np.asarray(ring)
+    out = np.empty_like(ring)
+    for s, hd in enumerate(np.asarray(heads)):
+        for k in range(3):
+            out[s, k] = ring[s, (int(hd) + k) % 3]
+    return out

@@ -76,10 +76,26 @@ def test_varlen_and_decode_argument_errors():
     st = lib.samba_scan_varlen(2, 4096, 10, 11, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None,
                                None, 4096, None, None, None, 0, None)
     assert st == 1 and b"max_seqlen" in lib.samba_last_error()
-    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None, 4096, 4096, None)
+    # decode: (nseq, D, N, io, x, dt, B, C, z, params, h, conv_ring, ring_head_in, ring_head_out, out, stream)
+    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), None, 4096, 8192, None,
+                               4096, None)
     assert st == 1 and b"h is NULL" in lib.samba_last_error()
+    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), 4096, 4096, None, None,
+                               4096, None)
+    assert st == 1 and b"ring_head_in is NULL" in lib.samba_last_error()
+    # the heads are double-buffered: head_out may not overlap head_in
+    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), 4096, 4096, 8192, 8200,
+                               4096, None)
+    assert st == 1 and b"overlaps ring_head_in" in lib.samba_last_error()
+    st = lib.samba_scan_decode(4, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), 4096, 4096, 8194, None,
+                               4096, None)
+    assert st == 1 and b"4-byte aligned" in lib.samba_last_error()
+    # one grid row per sequence: more than 65535 sequences is refused before any launch
+    st = lib.samba_scan_decode(65536, 8, 16, 1, 4096, 4096, 4096, 4096, None, ctypes.byref(p), 4096, 4096, 8192,
+                               None, 4096, None)
+    assert st == 2 and b"65535" in lib.samba_last_error()
     assert lib.samba_scan_decode(0, 8, 16, 1, None, None, None, None, None, ctypes.byref(p), None, None, None,
-                                 None) == 0
+                                 None, None, None) == 0
 
 
 def test_binding_refuses_cpu_tensors_before_calling():
@@ -90,7 +106,7 @@ def test_binding_refuses_cpu_tensors_before_calling():
         ss.prefill(x, x, Bm, Bm, x, torch.zeros((8, 16)), None, None, torch.zeros((8, 4)), None)
     with pytest.raises(ValueError, match="on a GPU"):
         ss.decode(x[0], x[0], Bm[0], Bm[0], x[0], torch.zeros((8, 16)), None, None, torch.zeros((8, 4)), None,
-                  torch.zeros((4, 8, 16)), torch.zeros((4, 3, 8), dtype=torch.bfloat16))
+                  torch.zeros((4, 8, 16)), torch.zeros((4, 3, 8), dtype=torch.bfloat16), torch.zeros(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="on a GPU"):
         ss.varlen(torch.zeros(2, dtype=torch.int32), x[0], x[0], Bm[0], Bm[0], x[0], torch.zeros((8, 16)), None,
                   None, torch.zeros((8, 4)), None, max_seqlen=4)

@@ -12,7 +12,7 @@ import torch
 import oracle
 import selective_state_space_samba_amd as ss
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, rel_err, tf32
+from tests.helpers import TOL, ordered_from_ring, rel_err, tf32
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -176,7 +176,8 @@ def test_streaming_decode_256_sequences_65536_steps():
     pool = synth.make_tokens(seed, (P, S), D, N, "bf16", tag="pool")
     # GPU: 65536 decode steps, gathering the sampled outputs on the device
     h = tf32(h0, DEV)
-    cs = bf16(conv0)
+    cs = bf16(conv0)  # the ring with head 0
+    heads = [torch.zeros(S, dtype=torch.int32, device=DEV), torch.zeros(S, dtype=torch.int32, device=DEV)]
     px, pdt, pz, pB, pC = (bf16(a) for a in (pool.x, pool.dt, pool.z, pool.B, pool.C))
     prm = params_dev(p)
     si = torch.from_numpy(seqs).to(DEV)
@@ -186,10 +187,11 @@ def test_streaming_decode_256_sequences_65536_steps():
     print("case: decode S=%d steps=%d" % (S, steps), flush=True)
     for k in range(steps):
         q = k % P
-        ss.decode(px[q], pdt[q], pB[q], pC[q], pz[q], *prm, h, cs, out=y)
+        ss.decode(px[q], pdt[q], pB[q], pC[q], pz[q], *prm, h, cs, heads[k % 2], heads[(k + 1) % 2], out=y)
         ys[k] = y.index_select(0, si).index_select(1, ci)
     hg = h.index_select(0, si).index_select(1, ci).cpu().numpy()
-    cg = cs.index_select(0, si).index_select(2, ci).float().cpu().numpy()
+    cg = ordered_from_ring(cs.index_select(0, si).index_select(2, ci).float().cpu().numpy(),
+                           heads[steps % 2].index_select(0, si).cpu().numpy())
     yg = ys.float().cpu().numpy()
     torch.cuda.synchronize()
     # oracle: each sampled sequence as one prefill over its step stream

@@ -9,7 +9,7 @@ import torch
 import selective_state_space_samba_amd as ss
 from oracle import model
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, host, rel_err
+from tests.helpers import TOL, host, rel_err, ring_from_ordered
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -27,14 +27,17 @@ def tol_stack(n_layers):
 # what remains is float32 vs float64 arithmetic (~1e-7: many steps match to that), the
 # attention's own float32 softmax (~2e-3 over a 2049-key window) and values within float32
 # error of a bf16 rounding boundary, which the two sides round one bf16 ulp (2^-8 relative)
-# apart.  A layer alone stays within 5e-3 (TOL_LAYER); in a stack each flip moves a full
-# 2048-wide normed input of the next layers, flips add up over layers and steps (the Mamba
-# state carries them), and the bound becomes that of the plain comparison.
+# apart.  A layer alone stays within 5e-3 (TOL_LAYER; measured up to 1.9e-3).  In a stack each
+# such flip moves a full normed input of the next layers and the flips add up over layers
+# and steps (the Mamba state carries them): measured up to 1.8e-3 (6 narrow layers), 1.3e-2
+# (48 narrow layers) and 1.4e-2 (6 layers at the 1.7B widths).  The matched bound for a
+# stack is therefore the bf16 tolerance itself, 2e-2, at every depth -- it does not grow
+# with the layer count as the plain comparison's bound does.
 TOL_LAYER = 5e-3
 
 
 def tol_matched(n_layers):
-    return tol_stack(n_layers)
+    return TOL["bf16"]
 
 
 def bf16_act(a):
@@ -67,17 +70,21 @@ def run_steps(cfg, n_layers, S, steps, seed, pos0=None, prep=None, kinds=None, m
     st = model.DecodeState(cfg, layers, S)
     stm = model.DecodeState(cfg, layers, S)
     pos_np = np.zeros(S, dtype=np.int32) if pos0 is None else np.asarray(pos0, dtype=np.int32).copy()
+    # the Mamba conv rings start at different heads per sequence (the oracle keeps its
+    # history oldest first; prep writes the rings from it with these heads)
+    head_np = (np.arange(S, dtype=np.int32) * 2 + 1) % 3
     if prep is not None:
-        prep(layers, dev_layers, st, pos_np)
+        prep(layers, dev_layers, st, pos_np, heads=head_np)
         prep(layers, None, stm, pos_np, matched=True)
     fnw = torch.from_numpy(fn).to(DEV)
     step = ss.DecodeStep(cfg, dev_layers, fnw, S)
     pos = torch.from_numpy(pos_np.copy()).to(DEV)
+    head = torch.from_numpy(head_np.copy()).to(DEV)
     worst = 0.0
     for t in range(steps):
         emb = synth.make_hidden(seed, t, S, cfg["d_model"])
         hid = torch.from_numpy(emb).to(DEV)
-        out = step(hid, pos)
+        out = step(hid, pos, head)
         torch.cuda.synchronize()
         rh, ro = model.decode_step(cfg, layers, fn, emb, st, pos_np)
         mh, mo = model.decode_step(cfg, layers, fn, emb, stm, pos_np, act=bf16_act)
@@ -91,6 +98,7 @@ def run_steps(cfg, n_layers, S, steps, seed, pos0=None, prep=None, kinds=None, m
         assert eh <= tol_stack(n_layers) and eo <= tol_stack(n_layers)
         assert fi <= mtol
         np.testing.assert_array_equal(host(pos), pos_np)
+        np.testing.assert_array_equal(host(head), (head_np + t + 1) % 3)
     return worst
 
 
@@ -113,7 +121,7 @@ def _prep_1p7b(S, P):
     filled from a random P-token key/value history, every sequence at position P."""
     cfg = synth.MODEL_1P7B
 
-    def prep(layers, dev_layers, st, pos_np, matched=False):
+    def prep(layers, dev_layers, st, pos_np, matched=False, heads=None):
         for i, ly in enumerate(layers):
             if ly["kind"] == "mamba":
                 h, hist = synth.make_state(500 + i, S, cfg["d_inner"], cfg["d_state"], "bf16", scale=0.5)
@@ -121,7 +129,8 @@ def _prep_1p7b(S, P):
                 st.hist[i][...] = hist
                 if dev_layers is not None:
                     dev_layers[i]["h"].copy_(torch.from_numpy(h))
-                    dev_layers[i]["conv_state"].copy_(torch.from_numpy(hist).to(torch.bfloat16))
+                    ring = ring_from_ordered(hist, heads)
+                    dev_layers[i]["conv_state"].copy_(torch.from_numpy(ring).to(torch.bfloat16))
             elif ly["kind"] == "swa":
                 shape = (S, P, cfg["n_kv_heads"], cfg["head_dim"])
                 k = synth._normal(600 + i, "k", shape, io="bf16")
@@ -168,26 +177,28 @@ def test_decode_step_graph_replay_matches_eager(cfg):
         dl = ss.upload_stack(cfg, layers, S, DEV)
         step = ss.DecodeStep(cfg, dl, fnw, S)
         pos = torch.zeros(S, dtype=torch.int32, device=DEV)
+        head = torch.zeros(S, dtype=torch.int32, device=DEV)
         hid = torch.zeros((S, cfg["d_model"]), device=DEV)
         out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=DEV)
         res = []
         if mode == "graph":  # every kernel has been launched once by the eager run
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(hid, pos, out)
+                step(hid, pos, head, out)
         for t in range(3):
             hid.copy_(torch.from_numpy(synth.make_hidden(31, t, S, cfg["d_model"])))
             if mode == "graph":
                 g.replay()
             else:
-                step(hid, pos, out)
+                step(hid, pos, head, out)
             torch.cuda.synchronize()
-            res.append((host(hid), host(out), host(pos)))
+            res.append((host(hid), host(out), host(pos), host(head)))
         runs.append(res)
-    for (h1, o1, p1), (h2, o2, p2) in zip(*runs):
+    for (h1, o1, p1, c1), (h2, o2, p2, c2) in zip(*runs):
         np.testing.assert_array_equal(h1, h2)
         np.testing.assert_array_equal(o1, o2)
         np.testing.assert_array_equal(p1, p2)
+        np.testing.assert_array_equal(c1, c2)
 
 
 def test_decode_step_fused_reduces_are_bitwise_the_separate_kernels(monkeypatch):
@@ -206,11 +217,12 @@ def test_decode_step_fused_reduces_are_bitwise_the_separate_kernels(monkeypatch)
         dl = ss.upload_stack(cfg, layers, S, DEV)
         step = ss.DecodeStep(cfg, dl, fnw, S)
         pos = torch.zeros(S, dtype=torch.int32, device=DEV)
+        head = torch.tensor([2, 0, 1], dtype=torch.int32, device=DEV)
         hid = torch.zeros((S, cfg["d_model"]), device=DEV)
         out = torch.empty((S, cfg["d_model"]), dtype=torch.bfloat16, device=DEV)
         for t in range(2):  # the second step reads the conv state and rings the first one wrote
             hid.copy_(torch.from_numpy(synth.make_hidden(37, t, S, cfg["d_model"])))
-            step(hid, pos, out)
+            step(hid, pos, head, out)
         torch.cuda.synchronize()
         res.append((host(hid), host(out), host(dl[0]["h"]), host(dl[0]["conv_state"])))
         monkeypatch.delenv("SAMBA_DECODE_NOFUSE", raising=False)

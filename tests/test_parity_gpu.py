@@ -11,7 +11,7 @@ import torch
 import oracle
 import selective_state_space_samba_amd as ss
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, host, rel_err, tdev, tf32
+from tests.helpers import TOL, host, ordered_from_ring, rel_err, ring_from_ordered, tdev, tf32
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -159,31 +159,62 @@ def test_varlen_fresh_sequences():
                                          ("f32", 72, False)])
 def test_decode_steps(io, D, gate):
     """24 decode steps on 5 sequences; D = 200 and 72 leave a partly filled last wave of 64
-    channels, and z = None exercises the ungated output."""
+    channels, and z = None exercises the ungated output.  The conv ring starts with a
+    different head per sequence (including values outside 0..2, taken mod 3) and the heads
+    ping-pong between two buffers, so every slot is overwritten eight times."""
     S, N, steps = 5, 16, 24
     seed = 600
     p = synth.make_params(seed, D, N, random_A=True, conv_bias=True)
     h0, c0 = synth.make_state(seed, S, D, N, io, scale=0.5)
+    heads0 = np.array([0, 1, 2, 5, -1], dtype=np.int32)
     h = tf32(h0, DEV)
-    cs = tdev(c0, io, DEV)
+    ring = tdev(ring_from_ordered(c0, heads0 % 3), io, DEV)
+    heads = [torch.from_numpy(heads0).to(DEV), torch.full((S,), -7, dtype=torch.int32, device=DEV)]
     hr = h0.astype(np.float64).copy()
     cr = c0.astype(np.float64).copy()
     args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
     for k in range(steps):
         st = synth.make_tokens(seed, (S,), D, N, io, tag="s%d" % k)
+        hin, hout = heads[k % 2], heads[(k + 1) % 2]
         y = ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
-                      tdev(st.z, io, DEV) if gate else None, *args, h, cs)
+                      tdev(st.z, io, DEV) if gate else None, *args, h, ring, hin, hout)
         yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z if gate else None, p.A, p.Dskip, p.dt_bias,
                                 p.conv_w, p.conv_b, hr, cr)
         torch.cuda.synchronize()
         e = rel_err(host(y), yr)
         assert e <= TOL[io], "step %d err %.3e" % (k, e)
+        np.testing.assert_array_equal(hout.cpu().numpy(), (heads0 % 3 + k + 1) % 3)
     assert rel_err(host(h), hr) <= TOL[io]
-    np.testing.assert_array_equal(host(cs), cr)
+    np.testing.assert_array_equal(ordered_from_ring(host(ring), heads[steps % 2].cpu().numpy()), cr)
+
+
+def test_decode_writes_one_ring_slot_per_step():
+    """A step overwrites only the head slot of the ring (with the new input x_t): the other
+    two slots are left exactly as they were; with no head_out the heads are not touched."""
+    io, S, D, N = "bf16", 3, 128, 16
+    seed = 650
+    p = synth.make_params(seed, D, N, conv_bias=True)
+    h0, c0 = synth.make_state(seed, S, D, N, io, scale=0.5)
+    heads = np.array([2, 0, 1], dtype=np.int32)
+    ring0 = ring_from_ordered(c0, heads)
+    ring = tdev(ring0, io, DEV)
+    hd = torch.from_numpy(heads).to(DEV)
+    st = synth.make_tokens(seed, (S,), D, N, io, tag="one")
+    args = [tf32(a, DEV) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
+              tdev(st.z, io, DEV), *args, tf32(h0, DEV), ring, hd)
+    torch.cuda.synchronize()
+    got = host(ring)
+    for s in range(S):
+        for slot in range(3):
+            want = st.x[s] if slot == heads[s] else ring0[s, slot]
+            np.testing.assert_array_equal(got[s, slot], want)
+    np.testing.assert_array_equal(hd.cpu().numpy(), heads)
 
 
 def test_decode_continues_prefill():
-    """GPU prefill then GPU decode equals the oracle's prefill then decode."""
+    """GPU prefill then GPU decode equals the oracle's prefill then decode: the prefill's
+    conv_final is the ring with head 0."""
     io = "bf16"
     b, L, D, N = 3, 300, 128, 16
     seed = 700
@@ -193,14 +224,15 @@ def test_decode_continues_prefill():
     _, h, cs = ss.prefill(tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
                           tdev(tk.z, io, DEV), *args)
     _, hr, cr = oracle.prefill(tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)
+    heads = [torch.zeros(b, dtype=torch.int32, device=DEV), torch.zeros(b, dtype=torch.int32, device=DEV)]
     for k in range(5):
         st = synth.make_tokens(seed, (b,), D, N, io, tag="d%d" % k)
         y = ss.decode(tdev(st.x, io, DEV), tdev(st.dt, io, DEV), tdev(st.B, io, DEV), tdev(st.C, io, DEV),
-                      tdev(st.z, io, DEV), *args, h, cs)
+                      tdev(st.z, io, DEV), *args, h, cs, heads[k % 2], heads[(k + 1) % 2])
         yr = oracle.decode_step(st.x, st.dt, st.B, st.C, st.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b, hr, cr)
         torch.cuda.synchronize()
         assert rel_err(host(y), yr) <= TOL[io]
-    np.testing.assert_array_equal(host(cs), cr)
+    np.testing.assert_array_equal(ordered_from_ring(host(cs), heads[5 % 2].cpu().numpy()), cr)
 
 
 def test_extreme_delta():
