@@ -27,26 +27,34 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# Peaks used for the roofline fractions.
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
-# Vector ALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32 T lane-slots/s.
-# (The 157.3 TFLOP/s fp32 vector figure is this rate x 2 for FMA x 2 for packed fp32.)
-# One transcendental (v_exp/v_log/v_rcp_f32) costs two slots: measured half rate.
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Peaks used for the roofline fractions (MI355X published figures).
+HBM_PEAK_GBS = 8000.0  # HBM3E, GB/s
+# Vector ALU: the published fp32 vector rate, 157.3 TFLOP/s, is 256 CUs x 4 SIMDs x 32 lanes
+# x 2.4 GHz FMA lane-operations (2 flops each) = 78.64 T lane-slots/s.  Plain (unpacked)
+# v_fma_f32 reaches it: the issue-rate probe (bench.py --valu-probe) measures one wave64 FMA
+# every 2.13-2.16 SIMD cycles at the clock of the run.  A slot is one lane-FMA.
+VALU_PEAK_TSLOTS = 256 * 4 * 32 * 2.4e9 / 1e12
+# A transcendental (v_exp_f32, v_log_f32, v_rcp_f32) issues at a quarter of that rate (probe:
+# 8.14 cycles per wave64 v_exp_f32) and does not overlap the FMAs (probe: a 1:4 mix costs at
+# least the sum of its parts), so it counts as 4 slots.
+TRANS_SLOTS = 4
+TRANS_PEAK_TOPS = VALU_PEAK_TSLOTS / TRANS_SLOTS
 
 D_INNER, D_STATE = 4096, 16
-# Algorithmic work per token.channel (prefill and decode alike):
-#   per state n (16x): mul (Delta*A) + exp (2 slots) + mul (Delta*u*B) + fma (state) + fma (readout) = 6
-#   per token.channel: conv 4 fma; SiLU 6 (exp 2, add, rcp 2, mul); softplus 5 (exp 2, add, log 2);
-#   dt+bias 1; Delta*u 1; D*u 1; gate 7 (SiLU(z) 6 + mul)                                          = 25
-SLOTS_PER_TC = 16 * 6 + 25
-# Algorithmic work of the gradients per token.channel: one forward recompute without the
-# readout (per state mul, exp (2 slots), mul, fma = 5; front end 17: conv 4, SiLU 6, softplus
-# 5, Delta*u 2), the reverse per state (the readout y fma, G fma, G*Abar, *h_{t-1}, the
-# dDelta, dA and dB-sum fmas, the dB and dC products = 9) and per token.channel (dz 8 with
-# its sigmoid, gy 1, dD 1, du 2, softplus' 5, SiLU' 7, conv transpose 4, dconv_w 4, dconv_b
-# 1 = 33): 16 * 14 + 17 + 33 = 274.
-BWD_SLOTS_PER_TC = 16 * 14 + 17 + 33
+# Algorithmic work per token.channel (prefill and decode alike), in slots:
+#   per state n (16x): mul (Delta*A) + exp (4) + mul (Delta*u*B) + fma (state) + fma (readout) = 8
+#   per token.channel: conv 4 fma; SiLU 10 (exp 4, add, rcp 4, mul); softplus 10 (dt+bias, exp 4,
+#   add, log 4); Delta*u 1; D*u 1; gate 11 (SiLU(z) 10 + mul)                                     = 37
+SLOTS_PER_TC = 16 * (4 + TRANS_SLOTS) + 37
+TRANS_PER_TC = 16 + 6  # 16 exp for Abar; exp + log (softplus); exp + rcp (SiLU) twice
+# Algorithmic work of the gradients per token.channel, in slots: one forward recompute
+# without the readout (per state mul, exp 4, mul, fma = 7; front end 26: conv 4, SiLU 10,
+# softplus 10 with the dt+bias add, Delta*u 2), the reverse per state (the readout y fma, G
+# fma, G*Abar, *h_{t-1}, the dDelta, dA and dB-sum fmas, the dB and dC products = 9) and per
+# token.channel (dz 12: SiLU(z)' with its sigmoid (exp, rcp) and 4 more; gy 1, dD 1, du 2;
+# softplus' 9: a sigmoid (exp, rcp) and a mul; SiLU' 11: a sigmoid (exp, rcp) and 3 more;
+# conv transpose 4, dconv_w 4, dconv_b 1 = 45): 16 * 16 + 26 + 45 = 327.
+BWD_SLOTS_PER_TC = 16 * (7 + 9) + 26 + 45
 # Algorithmic HBM bytes per token for bf16 I/O: read x, dt, z (2 B each per channel), write y
 # (2 B per channel), read B and C (2 B each per state).
 BYTES_PER_TOKEN = 8 * D_INNER + 4 * D_STATE
@@ -628,6 +636,8 @@ def main():
     achieved_alu = slots / t_step / 1e12
     hbm_bytes = tokens * BYTES_PER_TOKEN
     achieved_hbm = hbm_bytes / t_step / 1e9
+    trans = tokens * D_INNER * TRANS_PER_TC
+    achieved_trans = trans / t_step / 1e12
     line = {
         "metric": "selective-scan Mtok/s at L=128K,d_inner=4096",
         "value": round(value, 3),
@@ -647,9 +657,17 @@ def main():
         "roofline": {"bound": "alu", "achieved": round(achieved_alu, 3), "peak": round(VALU_PEAK_TSLOTS, 3),
                      "unit": "T VALU-slots/s", "frac": round(achieved_alu / VALU_PEAK_TSLOTS, 4),
                      "traffic": committed_traffic("rows_split_prompt128k_traffic.md"),
-                     "work_per_launch": "%d tokens x %d channels x %d slots" % (tokens, D_INNER, SLOTS_PER_TC)},
+                     "work_per_launch": "%d tokens x %d channels x %d slots (a slot is one lane-FMA; a "
+                                        "transcendental counts %d)" % (tokens, D_INNER, SLOTS_PER_TC, TRANS_SLOTS),
+                     "peak_derivation": "256 CUs x 4 SIMDs x 32 fp32 FMA lanes x 2.4 GHz = the published "
+                                        "157.3 TFLOP/s fp32 vector rate / 2"},
         "roofline_hbm": {"achieved": round(achieved_hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved_hbm / HBM_PEAK_GBS, 4), "bytes_per_launch": hbm_bytes},
+        "roofline_trans": {"achieved": round(achieved_trans, 3), "peak": round(TRANS_PEAK_TOPS, 3),
+                           "unit": "T transcendental ops/s", "frac": round(achieved_trans / TRANS_PEAK_TOPS, 4),
+                           "ops_per_launch": trans,
+                           "note": "the exp-throughput bound alone (22 per token.channel at a quarter of the "
+                                   "FMA rate); the VALU bound above includes it"},
         "tok_ch_per_s": tokens * D_INNER / t_step,
         "kernel": "samba_scan_prefill (one kernel launch per step)",
     }
@@ -659,6 +677,8 @@ def main():
         ctl = decode_summary(bench_decode(args, dev, S=1024, P=16, warm_prefill=False, steps=1024))
         ctl["note"] = "control: random start state, inputs from a pool of 16 steps; state exceeds the MALL"
         line["decode_s1024"] = ctl
+    if not args.prefill_only:
+        line["valu_probe"] = valu_probe()
     if not args.prefill_only and not args.no_extra:
         line["extra"] = bench_extra(dev)
         line["extra"]["gemm"] = bench_gemm(dev, 10, 3)
