@@ -20,7 +20,8 @@
  * Hybrid Mamba & Sliding Window Architecture", "Step 1: The Selective State Space (Mamba)
  * Layer".  The scan entry points take x, dt, B, C and z as inputs; the projections that
  * make them (and the layer's output projection, the attention and MLP projections) are
- * bf16 matrix-core GEMMs of their own, samba_gemm below.
+ * bf16 matrix-core GEMMs of their own, samba_gemm below.  samba_scan_prefill_u /
+ * samba_scan_varlen_u take the post-conv activation u instead of x.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -131,6 +132,26 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
                                const float *h0, const void *conv0,
                                void *out, float *h_final, void *conv_final,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same two calls from a precomputed u = SiLU(conv_b + sum_k conv_w[k] x_{t-3+k}) instead
+ * of x: in a full Mamba layer, Delta, B and C are projections of u (page 1 section 3.4,
+ * "Input-Dependent SSM Parameters": x_proj reads u), so u already exists -- samba_conv_silu
+ * computes it, with the outgoing conv history -- before the scan runs.  The scan then skips
+ * the conv: Delta = softplus(dt + dt_bias), h_t = exp(Delta A) h_{t-1} + Delta B_t u_t,
+ * out = (C_t . h_t + D u_t) SiLU(z_t).
+ *   u        [batch][seqlen][d_inner] (prefill_u) or [total_tokens][d_inner] (varlen_u), io dtype
+ *   params   A required; D and dt_bias as above; conv_w and conv_b are not read (may be NULL)
+ * Every other argument as for samba_scan_prefill / samba_scan_varlen (there is no conv
+ * history in or out). */
+samba_status samba_scan_prefill_u(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                                  const void *u, const void *dt, const void *B, const void *C,
+                                  const void *z, const samba_params *params, const float *h0,
+                                  void *out, float *h_final, void *workspace, size_t workspace_bytes, void *stream);
+samba_status samba_scan_varlen_u(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
+                                 int d_inner, int d_state, samba_dtype io, const void *u, const void *dt,
+                                 const void *B, const void *C, const void *z, const samba_params *params,
+                                 const float *h0, void *out, float *h_final, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* One decode step: one new token for each of nseq resident sequences (the constant
  * per-token cost of the fixed-size state, page 1 section 5 "Experimental Analysis",

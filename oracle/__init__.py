@@ -59,6 +59,8 @@ def _declare(lib):
     lib.oracle_prefill.argtypes = [I, I, I, I] + [P] * 13
     lib.oracle_varlen.argtypes = [I, P, I, I] + [P] * 13
     lib.oracle_decode_step.argtypes = [I, I, I] + [P] * 13
+    lib.oracle_scan_u_varlen.argtypes = [I, P, I, I] + [P] * 10
+    lib.oracle_scan_u_varlen.restype = None
     lib.oracle_conv_silu_varlen.argtypes = [I, P, I, P, P, P, P, P]
     lib.oracle_conv_silu_varlen.restype = None
     lib.oracle_backward.argtypes = [I, P, I, I] + [P] * 27
@@ -182,6 +184,37 @@ def varlen(cu_seqlens, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=Non
     lib.oracle_varlen(nseq, _ptr(cu), nch, N, _ptr(xs), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
                       _ptr(Dp), _ptr(bp), _ptr(wp), _ptr(cbp), _ptr(h), _ptr(hist), _ptr(y))
     return y, h, hist
+
+
+def scan_u(u, dt, B, C, z, A, Dskip, dt_bias, h0=None, cu_seqlens=None, chans=None):
+    """The scan from a precomputed u = SiLU(conv(x)) (no conv).  Fixed length: u, dt, z
+    [b, L, D], B, C [b, L, N], h0 [b, D, N] or None.  Packed: u, dt, z [T, D], B, C [T, N] with
+    cu_seqlens [nseq+1], h0 [nseq, D, N] or None.  Returns (y shaped like u restricted to
+    ``chans``, h [nseq, nch, N]) in float64."""
+    lib = _load()
+    u = np.asarray(u)
+    if cu_seqlens is None:
+        b, L, D = u.shape
+        cu = (np.arange(b + 1) * L).astype(np.int32)
+        flat = lambda a: None if a is None else np.asarray(a).reshape(b * L, np.asarray(a).shape[-1])
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        flat = lambda a: None if a is None else np.asarray(a)
+    nseq = cu.shape[0] - 1
+    sel = (lambda a: a) if chans is None else (lambda a: a[:, chans])
+    us, dts = _f64(sel(flat(u))), _f64(sel(flat(dt)))
+    zs = None if z is None else _f64(sel(flat(z)))
+    Bs, Cs = _f64(flat(B)), _f64(flat(C))
+    nch, N = us.shape[1], Bs.shape[1]
+    Ap, Dp, bp, _, _ = _params(A, Dskip, dt_bias, None, None, chans)
+    h = np.zeros((nseq, nch, N)) if h0 is None else \
+        _f64(np.asarray(h0)[:, chans, :] if chans is not None else h0).copy()
+    y = np.empty_like(us)
+    lib.oracle_scan_u_varlen(nseq, _ptr(cu), nch, N, _ptr(us), _ptr(dts), _ptr(Bs), _ptr(Cs), _ptr(zs), _ptr(Ap),
+                             _ptr(Dp), _ptr(bp), _ptr(h), _ptr(y))
+    if cu_seqlens is None:
+        y = y.reshape(u.shape[0], u.shape[1], nch)
+    return y, h
 
 
 def decode_step(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h, hist, chans=None):

@@ -148,6 +148,51 @@ void oracle_varlen(int nseq, const int32_t *cu, int nch, int N,
     }
 }
 
+/*
+ * The scan from a precomputed activation U (the post-conv, post-SiLU input; [P1] "Input-
+ * Dependent SSM Parameters": in a full layer Delta, B and C are projections of U, so U is
+ * computed before the scan).  Packed sequences as in oracle_varlen (fixed length: cu[s] =
+ * s*L); per channel and token, in the order of [P1] section 3.4:
+ *   Delta = Softplus(dt + b);  Z_t = exp(Delta A) . Z_{t-1} + Delta (B_t x U_t);
+ *   Y_t = Z_t C_t + D U_t;     O = Y . SiLU(z)
+ * u, dt, z, y [T][nch]; B, C [T][N]; h [nseq][nch][N] in: initial state, out: final state.
+ */
+void oracle_scan_u_varlen(int nseq, const int32_t *cu, int nch, int N,
+                          const double *u, const double *dt, const double *B, const double *C,
+                          const double *z, const double *A, const double *Dskip,
+                          const double *dt_bias, double *h, double *y)
+{
+    int s;
+    for (s = 0; s < nseq; ++s) {
+        const int t0 = cu[s], t1 = cu[s + 1];
+        double *hseq = h + (size_t)s * nch * N;
+        int d;
+#pragma omp parallel for schedule(static)
+        for (d = 0; d < nch; ++d) {
+            double hs[64];
+            const double dsk = Dskip ? Dskip[d] : 0.0;
+            const double bias = dt_bias ? dt_bias[d] : 0.0;
+            int n, t;
+            for (n = 0; n < N; ++n) hs[n] = hseq[(size_t)d * N + n];
+            for (t = t0; t < t1; ++t) {
+                const size_t ix = (size_t)t * nch + d;
+                const double uu = u[ix];
+                const double delta = oracle_softplus(dt[ix] + bias);
+                const double du = delta * uu;
+                double acc = 0.0;
+                for (n = 0; n < N; ++n) {
+                    const double abar = exp(delta * A[(size_t)d * N + n]);
+                    hs[n] = abar * hs[n] + du * B[(size_t)t * N + n];
+                    acc += C[(size_t)t * N + n] * hs[n];
+                }
+                acc += dsk * uu;
+                y[ix] = z ? acc * oracle_silu(z[ix]) : acc;
+            }
+            for (n = 0; n < N; ++n) hseq[(size_t)d * N + n] = hs[n];
+        }
+    }
+}
+
 /* One decode step for nseq sequences: token arrays are [nseq][nch] (B, C: [nseq][N]);
  * h [nseq][nch][N] and hist [nseq][3][nch] are the resident state, updated in place.
  * This is the same recurrence with L = 1 ([P1] section 5, constant per-token

@@ -5,7 +5,7 @@ A thin ctypes layer over ``libsamba_scan.so`` (C ABI declared in
 and the current HIP stream; every step of the computation runs in the library's HIP
 kernels.  There is no CPU or PyTorch fallback: if the library is missing the calls raise.
 
-Entry points mirror the C ABI: ``prefill``, ``varlen``, ``decode``, ``conv_silu``,
+Entry points mirror the C ABI: ``prefill``, ``prefill_u``, ``varlen``, ``varlen_u``, ``decode``, ``conv_silu``,
 ``backward``, ``swa`` (sliding window attention), ``swa_decode`` and ``swa_kv_fill``.
 """
 from __future__ import annotations
@@ -17,7 +17,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["prefill", "varlen", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill", "gemm", "rmsnorm",
+__all__ = ["prefill", "prefill_u", "varlen", "varlen_u", "decode", "conv_silu", "backward", "swa", "swa_decode", "swa_kv_fill", "gemm", "rmsnorm",
            "decode_step", "decode_step_workspace_bytes",
            "workspace_bytes", "lib_path", "SambaError", "version"]
 
@@ -77,6 +77,11 @@ def load():
         lib.samba_scan_workspace_bytes.argtypes = [I, I, I, I]
         lib.samba_scan_prefill.restype = I
         lib.samba_scan_prefill.argtypes = [I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P, P, Z, P]
+        lib.samba_scan_prefill_u.restype = I
+        lib.samba_scan_prefill_u.argtypes = [I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, Z, P]
+        lib.samba_scan_varlen_u.restype = I
+        lib.samba_scan_varlen_u.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, Z,
+                                            P]
         lib.samba_scan_varlen.restype = I
         lib.samba_scan_varlen.argtypes = [I, P, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(Params), P, P, P, P, P,
                                           P, Z, P]
@@ -145,9 +150,9 @@ def _shape(t, shape, name):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
-def _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N):
+def _params(A, Dskip, dt_bias, conv_w, conv_b, dev, D, N, needs_conv=True):
     f = torch.float32
-    if A is None or conv_w is None:
+    if A is None or (needs_conv and conv_w is None):
         raise ValueError("A and conv_w are required")
     _shape(A, (D, N), "A")
     _shape(Dskip, (D,), "Dskip")
@@ -220,6 +225,71 @@ def prefill(x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=No
         _ptr(ws, "workspace"), wsb, _stream(dev))
     _check(st)
     return out, h_final, conv_final
+
+
+def prefill_u(u, dt, B, C, z, A, Dskip, dt_bias, h0=None, *, out=None, h_final=None, want_state=True,
+              workspace=None):
+    """Fixed-length prefill from a precomputed u = SiLU(conv(x)) (samba_scan_prefill_u: the
+    activation a full layer computes once for x_proj, see conv_silu).  u, dt, z: [b, L, D];
+    B, C: [b, L, N]; A [D, N], Dskip/dt_bias [D] float32; h0 [b, D, N] or None.  Returns
+    (out, h_final); h_final is None when want_state is False."""
+    dev = _gpu_device(u)
+    b, L, D = u.shape
+    N = B.shape[-1]
+    io = _io(u)
+    if out is None:
+        out = torch.empty_like(u)
+    if want_state and h_final is None:
+        h_final = torch.empty((b, D, N), dtype=torch.float32, device=dev)
+    for t, n in ((dt, "dt"), (z, "z"), (out, "out")):
+        _shape(t, (b, L, D), n)
+    _shape(B, (b, L, N), "B")
+    _shape(C, (b, L, N), "C")
+    _shape(h0, (b, D, N), "h0")
+    _shape(h_final, (b, D, N), "h_final")
+    p = _params(A, Dskip, dt_bias, None, None, dev, D, N, needs_conv=False)
+    ws, wsb = _workspace(b, L, D, N, dev, workspace)
+    st = load().samba_scan_prefill_u(
+        b, L, D, N, io, _ptr(u, "u", u.dtype, dev), _ptr(dt, "dt", u.dtype, dev), _ptr(B, "B", u.dtype, dev),
+        _ptr(C, "C", u.dtype, dev), _ptr(z, "z", u.dtype, dev), ctypes.byref(p),
+        _ptr(h0, "h0", torch.float32, dev), _ptr(out, "out", u.dtype, dev),
+        _ptr(h_final, "h_final", torch.float32, dev), _ptr(ws, "workspace"), wsb, _stream(dev))
+    _check(st)
+    return out, h_final
+
+
+def varlen_u(cu_seqlens, u, dt, B, C, z, A, Dskip, dt_bias, h0=None, *, max_seqlen=None, out=None, h_final=None,
+             workspace=None):
+    """Packed variable-length prefill from a precomputed u (samba_scan_varlen_u); layouts as
+    for varlen.  Returns (out, h_final [nseq, D, N])."""
+    dev = _gpu_device(u)
+    T, D = u.shape
+    N = B.shape[-1]
+    nseq = cu_seqlens.numel() - 1
+    io = _io(u)
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+    if out is None:
+        out = torch.empty_like(u)
+    if h_final is None:
+        h_final = torch.empty((nseq, D, N), dtype=torch.float32, device=dev)
+    for t, n in ((dt, "dt"), (z, "z"), (out, "out")):
+        _shape(t, (T, D), n)
+    _shape(B, (T, N), "B")
+    _shape(C, (T, N), "C")
+    _shape(cu_seqlens, (nseq + 1,), "cu_seqlens")
+    _shape(h0, (nseq, D, N), "h0")
+    _shape(h_final, (nseq, D, N), "h_final")
+    p = _params(A, Dskip, dt_bias, None, None, dev, D, N, needs_conv=False)
+    ws, wsb = _workspace(nseq, max_seqlen, D, N, dev, workspace)
+    st = load().samba_scan_varlen_u(
+        nseq, _ptr(cu_seqlens, "cu_seqlens", torch.int32, dev), T, int(max_seqlen), D, N, io,
+        _ptr(u, "u", u.dtype, dev), _ptr(dt, "dt", u.dtype, dev), _ptr(B, "B", u.dtype, dev),
+        _ptr(C, "C", u.dtype, dev), _ptr(z, "z", u.dtype, dev), ctypes.byref(p),
+        _ptr(h0, "h0", torch.float32, dev), _ptr(out, "out", u.dtype, dev),
+        _ptr(h_final, "h_final", torch.float32, dev), _ptr(ws, "workspace"), wsb, _stream(dev))
+    _check(st)
+    return out, h_final
 
 
 def varlen(cu_seqlens, x, dt, B, C, z, A, Dskip, dt_bias, conv_w, conv_b, h0=None, conv0=None, *,

@@ -24,7 +24,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;  // loop body: kUnroll groups of 8 chains
 
-enum Kind { kFma = 0, kExp = 1, kMix = 2, kFmac = 3, kMixWaves = 4, kFmaLat = 5, kExpLat = 6 };
+enum Kind {
+    kFma = 0, kExp = 1, kMix = 2, kFmac = 3, kMixWaves = 4, kFmaLat = 5, kExpLat = 6,
+    kAddDpp = 7, kMulBcast = 8, kCndmask = 9, kMul = 10
+};
 
 __device__ inline void fma8(float (&v)[8], float m, float c)
 {
@@ -35,6 +38,30 @@ __device__ inline void fmac8(float (&v)[8], float m, float c)
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("v_fmac_f32 %0, %1, %2" : "+v"(v[i]) : "v"(m), "v"(c));
+}
+// Cross-lane forms used by the scan kernels (each chain reads a register last written 8
+// instructions earlier, beyond the 2 wait states a DPP read of a fresh VALU result needs).
+__device__ inline void add_dpp8(float (&v)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        asm volatile("v_add_f32_dpp %0, %0, %0 row_shl:1 row_mask:0xf bank_mask:0xf bound_ctrl:1" : "+v"(v[i]));
+}
+__device__ inline void mul_bcast8(float (&v)[8], float m)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        asm volatile("v_mul_f32_dpp %0, %0, %1 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1" : "+v"(v[i]) : "v"(m));
+}
+__device__ inline void cndmask8(float (&v)[8], float o)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("v_cndmask_b32_e64 %0, %0, %1, s[0:1]" : "+v"(v[i]) : "v"(o) : "s0", "s1");
+}
+__device__ inline void mul8(float (&v)[8], float m)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("v_mul_f32_e32 %0, %1, %0" : "+v"(v[i]) : "v"(m));
 }
 __device__ inline void exp8(float (&v)[8])
 {
@@ -86,6 +113,10 @@ __global__ __launch_bounds__(512) void probe_kernel(int iters, float seed, float
                     fma8(v, m, c);
                 }
             }
+            if (kKind == kAddDpp) add_dpp8(v);
+            if (kKind == kMulBcast) mul_bcast8(v, m);
+            if (kKind == kCndmask) cndmask8(v, c);
+            if (kKind == kMul) mul8(v, m);
             if (kKind == kFmaLat) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(v[0]) : "v"(m), "v"(c));
@@ -119,7 +150,9 @@ extern "C" {
 //   4 the same 1 : 4 mix split between waves (workgroups of 512 threads: on every SIMD one
 //     wave of exponentials beside one of FMAs);
 //   5 one dependent v_fma_f32 chain per lane; 6 one dependent v_exp_f32 chain per lane
-//     (use one workgroup of 64 threads per SIMD for these two).
+//     (use one workgroup of 64 threads per SIMD for these two);
+//   7 v_add_f32 with a DPP row_shl source, 8 v_mul_f32 with a DPP row_newbcast source,
+//   9 v_cndmask_b32 (VOP3, SGPR-pair mask), 10 v_mul_f32 (VOP2): 8 chains per lane.
 // Returns 0 on success.  Outputs:
 //   out[0] seconds of the launch (HIP events)
 //   out[1] lane-instructions executed (an exponential counts as one)
@@ -127,7 +160,7 @@ extern "C" {
 //   out[3] median shader clock over the workgroups in GHz (s_memtime ticks / real time)
 int samba_probe_rates(int kind, int workgroups, int iters, double *out)
 {
-    if (kind < 0 || kind > 6 || workgroups < 1 || iters < 1 || out == nullptr) return 1;
+    if (kind < 0 || kind > 10 || workgroups < 1 || iters < 1 || out == nullptr) return 1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 2;
     int wall_khz = 0;
@@ -150,6 +183,10 @@ int samba_probe_rates(int kind, int workgroups, int iters, double *out)
         case kMixWaves: probe_kernel<kMixWaves><<<workgroups, 512>>>(n, 0.5f, sink, stamps); break;
         case kFmaLat: probe_kernel<kFmaLat><<<workgroups, 64>>>(n, 0.5f, sink, stamps); break;
         case kExpLat: probe_kernel<kExpLat><<<workgroups, 64>>>(n, 0.5f, sink, stamps); break;
+        case kAddDpp: probe_kernel<kAddDpp><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
+        case kMulBcast: probe_kernel<kMulBcast><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
+        case kCndmask: probe_kernel<kCndmask><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
+        case kMul: probe_kernel<kMul><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         default: probe_kernel<kFmac><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         }
     };

@@ -103,7 +103,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     } while (0)
 
 samba_status check_common(const char *fn, int d_inner, int d_state, samba_dtype io,
-                          const samba_params *p)
+                          const samba_params *p, bool needs_conv = true)
 {
     if (d_inner < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: d_inner=%d must be >= 1", fn, d_inner);
     if (d_state < 1) return fail(SAMBA_ERR_INVALID_ARG, "%s: d_state=%d must be >= 1", fn, d_state);
@@ -113,7 +113,7 @@ samba_status check_common(const char *fn, int d_inner, int d_state, samba_dtype 
     if (io != SAMBA_F32 && io != SAMBA_BF16) return fail(SAMBA_ERR_INVALID_ARG, "%s: unknown io dtype %d", fn, (int)io);
     if (p == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: params is NULL", fn);
     REQUIRE_PTR(p->A, "params->A");
-    REQUIRE_PTR(p->conv_w, "params->conv_w");
+    if (needs_conv) REQUIRE_PTR(p->conv_w, "params->conv_w");
     OPTIONAL_PTR(p->D, "params->D");
     OPTIONAL_PTR(p->dt_bias, "params->dt_bias");
     OPTIONAL_PTR(p->conv_b, "params->conv_b");
@@ -184,19 +184,19 @@ size_t samba_scan_workspace_bytes(int nseq, int max_seqlen, int d_inner, int d_s
     return 0;
 }
 
-samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
-                                const void *x, const void *dt, const void *B, const void *C,
-                                const void *z, const samba_params *params,
-                                const float *h0, const void *conv0,
-                                void *out, float *h_final, void *conv_final,
-                                void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Fixed-length prefill, x (pre-conv) or u (u_in) as the token input.
+samba_status prefill_impl(const char *fn, bool u_in, int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                          const void *x, const void *dt, const void *B, const void *C, const void *z,
+                          const samba_params *params, const float *h0, const void *conv0, void *out, float *h_final,
+                          void *conv_final, void *stream)
 {
-    const char *fn = "samba_scan_prefill";
-    (void)workspace;
-    (void)workspace_bytes;
     if (batch < 0 || seqlen < 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: batch=%d seqlen=%d must be >= 0", fn, batch, seqlen);
-    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    samba_status st = check_common(fn, d_inner, d_state, io, params, !u_in);
     if (st != SAMBA_OK) return st;
     if (batch == 0) {
         g_err.clear();
@@ -206,7 +206,7 @@ samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state,
         return fail(SAMBA_ERR_UNSUPPORTED, "%s: batch*seqlen=%zu exceeds 2^31-1 tokens", fn,
                     (size_t)batch * (size_t)seqlen);
     if (seqlen > 0) {
-        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(x, u_in ? "u" : "x");
         REQUIRE_PTR(dt, "dt");
         REQUIRE_PTR(B, "B");
         REQUIRE_PTR(C, "C");
@@ -219,25 +219,21 @@ samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state,
     OPTIONAL_PTR(conv_final, "conv_final");
     samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
+    a.u_in = u_in;
     launch_scan(a, io, stream);
     return launched(fn);
 }
 
-samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
-                               int d_inner, int d_state, samba_dtype io,
-                               const void *x, const void *dt, const void *B, const void *C,
-                               const void *z, const samba_params *params,
-                               const float *h0, const void *conv0,
-                               void *out, float *h_final, void *conv_final,
-                               void *workspace, size_t workspace_bytes, void *stream)
+// Packed variable-length prefill, x (pre-conv) or u (u_in) as the token input.
+samba_status varlen_impl(const char *fn, bool u_in, int nseq, const int32_t *cu_seqlens, int total_tokens,
+                         int max_seqlen, int d_inner, int d_state, samba_dtype io, const void *x, const void *dt,
+                         const void *B, const void *C, const void *z, const samba_params *params, const float *h0,
+                         const void *conv0, void *out, float *h_final, void *conv_final, void *stream)
 {
-    const char *fn = "samba_scan_varlen";
-    (void)workspace;
-    (void)workspace_bytes;
     if (nseq < 0 || total_tokens < 0 || max_seqlen < 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: nseq=%d total_tokens=%d max_seqlen=%d must be >= 0", fn, nseq,
                     total_tokens, max_seqlen);
-    samba_status st = check_common(fn, d_inner, d_state, io, params);
+    samba_status st = check_common(fn, d_inner, d_state, io, params, !u_in);
     if (st != SAMBA_OK) return st;
     if (nseq == 0) {
         g_err.clear();
@@ -247,7 +243,7 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
     if (max_seqlen > total_tokens)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total_tokens=%d", fn, max_seqlen, total_tokens);
     if (total_tokens > 0) {
-        REQUIRE_PTR(x, "x");
+        REQUIRE_PTR(x, u_in ? "u" : "x");
         REQUIRE_PTR(dt, "dt");
         REQUIRE_PTR(B, "B");
         REQUIRE_PTR(C, "C");
@@ -261,8 +257,63 @@ samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_to
     samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.total = total_tokens;
+    a.u_in = u_in;
     launch_scan(a, io, stream);
     return launched(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+samba_status samba_scan_prefill(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                                const void *x, const void *dt, const void *B, const void *C,
+                                const void *z, const samba_params *params,
+                                const float *h0, const void *conv0,
+                                void *out, float *h_final, void *conv_final,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_impl("samba_scan_prefill", false, batch, seqlen, d_inner, d_state, io, x, dt, B, C, z, params, h0,
+                        conv0, out, h_final, conv_final, stream);
+}
+
+samba_status samba_scan_prefill_u(int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
+                                  const void *u, const void *dt, const void *B, const void *C,
+                                  const void *z, const samba_params *params, const float *h0,
+                                  void *out, float *h_final, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return prefill_impl("samba_scan_prefill_u", true, batch, seqlen, d_inner, d_state, io, u, dt, B, C, z, params, h0,
+                        nullptr, out, h_final, nullptr, stream);
+}
+
+samba_status samba_scan_varlen(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
+                               int d_inner, int d_state, samba_dtype io,
+                               const void *x, const void *dt, const void *B, const void *C,
+                               const void *z, const samba_params *params,
+                               const float *h0, const void *conv0,
+                               void *out, float *h_final, void *conv_final,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return varlen_impl("samba_scan_varlen", false, nseq, cu_seqlens, total_tokens, max_seqlen, d_inner, d_state, io, x,
+                       dt, B, C, z, params, h0, conv0, out, h_final, conv_final, stream);
+}
+
+samba_status samba_scan_varlen_u(int nseq, const int32_t *cu_seqlens, int total_tokens, int max_seqlen,
+                                 int d_inner, int d_state, samba_dtype io, const void *u, const void *dt,
+                                 const void *B, const void *C, const void *z, const samba_params *params,
+                                 const float *h0, void *out, float *h_final, void *workspace,
+                                 size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return varlen_impl("samba_scan_varlen_u", true, nseq, cu_seqlens, total_tokens, max_seqlen, d_inner, d_state, io,
+                       u, dt, B, C, z, params, h0, nullptr, out, h_final, nullptr, stream);
 }
 
 samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype io,

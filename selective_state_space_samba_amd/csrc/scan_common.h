@@ -40,6 +40,9 @@ struct ScanArgs {
     // receives (head + 1) mod 3.  head_in == nullptr: the history is stored oldest first.
     const int32_t *head_in;
     int32_t *head_out;
+    // Prefill / varlen: x holds u = SiLU(conv(x)), computed beforehand; the conv, its
+    // parameters, conv0 and conv_final are not used.
+    bool u_in;
 };
 
 // Ring slot of the history entry k (0 = oldest) for a head value from device memory.

@@ -73,7 +73,9 @@ struct BcWords {
 
 }  // namespace lane
 
-template <class Io, bool kFullN>
+// kUIn: x holds u = SiLU(conv(x)) already (the conv, its parameters and the history are
+// not used).
+template <class Io, bool kFullN, bool kUIn>
 __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
 {
     using namespace lane;
@@ -95,9 +97,9 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
         Ad[n] = on ? a.A[static_cast<size_t>(d) * N + n] : 0.0f;
         h[n] = (on && a.h0 != nullptr) ? a.h0[hbase + n] : 0.0f;
     }
-    const float w0 = a.conv_w[d * kConvK + 0], w1 = a.conv_w[d * kConvK + 1];
-    const float w2 = a.conv_w[d * kConvK + 2], w3 = a.conv_w[d * kConvK + 3];
-    const float cb = a.conv_b ? a.conv_b[d] : 0.0f;
+    const float w0 = kUIn ? 0.0f : a.conv_w[d * kConvK + 0], w1 = kUIn ? 0.0f : a.conv_w[d * kConvK + 1];
+    const float w2 = kUIn ? 0.0f : a.conv_w[d * kConvK + 2], w3 = kUIn ? 0.0f : a.conv_w[d * kConvK + 3];
+    const float cb = (!kUIn && a.conv_b) ? a.conv_b[d] : 0.0f;
     const float dsk = a.Dskip ? a.Dskip[d] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
     const size_t cbase = static_cast<size_t>(s) * 3 * D + d;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
     const size_t e1 = cbase + static_cast<size_t>(ring_slot(hd, 1)) * D;
     const size_t e2 = cbase + static_cast<size_t>(ring_slot(hd, 2)) * D;
     float x0 = 0.0f, x1 = 0.0f, x2 = 0.0f;  // x_{t-3}, x_{t-2}, x_{t-1}
-    if (a.conv0 != nullptr) {
+    if (!kUIn && a.conv0 != nullptr) {
         x0 = Io::ld(a.conv0, e0);
         x1 = Io::ld(a.conv0, e1);
         x2 = Io::ld(a.conv0, e2);
@@ -120,14 +122,19 @@ __global__ __launch_bounds__(256) void lane_scan_kernel(ScanArgs a)
 
     // One token of the recurrence; B_t / C_t in b / c.
     auto step = [&](float xv, float dtv, float zv, const float *b, const float *c) -> float {
-        float pre = __builtin_fmaf(w0, x0, cb);
-        pre = __builtin_fmaf(w1, x1, pre);
-        pre = __builtin_fmaf(w2, x2, pre);
-        pre = __builtin_fmaf(w3, xv, pre);
-        const float u = silu(pre);
-        x0 = x1;
-        x1 = x2;
-        x2 = xv;
+        float u;
+        if constexpr (kUIn) {
+            u = xv;
+        } else {
+            float pre = __builtin_fmaf(w0, x0, cb);
+            pre = __builtin_fmaf(w1, x1, pre);
+            pre = __builtin_fmaf(w2, x2, pre);
+            pre = __builtin_fmaf(w3, xv, pre);
+            u = silu(pre);
+            x0 = x1;
+            x1 = x2;
+            x2 = xv;
+        }
         // Delta in log2 units, then Delta * u
         const float lg = softplus_log2(dtv + bias);
         const float du = (lg * kLn2) * u;
@@ -226,7 +233,7 @@ done:
         for (int n = 0; n < kMaxState; ++n)
             if (kFullN || n < N) a.h_final[hbase + n] = h[n];
     }
-    if (a.conv_final != nullptr) {
+    if (!kUIn && a.conv_final != nullptr) {
         if (a.head_in != nullptr) {
             // ring after one token: the new head is the old head + 1, so the entries
             // (oldest first) go to slots head + 1, head + 2 and head
@@ -247,17 +254,21 @@ inline void launch_lane_scan(const ScanArgs &a, samba_dtype io, hipStream_t stre
     const dim3 block(256);
     const dim3 grid((a.D + 255) / 256, a.nseq);
     const bool full = a.N == kMaxState;
+#define SAMBA_LANE(IO, FULL, UIN) lane_scan_kernel<IO, FULL, UIN><<<grid, block, 0, stream>>>(a)
     if (io == SAMBA_BF16) {
-        if (full)
-            lane_scan_kernel<IoBf16, true><<<grid, block, 0, stream>>>(a);
-        else
-            lane_scan_kernel<IoBf16, false><<<grid, block, 0, stream>>>(a);
+        if (a.u_in) {
+            if (full) SAMBA_LANE(IoBf16, true, true); else SAMBA_LANE(IoBf16, false, true);
+        } else {
+            if (full) SAMBA_LANE(IoBf16, true, false); else SAMBA_LANE(IoBf16, false, false);
+        }
     } else {
-        if (full)
-            lane_scan_kernel<IoF32, true><<<grid, block, 0, stream>>>(a);
-        else
-            lane_scan_kernel<IoF32, false><<<grid, block, 0, stream>>>(a);
+        if (a.u_in) {
+            if (full) SAMBA_LANE(IoF32, true, true); else SAMBA_LANE(IoF32, false, true);
+        } else {
+            if (full) SAMBA_LANE(IoF32, true, false); else SAMBA_LANE(IoF32, false, false);
+        }
     }
+#undef SAMBA_LANE
 }
 
 }  // namespace samba

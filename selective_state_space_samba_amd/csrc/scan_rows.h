@@ -126,6 +126,7 @@ struct Smem {
     static constexpr int kBPitch = kStage + 4;   // LDS pitch of one state's B column (floats)
     static constexpr int kTokPitch = tok_pitch_bytes<T>();
     static constexpr bool kCSwizzle = true;      // C rows in the swizzled token-row layout
+    static constexpr bool kCCols = false;        // C as token rows (not columns)
     float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
     float crow[2][kStage][kPPitch];              // [buffer][token][state]: C rows
     float p[kWaves][kRowsPerWave * kRowPitch];   // [wave][row][token][state]: states h_t (padded)
@@ -183,7 +184,9 @@ struct Stager {
         }
     }
 
-    template <class S>  // LDS layout with bcol[2][kMaxState][>= kStage], crow[2][kStage][>= 16] (swizzled if S::kCSwizzle)
+    // LDS layout with bcol[2][kMaxState][>= kStage] and either (S::kCCols) C columns
+    // ccol[2][kMaxState][>= kStage] or C rows crow[2][kStage][>= 16] (swizzled if S::kCSwizzle)
+    template <class S>
     __device__ inline void store(S &sm, int buf, int rtid) const
     {
         const int pair = rtid / kParts;
@@ -212,6 +215,10 @@ struct Stager {
             // B: transposed, one column per state (read by the lane that owns the state)
 #pragma unroll
             for (int k = 0; k < kPer; ++k) sm.bcol[buf][n0 + k][tt] = f[k];
+        } else if constexpr (S::kCCols) {
+            // C: transposed like B (read by the lane that owns the state)
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) sm.ccol[buf][n0 + k][tt] = f[k];
         } else {
             // C: token rows (read by the lane that finishes the token's readout)
 #pragma unroll
@@ -284,7 +291,9 @@ struct TokStager {
 
 }  // namespace rows
 
-template <class Io, int kStage, bool kFullN>
+// kUIn: the x rows hold u = SiLU(conv(x)) already (the conv, its parameters and the
+// history are not used).
+template <class Io, int kStage, bool kFullN, bool kUIn>
 __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
 {
     using namespace rows;
@@ -314,9 +323,9 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     const int L = static_cast<int>(t1 - t0);
 
     const float An = state_ok ? a.A[static_cast<size_t>(cc) * N + j] : 0.0f;
-    const float w0 = a.conv_w[cc * kConvK + 0], w1 = a.conv_w[cc * kConvK + 1];
-    const float w2 = a.conv_w[cc * kConvK + 2], w3 = a.conv_w[cc * kConvK + 3];
-    const float cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+    const float w0 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 0], w1 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 1];
+    const float w2 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 2], w3 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 3];
+    const float cbias = (!kUIn && a.conv_b) ? a.conv_b[cc] : 0.0f;
     const float dsk = a.Dskip ? a.Dskip[cc] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
     const size_t hidx = (static_cast<size_t>(s) * D + cc) * N + j;
@@ -328,16 +337,18 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     // read before any store, since conv_final may alias conv0.
     const size_t cbase = static_cast<size_t>(s) * 3 * D + cc;
     float xprev = 0.0f;
-    if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
-    if (a.conv_final != nullptr && chan_ok && j >= 13) {
-        const int k = j - 13;
-        const int tk = L - 3 + k;  // token index relative to t0
-        float hv;
-        if (tk >= 0)
-            hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
-        else
-            hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
-        Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
+    if constexpr (!kUIn) {
+        if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
+        if (a.conv_final != nullptr && chan_ok && j >= 13) {
+            const int k = j - 13;
+            const int tk = L - 3 + k;  // token index relative to t0
+            float hv;
+            if (tk >= 0)
+                hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
+            else
+                hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
+            Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
+        }
     }
 
     const int nstages = (L + kStage - 1) / kStage;
@@ -444,11 +455,15 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
         const bool act = tb + j < L;
         f.x = to_f32(r.x);
         f.zv = to_f32(r.z);
-        float pre = __builtin_fmaf(w3, f.x, cbias);
-        pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
-        pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
-        pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
-        f.u = silu(pre);
+        if constexpr (kUIn) {
+            f.u = f.x;
+        } else {
+            float pre = __builtin_fmaf(w3, f.x, cbias);
+            pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
+            pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
+            pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
+            f.u = silu(pre);
+        }
         const float lg = softplus_log2(to_f32(r.dt) + bias);
         f.lg = act ? lg : 0.0f;
         f.du = act ? (lg * kLn2) * f.u : 0.0f;
@@ -580,17 +595,21 @@ inline void launch_rows_single(const ScanArgs &a, samba_dtype io, hipStream_t st
     const int ncb = (a.D + rows::kChannels - 1) / rows::kChannels;
     const dim3 grid(ncb * a.nseq), block(256);
     const bool full = a.N == kMaxState;
+#define SAMBA_ROWS(IO, FULL, UIN) rows_scan_kernel<IO, 64, FULL, UIN><<<grid, block, 0, stream>>>(a, ncb)
     if (io == SAMBA_BF16) {
-        if (full)
-            rows_scan_kernel<IoBf16, 64, true><<<grid, block, 0, stream>>>(a, ncb);
-        else
-            rows_scan_kernel<IoBf16, 64, false><<<grid, block, 0, stream>>>(a, ncb);
+        if (a.u_in) {
+            if (full) SAMBA_ROWS(IoBf16, true, true); else SAMBA_ROWS(IoBf16, false, true);
+        } else {
+            if (full) SAMBA_ROWS(IoBf16, true, false); else SAMBA_ROWS(IoBf16, false, false);
+        }
     } else {
-        if (full)
-            rows_scan_kernel<IoF32, 64, true><<<grid, block, 0, stream>>>(a, ncb);
-        else
-            rows_scan_kernel<IoF32, 64, false><<<grid, block, 0, stream>>>(a, ncb);
+        if (a.u_in) {
+            if (full) SAMBA_ROWS(IoF32, true, true); else SAMBA_ROWS(IoF32, false, true);
+        } else {
+            if (full) SAMBA_ROWS(IoF32, true, false); else SAMBA_ROWS(IoF32, false, false);
+        }
     }
+#undef SAMBA_ROWS
 }
 
 }  // namespace samba

@@ -25,10 +25,14 @@
 // roles then shares the SIMD while each role's LDS / memory / scalar instructions and
 // stalls are covered by the other role.
 //
-// Per stage of kStage tokens the scan waves stage B and C (shared by the workgroup's 16
+// Per stage of kStage tokens the token waves stage B and C (shared by the workgroup's 16
 // channels) into LDS as float32 (B transposed to [state][token], C as token rows) and the
-// token waves stage the x / dt / z rows of the 16 channels (16-byte buffer loads), both
-// into the other half of double buffers, with the loads issued one stage ahead.
+// x / dt / z rows of the 16 channels (16-byte buffer loads), both into the other half of
+// double buffers, with the loads issued one stage ahead.
+//
+// With a precomputed u (kUIn: u = SiLU(conv(x)) from samba_conv_silu, the activation a
+// full layer also feeds to x_proj), the token rows carry u instead of x and the conv is
+// skipped.
 #pragma once
 
 #include "scan_rows.h"
@@ -58,6 +62,7 @@ struct SplitSmem {
     static constexpr int kTokPitch = rows::tok_pitch_bytes<T>();
     float bcol[2][kMaxState][kBPitch];           // [buffer][state][token]: B, transposed
     static constexpr bool kCSwizzle = false;     // C rows unswizzled (see kSPPitch)
+    static constexpr bool kCCols = false;        // C as token rows (read by the token role)
     float crow[2][kStage][kSPPitch];             // [buffer][token][state]: C rows
     float hs[kHsSlots][rows::kChannels * kSRowPitch];  // [block slot][channel][token][state]: h_t
     float lg[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * log2(e)
@@ -67,7 +72,7 @@ struct SplitSmem {
 
 }  // namespace split
 
-template <class Io, int kStage, bool kFullN, int kDist>
+template <class Io, int kStage, bool kFullN, int kDist, bool kUIn>
 __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a, int ncb)
 {
     using namespace rows;
@@ -225,9 +230,9 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     }
 
     // ==================================================================== token role
-    const float w0 = a.conv_w[cc * kConvK + 0], w1 = a.conv_w[cc * kConvK + 1];
-    const float w2 = a.conv_w[cc * kConvK + 2], w3 = a.conv_w[cc * kConvK + 3];
-    const float cbias = a.conv_b ? a.conv_b[cc] : 0.0f;
+    const float w0 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 0], w1 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 1];
+    const float w2 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 2], w3 = kUIn ? 0.0f : a.conv_w[cc * kConvK + 3];
+    const float cbias = (!kUIn && a.conv_b) ? a.conv_b[cc] : 0.0f;
     const float dsk = a.Dskip ? a.Dskip[cc] : 0.0f;
     const float bias = a.dt_bias ? a.dt_bias[cc] : 0.0f;
 
@@ -237,16 +242,18 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     // read before any store, since conv_final may alias conv0.
     const size_t cbase = static_cast<size_t>(s) * 3 * D + cc;
     float xprev = 0.0f;
-    if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
-    if (a.conv_final != nullptr && chan_ok && j >= 13) {
-        const int k = j - 13;
-        const int tk = L - 3 + k;  // token index relative to t0
-        float hv;
-        if (tk >= 0)
-            hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
-        else
-            hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
-        Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
+    if constexpr (!kUIn) {
+        if (a.conv0 != nullptr && j >= 13) xprev = Io::ld(a.conv0, cbase + static_cast<size_t>(j - 13) * D);
+        if (a.conv_final != nullptr && chan_ok && j >= 13) {
+            const int k = j - 13;
+            const int tk = L - 3 + k;  // token index relative to t0
+            float hv;
+            if (tk >= 0)
+                hv = Io::ld(a.x, (t0 + static_cast<size_t>(tk)) * D + cc);
+            else
+                hv = (a.conv0 != nullptr) ? Io::ld(a.conv0, cbase + static_cast<size_t>(k + L) * D) : 0.0f;
+            Io::st(a.conv_final, cbase + static_cast<size_t>(k) * D, hv);
+        }
     }
 
     const bool has_z = a.z != nullptr;
@@ -294,11 +301,15 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         const bool act = tb + j < L;
         f.x = to_f32(r.x);
         f.zv = to_f32(r.z);
-        float pre = __builtin_fmaf(w3, f.x, cbias);
-        pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
-        pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
-        pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
-        f.u = silu(pre);
+        if constexpr (kUIn) {
+            f.u = f.x;
+        } else {
+            float pre = __builtin_fmaf(w3, f.x, cbias);
+            pre = __builtin_fmaf(tap<1>(f.x, xp, j), w2, pre);
+            pre = __builtin_fmaf(tap<2>(f.x, xp, j), w1, pre);
+            pre = __builtin_fmaf(tap<3>(f.x, xp, j), w0, pre);
+            f.u = silu(pre);
+        }
         const float lg = softplus_log2(to_f32(r.dt) + bias);
         sm.lg[slot][ch * kBlock + j] = act ? lg : 0.0f;
         sm.du[slot][ch * kBlock + j] = act ? (lg * kLn2) * f.u : 0.0f;
@@ -439,17 +450,21 @@ inline void launch_rows_split(const ScanArgs &a, samba_dtype io, hipStream_t str
     const bool full = a.N == kMaxState;
     // Hand-over distance 2 (a barrier every other step) needs 4 state-tile slots, which fit
     // next to the 2-byte token tiles; with 4-byte token tiles the kernel syncs every step.
+#define SAMBA_SPLIT(IO, FULL, DIST, UIN) rows_split_kernel<IO, 128, FULL, DIST, UIN><<<grid, block, 0, stream>>>(a, ncb)
     if (io == SAMBA_BF16) {
-        if (full)
-            rows_split_kernel<IoBf16, 128, true, 2><<<grid, block, 0, stream>>>(a, ncb);
-        else
-            rows_split_kernel<IoBf16, 128, false, 2><<<grid, block, 0, stream>>>(a, ncb);
+        if (a.u_in) {
+            if (full) SAMBA_SPLIT(IoBf16, true, 2, true); else SAMBA_SPLIT(IoBf16, false, 2, true);
+        } else {
+            if (full) SAMBA_SPLIT(IoBf16, true, 2, false); else SAMBA_SPLIT(IoBf16, false, 2, false);
+        }
     } else {
-        if (full)
-            rows_split_kernel<IoF32, 128, true, 1><<<grid, block, 0, stream>>>(a, ncb);
-        else
-            rows_split_kernel<IoF32, 128, false, 1><<<grid, block, 0, stream>>>(a, ncb);
+        if (a.u_in) {
+            if (full) SAMBA_SPLIT(IoF32, true, 1, true); else SAMBA_SPLIT(IoF32, false, 1, true);
+        } else {
+            if (full) SAMBA_SPLIT(IoF32, true, 1, false); else SAMBA_SPLIT(IoF32, false, 1, false);
+        }
     }
+#undef SAMBA_SPLIT
 }
 
 }  // namespace samba

@@ -84,6 +84,30 @@ def test_long_prompt_prefill_131072():
     assert torch.isfinite(y.float()).all()
 
 
+def test_long_prompt_prefill_from_precomputed_u():
+    """samba_scan_prefill_u at the long-prompt shape (batch 1, L = 131072, bf16): u from the
+    oracle's conv of the prompt (sampled channels), rounded to bf16; the GPU runs all 4096
+    channels on the same bf16 u (the unsampled channels' u are the workload's x values)."""
+    seed = synth.seed_for(2)
+    b, L = 1, 131072
+    print("case: prefill_u batch %d L %d" % (b, L), flush=True)
+    p = synth.make_params(seed, D, N, conv_bias=True)
+    tk = synth.make_tokens(seed, (b, L), D, N, "bf16")
+    chans = sample_channels(seed)
+    u_s = synth.round_bf16(oracle.conv_silu(tk.x, p.conv_w, p.conv_b, chans=chans)[0].astype(np.float32))
+    u = tk.x.copy()
+    u[:, :, chans] = u_s
+    y, hf = ss.prefill_u(bf16(u), bf16(tk.dt), bf16(tk.B), bf16(tk.C), bf16(tk.z), tf32(p.A, DEV),
+                         tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV))
+    ci = torch.from_numpy(chans).to(DEV)
+    yg = y.index_select(2, ci).float().cpu().numpy()
+    hg = hf.index_select(1, ci).cpu().numpy()
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_u(u, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, chans=chans)
+    check("y", yg, yr)
+    check("h_final", hg, hr)
+
+
 def test_training_length_backward_4x4096():
     """Gradients at the training shape (batch 4, L = 4096), every output against the
     oracle's gradients over all 4096 channels (dB and dC are sums over all of them)."""

@@ -62,6 +62,12 @@ MUTANTS = {
     "swa_scale_missing": ("sc[j - lo] = dot / sqrt((double)dh);", "sc[j - lo] = dot;"),
     "swa_kv_head_interleaved": ("const int hk = h / group;", "const int hk = h % Hkv;"),
     "swa_absolute_positions": ("oracle_rope(kv, dh, (double)(j - t0), base);", "oracle_rope(kv, dh, (double)j, base);"),
+    "u_scan_drop_skip": ("acc += dsk * uu;", "acc += 0.0 * uu;"),
+    "u_scan_input_without_u": ("const double du = delta * uu;", "const double du = delta;"),
+    "u_scan_bias_dropped": ("const double delta = oracle_softplus(dt[ix] + bias);\n                const double du = delta * uu;",
+                            "const double delta = oracle_softplus(dt[ix]);\n                const double du = delta * uu;"),
+    "u_scan_gate_missing": ("y[ix] = z ? acc * oracle_silu(z[ix]) : acc;\n            }\n            for (n = 0; n < N; ++n) hseq",
+                            "y[ix] = acc;\n            }\n            for (n = 0; n < N; ++n) hseq"),
     "history_not_carried_in": ("for (k = 0; k < ORACLE_K - 1; ++k) win[k] = hist[(size_t)k * ldh + d];",
                                "for (k = 0; k < ORACLE_K - 1; ++k) win[k] = 0.0;"),
 }

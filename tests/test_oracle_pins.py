@@ -572,3 +572,53 @@ def test_swa_packed_equals_separate_sequences():
         if n:
             ref = oracle.swa(q[sl], k[sl], v[sl], window=4, cu_seqlens=np.array([0, n]))
             np.testing.assert_array_equal(out[sl], ref)
+
+
+# ---------------------------------------------------------------- the scan from a precomputed u
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_scan_from_u_composed_with_conv_is_the_prefill(with_h0):
+    """oracle.scan_u applied to u = oracle.conv_silu(x) (history included) equals the prefill
+    from x exactly: the same steps of [P1] section 3.4 once the conv has been taken out."""
+    rng = np.random.default_rng(41)
+    b, L, D, N = 2, 37, 5, 16
+    c = rand_case(rng, b, L, D, N, h0=with_h0, hist=True)
+    y, h, _ = run_prefill(c)
+    u, _ = oracle.conv_silu(c["x"], c["conv_w"], c["conv_b"], conv0=c["conv0"])
+    yu, hu = oracle.scan_u(u, c["dt"], c["B"], c["C"], c["z"], c["A"], c["Dskip"], c["dt_bias"], h0=c["h0"])
+    np.testing.assert_array_equal(yu, y)
+    np.testing.assert_array_equal(hu, h)
+    # and against torch's conv for u: the conv taken out is the library routine's
+    u_t = np.stack([torch_conv_silu(c["x"][s], c["conv_w"], c["conv_b"], c["conv0"][s]) for s in range(b)])
+    yt, _ = oracle.scan_u(u_t, c["dt"], c["B"], c["C"], c["z"], c["A"], c["Dskip"], c["dt_bias"], h0=c["h0"])
+    np.testing.assert_allclose(yt, y, rtol=1e-11, atol=1e-12)
+
+
+def test_scan_from_u_packed_equals_fixed_length_pieces():
+    """Packed sequences (lengths 0, 1, 9, 4) equal the same sequences run one at a time."""
+    rng = np.random.default_rng(42)
+    D, N = 3, 16
+    lens = [0, 1, 9, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    u, dt, z = rng.standard_normal((T, D)), 0.5 * rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    B, C = rng.standard_normal((T, N)), rng.standard_normal((T, N))
+    c = rand_case(rng, 1, 1, D, N)
+    h0 = rng.standard_normal((len(lens), D, N))
+    y, h = oracle.scan_u(u, dt, B, C, z, c["A"], c["Dskip"], c["dt_bias"], h0=h0, cu_seqlens=cu)
+    for s, L in enumerate(lens):
+        sl = slice(cu[s], cu[s + 1])
+        ys, hs = oracle.scan_u(u[sl][None], dt[sl][None], B[sl][None], C[sl][None], z[sl][None], c["A"], c["Dskip"],
+                               c["dt_bias"], h0=h0[s:s + 1])
+        np.testing.assert_array_equal(y[sl], ys[0])
+        np.testing.assert_array_equal(h[s], hs[0])
+
+
+def test_scan_from_u_delta_to_zero_is_the_gated_skip():
+    """Delta -> 0 from a zero state: out = D u SiLU(z) (closed form, scipy's sigmoid)."""
+    rng = np.random.default_rng(43)
+    L, D, N = 12, 4, 16
+    c = rand_case(rng, 1, L, D, N)
+    u = rng.standard_normal((1, L, D))
+    dt = np.full((1, L, D), -60.0)
+    y, h = oracle.scan_u(u, dt, c["B"], c["C"], c["z"], c["A"], c["Dskip"], np.zeros(D))
+    np.testing.assert_allclose(y[0], c["Dskip"] * u[0] * np_silu(c["z"][0]), rtol=1e-12, atol=1e-20)

@@ -269,3 +269,72 @@ def test_invalid_arguments_raise():
     with pytest.raises(ss.SambaError) as ei:
         ss.prefill(x, x, Bm, Bm, x, A, None, None, w, None)
     assert ei.value.status == 2
+
+
+def _round_io(a, io):
+    """Values as the I/O dtype stores them (bf16: round to nearest even), as float32."""
+    a = np.asarray(a, dtype=np.float32)
+    return synth.round_bf16(a) if io == "bf16" else a
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_prefill_from_precomputed_u(io, with_state):
+    """samba_scan_prefill_u: the scan from u = SiLU(conv(x)) computed beforehand (here by the
+    oracle's conv, rounded to the I/O dtype), against the oracle's scan from the same u;
+    ragged length, d_inner not a multiple of 64, random A."""
+    p, tk, h0, _, gate = make_case(1100, 3, 333, 320, 16, io, random_A=True, with_state=with_state)
+    u = _round_io(oracle.conv_silu(tk.x, p.conv_w, p.conv_b)[0], io)
+    print("case: prefill_u", u.shape, io, "state", with_state, flush=True)
+    y, hf = ss.prefill_u(tdev(u, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
+                         tdev(tk.z, io, DEV), tf32(p.A, DEV), tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV),
+                         None if h0 is None else tf32(h0, DEV))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_u(u, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, h0=h0)
+    ey, eh = rel_err(host(y), yr), rel_err(host(hf), hr)
+    print("  y err %.3e  h err %.3e  (tol %.0e)" % (ey, eh, TOL[io]), flush=True)
+    assert ey <= TOL[io] and eh <= TOL[io]
+
+
+@pytest.mark.parametrize("N", [1, 5])
+def test_prefill_from_u_small_state_and_short(N):
+    p, tk, h0, _, _ = make_case(1150 + N, 2, 7, 96, N, "f32", with_state=True)
+    u = _round_io(oracle.conv_silu(tk.x, p.conv_w, p.conv_b)[0], "f32")
+    y, hf = ss.prefill_u(tdev(u, "f32", DEV), tdev(tk.dt, "f32", DEV), tdev(tk.B, "f32", DEV),
+                         tdev(tk.C, "f32", DEV), None, tf32(p.A, DEV), tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV),
+                         tf32(h0, DEV))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_u(u, tk.dt, tk.B, tk.C, None, p.A, p.Dskip, p.dt_bias, h0=h0)
+    assert rel_err(host(y), yr) <= TOL["f32"] and rel_err(host(hf), hr) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_varlen_from_precomputed_u(io):
+    lens = [0, 1, 2, 3, 5, 100, 257, 0, 64]
+    cu = synth.cu_from_lengths(lens)
+    T, D, N = int(cu[-1]), 192, 16
+    seed = 1200
+    p = synth.make_params(seed, D, N, random_A=True, conv_bias=True)
+    tk = synth.make_tokens(seed, (T,), D, N, io)
+    h0, _ = synth.make_state(seed, len(lens), D, N, io, scale=0.5)
+    u = _round_io(oracle.conv_silu(tk.x, p.conv_w, p.conv_b, cu_seqlens=cu)[0], io)
+    print("case: varlen_u", lens, io, flush=True)
+    y, hf = ss.varlen_u(torch.from_numpy(cu).to(DEV), tdev(u, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV),
+                        tdev(tk.C, io, DEV), tdev(tk.z, io, DEV), tf32(p.A, DEV), tf32(p.Dskip, DEV),
+                        tf32(p.dt_bias, DEV), tf32(h0, DEV))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_u(u, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, h0=h0, cu_seqlens=cu)
+    assert rel_err(host(y), yr) <= TOL[io] and rel_err(host(hf), hr) <= TOL[io]
+
+
+def test_prefill_u_ignores_conv_parameters():
+    """conv_w and conv_b are not read by the u entry points: NULL is accepted (the binding
+    passes none)."""
+    io = "bf16"
+    p, tk, _, _, _ = make_case(1300, 1, 50, 64, 16, io)
+    u = _round_io(oracle.conv_silu(tk.x, p.conv_w, p.conv_b)[0], io)
+    y, _ = ss.prefill_u(tdev(u, io, DEV), tdev(tk.dt, io, DEV), tdev(tk.B, io, DEV), tdev(tk.C, io, DEV),
+                        tdev(tk.z, io, DEV), tf32(p.A, DEV), None, None)
+    torch.cuda.synchronize()
+    yr, _ = oracle.scan_u(u, tk.dt, tk.B, tk.C, tk.z, p.A, None, None)
+    assert rel_err(host(y), yr) <= TOL[io]
