@@ -278,6 +278,25 @@ samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_di
                               void *k_cache, void *v_cache, void *out, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/* samba_swa_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * arguments without a workspace.  The split partials go to a device array inside the library
+ * (samba_swa_decode_noalloc_max_bytes() bytes, 24 MiB, one copy per GPU held until the
+ * process ends); the call allocates nothing.
+ *   Limit: samba_swa_decode_workspace_bytes(nseq, n_heads, head_dim) must not exceed the
+ *   array (e.g. 256 sequences x 32 heads x head_dim 128 fit); SAMBA_ERR_UNSUPPORTED
+ *   otherwise, before anything is enqueued.
+ *   Every call on one GPU uses that GPU's single array: calls that overlap on one GPU (on
+ *   different streams, or from different threads) race and must be serialised by the
+ *   caller.  The first call on a device looks the array's address up (hipGetSymbolAddress);
+ *   a failure returns SAMBA_ERR_HIP. */
+samba_status samba_swa_decode_noalloc(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
+                                      samba_dtype io, const void *q, const void *k, const void *v, const int32_t *pos,
+                                      void *k_cache, void *v_cache, void *out, void *stream);
+
+/* Size in bytes of the device array samba_swa_decode_noalloc uses. */
+size_t samba_swa_decode_noalloc_max_bytes(void);
+
 /* Fills the ring-buffer caches from a prefill's keys and values (fixed length when
  * cu_seqlens is NULL, else packed as for samba_scan_varlen): each sequence's last
  * min(L, window + 1) tokens go to entry position mod (window + 1), keys rotated, so that a

@@ -100,6 +100,10 @@ def load():
         lib.samba_swa_decode_workspace_bytes.argtypes = [I, I, I]
         lib.samba_swa_decode.restype = I
         lib.samba_swa_decode.argtypes = [I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, Z, P]
+        lib.samba_swa_decode_noalloc.restype = I
+        lib.samba_swa_decode_noalloc.argtypes = [I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P, P, P, P]
+        lib.samba_swa_decode_noalloc_max_bytes.restype = Z
+        lib.samba_swa_decode_noalloc_max_bytes.argtypes = []
         lib.samba_swa_kv_fill.restype = I
         lib.samba_swa_kv_fill.argtypes = [I, P, I, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
         lib.samba_conv_silu.restype = I
@@ -516,6 +520,27 @@ def swa_decode(q, k, v, pos, k_cache, v_cache, *, window=2048, rope_base=10000.0
         _ptr(v, "v", q.dtype, dev), _ptr(pos, "pos", torch.int32, dev), _ptr(k_cache, "k_cache", q.dtype, dev),
         _ptr(v_cache, "v_cache", q.dtype, dev), _ptr(out, "out", q.dtype, dev), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return out
+
+
+def swa_decode_noalloc(q, k, v, pos, k_cache, v_cache, *, window=2048, rope_base=10000.0, out=None):
+    """swa_decode through samba_swa_decode_noalloc: no workspace, the split partials in the
+    library's own device array (calls on one GPU must not overlap)."""
+    dev = _gpu_device(q)
+    S, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    _shape(k, (S, Hkv, dh), "k")
+    _shape(v, (S, Hkv, dh), "v")
+    _shape(pos, (S,), "pos")
+    _shape(k_cache, (S, Hkv, int(window) + 1, dh), "k_cache")
+    _shape(v_cache, (S, Hkv, int(window) + 1, dh), "v_cache")
+    if out is None:
+        out = torch.empty_like(q)
+    st = load().samba_swa_decode_noalloc(
+        S, Hq, Hkv, dh, int(window), float(rope_base), _io(q), _ptr(q, "q", q.dtype, dev), _ptr(k, "k", q.dtype, dev),
+        _ptr(v, "v", q.dtype, dev), _ptr(pos, "pos", torch.int32, dev), _ptr(k_cache, "k_cache", q.dtype, dev),
+        _ptr(v_cache, "v_cache", q.dtype, dev), _ptr(out, "out", q.dtype, dev), _stream(dev))
     _check(st)
     return out
 

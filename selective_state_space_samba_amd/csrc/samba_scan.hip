@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/samba_scan.h"
@@ -36,6 +37,42 @@
 namespace {
 
 thread_local std::string g_err;
+
+// Device memory of the allocation-free entry point (samba_swa_decode_noalloc): the split
+// partials of the attention decode live in this file-scope array instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device with hipGetSymbolAddress (scratch_on) and only that address
+// is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(24) << 20;  // 24 MiB
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call per
+// device); nullptr, with the reason in g_err, when the lookup fails.
+void *scratch_on(const char *fn)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        g_err = std::string(fn) + ": no usable current device: " + hipGetErrorString(e);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            g_err = std::string(fn) + ": hipGetSymbolAddress(scratch) failed: " + hipGetErrorString(e);
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 samba_status fail(samba_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 samba_status fail(samba_status st, const char *fmt, ...)
@@ -678,6 +715,41 @@ samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_di
     REQUIRE_PTR(workspace, "workspace");
     samba::SwaDecArgs a = swa_dec_args(nseq, n_heads, n_kv_heads, head_dim, window, rope_base, q, k, v, pos, k_cache,
                                        v_cache, out, workspace);
+    samba::launch_swa_decode(a, static_cast<hipStream_t>(stream));
+    return launched(fn);
+}
+
+size_t samba_swa_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+samba_status samba_swa_decode_noalloc(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
+                                      samba_dtype io, const void *q, const void *k, const void *v, const int32_t *pos,
+                                      void *k_cache, void *v_cache, void *out, void *stream)
+{
+    const char *fn = "samba_swa_decode_noalloc";
+    samba_status st = swa_dec_common(fn, nseq, n_heads, n_kv_heads, head_dim, window, rope_base, io, true);
+    if (st != SAMBA_OK) return st;
+    if (nseq == 0) {
+        g_err.clear();
+        return SAMBA_OK;
+    }
+    const size_t need = samba::swa_decode_workspace_bytes(nseq, n_heads, head_dim);
+    if (need > kNoAllocScratchBytes)
+        return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d x n_heads=%d x head_dim=%d needs %zu bytes of split partials, "
+                    "more than the %zu bytes of the library's scratch array (use samba_swa_decode with a "
+                    "workspace)", fn, nseq, n_heads, head_dim, need, kNoAllocScratchBytes);
+    REQUIRE_PTR(q, "q");
+    REQUIRE_PTR(k, "k");
+    REQUIRE_PTR(v, "v");
+    REQUIRE_PTR(out, "out");
+    REQUIRE_PTR(k_cache, "k_cache");
+    REQUIRE_PTR(v_cache, "v_cache");
+    if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
+    void *part = scratch_on(fn);
+    if (part == nullptr) return SAMBA_ERR_HIP;
+    // Every partial the combine reads is written by the attention kernel of the same call
+    // (inactive sequences included), so the array needs no clearing.
+    samba::SwaDecArgs a = swa_dec_args(nseq, n_heads, n_kv_heads, head_dim, window, rope_base, q, k, v, pos, k_cache,
+                                       v_cache, out, part);
     samba::launch_swa_decode(a, static_cast<hipStream_t>(stream));
     return launched(fn);
 }
