@@ -12,7 +12,7 @@ sequences (65536 single-token steps replayed from HIP graphs), and the packed-va
 training-length and batch-64 prefills.  The CPU baseline is the fp64 oracle timed on a bounded sample
 of the same prompt (a subset of channels; channels are independent).
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-decode] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 10] [--no-decode] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -74,7 +74,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the varlen / training-length timings")

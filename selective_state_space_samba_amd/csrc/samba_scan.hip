@@ -88,7 +88,7 @@ samba_status fail(samba_status st, const char *fmt, ...)
 
 // Kernel choice for prefill / varlen.  The lane kernel (one lane per channel, 16 states
 // in registers) is the cheapest per token when sequences x channels alone give at least
-// four waves per SIMD; otherwise the row kernels (16 lanes per channel) supply the
+// two waves per SIMD (131072 lanes); otherwise the row kernels (16 lanes per channel) supply the
 // parallelism: the two-role row kernel while the grid has at most one workgroup per CU,
 // the single-role one (two workgroups per CU) beyond that.  SAMBA_SCAN_PATH=lane|single|
 // split forces one of them (the tests run every kernel on every shape); the lane kernel is

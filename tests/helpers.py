@@ -27,6 +27,24 @@ def plain_rel_err(g, r, floor=1e-2):
     return float(np.max(np.abs(g[m] - r[m]) / np.abs(r[m]))) if m.any() else 0.0
 
 
+def max_rel_err(g, r):
+    """max |g - r| / max |r| over the tensor (reported only)."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    m = float(np.max(np.abs(r)))
+    return float(np.max(np.abs(g - r))) / m if m > 0 else float(np.max(np.abs(g - r)))
+
+
+def metrics(g, r):
+    """The primary metric (rel_err, asserted) and the two secondary ones (reported): a
+    printable string and the primary value."""
+    e = rel_err(g, r)
+    return "err %.3e (max|g-r|/max|r| %.3e, elementwise rel. over |r| >= 1e-2 max|r| %.3e)" % (
+        e, max_rel_err(g, r), plain_rel_err(g, r)), e
+
+
 def tdev(a, io, dev):
     import torch
     dt = torch.float32 if io == "f32" else torch.bfloat16

@@ -12,7 +12,7 @@ import torch
 import oracle
 import selective_state_space_samba_amd as ss
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, ordered_from_ring, rel_err, tf32
+from tests.helpers import TOL, metrics, ordered_from_ring, tf32
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -35,8 +35,8 @@ def params_dev(p):
 
 
 def check(name, g, r, io="bf16"):
-    e = rel_err(g, r)
-    print("  %s err %.3e (tol %.0e)" % (name, e, TOL[io]), flush=True)
+    s, e = metrics(g, r)
+    print("  %s %s (tol %.0e)" % (name, s, TOL[io]), flush=True)
     assert e <= TOL[io], name
 
 

@@ -11,7 +11,7 @@ import torch
 import oracle
 import selective_state_space_samba_amd as ss
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, host, ordered_from_ring, rel_err, ring_from_ordered, tdev, tf32
+from tests.helpers import TOL, host, metrics, ordered_from_ring, rel_err, ring_from_ordered, tdev, tf32
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -52,8 +52,8 @@ def run_both(p, tk, h0, conv0, gate, io):
 
 def check(g, r, io):
     (y, hf, cf), (yr, hr, cr) = g, r
-    ey, eh = rel_err(y, yr), rel_err(hf, hr)
-    print("  y err %.3e  h err %.3e  (tol %.0e)" % (ey, eh, TOL[io]), flush=True)
+    (sy, ey), (sh, eh) = metrics(y, yr), metrics(hf, hr)
+    print("  y %s\n  h %s  (tol %.0e)" % (sy, sh, TOL[io]), flush=True)
     assert ey <= TOL[io]
     assert eh <= TOL[io]
     np.testing.assert_array_equal(cf, cr)  # the conv history is a copy: bit-exact

@@ -7,7 +7,7 @@ import torch
 import oracle
 import selective_state_space_samba_amd as ss
 from selective_state_space_samba_amd import synth
-from tests.helpers import TOL, host, rel_err
+from tests.helpers import TOL, host, metrics
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -44,8 +44,8 @@ def check(got, ref, rows=None):
     if rows is not None:
         got = got.reshape((-1,) + got.shape[-2:])[rows]
         ref = ref.reshape((-1,) + ref.shape[-2:])[rows]
-    e = rel_err(got, ref)
-    print("  out err %.3e (tol %.0e)" % (e, TOL["bf16"]), flush=True)
+    s, e = metrics(got, ref)
+    print("  out %s (tol %.0e)" % (s, TOL["bf16"]), flush=True)
     assert e <= TOL["bf16"]
 
 
@@ -91,6 +91,21 @@ def test_swa_training_shape_sampled_rows():
     rng = np.random.default_rng(1)
     per = np.unique(np.concatenate([[0, 1, 63, 64, 2047, 2048, 2049, 2111, 2112, 4095], rng.integers(0, 4096, 20)]))
     rows = np.concatenate([per, 4096 + per])
+    got, ref = run(q, k, v, 2048, rows=rows)
+    check(got, ref, rows=rows)
+
+
+def test_swa_long_prompt_timed_shape_sampled_rows():
+    """The shape the benchmark times: one 131072-token prompt, 32 query heads, 4 KV heads,
+    head_dim 64, window 2048 (the same launch: the prefill kernel's grid over all rows and
+    heads).  Sampled rows: the first ones, the window edge (2047..2049), query-tile edges
+    (multiples of 64 and 128 and their neighbours), rows whose window crosses a key-tile
+    edge, the last rows, and random rows; every head of each."""
+    q, k, v = make_qkv(3600, (1, 131072), 32, 4, 64)
+    rng = np.random.default_rng(2)
+    edges = [0, 1, 2, 63, 64, 65, 127, 128, 129, 2046, 2047, 2048, 2049, 2050, 2111, 2112, 2175, 2176, 4095, 4096,
+             65535, 65536, 65600, 131007, 131008, 131070, 131071]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, 131072, 24)]))
     got, ref = run(q, k, v, 2048, rows=rows)
     check(got, ref, rows=rows)
 
