@@ -42,8 +42,10 @@
  *   with head 0.
  * - d_state must be in [1, 16]; d_inner >= 1; every pointer must be aligned to 16 bytes.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
- *   return once the work is enqueued.  Outputs must not overlap inputs, except the
- *   deliberately in/out arguments of samba_scan_decode.
+ *   return once the work is enqueued.  Outputs must not overlap inputs or each other,
+ *   except the in/out arguments of the decode steps and a prefill's h_final / conv_final
+ *   passed as the very same pointers as h0 / conv0; the byte ranges the shapes define are
+ *   compared on the host and an overlap is refused with SAMBA_ERR_INVALID_ARG.
  * - Errors: arguments are checked on the host before anything is enqueued; a failing
  *   check returns a non-zero samba_status, enqueues nothing and sets a thread-local
  *   message readable with samba_last_error().  A launch failure returns SAMBA_ERR_HIP.
@@ -66,7 +68,10 @@
 extern "C" {
 #endif
 
-typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
+/* Each enum below also lists a FORCE_INT32 value that is never a valid argument: it makes
+ * every int a value of the type, so an out-of-range argument is rejected by the checks
+ * (SAMBA_ERR_INVALID_ARG) instead of being undefined behaviour in the C++ implementation. */
+typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1, SAMBA_DTYPE_FORCE_INT32 = -2147483647 - 1 } samba_dtype;
 
 typedef enum {
     SAMBA_OK = 0,
@@ -309,7 +314,8 @@ samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, 
 typedef enum {
     SAMBA_GEMM_STORE = 0,  /* out bf16 = A . W^T */
     SAMBA_GEMM_ADD_F32 = 1, /* out fp32 = residual fp32 + A . W^T (the residual stream) */
-    SAMBA_GEMM_SWIGLU = 2  /* W = [W1; W2] (2N rows): out bf16 = (A . W1^T) * SiLU(A . W2^T) */
+    SAMBA_GEMM_SWIGLU = 2, /* W = [W1; W2] (2N rows): out bf16 = (A . W1^T) * SiLU(A . W2^T) */
+    SAMBA_GEMM_FORCE_INT32 = -2147483647 - 1
 } samba_gemm_epilogue;
 
 /* Size in bytes of the workspace samba_gemm needs for this shape (0 when the K range is
@@ -359,7 +365,12 @@ typedef struct {
     float norm_eps;  /* RMSNorm epsilon */
 } samba_model_config;
 
-typedef enum { SAMBA_LAYER_MAMBA = 0, SAMBA_LAYER_SWA = 1, SAMBA_LAYER_MLP = 2 } samba_layer_kind;
+typedef enum {
+    SAMBA_LAYER_MAMBA = 0,
+    SAMBA_LAYER_SWA = 1,
+    SAMBA_LAYER_MLP = 2,
+    SAMBA_LAYER_FORCE_INT32 = -2147483647 - 1
+} samba_layer_kind;
 
 /* One layer of the stack: its kind, its RMSNorm weight, its weights (bf16, one row per output
  * feature, the projections that read the same input stacked into one matrix) and its decode

@@ -25,11 +25,18 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "samba_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt copy of the oracle to load instead (the sanitizer test runs the pins against an
+# AddressSanitizer / UndefinedBehaviorSanitizer build); it is used as is, never rebuilt.
+_PREBUILT = os.environ.get("SAMBA_ORACLE_LIB") or None
+if _PREBUILT:
+    _LIB = _PREBUILT
 _lib = None
 
 
 def build(force: bool = False) -> str:
     """Compile samba_oracle.c with gcc (OpenMP) into oracle/liboracle.so."""
+    if _PREBUILT:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])

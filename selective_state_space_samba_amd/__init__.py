@@ -22,7 +22,9 @@ __all__ = ["prefill", "prefill_u", "varlen", "varlen_u", "decode", "conv_silu", 
            "workspace_bytes", "lib_path", "SambaError", "version"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsamba_scan.so")
+# SAMBA_LIB names another build of the same sources to load instead (the sanitizer test loads
+# a host-AddressSanitizer / UndefinedBehaviorSanitizer build this way).
+LIB_PATH = os.environ.get("SAMBA_LIB") or os.path.join(_PKG, "libsamba_scan.so")
 _lib = None
 
 SAMBA_F32, SAMBA_BF16 = 0, 1

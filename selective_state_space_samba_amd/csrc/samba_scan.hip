@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -165,7 +166,6 @@ samba_status launched(const char *fn)
     return SAMBA_OK;
 }
 
-// Builds the argument block shared by every kernel.
 // Whether the byte ranges [p, p + pb) and [q, q + qb) share a byte.
 bool overlaps(const void *p, size_t pb, const void *q, size_t qb)
 {
@@ -173,6 +173,47 @@ bool overlaps(const void *p, size_t pb, const void *q, size_t qb)
     const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
     return a < b + qb && b < a + pb;
 }
+
+// A named byte range of a call's arguments.
+struct Span {
+    const void *p;
+    size_t bytes;
+    const char *name;
+};
+
+// Fails (SAMBA_ERR_INVALID_ARG) when an output range shares a byte with an input range or with
+// another output range.  Null pointers and empty ranges overlap nothing.
+samba_status check_disjoint(const char *fn, std::initializer_list<Span> outs, std::initializer_list<Span> ins)
+{
+    for (const Span *o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span &i : ins)
+            if (overlaps(o->p, o->bytes, i.p, i.bytes))
+                return fail(SAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, o->name, i.name);
+        for (const Span *o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(o->p, o->bytes, o2->p, o2->bytes))
+                return fail(SAMBA_ERR_INVALID_ARG, "%s: %s overlaps %s", fn, o->name, o2->name);
+    }
+    return SAMBA_OK;
+}
+
+// Output / input disjointness of a prefill, varlen or backward call: token arrays of `tokens`
+// rows, state and history arrays of `nseq` rows.
+struct ScanSizes {
+    size_t tok, bc, state, hist, vec, cw, a;
+    ScanSizes(size_t tokens, int nseq, int d_inner, int d_state, samba_dtype io)
+    {
+        const size_t e = io == SAMBA_BF16 ? 2 : 4, D = static_cast<size_t>(d_inner), N = static_cast<size_t>(d_state);
+        tok = tokens * D * e;
+        bc = tokens * N * e;
+        state = static_cast<size_t>(nseq) * D * N * 4;
+        hist = static_cast<size_t>(nseq) * 3 * D * e;
+        vec = D * 4;
+        cw = D * samba::kConvK * 4;
+        a = D * N * 4;
+    }
+};
+
+// Builds the argument block shared by every kernel.
 
 samba::ScanArgs make_args(int nseq, int seqlen, const int32_t *cu, int d_inner, int d_state,
                           const void *x, const void *dt, const void *B, const void *C, const void *z,
@@ -225,6 +266,27 @@ size_t samba_scan_workspace_bytes(int nseq, int max_seqlen, int d_inner, int d_s
 
 namespace {
 
+// Outputs of a prefill / varlen call (out, h_final, conv_final) against its inputs and each
+// other.  h_final may be h0 itself and conv_final conv0 itself (the state updated in place:
+// every channel's state and history are read before they are written, by the same threads
+// or across a workgroup barrier); any other overlap is refused.
+samba_status scan_disjoint(const char *fn, bool u_in, size_t tokens, int nseq, int d_inner, int d_state,
+                           samba_dtype io, const int32_t *cu, const void *x, const void *dt, const void *B,
+                           const void *C, const void *z, const samba_params *p, const float *h0, const void *conv0,
+                           const void *out, const float *h_final, const void *conv_final)
+{
+    const ScanSizes n(tokens, nseq, d_inner, d_state, io);
+    const size_t hist = u_in ? 0 : n.hist;
+    return check_disjoint(fn, {{out, n.tok, "out"}, {h_final, n.state, "h_final"}, {conv_final, hist, "conv_final"}},
+                          {{x, n.tok, u_in ? "u" : "x"}, {dt, n.tok, "dt"}, {z, n.tok, "z"}, {B, n.bc, "B"},
+                           {C, n.bc, "C"}, {h0 == h_final ? nullptr : h0, n.state, "h0"},
+                           {conv0 == conv_final ? nullptr : conv0, hist, "conv0"},
+                           {cu, cu != nullptr ? (static_cast<size_t>(nseq) + 1) * 4 : 0, "cu_seqlens"},
+                           {p->A, n.a, "params->A"}, {p->D, n.vec, "params->D"}, {p->dt_bias, n.vec, "params->dt_bias"},
+                           {u_in ? nullptr : p->conv_w, n.cw, "params->conv_w"},
+                           {u_in ? nullptr : p->conv_b, n.vec, "params->conv_b"}});
+}
+
 // Fixed-length prefill, x (pre-conv) or u (u_in) as the token input.
 samba_status prefill_impl(const char *fn, bool u_in, int batch, int seqlen, int d_inner, int d_state, samba_dtype io,
                           const void *x, const void *dt, const void *B, const void *C, const void *z,
@@ -254,6 +316,9 @@ samba_status prefill_impl(const char *fn, bool u_in, int batch, int seqlen, int 
     OPTIONAL_PTR(conv0, "conv0");
     OPTIONAL_PTR(h_final, "h_final");
     OPTIONAL_PTR(conv_final, "conv_final");
+    st = scan_disjoint(fn, u_in, static_cast<size_t>(batch) * static_cast<size_t>(seqlen), batch, d_inner, d_state, io,
+                       nullptr, x, dt, B, C, z, params, h0, conv0, out, h_final, conv_final);
+    if (st != SAMBA_OK) return st;
     samba::ScanArgs a = make_args(batch, seqlen, nullptr, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.u_in = u_in;
@@ -291,6 +356,9 @@ samba_status varlen_impl(const char *fn, bool u_in, int nseq, const int32_t *cu_
     OPTIONAL_PTR(conv0, "conv0");
     OPTIONAL_PTR(h_final, "h_final");
     OPTIONAL_PTR(conv_final, "conv_final");
+    st = scan_disjoint(fn, u_in, static_cast<size_t>(total_tokens), nseq, d_inner, d_state, io, cu_seqlens, x, dt, B, C,
+                       z, params, h0, conv0, out, h_final, conv_final);
+    if (st != SAMBA_OK) return st;
     samba::ScanArgs a = make_args(nseq, max_seqlen, cu_seqlens, d_inner, d_state, x, dt, B, C, z, params, h0,
                                   conv0, out, h_final, conv_final);
     a.total = total_tokens;
@@ -384,6 +452,17 @@ samba_status samba_scan_decode(int nseq, int d_inner, int d_state, samba_dtype i
         return fail(SAMBA_ERR_INVALID_ARG, "%s: ring_head_out overlaps ring_head_in (the heads are double-buffered: "
                     "every workgroup of a sequence reads its head)", fn);
     OPTIONAL_PTR(z, "z");
+    {
+        // h and the conv ring are read and written in place: they may not overlap anything else.
+        const ScanSizes n(static_cast<size_t>(nseq), nseq, d_inner, d_state, io);
+        st = check_disjoint(fn, {{out, n.tok, "out"}, {h, n.state, "h"}, {conv_ring, n.hist, "conv_ring"},
+                                 {ring_head_out, head_bytes, "ring_head_out"}},
+                            {{x, n.tok, "x"}, {dt, n.tok, "dt"}, {z, n.tok, "z"}, {B, n.bc, "B"}, {C, n.bc, "C"},
+                             {ring_head_in, head_bytes, "ring_head_in"}, {params->A, n.a, "params->A"},
+                             {params->D, n.vec, "params->D"}, {params->dt_bias, n.vec, "params->dt_bias"},
+                             {params->conv_w, n.cw, "params->conv_w"}, {params->conv_b, n.vec, "params->conv_b"}});
+        if (st != SAMBA_OK) return st;
+    }
     // A decode step is the recurrence over a single token whose state and history are
     // read and written in place.
     samba::ScanArgs a = make_args(nseq, 1, nullptr, d_inner, d_state, x, dt, B, C, z, params, h, conv_ring,
@@ -524,6 +603,23 @@ samba_status samba_scan_backward(int nseq, const int32_t *cu_seqlens, int seqlen
                     workspace == nullptr ? (size_t)0 : workspace_bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(SAMBA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+    {
+        const ScanSizes n(tokens, nseq, d_inner, d_state, io);
+        st = check_disjoint(
+            fn,
+            {{dx, n.tok, "dx"}, {ddt, n.tok, "ddt"}, {dz, z != nullptr ? n.tok : 0, "dz"}, {dB, n.bc, "dB"},
+             {dC, n.bc, "dC"}, {dA, n.a, "dA"}, {dD, n.vec, "dD"}, {ddt_bias, n.vec, "ddt_bias"},
+             {dconv_w, n.cw, "dconv_w"}, {dconv_b, n.vec, "dconv_b"}, {dh0, n.state, "dh0"},
+             {dconv0, n.hist, "dconv0"}, {workspace, need, "workspace"}},
+            {{x, n.tok, "x"}, {dt, n.tok, "dt"}, {z, n.tok, "z"}, {dout, n.tok, "dout"}, {B, n.bc, "B"},
+             {C, n.bc, "C"}, {h0, n.state, "h0"}, {dh_final, n.state, "dh_final"}, {conv0, n.hist, "conv0"},
+             {dconv_final, n.hist, "dconv_final"},
+             {cu_seqlens, cu_seqlens != nullptr ? (static_cast<size_t>(nseq) + 1) * 4 : 0, "cu_seqlens"},
+             {params->A, n.a, "params->A"}, {params->D, n.vec, "params->D"},
+             {params->dt_bias, n.vec, "params->dt_bias"}, {params->conv_w, n.cw, "params->conv_w"},
+             {params->conv_b, n.vec, "params->conv_b"}});
+        if (st != SAMBA_OK) return st;
+    }
     samba::BwdArgs a{};
     a.nseq = nseq;
     a.seqlen = seqlen;
@@ -615,6 +711,14 @@ samba_status samba_swa_prefill(int nseq, const int32_t *cu_seqlens, int seqlen, 
         return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace == nullptr ? (size_t)0 : workspace_bytes);
     REQUIRE_PTR(workspace, "workspace");
+    {
+        const size_t qo = tokens * n_heads * head_dim * 2, kv = tokens * n_kv_heads * head_dim * 2;
+        samba_status st = check_disjoint(
+            fn, {{out, qo, "out"}, {workspace, need, "workspace"}},
+            {{q, qo, "q"}, {k, kv, "k"}, {v, kv, "v"},
+             {cu_seqlens, cu_seqlens != nullptr ? (static_cast<size_t>(nseq) + 1) * 4 : 0, "cu_seqlens"}});
+        if (st != SAMBA_OK) return st;
+    }
     samba::SwaArgs a{};
     a.nseq = nseq;
     a.seqlen = seqlen;
@@ -687,6 +791,21 @@ samba_status swa_dec_common(const char *fn, int nseq, int n_heads, int n_kv_head
     if (nseq > 65535) return fail(SAMBA_ERR_UNSUPPORTED, "%s: nseq=%d exceeds 65535", fn, nseq);
     return SAMBA_OK;
 }
+
+// Outputs of an attention decode step (out, both rings, the partials) against its inputs and
+// each other; rings are [nseq][n_kv_heads][window + 1][head_dim] bf16.
+samba_status swa_dec_disjoint(const char *fn, int nseq, int n_heads, int n_kv_heads, int head_dim, int window,
+                              const void *q, const void *k, const void *v, const int32_t *pos, const void *k_cache,
+                              const void *v_cache, const void *out, const void *workspace, size_t ws_bytes)
+{
+    const size_t S = static_cast<size_t>(nseq), dh = static_cast<size_t>(head_dim);
+    const size_t qo = S * n_heads * dh * 2, kv = S * n_kv_heads * dh * 2;
+    const size_t ring = S * n_kv_heads * (static_cast<size_t>(window) + 1) * dh * 2;
+    return check_disjoint(fn,
+                          {{out, qo, "out"}, {k_cache, ring, "k_cache"}, {v_cache, ring, "v_cache"},
+                           {workspace, ws_bytes, "workspace"}},
+                          {{q, qo, "q"}, {k, kv, "k"}, {v, kv, "v"}, {pos, S * 4, "pos"}});
+}
 }  // namespace
 
 samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_dim, int window, float rope_base,
@@ -713,6 +832,9 @@ samba_status samba_swa_decode(int nseq, int n_heads, int n_kv_heads, int head_di
         return fail(SAMBA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     workspace == nullptr ? (size_t)0 : workspace_bytes);
     REQUIRE_PTR(workspace, "workspace");
+    st = swa_dec_disjoint(fn, nseq, n_heads, n_kv_heads, head_dim, window, q, k, v, pos, k_cache, v_cache, out,
+                          workspace, need);
+    if (st != SAMBA_OK) return st;
     samba::SwaDecArgs a = swa_dec_args(nseq, n_heads, n_kv_heads, head_dim, window, rope_base, q, k, v, pos, k_cache,
                                        v_cache, out, workspace);
     samba::launch_swa_decode(a, static_cast<hipStream_t>(stream));
@@ -744,6 +866,9 @@ samba_status samba_swa_decode_noalloc(int nseq, int n_heads, int n_kv_heads, int
     REQUIRE_PTR(k_cache, "k_cache");
     REQUIRE_PTR(v_cache, "v_cache");
     if (pos == nullptr) return fail(SAMBA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
+    st = swa_dec_disjoint(fn, nseq, n_heads, n_kv_heads, head_dim, window, q, k, v, pos, k_cache, v_cache, out,
+                          nullptr, 0);
+    if (st != SAMBA_OK) return st;
     void *part = scratch_on(fn);
     if (part == nullptr) return SAMBA_ERR_HIP;
     // Every partial the combine reads is written by the attention kernel of the same call
@@ -777,6 +902,15 @@ samba_status samba_swa_kv_fill(int nseq, const int32_t *cu_seqlens, int seqlen, 
     }
     REQUIRE_PTR(k_cache, "k_cache");
     REQUIRE_PTR(v_cache, "v_cache");
+    {
+        const size_t kv = tokens * n_kv_heads * static_cast<size_t>(head_dim) * 2;
+        const size_t ring = static_cast<size_t>(nseq) * n_kv_heads * (static_cast<size_t>(window) + 1) * head_dim * 2;
+        st = check_disjoint(fn, {{k_cache, ring, "k_cache"}, {v_cache, ring, "v_cache"}},
+                            {{k, kv, "k"}, {v, kv, "v"},
+                             {cu_seqlens, cu_seqlens != nullptr ? (static_cast<size_t>(nseq) + 1) * 4 : 0,
+                              "cu_seqlens"}});
+        if (st != SAMBA_OK) return st;
+    }
     samba::SwaDecArgs a{};
     a.S = nseq;
     a.Hq = n_kv_heads;
