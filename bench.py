@@ -83,6 +83,7 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true", help="time only the long-prompt prefill (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="time only the streaming decode (profiling)")
     ap.add_argument("--model-only", action="store_true", help="time only the GEMMs and the whole-model decode step")
+    ap.add_argument("--model-step-only", action="store_true", help="time only the whole-model decode step (profiling)")
     ap.add_argument("--valu-probe", action="store_true", help="run only the vector-ALU issue-rate probe")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the prefill and a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -358,7 +359,10 @@ def bench_swa(dev, steps, warmup):
 def bench_gemm(dev, steps, warmup):
     """The layer projections on the matrix cores at the 1.7B widths (bf16 operands, fp32
     accumulation): prefill shapes (4 x 4096 tokens) against the bf16 MFMA peak, and the
-    decode shapes (256 tokens) against HBM for their weights."""
+    decode shapes (256 tokens) against HBM for their weights.  A decode shape is timed as in
+    the decode step: calls back to back (one HIP graph of 40 calls, so no launch gaps) on
+    weights that are not in any cache (the calls rotate over copies totalling >= 600 MB,
+    more than the 256 MB MALL)."""
     import torch
     import selective_state_space_samba_amd as ss
     g = torch.Generator(device=dev)
@@ -366,17 +370,40 @@ def bench_gemm(dev, steps, warmup):
     res = {}
     shapes = [("in_proj_16k", 16384, 4096, 2048, "store"), ("out_proj_16k", 16384, 2048, 4096, "add"),
               ("mlp_w12_swiglu_16k", 16384, 8200, 2048, "swiglu"), ("mlp_w3_16k", 16384, 2048, 8200, "add"),
-              ("in_proj_decode256", 256, 4096, 2048, "store"), ("mlp_w12_swiglu_decode256", 256, 8200, 2048, "swiglu")]
+              ("in_proj_decode256", 256, 4096, 2048, "store"), ("mlp_w12_swiglu_decode256", 256, 8200, 2048, "swiglu"),
+              # the rest of the decode step's projections (1.7B widths, 256 rows)
+              ("in_gate_decode256", 256, 8192, 2048, "store"), ("x_proj_decode256", 256, 160, 4096, "store"),
+              ("dt_up_decode256", 256, 4096, 128, "store"), ("out_proj_decode256", 256, 2048, 4096, "add"),
+              ("qkv_decode256", 256, 2560, 2048, "store"), ("w_o_decode256", 256, 2048, 2048, "add"),
+              ("mlp_w3_decode256", 256, 2048, 8200, "add")]
     for name, M, N, K, epi in shapes:
         Nw = 2 * N if epi == "swiglu" else N
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
-        w = (torch.randn((Nw, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16)
+        copies = max(2, -(-600_000_000 // (Nw * K * 2))) if M <= 256 else 1
+        ws_ = [(torch.randn((Nw, K), generator=g, device=dev) * K ** -0.5).to(torch.bfloat16) for _ in range(copies)]
+        w = ws_[0]
         r = torch.randn((M, N), generator=g, device=dev) if epi == "add" else None
         out = torch.empty((M, N), device=dev, dtype=torch.float32 if epi == "add" else torch.bfloat16)
         need = int(ss.load().samba_gemm_workspace_bytes(M, N, K, ss.GEMM_EPILOGUES[epi]))
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        _, per = time_calls(lambda: ss.gemm(a, w, epilogue=epi, out=out, residual=r, workspace=ws), steps, warmup)
-        sec = float(np.median(per))
+        if M <= 256:
+            calls = 40
+            for i in range(3):
+                ss.gemm(a, ws_[i % copies], epilogue=epi, out=out, residual=r, workspace=ws)
+            graph, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap), torch.cuda.graph(graph, stream=cap):
+                for i in range(calls):
+                    ss.gemm(a, ws_[i % copies], epilogue=epi, out=out, residual=r, workspace=ws)
+            torch.cuda.current_stream().wait_stream(cap)
+            graph.replay()
+            torch.cuda.synchronize()
+            _, per = time_calls(graph.replay, max(3, steps // 3), 1)
+            sec = float(np.median(per)) / calls
+            del graph
+        else:
+            _, per = time_calls(lambda: ss.gemm(a, w, epilogue=epi, out=out, residual=r, workspace=ws), steps, warmup)
+            sec = float(np.median(per))
         fl = 2.0 * M * K * Nw
         d = dict(workload="M=%d N=%d K=%d %s" % (M, N, K, epi), us=sec * 1e6,
                  roofline=dict(bound="mfma", achieved=round(fl / sec / 1e12, 1), peak=2500.0, unit="TFLOP/s",
@@ -385,7 +412,7 @@ def bench_gemm(dev, steps, warmup):
             wb = Nw * K * 2
             d["weights_gbs"] = round(wb / sec / 1e9, 1)
         res[name] = d
-        del a, w, r, out, ws
+        del a, w, ws_, r, out, ws
     return res
 
 
@@ -621,6 +648,9 @@ def main():
 
     if args.valu_probe:
         print(json.dumps({"valu_probe": valu_probe()}), flush=True)
+        return
+    if args.model_step_only:
+        print(json.dumps({"model_decode_1p7b": bench_model_decode(dev, args.steps, args.warmup)}), flush=True)
         return
     if args.model_only:
         print(json.dumps({"gemm": bench_gemm(dev, args.steps, args.warmup),

@@ -27,6 +27,8 @@
 #include "scan_common.h"
 
 #include <algorithm>
+#include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -402,6 +404,277 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_ring_kernel(GemmArgs a)
     store_tile_out<FM, FN, kOutCols, kEpi>(a, acc, m0, n0, wm, wn, lane, split);
 }
 
+// Skinny products: the decode step's projections, a few hundred token rows against 2K-16K
+// weight rows.  Every weight is used by few rows, so the work is streaming operands at a
+// memory latency of a few microseconds under load, and the kernel is built for loads in
+// flight and for independent waves:
+// - the K range of a tile is split over the workgroup's KW waves (contiguous 64-wide
+//   blocks per wave), and each wave streams its own blocks through its own NS LDS slots
+//   with loads straight into LDS (buffer_load_dwordx4 ... lds: 8 rows x 128 bytes per
+//   instruction, whole cache lines), NS - 1 blocks in flight while the current one is
+//   multiplied; a wave reads only what it loaded itself, so the loop has no barrier;
+// - fragments are read from LDS with the XOR swizzle of the other kernels (conflict-free);
+// - at the end the waves' fp32 tiles are summed through LDS in wave order (a fixed order:
+//   the result does not depend on timing), so a tile needs no partial sums in memory
+//   unless its K range is also split across workgroups (a.splits > 1: kPartial, summed by
+//   the reduce kernels below).
+// Rows past M and W rows past the tile's extent load zeros through the buffer resources; K
+// past the wave's range loads zeros through kOob.  The epilogue (bf16 store with the optional
+// conv of the new token, fp32 residual add, SwiGLU or fp32 partials) reads the summed tile
+// in row order, 4 consecutive outputs per thread, so its global traffic is whole vectors.
+template <int FM, int FN, int NS, int kEpi>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
+{
+    constexpr int KW = 4;
+    constexpr int TM = 16 * FM, TN = 16 * FN;
+    constexpr int kOutCols = kEpi == kSwiglu ? TN / 2 : TN;
+    constexpr int kRows = TM + TN;                 // rows of one block: A rows, then W rows
+    constexpr int kLd = kRows / 8;                 // load instructions per block
+    constexpr int kSlot = kRows * kPitch;          // elements of one slot
+    static_assert(kEpi != kSwiglu || FN % 2 == 0, "SwiGLU tiles pair W1 and W2 blocks");
+    static_assert(FM * FN * 64 * 16 <= NS * kSlot * 2, "the summing area of a wave fits in its slots");
+    static_assert(NS >= 2 && (NS - 1) * kLd <= 63, "the wait count of NS - 1 blocks in flight must fit vmcnt");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[KW][NS][kSlot];
+
+    int tm, tn, split;
+    tile_of(a, tm, tn, split);
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m0 = tm * TM, n0 = tn * kOutCols;
+    const int kbeg = split * a.ksplit;
+    const int kend = min(a.K, kbeg + a.ksplit);
+    const int nb = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+    const int b0 = nb * w / KW, b1 = nb * (w + 1) / KW;
+
+    const int rows_a = min(TM, a.M - m0);
+    const Rsrc ra = make_rsrc(a.A + static_cast<size_t>(m0) * a.lda,
+                              rows_a > 0 ? static_cast<uint32_t>(((rows_a - 1) * a.lda + a.K) * 2) : 0u);
+    Rsrc rw, rw2;
+    if constexpr (kEpi == kSwiglu) {
+        const int rows = max(0, min(kOutCols, a.N - n0));
+        const uint32_t ext = static_cast<uint32_t>(rows * a.K * 2);
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, ext);
+        rw2 = make_rsrc(a.W + static_cast<size_t>(a.N + n0) * a.K, ext);
+    } else {
+        const int rows = max(0, min(TN, a.Nw - n0));
+        rw = make_rsrc(a.W + static_cast<size_t>(n0) * a.K, static_cast<uint32_t>(rows * a.K * 2));
+        rw2 = rw;
+    }
+    // Load instruction j of a block covers slot rows 8 j .. 8 j + 7; lane l loads row
+    // 8 j + l / 8 at the 16-byte chunk that the swizzle stores at position l % 8.
+    uint32_t off[kLd];
+    int qk[kLd];
+#pragma unroll
+    for (int j = 0; j < kLd; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        qk[j] = ((lane & 7) ^ swz(r)) * 8;
+        if (8 * j < TM) {
+            off[j] = static_cast<uint32_t>(r * a.lda * 2);
+        } else {
+            const int wr = r - TM;
+            // SwiGLU: W rows alternate 16-row blocks of W1 and W2 (the W2 resource)
+            const int wrow = kEpi == kSwiglu ? ((wr >> 4) >> 1) * 16 + (wr & 15) : wr;
+            off[j] = static_cast<uint32_t>(wrow * a.K * 2);
+        }
+    }
+    auto issue = [&](int b, int slot) {
+        // blocks past the wave's range: every K index is past the limit
+        const int lim = __builtin_amdgcn_readfirstlane(b < b1 ? kend : INT32_MIN);
+        const int kb = kbeg + b * kTK;
+#pragma unroll
+        for (int j = 0; j < kLd; ++j) {
+            const int k = kb + qk[j];
+            const uint32_t o = k < lim ? off[j] + static_cast<uint32_t>(k) * 2u : kOob;
+            const bool w2 = kEpi == kSwiglu && 8 * j >= TM && (((8 * j - TM) >> 4) & 1);
+            const Rsrc rs = 8 * j < TM ? ra : (w2 ? rw2 : rw);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void *)&lds[w][slot][8 * j * kPitch], 16, o, 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int frow = lane & 15, fk = 8 * (lane >> 4);
+    auto mult = [&](int slot) {
+        const uint16_t *as = &lds[w][slot][frow * kPitch];
+        const uint16_t *bs = &lds[w][slot][(TM + frow) * kPitch];
+        bf16x8 af[2][FM], bf[2][FN];
+#pragma unroll
+        for (int h = 0; h < kTK / 32; ++h) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[h][i] = *reinterpret_cast<const bf16x8 *>(as + i * 16 * kPitch + (((h * 4 + (fk >> 3)) ^ swz(frow)) << 3));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bf[h][j] = *reinterpret_cast<const bf16x8 *>(bs + j * 16 * kPitch + (((h * 4 + (fk >> 3)) ^ swz(frow)) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int h = 0; h < kTK / 32; ++h)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[h][i], bf[h][j], acc[i][j], 0, 0, 0);
+    };
+
+    // Blocks b + 1 .. b + NS - 1 are in flight while block b is multiplied; every iteration
+    // issues the same loads (blocks past the range load zeros), so one wait count fits every
+    // path.  A slot is overwritten only after the products that read it: their LDS reads
+    // completed before the MFMAs that consume them.
+    if (b0 < b1) {
+#pragma unroll
+        for (int q = 0; q < NS - 1; ++q) issue(b0 + q, q);
+        int slot = 0;
+        for (int b = b0; b < b1; ++b) {
+            issue(b + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kLd));
+            asm volatile("" ::: "memory");
+            mult(slot);
+            __builtin_amdgcn_sched_barrier(0);
+            slot = slot == NS - 1 ? 0 : slot + 1;
+        }
+        // the last issues (zeros) may still be writing their slots
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+
+    // the waves' tiles summed in wave order, each wave's tile in its own slots
+    f32x4 *red = reinterpret_cast<f32x4 *>(&lds[w][0][0]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) red[(i * FN + j) * 64 + lane] = acc[i][j];
+    __syncthreads();
+
+    // Epilogue in row order: thread t owns 4 consecutive output columns of a row, so global
+    // reads and writes are whole 8- or 16-byte vectors along rows.  Element (r, c) of the
+    // product tile (i, j) sits in lane c % 16 + 16 ((r % 16) / 4), component r % 4.
+    constexpr int kTpr = kOutCols / 4;            // threads per output row
+    constexpr int kRpp = 256 / kTpr;              // rows per pass
+    static_assert(kOutCols % 4 == 0 && 256 % kTpr == 0, "epilogue thread map");
+    const int tid = threadIdx.x;
+    const int c4 = 4 * (tid % kTpr);              // first output column in the tile
+    const int cblk = c4 >> 4, clane = c4 & 15;
+    auto summed = [&](int tile, int ln, int e) {
+        const float *base = reinterpret_cast<const float *>(&lds[0][0][0]);
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KW; ++q)
+            v += base[q * (NS * kSlot / 2) + ((tile * 64 + ln) * 4 + e)];
+        return v;
+    };
+    const int col = n0 + c4;
+    const bool vec_out = kEpi == kPartial ? (a.Nw % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0) :
+                         kEpi == kAdd ? (a.ldo % 4 == 0 && a.ldr % 4 == 0 &&
+                                         (reinterpret_cast<uintptr_t>(a.out) & 15u) == 0 &&
+                                         (reinterpret_cast<uintptr_t>(a.R) & 15u) == 0)
+                                      : (a.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(a.out) & 7u) == 0);
+    constexpr int kPasses = (TM + kRpp - 1) / kRpp;
+    uint2 xpk[kPasses];                           // the stored x of each pass (conv input)
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int r = pass * kRpp + tid / kTpr;   // row in the tile
+        const int row = m0 + r;
+        if (r >= TM || row >= a.M) continue;
+        const int ln0 = clane + 16 * ((r & 15) >> 2), e = r & 3;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if constexpr (kEpi == kSwiglu) {
+                const int t1 = (r >> 4) * FN + 2 * cblk;
+                v[u] = summed(t1, ln0 + u, e) * silu_f(summed(t1 + 1, ln0 + u, e));
+            } else {
+                v[u] = summed((r >> 4) * FN + cblk, ln0 + u, e);
+            }
+        }
+        const int ncols = kEpi == kPartial ? a.Nw : a.N;
+        if constexpr (kEpi == kPartial) {
+            float *dst = a.part + (static_cast<size_t>(split) * a.M + row) * a.Nw + col;
+            if (vec_out && col + 3 < ncols) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (col + u < ncols) dst[u] = v[u];
+            }
+        } else if constexpr (kEpi == kAdd) {
+            float *dst = static_cast<float *>(a.out) + static_cast<size_t>(row) * a.ldo + col;
+            const float *res = a.R + static_cast<size_t>(row) * a.ldr + col;
+            if (vec_out && col + 3 < ncols) {
+                const float4 rv = *reinterpret_cast<const float4 *>(res);
+                *reinterpret_cast<float4 *>(dst) = make_float4(rv.x + v[0], rv.y + v[1], rv.z + v[2], rv.w + v[3]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (col + u < ncols) dst[u] = res[u] + v[u];
+            }
+        } else {
+            uint16_t *dst = static_cast<uint16_t *>(a.out) + static_cast<size_t>(row) * a.ldo + col;
+            if (vec_out && col + 3 < ncols) {
+                const uint2 pk = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+                *reinterpret_cast<uint2 *>(dst) = pk;
+                if constexpr (kEpi == kStore) xpk[pass] = pk;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (col + u < ncols) dst[u] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[u]));
+            }
+        }
+    }
+    if constexpr (kEpi == kStore) {
+        // the conv of the one new token for the columns below cD, in the order and precision
+        // of conv_silu_kernel: x as stored (bf16), the history as stored.  All loads of the
+        // thread's rows are issued before any is used: the three ring slots of every row (the
+        // ring head only selects among them), its head, the weights and the bias of its 4
+        // columns.  conv_fusable guarantees whole 4-column groups (vec_out) here.
+        if (a.cu != nullptr && col < a.cD && vec_out) {
+            uint2 hs[kPasses][3];
+            int hd[kPasses];
+#pragma unroll
+            for (int pass = 0; pass < kPasses; ++pass) {
+                const int r = pass * kRpp + tid / kTpr, row = m0 + r;
+                const bool ok = r < TM && row < a.M;
+                const uint16_t *h = a.c0 + static_cast<size_t>(ok ? row : 0) * 3 * a.cD + col;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) hs[pass][k] = *reinterpret_cast<const uint2 *>(h + k * a.cD);
+                hd[pass] = ok && a.chead != nullptr ? a.chead[row] : 0;
+            }
+            float4 cwv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cwv[u] = *reinterpret_cast<const float4 *>(a.cw + static_cast<size_t>(col + u) * 4);
+            const float4 cbv = a.cb != nullptr ? make_float4(a.cb[col], a.cb[col + 1], a.cb[col + 2], a.cb[col + 3])
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float cbs[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+#pragma unroll
+            for (int pass = 0; pass < kPasses; ++pass) {
+                const int r = pass * kRpp + tid / kTpr, row = m0 + r;
+                if (r >= TM || row >= a.M) continue;
+                const uint2 pk = xpk[pass];
+                const float xs[4] = {bf16lo(pk.x), bf16hi(pk.x), bf16lo(pk.y), bf16hi(pk.y)};
+                const int s0 = ring_slot(hd[pass], 0);
+                const uint2 h0 = s0 == 0 ? hs[pass][0] : (s0 == 1 ? hs[pass][1] : hs[pass][2]);
+                const uint2 h1 = s0 == 0 ? hs[pass][1] : (s0 == 1 ? hs[pass][2] : hs[pass][0]);
+                const uint2 h2 = s0 == 0 ? hs[pass][2] : (s0 == 1 ? hs[pass][0] : hs[pass][1]);
+                const float w0[4] = {bf16lo(h0.x), bf16hi(h0.x), bf16lo(h0.y), bf16hi(h0.y)};
+                const float w1[4] = {bf16lo(h1.x), bf16hi(h1.x), bf16lo(h1.y), bf16hi(h1.y)};
+                const float w2[4] = {bf16lo(h2.x), bf16hi(h2.x), bf16lo(h2.y), bf16hi(h2.y)};
+                float uu[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float pre = __builtin_fmaf(cwv[u].x, w0[u], cbs[u]);
+                    pre = __builtin_fmaf(cwv[u].y, w1[u], pre);
+                    pre = __builtin_fmaf(cwv[u].z, w2[u], pre);
+                    pre = __builtin_fmaf(cwv[u].w, xs[u], pre);
+                    uu[u] = silu_f(pre);
+                }
+                *reinterpret_cast<uint2 *>(a.cu + static_cast<size_t>(row) * a.cD + col) =
+                    make_uint2(pack_bf16(uu[0], uu[1]), pack_bf16(uu[2], uu[3]));
+            }
+        }
+    }
+}
+
 // Sums the split partials in split order and applies the epilogue; one thread per kVec
 // consecutive outputs of a row (kVec = 4: 16-byte partial loads, when N, the row pitches and
 // the output are aligned for them; see vec_ok).
@@ -557,10 +830,125 @@ __global__ __launch_bounds__(256) void gemm_reduce_add_norm_kernel(GemmArgs a)
 struct Plan {
     int fm, fn;       // tile config
     bool w8;          // 256 x 256 tiles on 8 waves (4 along M x 2 along N), gemm_ring_kernel
+    bool stream;      // gemm_stream_kernel with a 16 fm x 16 fn tile and ns LDS slots per wave
+    int ns;
+    int ring;         // > 0: 128 x 128 tiles on gemm_ring_kernel with this many stages
     int splits, ksplit;
     int tiles_m, tiles_n;
     size_t part_bytes;
 };
+
+// The stream kernel's tile shapes (FM, FN, LDS slots per wave).  Two slots measured best
+// (three to five slots per wave, i.e. more blocks in flight, were slower on every decode
+// shape: the operand traffic through L2, not the latency, bounds these products).
+constexpr int kStreamShapes[][3] = {{4, 4, 2}, {4, 2, 2}, {2, 4, 2}, {2, 2, 2}};
+
+// Plan of a skinny product: the stream kernel's shape and split count of least estimated
+// time, or, for SwiGLU, 128 x 128 tiles on the two-stage ring kernel.  SAMBA_GEMM_STREAM =
+// "FMxFNnNSsS" (the n and s parts optional) forces a built stream shape, "rNSsS" the ring
+// kernel with NS stages, for tests and timing.
+inline bool plan_stream(int M, int N, int K, int epi, Plan &p)
+{
+    const int Nw = epi == kSwiglu ? 2 * N : N;
+    const int nk = (K + kTK - 1) / kTK;
+    auto grid_of = [&](int fm, int fn, int s) {
+        const int TM = 16 * fm, TN = 16 * fn;
+        const long long tn = s > 1 || epi != kSwiglu ? (Nw + TN - 1) / TN : (N + TN / 2 - 1) / (TN / 2);
+        return static_cast<long long>((M + TM - 1) / TM) * tn * s;
+    };
+    int fm = 0, fn = 0, ns = 0, s = 1;
+    const char *force = getenv("SAMBA_GEMM_STREAM");
+    int st = 0;
+    if (force != nullptr && force[0] == 'r') {
+        if (sscanf(force, "r%ds%d", &st, &s) < 1 || st < 2 || st > 4 || s < 1) return false;
+    } else if ((force == nullptr || force[0] == '\0') && epi == kSwiglu &&
+               static_cast<long long>((M + 127) / 128) * ((N + 63) / 64) >= 128) {
+        // SwiGLU: the W1 / W2 pairs double the weight rows per output, and 128 x 128 tiles
+        // on the two-stage ring, two workgroups per CU, measured faster than the stream
+        // kernel (36 vs 52 us on the 1.7B MLP at 256 rows)
+        st = 2;
+    }
+    if (st > 0) {
+        p.stream = false;
+        p.w8 = false;
+        p.ring = st;
+        p.fm = 4;
+        p.fn = 4;
+        const int kt_per = (nk + s - 1) / s;
+        p.ksplit = std::max(1, kt_per) * kTK;
+        p.splits = nk > 0 ? (nk + kt_per - 1) / kt_per : 1;
+        p.tiles_m = (M + 127) / 128;
+        p.tiles_n = p.splits > 1 || epi != kSwiglu ? (Nw + 127) / 128 : (N + 63) / 64;
+        p.part_bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
+        return true;
+    }
+    if (force != nullptr && force[0] != '\0') {
+        const char *q = force;
+        char *e = nullptr;
+        fm = static_cast<int>(strtol(q, &e, 10));
+        if (e == q || *e != 'x') return false;
+        q = e + 1;
+        fn = static_cast<int>(strtol(q, &e, 10));
+        if (e == q) return false;
+        q = e;
+        if (*q == 'n') {
+            ns = static_cast<int>(strtol(q + 1, &e, 10));
+            q = e;
+        }
+        if (*q == 's') {
+            s = static_cast<int>(strtol(q + 1, &e, 10));
+            q = e;
+        }
+        if (*q != '\0' || s < 1 || (epi == kSwiglu && fn % 2 != 0)) return false;
+        bool known = false;
+        for (const auto &sh : kStreamShapes)
+            if (sh[0] == fm && sh[1] == fn && (ns == 0 || sh[2] == ns)) {
+                known = true;
+                ns = sh[2];
+                break;
+            }
+        if (!known) return false;
+    } else {
+        // Estimated time (microseconds) of each shape and split count, fitted to the decode
+        // projections measured on MI355X: a workgroup streams its operand bytes at about
+        // 55 GB/s when 128 or more run (up to twice that when few do), the chip at most
+        // about 11 TB/s; plus ~4 us of latency and ~4 us for the reduce of a split K range.
+        double best = 1e30;
+        for (const auto &sh : kStreamShapes) {
+            if (epi == kSwiglu && sh[1] % 2 != 0) continue;
+            const int lds = 4 * sh[2] * 16 * (sh[0] + sh[1]) * 128;
+            const int per_cu = std::max(1, (160 << 10) / lds);
+            for (int ss = 1; ss <= 8; ss *= 2) {
+                if (ss > 1 && nk < 4 * ss) break;
+                const long long g = grid_of(sh[0], sh[1], ss);
+                const double kslice = static_cast<double>((nk + ss - 1) / ss) * kTK;
+                const double wg_bytes = kslice * 16.0 * (sh[0] + sh[1]) * 2.0;
+                const double total = wg_bytes * static_cast<double>(g);
+                const double rounds = std::ceil(static_cast<double>(g) / (256.0 * per_cu));
+                const double cu_rate = 55e9 * std::min(2.0, std::max(1.0, 128.0 / static_cast<double>(g)));
+                const double t = 4.0 + std::max(total / 11e12, rounds * wg_bytes / cu_rate) * 1e6 + (ss > 1 ? 4.0 : 0.0);
+                if (t < best) {
+                    best = t;
+                    fm = sh[0], fn = sh[1], ns = sh[2], s = ss;
+                }
+            }
+        }
+        if (fm == 0) return false;
+    }
+    p.stream = true;
+    p.w8 = false;
+    p.fm = fm;
+    p.fn = fn;
+    p.ns = ns;
+    const int kt_per = (nk + s - 1) / s;
+    p.ksplit = std::max(1, kt_per) * kTK;
+    p.splits = nk > 0 ? (nk + kt_per - 1) / kt_per : 1;
+    const int TM = 16 * fm, TN = 16 * fn;
+    p.tiles_m = (M + TM - 1) / TM;
+    p.tiles_n = p.splits > 1 || epi != kSwiglu ? (Nw + TN - 1) / TN : (N + TN / 2 - 1) / (TN / 2);
+    p.part_bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * M * Nw * sizeof(float) : 0;
+    return true;
+}
 
 // Tile shape and split count for a problem.  Large problems take 256 x 256 tiles (one
 // 8-wave workgroup per CU, 128 KB of LDS); problems with fewer than 256 such tiles take
@@ -573,6 +961,15 @@ inline Plan plan(int M, int N, int K, int epi)
 {
     Plan p{};
     const int Nw = epi == kSwiglu ? 2 * N : N;
+    {
+        // skinny products (the decode step) stream the weights; 32-bit buffer offsets bound
+        // the operand sizes it takes
+        const char *off = getenv("SAMBA_GEMM_STREAM");
+        const bool no_stream = off != nullptr && strcmp(off, "0") == 0;
+        if (!no_stream && M <= 256 && static_cast<long long>(M) * K * 2 < (1ll << 31) &&
+            static_cast<long long>(Nw) * K * 2 < (1ll << 31) && plan_stream(M, N, K, epi, p))
+            return p;
+    }
     auto tiles = [&](int tm, int tn) {
         const long long outc = epi == kSwiglu ? tn / 2 : tn;
         return static_cast<long long>((M + tm - 1) / tm) * ((N + outc - 1) / outc);
@@ -618,7 +1015,8 @@ inline bool norm_fusable(const GemmArgs &a, int epi, const Plan &p)
 inline bool conv_fusable(const GemmArgs &a, int epi, const Plan &p)
 {
     const auto a_n = [](const void *q, unsigned n) { return (reinterpret_cast<uintptr_t>(q) & (n - 1u)) == 0; };
-    return a.cu != nullptr && a.cw != nullptr && a.c0 != nullptr && epi == kStore && p.splits > 1 && vec_ok(a, epi) &&
+    return a.cu != nullptr && a.cw != nullptr && a.c0 != nullptr && epi == kStore && (p.splits > 1 || p.stream) &&
+           vec_ok(a, epi) &&
            a.cD > 0 && a.cD % 4 == 0 && a.cD <= a.N && a_n(a.cw, 16) && a_n(a.c0, 8) && a_n(a.cu, 8);
 }
 
@@ -631,7 +1029,7 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool 
     if (normed != nullptr) *normed = false;
     if (conved != nullptr) *conved = false;
     if (!conv_fusable(a, epi, p)) a.cu = nullptr;
-    if (p.fm == 8 && p.splits > 1) return false;
+    if (p.fm == 8 && p.splits > 1 && !p.stream) return false;
     a.splits = p.splits;
     a.ksplit = p.ksplit;
     a.tiles_m = p.tiles_m;
@@ -643,7 +1041,42 @@ inline bool launch_gemm(GemmArgs a, int epi, const Plan &p, hipStream_t s, bool 
     const int kern_epi = p.splits > 1 ? kPartial : epi;
 #define SAMBA_GEMM_LAUNCH(FM, FN, E) hipLaunchKernelGGL((gemm_kernel<2, 2, FM, FN, E>), dim3(grid), dim3(256), 0, s, a)
 #define SAMBA_GEMM_LAUNCH8(E) hipLaunchKernelGGL((gemm_ring_kernel<4, 2, 4, 8, E, 2>), dim3(grid), dim3(512), 0, s, a)
-    if (p.fm == 8 && p.w8) {
+    if (p.ring > 0) {
+#define SAMBA_GEMM_RING128(S)                                                                                \
+    switch (kern_epi) {                                                                                      \
+    case kStore: hipLaunchKernelGGL((gemm_ring_kernel<2, 2, 4, 4, kStore, S>), dim3(grid), dim3(256), 0, s, a); break; \
+    case kAdd: hipLaunchKernelGGL((gemm_ring_kernel<2, 2, 4, 4, kAdd, S>), dim3(grid), dim3(256), 0, s, a); break;     \
+    case kSwiglu: hipLaunchKernelGGL((gemm_ring_kernel<2, 2, 4, 4, kSwiglu, S>), dim3(grid), dim3(256), 0, s, a); break; \
+    default: hipLaunchKernelGGL((gemm_ring_kernel<2, 2, 4, 4, kPartial, S>), dim3(grid), dim3(256), 0, s, a); break; \
+    }
+        if (p.ring == 2) {
+            SAMBA_GEMM_RING128(2)
+        } else if (p.ring == 3) {
+            SAMBA_GEMM_RING128(3)
+        } else {
+            SAMBA_GEMM_RING128(4)
+        }
+#undef SAMBA_GEMM_RING128
+    } else if (p.stream) {
+        bool ok = false;
+#define SAMBA_GEMM_STREAM_SHAPE(FM, FN, NS)                                                          \
+    if (p.fm == FM && p.fn == FN && p.ns == NS) {                                                    \
+        ok = true;                                                                                   \
+        switch (kern_epi) {                                                                          \
+        case kStore: hipLaunchKernelGGL((gemm_stream_kernel<FM, FN, NS, kStore>), dim3(grid), dim3(256), 0, s, a); break; \
+        case kAdd: hipLaunchKernelGGL((gemm_stream_kernel<FM, FN, NS, kAdd>), dim3(grid), dim3(256), 0, s, a); break;     \
+        case kSwiglu: hipLaunchKernelGGL((gemm_stream_kernel<FM, FN, NS, kSwiglu>), dim3(grid), dim3(256), 0, s, a); break; \
+        default: hipLaunchKernelGGL((gemm_stream_kernel<FM, FN, NS, kPartial>), dim3(grid), dim3(256), 0, s, a); break; \
+        }                                                                                            \
+    }
+        SAMBA_GEMM_STREAM_SHAPE(4, 4, 2)
+        SAMBA_GEMM_STREAM_SHAPE(4, 2, 2)
+        SAMBA_GEMM_STREAM_SHAPE(2, 4, 2)
+        SAMBA_GEMM_STREAM_SHAPE(2, 2, 2)
+#undef SAMBA_GEMM_STREAM_SHAPE
+        if (!ok) return false;
+        if (conved != nullptr && p.splits == 1) *conved = a.cu != nullptr;
+    } else if (p.fm == 8 && p.w8) {
         switch (kern_epi) {
         case kStore: SAMBA_GEMM_LAUNCH8(kStore); break;
         case kAdd: SAMBA_GEMM_LAUNCH8(kAdd); break;

@@ -127,6 +127,34 @@ def test_gemm_strided_rows_and_output_pitch():
     assert np.all(hb[:, :30] == 0) and np.all(hb[:, 78:] == 0)
 
 
+# Every kernel a skinny product can take (the plan picks one by an estimate; SAMBA_GEMM_STREAM
+# forces the stream kernel's tile shape and split count, "r2" the 128 x 128 ring kernel, "0"
+# the register-staged kernel), on ragged shapes and every epilogue.
+@pytest.mark.parametrize("force", ["4x4", "4x2", "2x4", "2x2", "4x4s2", "2x2s3", "4x2s8", "r2", "r3s2", "0"])
+@pytest.mark.parametrize("M,N,K,epi", [(37, 50, 72, "store"), (256, 300, 1000, "add"), (200, 100, 520, "swiglu"),
+                                       (256, 160, 4096, "store"), (3, 16, 8, "add")])
+def test_gemm_skinny_kernels(force, M, N, K, epi, monkeypatch):
+    monkeypatch.setenv("SAMBA_GEMM_STREAM", force)
+    print("case: gemm skinny", force, epi, M, N, K, flush=True)
+    Nw = 2 * N if epi == "swiglu" else N
+    a, w = operands(700 + M + N + K, M, N, K, wrows=Nw)
+    if epi == "add":
+        r = torch.from_numpy(np.random.default_rng(9).standard_normal((M, N)).astype(np.float32)).to(DEV)
+        r0 = host(r)
+        out = ss.gemm(a, w, epilogue="add", residual=r)
+        torch.cuda.synchronize()
+        check(out, r0 + model.linear(host(a), host(w)), TOL_F32_OUT)
+    elif epi == "swiglu":
+        out = ss.gemm(a, w, epilogue="swiglu")
+        torch.cuda.synchronize()
+        wh = host(w)
+        check(out, model.swiglu(host(a), wh[:N], wh[N:]), TOL_BF16_OUT)
+    else:
+        out = ss.gemm(a, w)
+        torch.cuda.synchronize()
+        check(out, model.linear(host(a), host(w)), TOL_BF16_OUT)
+
+
 def test_gemm_is_deterministic():
     a, w = operands(500, 256, 2048, 8200)
     o1 = host(ss.gemm(a, w))
@@ -141,6 +169,8 @@ def test_gemm_argument_errors():
     buf = torch.zeros(80, device=DEV)
     with pytest.raises(ss.SambaError, match="INVALID_ARG"):  # residual partially overlaps out
         ss.gemm(a, w, epilogue="add", residual=buf[:64].view(8, 8), out=buf[4:68].view(8, 8))
-    a2, w2 = operands(601, 256, 2048, 8200)
+    # a few rows and columns over a long K range: the K range is split across workgroups
+    a2, w2 = operands(601, 16, 64, 8192)
+    assert ss.load().samba_gemm_workspace_bytes(16, 64, 8192, 0) > 0
     with pytest.raises(ss.SambaError, match="WORKSPACE"):
         ss.gemm(a2, w2, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
