@@ -84,6 +84,7 @@ def parse():
     ap.add_argument("--decode-only", action="store_true", help="time only the streaming decode (profiling)")
     ap.add_argument("--model-only", action="store_true", help="time only the GEMMs and the whole-model decode step")
     ap.add_argument("--model-step-only", action="store_true", help="time only the whole-model decode step (profiling)")
+    ap.add_argument("--backward-only", action="store_true", help="time only the training-length gradients (profiling)")
     ap.add_argument("--valu-probe", action="store_true", help="run only the vector-ALU issue-rate probe")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the prefill and a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -211,6 +212,23 @@ def bench_decode(args, dev, S=256, P=256, warm_prefill=True, steps=None):
     t = a.elapsed_time(bev) / 1e3
     steps = reps * P
     return dict(S=S, steps=steps, seconds=t, per_step_eager=float(np.mean(per)))
+
+
+def bench_backward(dev, steps=5, warmup=2):
+    """The gradients alone at the training shape (batch 4 x 4096, bf16)."""
+    import torch
+    import selective_state_space_samba_amd as ss
+    from selective_state_space_samba_amd import synth
+    seed = synth.seed_for(1)
+    p = synth.make_params(seed, D_INNER, D_STATE)
+    prm = [to_dev(a, dev, bf16=False) for a in (p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b)]
+    tk = synth.make_tokens(seed, (4, 4096), D_INNER, D_STATE, "bf16")
+    ins = [to_dev(a, dev) for a in (tk.x, tk.dt, tk.B, tk.C, tk.z)]
+    g = to_dev(synth.make_tokens(seed, (4, 4096), D_INNER, D_STATE, "bf16", tag="grad").x, dev)
+    ws = torch.empty(int(ss.load().samba_scan_backward_workspace_bytes(4, 4096, 4 * 4096, D_INNER, D_STATE)),
+                     dtype=torch.uint8, device=dev)
+    _, per = time_calls(lambda: ss.backward(g, *ins, *prm, want_state_grads=False, workspace=ws), steps, warmup)
+    return dict(ms=float(np.mean(per) * 1e3), ms_median=float(np.median(per) * 1e3))
 
 
 def bench_extra(dev, steps=5, warmup=2):
@@ -648,6 +666,9 @@ def main():
 
     if args.valu_probe:
         print(json.dumps({"valu_probe": valu_probe()}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward_train4k": bench_backward(dev, args.steps, args.warmup)}), flush=True)
         return
     if args.model_step_only:
         print(json.dumps({"model_decode_1p7b": bench_model_decode(dev, args.steps, args.warmup)}), flush=True)
