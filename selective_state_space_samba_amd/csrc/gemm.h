@@ -523,9 +523,53 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
     // issues the same loads (blocks past the range load zeros), so one wait count fits every
     // path.  A slot is overwritten only after the products that read it: their LDS reads
     // completed before the MFMAs that consume them.
+    // The epilogue's thread map: thread t owns 4 consecutive output columns of a row, so
+    // global reads and writes are whole 8- or 16-byte vectors along rows.
+    constexpr int kTpr = kOutCols / 4;            // threads per output row
+    constexpr int kRpp = 256 / kTpr;              // rows per pass
+    constexpr int kPasses = (TM + kRpp - 1) / kRpp;
+    static_assert(kOutCols % 4 == 0 && 256 % kTpr == 0, "epilogue thread map");
+    const int tid = threadIdx.x;
+    const int c4 = 4 * (tid % kTpr);              // first output column in the tile
+    const int col = n0 + c4;
+    const bool vec_out = kEpi == kPartial ? (a.Nw % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0) :
+                         kEpi == kAdd ? (a.ldo % 4 == 0 && a.ldr % 4 == 0 &&
+                                         (reinterpret_cast<uintptr_t>(a.out) & 15u) == 0 &&
+                                         (reinterpret_cast<uintptr_t>(a.R) & 15u) == 0)
+                                      : (a.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(a.out) & 7u) == 0);
+
     if (b0 < b1) {
 #pragma unroll
         for (int q = 0; q < NS - 1; ++q) issue(b0 + q, q);
+    }
+    // The conv of the new token (store epilogue with a.cu): its inputs are loaded here, after
+    // the first blocks' loads and before the K loop, so that their latency hides behind the
+    // products instead of following them: the three ring slots of every row of the thread
+    // (the ring head only selects among them), the heads, the weights and the bias of its 4
+    // columns.  conv_fusable guarantees whole 4-column groups (vec_out) here.
+    [[maybe_unused]] uint2 hs[kPasses][3];
+    [[maybe_unused]] int hd[kPasses];
+    [[maybe_unused]] float4 cwv[4];
+    [[maybe_unused]] float cbs[4];
+    const bool conv = kEpi == kStore && a.cu != nullptr && col < a.cD && vec_out;
+    if constexpr (kEpi == kStore) {
+        if (conv) {
+#pragma unroll
+            for (int pass = 0; pass < kPasses; ++pass) {
+                const int r = pass * kRpp + tid / kTpr, row = m0 + r;
+                const bool ok = r < TM && row < a.M;
+                const uint16_t *h = a.c0 + static_cast<size_t>(ok ? row : 0) * 3 * a.cD + col;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) hs[pass][k] = *reinterpret_cast<const uint2 *>(h + k * a.cD);
+                hd[pass] = ok && a.chead != nullptr ? a.chead[row] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cwv[u] = *reinterpret_cast<const float4 *>(a.cw + static_cast<size_t>(col + u) * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cbs[u] = a.cb != nullptr ? a.cb[col + u] : 0.0f;
+        }
+    }
+    if (b0 < b1) {
         int slot = 0;
         for (int b = b0; b < b1; ++b) {
             issue(b + NS - 1, slot == 0 ? NS - 1 : slot - 1);
@@ -547,14 +591,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
         for (int j = 0; j < FN; ++j) red[(i * FN + j) * 64 + lane] = acc[i][j];
     __syncthreads();
 
-    // Epilogue in row order: thread t owns 4 consecutive output columns of a row, so global
-    // reads and writes are whole 8- or 16-byte vectors along rows.  Element (r, c) of the
-    // product tile (i, j) sits in lane c % 16 + 16 ((r % 16) / 4), component r % 4.
-    constexpr int kTpr = kOutCols / 4;            // threads per output row
-    constexpr int kRpp = 256 / kTpr;              // rows per pass
-    static_assert(kOutCols % 4 == 0 && 256 % kTpr == 0, "epilogue thread map");
-    const int tid = threadIdx.x;
-    const int c4 = 4 * (tid % kTpr);              // first output column in the tile
+    // Epilogue in row order (thread map above): element (r, c) of the product tile (i, j)
+    // sits in lane c % 16 + 16 ((r % 16) / 4), component r % 4.
     const int cblk = c4 >> 4, clane = c4 & 15;
     auto summed = [&](int tile, int ln, int e) {
         const float *base = reinterpret_cast<const float *>(&lds[0][0][0]);
@@ -564,13 +602,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
             v += base[q * (NS * kSlot / 2) + ((tile * 64 + ln) * 4 + e)];
         return v;
     };
-    const int col = n0 + c4;
-    const bool vec_out = kEpi == kPartial ? (a.Nw % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0) :
-                         kEpi == kAdd ? (a.ldo % 4 == 0 && a.ldr % 4 == 0 &&
-                                         (reinterpret_cast<uintptr_t>(a.out) & 15u) == 0 &&
-                                         (reinterpret_cast<uintptr_t>(a.R) & 15u) == 0)
-                                      : (a.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(a.out) & 7u) == 0);
-    constexpr int kPasses = (TM + kRpp - 1) / kRpp;
     uint2 xpk[kPasses];                           // the stored x of each pass (conv input)
 #pragma unroll
     for (int pass = 0; pass < kPasses; ++pass) {
@@ -624,28 +655,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
     }
     if constexpr (kEpi == kStore) {
         // the conv of the one new token for the columns below cD, in the order and precision
-        // of conv_silu_kernel: x as stored (bf16), the history as stored.  All loads of the
-        // thread's rows are issued before any is used: the three ring slots of every row (the
-        // ring head only selects among them), its head, the weights and the bias of its 4
-        // columns.  conv_fusable guarantees whole 4-column groups (vec_out) here.
-        if (a.cu != nullptr && col < a.cD && vec_out) {
-            uint2 hs[kPasses][3];
-            int hd[kPasses];
-#pragma unroll
-            for (int pass = 0; pass < kPasses; ++pass) {
-                const int r = pass * kRpp + tid / kTpr, row = m0 + r;
-                const bool ok = r < TM && row < a.M;
-                const uint16_t *h = a.c0 + static_cast<size_t>(ok ? row : 0) * 3 * a.cD + col;
-#pragma unroll
-                for (int k = 0; k < 3; ++k) hs[pass][k] = *reinterpret_cast<const uint2 *>(h + k * a.cD);
-                hd[pass] = ok && a.chead != nullptr ? a.chead[row] : 0;
-            }
-            float4 cwv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) cwv[u] = *reinterpret_cast<const float4 *>(a.cw + static_cast<size_t>(col + u) * 4);
-            const float4 cbv = a.cb != nullptr ? make_float4(a.cb[col], a.cb[col + 1], a.cb[col + 2], a.cb[col + 3])
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float cbs[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+        // of conv_silu_kernel: x as stored (bf16), the history as stored
+        if (conv) {
 #pragma unroll
             for (int pass = 0; pass < kPasses; ++pass) {
                 const int r = pass * kRpp + tid / kTpr, row = m0 + r;
@@ -653,9 +664,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a)
                 const uint2 pk = xpk[pass];
                 const float xs[4] = {bf16lo(pk.x), bf16hi(pk.x), bf16lo(pk.y), bf16hi(pk.y)};
                 const int s0 = ring_slot(hd[pass], 0);
-                const uint2 h0 = s0 == 0 ? hs[pass][0] : (s0 == 1 ? hs[pass][1] : hs[pass][2]);
-                const uint2 h1 = s0 == 0 ? hs[pass][1] : (s0 == 1 ? hs[pass][2] : hs[pass][0]);
-                const uint2 h2 = s0 == 0 ? hs[pass][2] : (s0 == 1 ? hs[pass][0] : hs[pass][1]);
+                // selected word by word: a select between whole uint2 values becomes a select
+                // between their addresses, which puts the array in scratch memory
+                const uint2 a0 = hs[pass][0], a1 = hs[pass][1], a2 = hs[pass][2];
+                auto pick = [s0](uint32_t v0, uint32_t v1, uint32_t v2) { return s0 == 0 ? v0 : (s0 == 1 ? v1 : v2); };
+                const uint2 h0 = make_uint2(pick(a0.x, a1.x, a2.x), pick(a0.y, a1.y, a2.y));
+                const uint2 h1 = make_uint2(pick(a1.x, a2.x, a0.x), pick(a1.y, a2.y, a0.y));
+                const uint2 h2 = make_uint2(pick(a2.x, a0.x, a1.x), pick(a2.y, a0.y, a1.y));
                 const float w0[4] = {bf16lo(h0.x), bf16hi(h0.x), bf16lo(h0.y), bf16hi(h0.y)};
                 const float w1[4] = {bf16lo(h1.x), bf16hi(h1.x), bf16lo(h1.y), bf16hi(h1.y)};
                 const float w2[4] = {bf16lo(h2.x), bf16hi(h2.x), bf16lo(h2.y), bf16hi(h2.y)};

@@ -106,7 +106,9 @@ def test_decode_step_small_stack_from_empty_state():
     """One repeat of the pattern (Mamba, MLP, Mamba, MLP, SWA, MLP), 3 sequences, 12 steps
     from an empty state: the 6-entry rings wrap twice."""
     print("case: small stack 6 layers", flush=True)
-    run_steps(SMALL, 6, 3, 12, 21)
+    # against the bf16-activation oracle this stack measured up to 1.8e-3: it is held to the
+    # single-layer bound
+    run_steps(SMALL, 6, 3, 12, 21, matched_tol=TOL_LAYER)
 
 
 def test_decode_step_deep_stack_and_inactive_sequence():
