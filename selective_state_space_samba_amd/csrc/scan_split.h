@@ -17,8 +17,9 @@
 //    and the readout of a finished block (C_t . h_t + D u_t, SiLU(z) gate, store);
 //  * the scan wave (lane n of a row = state n) steps the 16 states through the block,
 //    receiving Delta and Delta*u of token t from lane t by DPP row broadcast fused into
-//    the multiply, and writes the 16x16 tile of states h_t[n] to LDS, where the token
-//    wave reads it transposed (lane j: token j's 16 states).
+//    the multiply, and writes the 16x16 tile of states h_t[n] to LDS (lane n: its 16
+//    tokens as four 16-byte writes), where the token wave reads it transposed (lane j:
+//    token j's 16 states, 16 four-byte reads).
 // Both roles of a workgroup advance in lockstep, one 16-token block per step and one
 // workgroup barrier per step: at step k the scan waves run block k while the token waves
 // run the front end of block k+2 and the readout of block k-1.  The VALU work of the two
@@ -48,11 +49,12 @@ constexpr int kExSlots = 4;                                    // Delta hand-ove
 constexpr int kMaxSplitGrid = 256;                             // workgroups: one per CU
 static_assert(kRoleWaves * rows::kRowsPerWave == rows::kChannels && kRoleThreads == rows::kStagerThreads,
               "roles cover the 16 channels of a workgroup");
-// State tiles and C rows here keep 80-byte token rows (16 states + 4 floats of padding) and
-// 336-float channel tiles: the token lanes' 16-byte reads conflict (half their LDS cycles),
-// but the swizzled layout of the single-role kernel costs the scan waves address work on
-// their critical path and measured 4 % slower here, and a 320-float channel pitch (reads
-// conflict-free, the scan waves' 4-byte writes 2-way conflicted) 11 % slower.
+// State tiles keep one 80-byte row per state (16 tokens + 4 floats of padding) in 336-float
+// channel tiles: a scan lane writes its state's 16 tokens as four 16-byte writes and a token
+// lane reads its token's 16 states as 16 four-byte reads, both free of bank conflicts.  The
+// other orientation (token rows: 16 four-byte writes per scan lane, four 16-byte reads per
+// token lane) measured 2.5 % slower: it puts the larger instruction count on the scan waves,
+// the critical path.  C rows keep 80-byte token rows (16 states + 4 floats of padding).
 constexpr int kSPPitch = rows::kBlock + 4;
 constexpr int kSRowPitch = rows::kBlock * kSPPitch + 16;
 
@@ -64,7 +66,7 @@ struct SplitSmem {
     static constexpr bool kCSwizzle = false;     // C rows unswizzled (see kSPPitch)
     static constexpr bool kCCols = false;        // C as token rows (read by the token role)
     float crow[2][kStage][kSPPitch];             // [buffer][token][state]: C rows
-    float hs[kHsSlots][rows::kChannels * kSRowPitch];  // [block slot][channel][token][state]: h_t
+    float hs[kHsSlots][rows::kChannels * kSRowPitch];  // [block slot][channel][state][token]: h_t
     float lg[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * log2(e)
     float du[kExSlots][rows::kChannels * rows::kBlock];  // [slot][channel][token]: Delta * u
     alignas(16) unsigned char tok[2][3][kStage][kTokPitch];  // [buffer][x|dt|z][token][channels]
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         const float An = state_ok ? a.A[static_cast<size_t>(cc) * N + j] : 0.0f;
         const size_t hidx = (static_cast<size_t>(s) * D + cc) * N + j;
         float h = (a.h0 != nullptr && state_ok) ? a.h0[hidx] : 0.0f;
-        float *hw = &sm.hs[0][ch * kSRowPitch + j];  // this lane's state column of the tile
+        float *hw = &sm.hs[0][ch * kSRowPitch + j * kSPPitch];  // this lane's state row of the tile
 
         struct Cols {
             float4 b[kBlock / 4];
@@ -167,7 +169,8 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
                 {
                     float *hp = hw + ((bk + kHsSlots - 1) % kHsSlots) * (kChannels * kSRowPitch);
 #pragma unroll
-                    for (int t = 0; t < kBlock; ++t) hp[t * kSPPitch] = pp[t];
+                    for (int g = 0; g < kBlock / 4; ++g)
+                        *reinterpret_cast<float4 *>(hp + 4 * g) = make_float4(pp[4 * g], pp[4 * g + 1], pp[4 * g + 2], pp[4 * g + 3]);
                 }
                 // ---- next block's inputs (published by the token role kDist steps ago)
                 const int nslot = (bk + 1) % kExSlots;
@@ -222,7 +225,8 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
         if (nstages > 0) {
             float *hp = hw + ((nstages * kSB - 1) % kHsSlots) * (kChannels * kSRowPitch);
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) hp[t * kSPPitch] = pp[t];
+            for (int g = 0; g < kBlock / 4; ++g)
+                *reinterpret_cast<float4 *>(hp + 4 * g) = make_float4(pp[4 * g], pp[4 * g + 1], pp[4 * g + 2], pp[4 * g + 3]);
         }
         __syncthreads();
         if (a.h_final != nullptr && chan_ok && state_ok) a.h_final[hidx] = h;
@@ -338,13 +342,14 @@ __global__ __launch_bounds__(split::kThreads) void rows_split_kernel(ScanArgs a,
     };
     // A finished block's states for this lane's token (tile slot hslot) and the token's C
     // row (block cbk of stage buffer cbuf).
-    const float *hr = &sm.hs[0][ch * kSRowPitch + j * kSPPitch];
+    const float *hr = &sm.hs[0][ch * kSRowPitch + j];
     auto read_states = [&](int hslot, int cbuf, int cbk, float4 *py, float4 *pc) {
         const float *pr = hr + hslot * (kChannels * kSRowPitch);
         const float *cr = &sm.crow[cbuf][cbk * kBlock + j][0];
 #pragma unroll
         for (int g = 0; g < kBlock / 4; ++g) {
-            py[g] = *reinterpret_cast<const float4 *>(pr + 4 * g);
+            py[g] = make_float4(pr[(4 * g) * kSPPitch], pr[(4 * g + 1) * kSPPitch], pr[(4 * g + 2) * kSPPitch],
+                                pr[(4 * g + 3) * kSPPitch]);
             pc[g] = *reinterpret_cast<const float4 *>(cr + 4 * g);
         }
     };
