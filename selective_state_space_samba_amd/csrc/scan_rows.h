@@ -291,6 +291,37 @@ struct TokStager {
 
 }  // namespace rows
 
+namespace rows {
+
+constexpr int kLptMaxSeqs = 64;  // packed batches up to this many sequences run longest first
+
+// Packed batches: the workgroups of a sequence take time in proportion to its length, and
+// the hardware starts workgroups in index order, so the sequences are visited longest first
+// (ties by index): a long sequence started last would otherwise run alone at the end.
+// Returns the sequence of rank r in that order.  Every thread of the workgroup must call it
+// (one barrier); nseq <= kLptMaxSeqs.
+__device__ inline int longest_first(const ScanArgs &a, int r, int *order)
+{
+    const int t = threadIdx.x;
+    if (t < a.nseq) {
+        size_t b0, b1;
+        seq_range(a, t, b0, b1);
+        const size_t len = b1 - b0;
+        int rank = 0;
+        for (int u = 0; u < a.nseq; ++u) {
+            size_t c0, c1;
+            seq_range(a, u, c0, c1);
+            const size_t lu = c1 - c0;
+            rank += (lu > len || (lu == len && u < t)) ? 1 : 0;
+        }
+        order[rank] = t;
+    }
+    __syncthreads();
+    return order[r];
+}
+
+}  // namespace rows
+
 // kUIn: the x rows hold u = SiLU(conv(x)) already (the conv, its parameters and the
 // history are not used).
 template <class Io, int kStage, bool kFullN, bool kUIn>
@@ -300,11 +331,13 @@ __global__ __launch_bounds__(256) void rows_scan_kernel(ScanArgs a, int ncb)
     using T = typename Io::T;
     constexpr int kStageBlocks = kStage / kBlock;
     __shared__ Smem<T, kStage> sm;
+    __shared__ int seq_order[kLptMaxSeqs];
 
-    // Workgroup -> (sequence, block of 16 channels).
+    // Workgroup -> (sequence, block of 16 channels); packed batches longest sequence first.
     const int bid = logical_block(blockIdx.x, gridDim.x);
-    const int s = bid / ncb;
+    int s = bid / ncb;
     const int cb = bid - s * ncb;
+    if (a.cu != nullptr && a.nseq > 1 && a.nseq <= kLptMaxSeqs) s = longest_first(a, s, seq_order);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
