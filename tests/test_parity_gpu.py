@@ -140,6 +140,31 @@ def test_varlen_ragged(io):
     check((host(y), host(hf), host(cf)), r, io)
 
 
+def test_varlen_sequence_order():
+    """Packed batches are visited longest sequence first when there are at most 64 sequences
+    (ties by index) and in index order beyond that: 40 and 70 sequences of random lengths
+    with repeated lengths and empty ones, every per-sequence output checked."""
+    rng = np.random.default_rng(520)
+    for nseq in (40, 70):
+        lens = rng.integers(0, 48, nseq).tolist()
+        lens[3] = lens[5] = 47
+        lens[7] = 0
+        cu = synth.cu_from_lengths(lens)
+        T, D, N, io = int(cu[-1]), 64, 16, "bf16"
+        p = synth.make_params(520 + nseq, D, N, conv_bias=True)
+        tk = synth.make_tokens(520 + nseq, (T,), D, N, io)
+        h0, c0 = synth.make_state(520 + nseq, nseq, D, N, io, scale=0.5)
+        print("case: varlen", nseq, "sequences", flush=True)
+        y, hf, cf = ss.varlen(torch.from_numpy(cu).to(DEV), tdev(tk.x, io, DEV), tdev(tk.dt, io, DEV),
+                              tdev(tk.B, io, DEV), tdev(tk.C, io, DEV), tdev(tk.z, io, DEV), tf32(p.A, DEV),
+                              tf32(p.Dskip, DEV), tf32(p.dt_bias, DEV), tf32(p.conv_w, DEV), tf32(p.conv_b, DEV),
+                              tf32(h0, DEV), tdev(c0, io, DEV))
+        torch.cuda.synchronize()
+        r = oracle.varlen(cu, tk.x, tk.dt, tk.B, tk.C, tk.z, p.A, p.Dskip, p.dt_bias, p.conv_w, p.conv_b,
+                          h0=h0, conv0=c0)
+        check((host(y), host(hf), host(cf)), r, io)
+
+
 def test_varlen_fresh_sequences():
     """No initial state: every sequence starts from zero state and zero history."""
     lens = [17, 3, 40]
