@@ -405,9 +405,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_ring_kernel(GemmArgs a)
 }
 
 // Skinny products: the decode step's projections, a few hundred token rows against 2K-16K
-// weight rows.  Every weight is used by few rows, so the work is streaming operands at a
-// memory latency of a few microseconds under load, and the kernel is built for loads in
-// flight and for independent waves:
+// weight rows.  Every weight is used by few rows, so the work is streaming operands (the
+// weights once from memory, the token rows again for every column tile from L2), and the
+// kernel is built for loads in flight and for independent waves:
 // - the K range of a tile is split over the workgroup's KW waves (contiguous 64-wide
 //   blocks per wave), and each wave streams its own blocks through its own NS LDS slots
 //   with loads straight into LDS (buffer_load_dwordx4 ... lds: 8 rows x 128 bytes per
