@@ -342,6 +342,9 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
 {
     using namespace bwd;
     __shared__ float tile[kLanes * kTilePitch];
+    // States after 4 and 8 tokens of the chunk (lane-private, lane fastest), saved by the
+    // first forward pass over a full chunk so that sub-chunks 1 and 2 restart from them.
+    __shared__ float ck[kNSub - 2][kMaxState][kLanes];
     const int s = blockIdx.z, cg = blockIdx.y, wv = blockIdx.x;
     const int lane = threadIdx.x;
     const int d = wv * kLanes + lane;
@@ -402,19 +405,35 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
         }
         const float xc3 = x_at<Io>(a, s, t0, cs - 3, dc), xc2 = x_at<Io>(a, s, t0, cs - 2, dc);
         const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
+        // A full chunk's first pass (sub-chunk kNSub-1) walks tokens 0 .. 15 and leaves the
+        // states after tokens 4 and 8 in ck; sub-chunks 2 and 1 then recompute only their own
+        // 4 tokens (28 forward tokens per chunk instead of 40).  A partial chunk (the last of
+        // a sequence) recomputes every sub-chunk from the chunk start.
+        const bool full = n_t == kChunk;  // uniform
 #pragma unroll
         for (int j = kNSub - 1; j >= 0; --j) {
             if (j * kSub >= n_t) continue;  // uniform
-            // forward from the chunk start through sub-chunk j: hp = state before the
-            // sub-chunk, hs[e] = state after its token e, fs[e] = its front ends
+            // forward from the chunk start (or a checkpoint) through sub-chunk j: hp = state
+            // before the sub-chunk, hs[e] = state after its token e, fs[e] = its front ends
             float hp[kMaxState], hs[kSub][kMaxState];
             Front fs[kSub];
             {
+                const bool from_ck = full && j > 0 && j < kNSub - 1;  // uniform
                 float h[kMaxState];
-#pragma unroll
-                for (int n = 0; n < kMaxState; ++n) h[n] = hc[n];
                 float xm3 = xc3, xm2 = xc2, xm1 = xc1;
-                for (int i = 0; i < j * kSub; ++i) {  // earlier sub-chunks: states only
+                int i0 = 0;
+                if (from_ck) {
+#pragma unroll
+                    for (int n = 0; n < kMaxState; ++n) h[n] = ck[j - 1][n][lane];
+                    i0 = j * kSub;
+                    xm3 = x_at<Io>(a, s, t0, cs + i0 - 3, dc);
+                    xm2 = x_at<Io>(a, s, t0, cs + i0 - 2, dc);
+                    xm1 = x_at<Io>(a, s, t0, cs + i0 - 1, dc);
+                } else {
+#pragma unroll
+                    for (int n = 0; n < kMaxState; ++n) h[n] = hc[n];
+                }
+                for (int i = i0; i < j * kSub; ++i) {  // earlier sub-chunks: states only
                     const size_t t = t0 + static_cast<size_t>(cs + i);
                     const float xt = Io::ld(a.x, t * a.D + dc);
                     Front f;
@@ -427,6 +446,11 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
                     const float du = (f.lg * kLn2) * f.u;
 #pragma unroll
                     for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
+                    // first pass of a full chunk: keep the states that start sub-chunks 1 and 2
+                    if (full && j == kNSub - 1 && (i + 1) % kSub == 0 && (i + 1) / kSub < kNSub - 1) {
+#pragma unroll
+                        for (int n = 0; n < kMaxState; ++n) ck[(i + 1) / kSub - 1][n][lane] = h[n];
+                    }
                 }
 #pragma unroll
                 for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
