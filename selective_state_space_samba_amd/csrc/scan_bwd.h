@@ -49,6 +49,11 @@ constexpr int kTilePitch = kBC + 1;  // LDS tile pitch (floats): conflict-free c
 template <class T>
 using ConstPtr = const __attribute__((address_space(4))) T *;
 
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 }  // namespace bwd
 
 struct BwdArgs {
@@ -181,6 +186,150 @@ __device__ inline float gate_grad(float g, bool has_z, float zv)
 // ---------------------------------------------------------------- 1. local pass
 // grid (nwave, nchunk, nseq), 64 threads.  Chunk-local state H (zero start), decay sum S,
 // chunk-local adjoint E (zero end).
+namespace bwd {
+
+// An element as stored (bf16 bits or float) and its float value.
+template <class Io>
+__device__ inline float widen(typename Io::T r)
+{
+    if constexpr (sizeof(typename Io::T) == 2)
+        return __uint_as_float(static_cast<uint32_t>(r) << 16);
+    else
+        return r;
+}
+
+// v unchanged, but computed by here: an empty asm that reads and writes it.
+__device__ inline void hold(float &v) { asm volatile("" : "+v"(v)); }
+
+// The B_t or C_t row (as row16), its load issued only once dep (uniform) and vdep (per lane)
+// are known: the empty asm ties the row's address to both.  Scalar loads of read-only rows
+// are otherwise hoisted to the top of an unrolled chunk, more rows than there are scalar
+// registers (spilled to vector lanes).
+template <class Io, bool kFullN>
+__device__ inline void row16_after(const void *p, size_t t, int N, float dep, float vdep, float *f)
+{
+    asm volatile("" : "+s"(p) : "s"(dep), "v"(vdep));
+    row16<Io, kFullN>(p, t, N, f);
+}
+
+// Local pass over one chunk, one sweep in time order.  The zero-end adjoint needs no reverse
+// sweep: unrolling E = Abar_0 (gy_0 C_0 + Abar_1 (gy_1 C_1 + ...)) gives
+// E = sum_i P_i gy_i C_i with P_i = Abar_0 ... Abar_i, a running product of the factors the
+// forward computes anyway (one multiply per state and token instead of a second exp).
+// kFull (all kChunk tokens present): the chunk's x, dt, dout and z of this lane's channel
+// are loaded in one batch before any arithmetic (one memory latency per chunk instead of one
+// per token and input), and token i+1's B / C rows are loaded while token i is computed.  A
+// partial chunk (the last of a sequence) loads token by token.
+template <class Io, bool kFullN, bool kFull>
+__device__ inline void local_chunk(const BwdArgs &a, int s, int c, int d, bool dok, int dc, size_t t0, int cs, int n_t)
+{
+    using T = typename Io::T;
+    constexpr int kR = kFull ? kChunk : 1;  // batched registers (unused for a partial chunk)
+    Chan ch;
+    load_chan(a, dc, ch);
+    const bool has_z = a.z != nullptr;
+
+    float xm3 = x_at<Io>(a, s, t0, cs - 3, dc), xm2 = x_at<Io>(a, s, t0, cs - 2, dc), xm1 = x_at<Io>(a, s, t0, cs - 1, dc);
+    T xr[kR], dr[kR], gr[kR], zr[kR];
+    float bn[kMaxState], cn[kMaxState];  // B / C rows of the next token (kFull)
+    if constexpr (kFull) {
+        const size_t base = (t0 + static_cast<size_t>(cs)) * a.D + dc;
+        const T *px = static_cast<const T *>(a.x), *pd = static_cast<const T *>(a.dt);
+        const T *pg = static_cast<const T *>(a.dout);
+        const T *pz = has_z ? static_cast<const T *>(a.z) : pg;  // without a gate: loaded, unused
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            xr[i] = px[base + static_cast<size_t>(i) * a.D];
+            dr[i] = pd[base + static_cast<size_t>(i) * a.D];
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            gr[i] = pg[base + static_cast<size_t>(i) * a.D];
+            zr[i] = pz[base + static_cast<size_t>(i) * a.D];
+        }
+        row16<Io, kFullN>(a.B, t0 + cs, a.N, bn);
+        row16<Io, kFullN>(a.C, t0 + cs, a.N, cn);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float h[kMaxState], P[kMaxState], E[kMaxState];
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) {
+        h[n] = 0.0f;
+        P[n] = 1.0f;
+        E[n] = 0.0f;
+    }
+    float S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        if (kFull || i < n_t) {
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            float xt, dtv, gy, b[kMaxState], cr[kMaxState];
+            if constexpr (kFull) {
+#pragma unroll
+                for (int n = 0; n < kMaxState; ++n) {
+                    b[n] = bn[n];
+                    cr[n] = cn[n];
+                }
+                if (i + 1 < kChunk) {  // after this token's rows and the previous token's states
+                    const float dep = b[kMaxState - 1] + cr[kMaxState - 1];
+                    row16_after<Io, kFullN>(a.B, t + 1, a.N, dep, h[kMaxState - 1], bn);
+                    row16_after<Io, kFullN>(a.C, t + 1, a.N, dep, h[kMaxState - 1], cn);
+                }
+                xt = widen<Io>(xr[i]);
+                dtv = widen<Io>(dr[i]);
+                const float g = widen<Io>(gr[i]);
+                gy = has_z ? gate_grad(g, true, widen<Io>(zr[i])) : g;
+            } else {
+                xt = Io::ld(a.x, t * a.D + dc);
+                dtv = Io::ld(a.dt, t * a.D + dc);
+                const float g = Io::ld(a.dout, t * a.D + dc);
+                gy = gate_grad(g, has_z, has_z ? Io::ld(a.z, t * a.D + dc) : 0.0f);
+                row16<Io, kFullN>(a.B, t, a.N, b);
+                row16<Io, kFullN>(a.C, t, a.N, cr);
+            }
+            Front f;
+            front(ch, xm3, xm2, xm1, xt, dtv, f);
+            xm3 = xm2;
+            xm2 = xm1;
+            xm1 = xt;
+            const float du = (f.lg * kLn2) * f.u;
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) {
+                const float ab = hw_exp2(f.lg * ch.A[n]);
+                h[n] = __builtin_fmaf(ab, h[n], du * b[n]);
+                P[n] *= ab;
+                E[n] = __builtin_fmaf(P[n], gy * cr[n], E[n]);
+            }
+            S += f.lg;
+        }
+        if constexpr (kFull) {
+            // one token at a time: its states are computed here, not sunk towards the stores
+            // at the end (which would keep every token's rows alive until then)
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) {
+                hold(h[n]);
+                hold(P[n]);
+                hold(E[n]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (dok) {
+        const size_t o = ((static_cast<size_t>(s) * a.nchunk + c) * a.D + d);
+        float4 *ph = reinterpret_cast<float4 *>(a.hck + o * kMaxState);
+        float4 *pe = reinterpret_cast<float4 *>(a.eck + o * kMaxState);
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            ph[g] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
+            pe[g] = make_float4(E[4 * g], E[4 * g + 1], E[4 * g + 2], E[4 * g + 3]);
+        }
+        a.lsum[o] = S;
+    }
+}
+
+}  // namespace bwd
+
 template <class Io, bool kFullN>
 __global__ __launch_bounds__(bwd::kLanes) void bwd_local_kernel(BwdArgs a)
 {
@@ -195,64 +344,10 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_local_kernel(BwdArgs a)
     const int cs = c * kChunk;
     if (cs >= L) return;  // chunk past this sequence's end (uniform)
     const int n_t = min(kChunk, L - cs);
-    Chan ch;
-    load_chan(a, dc, ch);
-
-    // forward from zero
-    float xm3 = x_at<Io>(a, s, t0, cs - 3, dc), xm2 = x_at<Io>(a, s, t0, cs - 2, dc), xm1 = x_at<Io>(a, s, t0, cs - 1, dc);
-    float h[kMaxState], lgs[kChunk];
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) h[n] = 0.0f;
-    float S = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        lgs[i] = 0.0f;
-        if (i < n_t) {
-            const size_t t = t0 + static_cast<size_t>(cs + i);
-            const float xt = Io::ld(a.x, t * a.D + dc);
-            Front f;
-            front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
-            xm3 = xm2;
-            xm2 = xm1;
-            xm1 = xt;
-            float b[kMaxState];
-            row16<Io, kFullN>(a.B, t, a.N, b);
-            const float du = (f.lg * kLn2) * f.u;
-#pragma unroll
-            for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
-            lgs[i] = f.lg;
-            S += f.lg;
-        }
-    }
-    // reverse from zero
-    const bool has_z = a.z != nullptr;
-    float R[kMaxState];
-#pragma unroll
-    for (int n = 0; n < kMaxState; ++n) R[n] = 0.0f;
-#pragma unroll
-    for (int i = kChunk - 1; i >= 0; --i) {
-        if (i < n_t) {
-            const size_t t = t0 + static_cast<size_t>(cs + i);
-            const float g = Io::ld(a.dout, t * a.D + dc);
-            const float gy = gate_grad(g, has_z, has_z ? Io::ld(a.z, t * a.D + dc) : 0.0f);
-            float cr[kMaxState];
-            row16<Io, kFullN>(a.C, t, a.N, cr);
-#pragma unroll
-            for (int n = 0; n < kMaxState; ++n)
-                R[n] = hw_exp2(lgs[i] * ch.A[n]) * __builtin_fmaf(gy, cr[n], R[n]);
-        }
-    }
-    if (dok) {
-        const size_t o = ((static_cast<size_t>(s) * a.nchunk + c) * a.D + d);
-        float4 *ph = reinterpret_cast<float4 *>(a.hck + o * kMaxState);
-        float4 *pe = reinterpret_cast<float4 *>(a.eck + o * kMaxState);
-#pragma unroll
-        for (int g = 0; g < kMaxState / 4; ++g) {
-            ph[g] = make_float4(h[4 * g], h[4 * g + 1], h[4 * g + 2], h[4 * g + 3]);
-            pe[g] = make_float4(R[4 * g], R[4 * g + 1], R[4 * g + 2], R[4 * g + 3]);
-        }
-        a.lsum[o] = S;
-    }
+    if (n_t == kChunk)  // uniform
+        local_chunk<Io, kFullN, true>(a, s, c, d, dok, dc, t0, cs, n_t);
+    else
+        local_chunk<Io, kFullN, false>(a, s, c, d, dok, dc, t0, cs, n_t);
 }
 
 // ---------------------------------------------------------------- 2. carry pass
