@@ -426,19 +426,349 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a)
 }
 
 // ---------------------------------------------------------------- 3. full pass
-// grid (nwave, ngroup, nseq), 64 threads (one wave: the LDS reduction of dB / dC needs no
-// workgroup barrier beyond the wave's own).  A lane takes a group of kGroup consecutive
-// chunks, last to first, carrying the adjoint from one chunk into the previous one.  Within
-// a chunk, sub-chunks of kSub tokens are handled last to first, each recomputing the
-// forward from the chunk's true start (no per-sub-chunk state is kept: registers, not
-// recomputation, limit how many waves share a SIMD here).
+// grid (nwave, ngroup, nseq), 64 threads: one wave, so the LDS reduction of dB / dC is the
+// wave's own and needs no workgroup barrier (LDS operations of one wave take effect in
+// order).  A lane takes a group of kGroup consecutive chunks, last to first, carrying the
+// adjoint from one chunk into the previous one.  Within a chunk, sub-chunks of kSub tokens
+// are handled last to first: the forward recomputed from the chunk's true start or from a
+// checkpoint, then the reverse with every per-token gradient.  The first pass over a full
+// chunk (sub-chunk kNSub-1) walks tokens 0 .. 15 and leaves the states after tokens 4 and 8
+// in LDS, so sub-chunks 2 and 1 recompute only their own 4 tokens (28 forward tokens per
+// chunk instead of 40); a partial chunk (the last of a sequence) recomputes every sub-chunk
+// from the chunk start.
+namespace bwd {
+
+template <int V>
+struct IntTag {
+    static constexpr int value = V;
+};
+
+// One forward token: front end, then h <- Abar h + Delta u B; the x history shifts by one.
+__device__ inline void fwd_step(const Chan &ch, float &xm3, float &xm2, float &xm1, float xt, float dtv,
+                                const float *b, float *h, Front &f)
+{
+    front(ch, xm3, xm2, xm1, xt, dtv, f);
+    xm3 = xm2;
+    xm2 = xm1;
+    xm1 = xt;
+    const float du = (f.lg * kLn2) * f.u;
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
+}
+
+// Per-lane accumulators of the reverse.
+struct RevAcc {
+    float R[kMaxState];  // adjoint of the state after the token being reversed
+    float dA[kMaxState];
+    float dD, dbias;
+};
+
+// Per-lane constants of the reverse.
+struct RevCtx {
+    float *tile;   // LDS [kLanes][kTilePitch]
+    float *trow;   // this lane's row of it
+    int ro, rp;    // reduction: column ro, half rp of the lanes
+    int wv;        // channel wave
+    bool dok;      // a real channel (not padding)
+    bool has_z;
+};
+
+// Order of this wave's LDS accesses without waiting for them: LDS operations of one wave take
+// effect in issue order, so the compiler only has to keep them in program order.
+__device__ inline void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Reverse of one token t (ix = its element): dz, ddt, dpre stored; the adjoint carried to the
+// token before; dA, dD, dbias accumulated; dB / dC summed over the wave's 64 channels through
+// the LDS tile and stored as this wave's partial.  hcur / hprev: states after / before it.
+template <class Io>
+__device__ inline void rev_step(const BwdArgs &a, const Chan &ch, const RevCtx &rc, const Front &f, float g, float zv,
+                                const float *br, const float *cr, const float *hcur, const float *hprev, size_t t,
+                                size_t ix, RevAcc &ac)
+{
+    const float delta = f.lg * kLn2;
+    // Abar recomputed from a copy of lg the compiler cannot see through: otherwise it keeps
+    // the forward's exp2(lg A) of the sub-chunk's tokens alive until here (64 registers).
+    float lgr = f.lg;
+    hold(lgr);
+    float y = ch.dsk * f.u;
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) y = __builtin_fmaf(cr[n], hcur[n], y);
+    float gy = g;
+    if (rc.has_z) {
+        const float sz = sigmoid(zv);
+        const float dzv = g * y * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
+        if (rc.dok) Io::st(a.dz, ix, dzv);
+        gy = g * (zv * sz);
+    }
+    ac.dD = __builtin_fmaf(gy, f.u, ac.dD);
+    float S1 = 0.0f, S2 = 0.0f;
+    const float dun = rc.dok ? delta * f.u : 0.0f;  // padding channels add zeros to dB / dC
+    const float gyc = rc.dok ? gy : 0.0f;
+    wave_lds_order();  // the previous token's tile reads come first
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) {
+        const float abar = hw_exp2(lgr * ch.A[n]);
+        const float G = __builtin_fmaf(gy, cr[n], ac.R[n]);
+        const float ga = G * abar;
+        const float q = ga * hprev[n];
+        S1 = __builtin_fmaf(q, ch.A[n], S1);
+        ac.dA[n] = __builtin_fmaf(q, delta, ac.dA[n]);
+        S2 = __builtin_fmaf(G, br[n], S2);
+        ac.R[n] = ga;
+        rc.trow[n] = G * dun;
+        rc.trow[kMaxState + n] = gyc * hcur[n];
+    }
+    const float ddel = __builtin_fmaf(f.u, S2, S1);
+    const float du = __builtin_fmaf(delta, S2, gy * ch.dsk);
+    const float da = ddel * sigmoid(f.a);
+    ac.dbias += da;
+    const float sp = sigmoid(f.pre);
+    const float dpre = du * sp * __builtin_fmaf(f.pre, 1.0f - sp, 1.0f);
+    if (rc.dok) {
+        Io::st(a.ddt, ix, da);
+        a.dpre[ix] = dpre;
+    }
+    // dB / dC: column ro over half rp of the lanes (the 32 reads issued together), then the
+    // halves added across lanes l and l ^ 32
+    wave_lds_order();
+    float v[32];
+#pragma unroll
+    for (int l = 0; l < 32; ++l) v[l] = rc.tile[(rc.rp * 32 + l) * kTilePitch + rc.ro];
+    float acc = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 32; ++l) acc += v[l];
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+    acc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    __attribute__((address_space(1))) float *pb = (__attribute__((address_space(1))) float *)a.pbc;
+    asm volatile("" : "+s"(pb));  // the lane's address recomputed, not kept (or spilled) from earlier tokens
+    if (rc.rp == 0) pb[(t * a.nwave + rc.wv) * kBC + rc.ro] = acc;
+}
+
+__device__ inline void hold_all(float *v)
+{
+#pragma unroll
+    for (int n = 0; n < kMaxState; ++n) hold(v[n]);
+}
+
+// A full chunk (all kChunk tokens).  Each sub-chunk loads its x, dt, dout and z in one batch
+// before its arithmetic (one memory latency per sub-chunk instead of one per token and
+// input); B / C rows are loaded one token ahead; every token ends with its states held and
+// a scheduling barrier, so the compiler neither hoists later rows (scalar registers) nor
+// sinks earlier arithmetic.
 template <class Io, bool kFullN>
-__global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
+__device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevCtx &rc, int s, size_t t0, int c,
+                                   int dc, int lane, float (*ck)[kMaxState][kLanes], RevAcc &ac)
+{
+    using T = typename Io::T;
+    const int cs = c * kChunk;
+    const size_t base = (t0 + static_cast<size_t>(cs)) * a.D + dc;  // token 0 of the chunk, this channel
+    const float4 *phc = reinterpret_cast<const float4 *>(a.hck + ((static_cast<size_t>(s) * a.nchunk + c) * a.D + dc) * kMaxState);
+    const T *px = static_cast<const T *>(a.x), *pd = static_cast<const T *>(a.dt);
+    const T *pg = static_cast<const T *>(a.dout);
+    const T *pz = rc.has_z ? static_cast<const T *>(a.z) : pg;  // without a gate: loaded, unused
+    const float xc3 = x_at<Io>(a, s, t0, cs - 3, dc), xc2 = x_at<Io>(a, s, t0, cs - 2, dc);
+    const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
+    const size_t tc = t0 + static_cast<size_t>(cs);  // token 0 of the chunk
+
+    auto sub = [&](auto jtag) __attribute__((always_inline)) {
+        constexpr int J = decltype(jtag)::value;
+        constexpr int e0 = J * kSub;                          // first own token
+        constexpr int w0 = (J == 1 || J == 2) ? e0 : 0;       // first token recomputed
+        constexpr bool from_hc = J == 0 || J == kNSub - 1;    // else from checkpoint J - 1
+        constexpr int nx = e0 + kSub - w0;                    // tokens w0 .. e0 + kSub - 1
+        // ---- the batch
+        T xr[nx], dr[nx], hx[3], gr[kSub], zr[kSub];
+        float h[kMaxState];
+        if constexpr (from_hc) {
+#pragma unroll
+            for (int g = 0; g < kMaxState / 4; ++g) {
+                const float4 q = phc[g];
+                h[4 * g] = q.x;
+                h[4 * g + 1] = q.y;
+                h[4 * g + 2] = q.z;
+                h[4 * g + 3] = q.w;
+            }
+        }
+        // the bases pass through an empty asm per sub-chunk, so the compiler recomputes the
+        // addresses instead of keeping earlier sub-chunks' alive (two registers each)
+        using GPtr = const __attribute__((address_space(1))) T *;  // global: not flat (flat loads count as LDS too)
+        GPtr qx = (GPtr)px, qd = (GPtr)pd, qg = (GPtr)pg, qz = (GPtr)pz;
+        asm volatile("" : "+s"(qx), "+s"(qd), "+s"(qg), "+s"(qz));
+#pragma unroll
+        for (int k = 0; k < nx; ++k) {
+            xr[k] = qx[base + static_cast<size_t>(w0 + k) * a.D];
+            dr[k] = qd[base + static_cast<size_t>(w0 + k) * a.D];
+        }
+        if constexpr (w0 > 0) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) hx[k] = qx[base + static_cast<size_t>(w0 - 3 + k) * a.D];
+        }
+#pragma unroll
+        for (int e = 0; e < kSub; ++e) {
+            gr[e] = qg[base + static_cast<size_t>(e0 + e) * a.D];
+            zr[e] = qz[base + static_cast<size_t>(e0 + e) * a.D];
+        }
+        float bn[kMaxState], cn[kMaxState];
+        row16_after<Io, kFullN>(a.B, tc + w0, a.N, 0.0f, ac.R[kMaxState - 1], bn);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!from_hc) {
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) h[n] = ck[J - 1][n][lane];
+        }
+        float xm3 = xc3, xm2 = xc2, xm1 = xc1;
+        if constexpr (w0 > 0) {
+            xm3 = widen<Io>(hx[0]);
+            xm2 = widen<Io>(hx[1]);
+            xm1 = widen<Io>(hx[2]);
+        }
+        // ---- earlier sub-chunks: states only (the first pass keeps two checkpoints)
+#pragma unroll
+        for (int i = w0; i < e0; ++i) {
+            float b[kMaxState];
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) b[n] = bn[n];
+            row16_after<Io, kFullN>(a.B, tc + i + 1, a.N, b[kMaxState - 1], h[kMaxState - 1], bn);
+            Front f;
+            fwd_step(ch, xm3, xm2, xm1, widen<Io>(xr[i - w0]), widen<Io>(dr[i - w0]), b, h, f);
+            if constexpr (J == kNSub - 1) {
+                if ((i + 1) % kSub == 0 && (i + 1) / kSub < kNSub - 1) {
+#pragma unroll
+                    for (int n = 0; n < kMaxState; ++n) ck[(i + 1) / kSub - 1][n][lane] = h[n];
+                }
+            }
+            hold_all(h);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- own tokens forward
+        float hp[kMaxState], hs[kSub][kMaxState];
+        Front fs[kSub];
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
+#pragma unroll
+        for (int e = 0; e < kSub; ++e) {
+            float b[kMaxState];
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) b[n] = bn[n];
+            if (e + 1 < kSub) {
+                row16_after<Io, kFullN>(a.B, tc + e0 + e + 1, a.N, b[kMaxState - 1], h[kMaxState - 1], bn);
+            } else {  // the reverse starts with this token: keep its B row, load its C row
+                row16_after<Io, kFullN>(a.C, tc + e0 + e, a.N, b[kMaxState - 1], h[kMaxState - 1], cn);
+            }
+            const int i = e0 + e - w0;
+            fwd_step(ch, xm3, xm2, xm1, widen<Io>(xr[i]), widen<Io>(dr[i]), b, h, fs[e]);
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
+            hold_all(h);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- reverse
+#pragma unroll
+        for (int e = kSub - 1; e >= 0; --e) {
+            float br[kMaxState], cr[kMaxState];
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) {
+                br[n] = bn[n];
+                cr[n] = cn[n];
+            }
+            if (e > 0) {
+                const float dep = br[kMaxState - 1] + cr[kMaxState - 1];
+                row16_after<Io, kFullN>(a.B, tc + e0 + e - 1, a.N, dep, ac.R[kMaxState - 1], bn);
+                row16_after<Io, kFullN>(a.C, tc + e0 + e - 1, a.N, dep, ac.R[kMaxState - 1], cn);
+            }
+            const size_t t = tc + static_cast<size_t>(e0 + e);
+            rev_step<Io>(a, ch, rc, fs[e], widen<Io>(gr[e]), widen<Io>(zr[e]), br, cr, hs[e], e > 0 ? hs[e > 0 ? e - 1 : 0] : hp,
+                         t, base + static_cast<size_t>(e0 + e) * a.D, ac);
+            hold_all(ac.R);
+            hold_all(ac.dA);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    sub(IntTag<3>{});
+    sub(IntTag<2>{});
+    sub(IntTag<1>{});
+    sub(IntTag<0>{});
+}
+
+// A partial chunk (n_t < kChunk tokens, the last of a sequence): every sub-chunk recomputes
+// the forward from the chunk start, token by token.
+template <class Io, bool kFullN>
+__device__ inline void part_chunk(const BwdArgs &a, const Chan &ch, const RevCtx &rc, int s, size_t t0, int c, int n_t,
+                                  int dc, RevAcc &ac)
+{
+    const int cs = c * kChunk;
+    float hc[kMaxState];
+    {
+        const float4 *ph = reinterpret_cast<const float4 *>(a.hck + ((static_cast<size_t>(s) * a.nchunk + c) * a.D + dc) * kMaxState);
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 q = ph[g];
+            hc[4 * g] = q.x;
+            hc[4 * g + 1] = q.y;
+            hc[4 * g + 2] = q.z;
+            hc[4 * g + 3] = q.w;
+        }
+    }
+    const float xc3 = x_at<Io>(a, s, t0, cs - 3, dc), xc2 = x_at<Io>(a, s, t0, cs - 2, dc);
+    const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
+#pragma unroll
+    for (int j = kNSub - 1; j >= 0; --j) {
+        if (j * kSub >= n_t) continue;  // uniform
+        float h[kMaxState], hp[kMaxState], hs[kSub][kMaxState];
+        Front fs[kSub];
+        float xm3 = xc3, xm2 = xc2, xm1 = xc1;
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) h[n] = hc[n];
+        for (int i = 0; i < j * kSub; ++i) {  // earlier sub-chunks: states only
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            float b[kMaxState];
+            row16<Io, kFullN>(a.B, t, a.N, b);
+            Front f;
+            fwd_step(ch, xm3, xm2, xm1, Io::ld(a.x, t * a.D + dc), Io::ld(a.dt, t * a.D + dc), b, h, f);
+        }
+#pragma unroll
+        for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
+#pragma unroll
+        for (int e = 0; e < kSub; ++e) {
+            const int i = j * kSub + e;
+            fs[e] = Front{0.0f, 0.0f, 0.0f, 0.0f};
+            if (i < n_t) {
+                const size_t t = t0 + static_cast<size_t>(cs + i);
+                float b[kMaxState];
+                row16<Io, kFullN>(a.B, t, a.N, b);
+                fwd_step(ch, xm3, xm2, xm1, Io::ld(a.x, t * a.D + dc), Io::ld(a.dt, t * a.D + dc), b, h, fs[e]);
+            }
+#pragma unroll
+            for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
+        }
+#pragma unroll
+        for (int e = kSub - 1; e >= 0; --e) {
+            const int i = j * kSub + e;
+            if (i >= n_t) continue;  // uniform
+            const size_t t = t0 + static_cast<size_t>(cs + i);
+            const size_t ix = t * a.D + dc;
+            float br[kMaxState], cr[kMaxState];
+            row16<Io, kFullN>(a.B, t, a.N, br);
+            row16<Io, kFullN>(a.C, t, a.N, cr);
+            const float g = Io::ld(a.dout, ix);
+            const float zv = rc.has_z ? Io::ld(a.z, ix) : 0.0f;
+            rev_step<Io>(a, ch, rc, fs[e], g, zv, br, cr, hs[e], e > 0 ? hs[e > 0 ? e - 1 : 0] : hp, t, ix, ac);
+        }
+    }
+}
+
+}  // namespace bwd
+
+template <class Io, bool kFullN>
+__global__ __launch_bounds__(bwd::kLanes, 2) void bwd_full_kernel(BwdArgs a)
 {
     using namespace bwd;
     __shared__ float tile[kLanes * kTilePitch];
-    // States after 4 and 8 tokens of the chunk (lane-private, lane fastest), saved by the
-    // first forward pass over a full chunk so that sub-chunks 1 and 2 restart from them.
+    // States after 4 and 8 tokens of a full chunk (lane-private, lane fastest).
     __shared__ float ck[kNSub - 2][kMaxState][kLanes];
     const int s = blockIdx.z, cg = blockIdx.y, wv = blockIdx.x;
     const int lane = threadIdx.x;
@@ -459,186 +789,39 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_full_kernel(BwdArgs a)
         return;
     }
     const int clast = min(cfirst + kGroup, nc) - 1;
-    const bool has_z = a.z != nullptr;
     Chan ch;
     load_chan(a, dc, ch);
-
-    float R[kMaxState], dA[kMaxState];
+    const RevCtx rc{tile, tile + lane * kTilePitch, lane & 31, lane >> 5, wv, dok, a.z != nullptr};
+    RevAcc ac;
     {
         const size_t o = (static_cast<size_t>(s) * a.nchunk + clast) * a.D + dc;
         const float4 *pe = reinterpret_cast<const float4 *>(a.eck + o * kMaxState);
 #pragma unroll
         for (int g = 0; g < kMaxState / 4; ++g) {
             const float4 v = pe[g];
-            R[4 * g] = v.x;
-            R[4 * g + 1] = v.y;
-            R[4 * g + 2] = v.z;
-            R[4 * g + 3] = v.w;
+            ac.R[4 * g] = v.x;
+            ac.R[4 * g + 1] = v.y;
+            ac.R[4 * g + 2] = v.z;
+            ac.R[4 * g + 3] = v.w;
         }
     }
 #pragma unroll
-    for (int n = 0; n < kMaxState; ++n) dA[n] = 0.0f;
-    float dDacc = 0.0f, dbacc = 0.0f;
-    float *trow = tile + lane * kTilePitch;
-    const int ro = lane & 31, rp = lane >> 5;  // reduction: column ro, half rp of the lanes
-
+    for (int n = 0; n < kMaxState; ++n) ac.dA[n] = 0.0f;
+    ac.dD = 0.0f;
+    ac.dbias = 0.0f;
     for (int c = clast; c >= cfirst; --c) {
-        const int cs = c * kChunk;
-        const int n_t = min(kChunk, L - cs);
-        const size_t o = (static_cast<size_t>(s) * a.nchunk + c) * a.D + dc;
-        float hc[kMaxState];  // true state entering the chunk
-        {
-            const float4 *ph = reinterpret_cast<const float4 *>(a.hck + o * kMaxState);
-#pragma unroll
-            for (int g = 0; g < kMaxState / 4; ++g) {
-                const float4 v = ph[g];
-                hc[4 * g] = v.x;
-                hc[4 * g + 1] = v.y;
-                hc[4 * g + 2] = v.z;
-                hc[4 * g + 3] = v.w;
-            }
-        }
-        const float xc3 = x_at<Io>(a, s, t0, cs - 3, dc), xc2 = x_at<Io>(a, s, t0, cs - 2, dc);
-        const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
-        // A full chunk's first pass (sub-chunk kNSub-1) walks tokens 0 .. 15 and leaves the
-        // states after tokens 4 and 8 in ck; sub-chunks 2 and 1 then recompute only their own
-        // 4 tokens (28 forward tokens per chunk instead of 40).  A partial chunk (the last of
-        // a sequence) recomputes every sub-chunk from the chunk start.
-        const bool full = n_t == kChunk;  // uniform
-#pragma unroll
-        for (int j = kNSub - 1; j >= 0; --j) {
-            if (j * kSub >= n_t) continue;  // uniform
-            // forward from the chunk start (or a checkpoint) through sub-chunk j: hp = state
-            // before the sub-chunk, hs[e] = state after its token e, fs[e] = its front ends
-            float hp[kMaxState], hs[kSub][kMaxState];
-            Front fs[kSub];
-            {
-                const bool from_ck = full && j > 0 && j < kNSub - 1;  // uniform
-                float h[kMaxState];
-                float xm3 = xc3, xm2 = xc2, xm1 = xc1;
-                int i0 = 0;
-                if (from_ck) {
-#pragma unroll
-                    for (int n = 0; n < kMaxState; ++n) h[n] = ck[j - 1][n][lane];
-                    i0 = j * kSub;
-                    xm3 = x_at<Io>(a, s, t0, cs + i0 - 3, dc);
-                    xm2 = x_at<Io>(a, s, t0, cs + i0 - 2, dc);
-                    xm1 = x_at<Io>(a, s, t0, cs + i0 - 1, dc);
-                } else {
-#pragma unroll
-                    for (int n = 0; n < kMaxState; ++n) h[n] = hc[n];
-                }
-                for (int i = i0; i < j * kSub; ++i) {  // earlier sub-chunks: states only
-                    const size_t t = t0 + static_cast<size_t>(cs + i);
-                    const float xt = Io::ld(a.x, t * a.D + dc);
-                    Front f;
-                    front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), f);
-                    xm3 = xm2;
-                    xm2 = xm1;
-                    xm1 = xt;
-                    float b[kMaxState];
-                    row16<Io, kFullN>(a.B, t, a.N, b);
-                    const float du = (f.lg * kLn2) * f.u;
-#pragma unroll
-                    for (int n = 0; n < kMaxState; ++n) h[n] = __builtin_fmaf(hw_exp2(f.lg * ch.A[n]), h[n], du * b[n]);
-                    // first pass of a full chunk: keep the states that start sub-chunks 1 and 2
-                    if (full && j == kNSub - 1 && (i + 1) % kSub == 0 && (i + 1) / kSub < kNSub - 1) {
-#pragma unroll
-                        for (int n = 0; n < kMaxState; ++n) ck[(i + 1) / kSub - 1][n][lane] = h[n];
-                    }
-                }
-#pragma unroll
-                for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
-#pragma unroll
-                for (int e = 0; e < kSub; ++e) {
-                    const int i = j * kSub + e;
-                    fs[e] = Front{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (i < n_t) {
-                        const size_t t = t0 + static_cast<size_t>(cs + i);
-                        const float xt = Io::ld(a.x, t * a.D + dc);
-                        front(ch, xm3, xm2, xm1, xt, Io::ld(a.dt, t * a.D + dc), fs[e]);
-                        xm3 = xm2;
-                        xm2 = xm1;
-                        xm1 = xt;
-                        float b[kMaxState];
-                        row16<Io, kFullN>(a.B, t, a.N, b);
-                        const float du = (fs[e].lg * kLn2) * fs[e].u;
-#pragma unroll
-                        for (int n = 0; n < kMaxState; ++n)
-                            h[n] = __builtin_fmaf(hw_exp2(fs[e].lg * ch.A[n]), h[n], du * b[n]);
-                    }
-#pragma unroll
-                    for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
-                }
-            }
-#pragma unroll
-            for (int e = kSub - 1; e >= 0; --e) {
-                const int i = j * kSub + e;
-                if (i >= n_t) continue;  // uniform
-                const size_t t = t0 + static_cast<size_t>(cs + i);
-                const size_t ix = t * a.D + dc;
-                const Front &f = fs[e];
-                const float delta = f.lg * kLn2;
-                float br[kMaxState], cr[kMaxState];
-                row16<Io, kFullN>(a.B, t, a.N, br);
-                row16<Io, kFullN>(a.C, t, a.N, cr);
-                const float g = Io::ld(a.dout, ix);
-                float y = ch.dsk * f.u;
-#pragma unroll
-                for (int n = 0; n < kMaxState; ++n) y = __builtin_fmaf(cr[n], hs[e][n], y);
-                float gy = g;
-                if (has_z) {
-                    const float zv = Io::ld(a.z, ix);
-                    const float sz = sigmoid(zv);
-                    const float dzv = g * y * sz * __builtin_fmaf(zv, 1.0f - sz, 1.0f);
-                    if (dok) Io::st(a.dz, ix, dzv);
-                    gy = g * (zv * sz);
-                }
-                dDacc = __builtin_fmaf(gy, f.u, dDacc);
-                float S1 = 0.0f, S2 = 0.0f;
-                const float dun = dok ? delta * f.u : 0.0f;  // padding channels add zeros to dB / dC
-                const float gyc = dok ? gy : 0.0f;
-#pragma unroll
-                for (int n = 0; n < kMaxState; ++n) {
-                    const float hprev = e > 0 ? hs[e > 0 ? e - 1 : 0][n] : hp[n];
-                    const float abar = hw_exp2(f.lg * ch.A[n]);
-                    const float G = __builtin_fmaf(gy, cr[n], R[n]);
-                    const float ga = G * abar;
-                    const float q = ga * hprev;
-                    S1 = __builtin_fmaf(q, ch.A[n], S1);
-                    dA[n] = __builtin_fmaf(q, delta, dA[n]);
-                    S2 = __builtin_fmaf(G, br[n], S2);
-                    R[n] = ga;
-                    trow[n] = G * dun;
-                    trow[kMaxState + n] = gyc * hs[e][n];
-                }
-                const float ddel = __builtin_fmaf(f.u, S2, S1);
-                const float du = __builtin_fmaf(delta, S2, gy * ch.dsk);
-                const float da = ddel * sigmoid(f.a);
-                dbacc += da;
-                const float sp = sigmoid(f.pre);
-                const float dpre = du * sp * __builtin_fmaf(f.pre, 1.0f - sp, 1.0f);
-                if (dok) {
-                    Io::st(a.ddt, ix, da);
-                    a.dpre[ix] = dpre;
-                }
-                // dB / dC: sum over the wave's 64 channels
-                __syncthreads();
-                float acc = 0.0f;
-#pragma unroll 8
-                for (int l = 0; l < 32; ++l) acc += tile[(rp * 32 + l) * kTilePitch + ro];
-                acc += __shfl_xor(acc, 32);
-                if (rp == 0) a.pbc[(t * a.nwave + wv) * kBC + ro] = acc;
-                __syncthreads();
-            }
-        }
+        const int n_t = min(kChunk, L - c * kChunk);
+        if (n_t == kChunk)  // uniform
+            full_chunk16<Io, kFullN>(a, ch, rc, s, t0, c, dc, lane, ck, ac);
+        else
+            part_chunk<Io, kFullN>(a, ch, rc, s, t0, c, n_t, dc, ac);
     }
     if (dok) {
         float *pp = a.ppar + ((static_cast<size_t>(s) * a.ngroup + cg) * a.D + d) * kPar;
 #pragma unroll
-        for (int n = 0; n < kMaxState; ++n) pp[n] = dA[n];
-        pp[kMaxState] = dDacc;
-        pp[kMaxState + 1] = dbacc;
+        for (int n = 0; n < kMaxState; ++n) pp[n] = ac.dA[n];
+        pp[kMaxState] = ac.dD;
+        pp[kMaxState + 1] = ac.dbias;
     }
 }
 
