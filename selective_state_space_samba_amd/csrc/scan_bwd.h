@@ -77,7 +77,8 @@ struct BwdArgs {
     void *dconv0;
     // workspace
     float *hck;   // [nseq][nchunk][D][16]  local end state -> true state entering the chunk
-    float *eck;   // [nseq][nchunk][D][16]  local adjoint carry -> adjoint entering from the right
+    float *eck;   // [nseq][nchunk][D][16]  local adjoint carry -> adjoint entering from the right (the full
+                  //                          pass reads it at the last chunk of each group only)
     float *lsum;  // [nseq][nchunk][D]      sum of Delta log2(e) over the chunk
     float *dpre;  // [total][D]             gradient of the conv output before SiLU
     float *ppar;  // [nseq][ngroup][D][kPar]
@@ -354,7 +355,8 @@ __global__ __launch_bounds__(bwd::kLanes) void bwd_local_kernel(BwdArgs a)
 // grid (ceil(D * 16 / 256), nseq), 256 threads: one lane per (sequence, channel, state),
 // sequential over chunks, the loads kPre chunks ahead (the loop body is one exp and one
 // FMA, so it is load-latency bound).  hck becomes the state entering each chunk, eck the
-// adjoint entering it from the right; the gradient of h0 is what is left at the start.
+// adjoint entering it from the right (stored for the last chunk of each full-pass group,
+// the only ones read); the gradient of h0 is what is left at the start.
 __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a)
 {
     using namespace bwd;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a)
                     const int cn = max(c - kPre, 0);
                     Eq[k] = a.eck[at(cn) * kMaxState + n];
                     Sq[k] = a.lsum[at(cn)];
-                    a.eck[at(c) * kMaxState + n] = R;
+                    if (c % kGroup == kGroup - 1 || c == nc - 1) a.eck[at(c) * kMaxState + n] = R;  // read at group ends only
                     R = __builtin_fmaf(hw_exp2(An * S), R, E);
                 }
             }
@@ -555,11 +557,13 @@ __device__ inline void hold_all(float *v)
     for (int n = 0; n < kMaxState; ++n) hold(v[n]);
 }
 
-// A full chunk (all kChunk tokens).  Each sub-chunk loads its x, dt, dout and z in one batch
-// before its arithmetic (one memory latency per sub-chunk instead of one per token and
-// input); B / C rows are loaded one token ahead; every token ends with its states held and
-// a scheduling barrier, so the compiler neither hoists later rows (scalar registers) nor
-// sinks earlier arithmetic.
+// A full chunk (all kChunk tokens).  Each sub-chunk's x, dt, dout and z come in one batch of
+// loads: the first sub-chunk's issued at the chunk start, every later one's during the two
+// last reverse tokens of the sub-chunk before it (the states of its two first tokens are dead
+// by then, which leaves the registers), so its memory latency overlaps arithmetic.  B / C rows
+// are loaded one token ahead; every token ends with its states held and a scheduling
+// barrier, so the compiler neither hoists later rows (scalar registers) nor sinks earlier
+// arithmetic.
 template <class Io, bool kFullN>
 __device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevCtx &rc, int s, size_t t0, int c,
                                    int dc, int lane, float (*ck)[kMaxState][kLanes], RevAcc &ac)
@@ -575,66 +579,76 @@ __device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevC
     const float xc1 = x_at<Io>(a, s, t0, cs - 1, dc);
     const size_t tc = t0 + static_cast<size_t>(cs);  // token 0 of the chunk
 
-    auto sub = [&](auto jtag) __attribute__((always_inline)) {
-        constexpr int J = decltype(jtag)::value;
-        constexpr int e0 = J * kSub;                          // first own token
-        constexpr int w0 = (J == 1 || J == 2) ? e0 : 0;       // first token recomputed
-        constexpr bool from_hc = J == 0 || J == kNSub - 1;    // else from checkpoint J - 1
-        constexpr int nx = e0 + kSub - w0;                    // tokens w0 .. e0 + kSub - 1
-        // ---- the batch
-        T xr[nx], dr[nx], hx[3], gr[kSub], zr[kSub];
+    // The inputs of one sub-chunk J (tokens w0 .. e0 + kSub - 1 of x and dt, the x history
+    // before w0 when w0 > 0, dout and z of its own tokens; h: the chunk's start state, for
+    // the sub-chunks that start there).
+    struct Batch {
+        T xr[kChunk], dr[kChunk], hx[3], gr[kSub], zr[kSub];
         float h[kMaxState];
-        if constexpr (from_hc) {
-#pragma unroll
-            for (int g = 0; g < kMaxState / 4; ++g) {
-                const float4 q = phc[g];
-                h[4 * g] = q.x;
-                h[4 * g + 1] = q.y;
-                h[4 * g + 2] = q.z;
-                h[4 * g + 3] = q.w;
-            }
-        }
-        // the bases pass through an empty asm per sub-chunk, so the compiler recomputes the
-        // addresses instead of keeping earlier sub-chunks' alive (two registers each)
+    };
+    auto load_in = [&](auto jtag, Batch &b) __attribute__((always_inline)) {
+        constexpr int J = decltype(jtag)::value;
+        constexpr int e0 = J * kSub;
+        constexpr int w0 = (J == 1 || J == 2) ? e0 : 0;
+        constexpr int nx = e0 + kSub - w0;
+        // the bases pass through an empty asm per batch, so the compiler recomputes the
+        // addresses instead of keeping earlier batches' alive (two registers each)
         using GPtr = const __attribute__((address_space(1))) T *;  // global: not flat (flat loads count as LDS too)
         GPtr qx = (GPtr)px, qd = (GPtr)pd, qg = (GPtr)pg, qz = (GPtr)pz;
         asm volatile("" : "+s"(qx), "+s"(qd), "+s"(qg), "+s"(qz));
 #pragma unroll
         for (int k = 0; k < nx; ++k) {
-            xr[k] = qx[base + static_cast<size_t>(w0 + k) * a.D];
-            dr[k] = qd[base + static_cast<size_t>(w0 + k) * a.D];
+            b.xr[k] = qx[base + static_cast<size_t>(w0 + k) * a.D];
+            b.dr[k] = qd[base + static_cast<size_t>(w0 + k) * a.D];
         }
         if constexpr (w0 > 0) {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) hx[k] = qx[base + static_cast<size_t>(w0 - 3 + k) * a.D];
+            for (int k = 0; k < 3; ++k) b.hx[k] = qx[base + static_cast<size_t>(w0 - 3 + k) * a.D];
         }
 #pragma unroll
         for (int e = 0; e < kSub; ++e) {
-            gr[e] = qg[base + static_cast<size_t>(e0 + e) * a.D];
-            zr[e] = qz[base + static_cast<size_t>(e0 + e) * a.D];
+            b.gr[e] = qg[base + static_cast<size_t>(e0 + e) * a.D];
+            b.zr[e] = qz[base + static_cast<size_t>(e0 + e) * a.D];
         }
+    };
+    auto load_h = [&](Batch &b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < kMaxState / 4; ++g) {
+            const float4 q = phc[g];
+            b.h[4 * g] = q.x;
+            b.h[4 * g + 1] = q.y;
+            b.h[4 * g + 2] = q.z;
+            b.h[4 * g + 3] = q.w;
+        }
+    };
+
+    // Sub-chunk J from its batch b; issues the next sub-chunk's batch into nb.
+    auto sub = [&](auto jtag, Batch &b, Batch &nb) __attribute__((always_inline)) {
+        constexpr int J = decltype(jtag)::value;
+        constexpr int e0 = J * kSub;                          // first own token
+        constexpr int w0 = (J == 1 || J == 2) ? e0 : 0;       // first token recomputed
+        constexpr bool from_hc = J == 0 || J == kNSub - 1;    // else from checkpoint J - 1
         float bn[kMaxState], cn[kMaxState];
         row16_after<Io, kFullN>(a.B, tc + w0, a.N, 0.0f, ac.R[kMaxState - 1], bn);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!from_hc) {
+        float h[kMaxState];
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) h[n] = ck[J - 1][n][lane];
-        }
+        for (int n = 0; n < kMaxState; ++n) h[n] = from_hc ? b.h[n] : ck[J > 0 ? J - 1 : 0][n][lane];
         float xm3 = xc3, xm2 = xc2, xm1 = xc1;
         if constexpr (w0 > 0) {
-            xm3 = widen<Io>(hx[0]);
-            xm2 = widen<Io>(hx[1]);
-            xm1 = widen<Io>(hx[2]);
+            xm3 = widen<Io>(b.hx[0]);
+            xm2 = widen<Io>(b.hx[1]);
+            xm1 = widen<Io>(b.hx[2]);
         }
         // ---- earlier sub-chunks: states only (the first pass keeps two checkpoints)
 #pragma unroll
         for (int i = w0; i < e0; ++i) {
-            float b[kMaxState];
+            float bb[kMaxState];
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) b[n] = bn[n];
-            row16_after<Io, kFullN>(a.B, tc + i + 1, a.N, b[kMaxState - 1], h[kMaxState - 1], bn);
+            for (int n = 0; n < kMaxState; ++n) bb[n] = bn[n];
+            row16_after<Io, kFullN>(a.B, tc + i + 1, a.N, bb[kMaxState - 1], h[kMaxState - 1], bn);
             Front f;
-            fwd_step(ch, xm3, xm2, xm1, widen<Io>(xr[i - w0]), widen<Io>(dr[i - w0]), b, h, f);
+            fwd_step(ch, xm3, xm2, xm1, widen<Io>(b.xr[i - w0]), widen<Io>(b.dr[i - w0]), bb, h, f);
             if constexpr (J == kNSub - 1) {
                 if ((i + 1) % kSub == 0 && (i + 1) / kSub < kNSub - 1) {
 #pragma unroll
@@ -651,16 +665,16 @@ __device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevC
         for (int n = 0; n < kMaxState; ++n) hp[n] = h[n];
 #pragma unroll
         for (int e = 0; e < kSub; ++e) {
-            float b[kMaxState];
+            float bb[kMaxState];
 #pragma unroll
-            for (int n = 0; n < kMaxState; ++n) b[n] = bn[n];
+            for (int n = 0; n < kMaxState; ++n) bb[n] = bn[n];
             if (e + 1 < kSub) {
-                row16_after<Io, kFullN>(a.B, tc + e0 + e + 1, a.N, b[kMaxState - 1], h[kMaxState - 1], bn);
+                row16_after<Io, kFullN>(a.B, tc + e0 + e + 1, a.N, bb[kMaxState - 1], h[kMaxState - 1], bn);
             } else {  // the reverse starts with this token: keep its B row, load its C row
-                row16_after<Io, kFullN>(a.C, tc + e0 + e, a.N, b[kMaxState - 1], h[kMaxState - 1], cn);
+                row16_after<Io, kFullN>(a.C, tc + e0 + e, a.N, bb[kMaxState - 1], h[kMaxState - 1], cn);
             }
             const int i = e0 + e - w0;
-            fwd_step(ch, xm3, xm2, xm1, widen<Io>(xr[i]), widen<Io>(dr[i]), b, h, fs[e]);
+            fwd_step(ch, xm3, xm2, xm1, widen<Io>(b.xr[i]), widen<Io>(b.dr[i]), bb, h, fs[e]);
 #pragma unroll
             for (int n = 0; n < kMaxState; ++n) hs[e][n] = h[n];
             hold_all(h);
@@ -669,6 +683,10 @@ __device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevC
         // ---- reverse
 #pragma unroll
         for (int e = kSub - 1; e >= 0; --e) {
+            if constexpr (J > 0) {  // the next sub-chunk's batch
+                if (e == 1) load_in(IntTag<J - 1>{}, nb);
+                if (J == 1 && e == 0) load_h(nb);
+            }
             float br[kMaxState], cr[kMaxState];
 #pragma unroll
             for (int n = 0; n < kMaxState; ++n) {
@@ -681,17 +699,20 @@ __device__ inline void full_chunk16(const BwdArgs &a, const Chan &ch, const RevC
                 row16_after<Io, kFullN>(a.C, tc + e0 + e - 1, a.N, dep, ac.R[kMaxState - 1], cn);
             }
             const size_t t = tc + static_cast<size_t>(e0 + e);
-            rev_step<Io>(a, ch, rc, fs[e], widen<Io>(gr[e]), widen<Io>(zr[e]), br, cr, hs[e], e > 0 ? hs[e > 0 ? e - 1 : 0] : hp,
+            rev_step<Io>(a, ch, rc, fs[e], widen<Io>(b.gr[e]), widen<Io>(b.zr[e]), br, cr, hs[e], e > 0 ? hs[e > 0 ? e - 1 : 0] : hp,
                          t, base + static_cast<size_t>(e0 + e) * a.D, ac);
             hold_all(ac.R);
             hold_all(ac.dA);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    sub(IntTag<3>{});
-    sub(IntTag<2>{});
-    sub(IntTag<1>{});
-    sub(IntTag<0>{});
+    Batch b3, b2, b1, b0;
+    load_in(IntTag<3>{}, b3);
+    load_h(b3);
+    sub(IntTag<3>{}, b3, b2);
+    sub(IntTag<2>{}, b2, b1);
+    sub(IntTag<1>{}, b1, b0);
+    sub(IntTag<0>{}, b0, b3);  // (issues nothing)
 }
 
 // A partial chunk (n_t < kChunk tokens, the last of a sequence): every sub-chunk recomputes
