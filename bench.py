@@ -526,7 +526,8 @@ def bench_model_decode(dev, steps, warmup, S=256):
 def valu_probe():
     """Issue rates of the vector ALU measured on this GPU (libsamba_probe.so): independent
     v_fma_f32 / v_fmac_f32 / v_exp_f32 chains, a 1:4 exp:FMA mix in one wave and split between
-    waves, dependent-chain latencies, and the shader clock during each run.  Reported beside
+    waves, dependent-chain latencies, FMA / multiply with a scalar-register operand, and the
+    shader clock during each run.  Reported beside
     the roofline so that its peak (unit counts x 2.4 GHz) can be checked against the chip."""
     import ctypes
     path = os.path.join(ROOT, "selective_state_space_samba_amd", "libsamba_probe.so")
@@ -539,7 +540,8 @@ def valu_probe():
                               (2, "exp_plus_4fma_one_wave", 4000), (4, "exp_plus_4fma_split_waves", 4000),
                               (5, "v_fma_f32_dependent", 20000), (6, "v_exp_f32_dependent", 8000),
                               (7, "v_add_f32_dpp_row_shl", 20000), (8, "v_mul_f32_dpp_row_newbcast", 20000),
-                              (9, "v_cndmask_b32_e64", 20000), (10, "v_mul_f32", 20000)):
+                              (9, "v_cndmask_b32_e64", 20000), (10, "v_mul_f32", 20000),
+                              (11, "v_fma_f32_scalar_operand", 20000), (12, "v_mul_f32_scalar_operand", 20000)):
         out = (ctypes.c_double * 4)()
         # rate probes: 2048 x 256 threads (1024 x 512 for the split mix): 8 waves per SIMD;
         # latency probes: one wave per SIMD

@@ -2,8 +2,9 @@
 // the selective scan: fp32 FMA (VOP3 v_fma_f32 and VOP2 v_fmac_f32), the transcendental
 // v_exp_f32, exponentials mixed 1:4 with independent FMAs in one wave and split between
 // waves (does the transcendental unit run beside the FMAs?), the latency of a dependent
-// FMA and of a dependent exponential (one chain per lane, one wave per SIMD), and the
-// shader clock during each run (s_memtime core-clock ticks against the constant-rate
+// FMA and of a dependent exponential (one chain per lane, one wave per SIMD), FMA and multiply
+// with one operand in a scalar register (a wave-uniform value), and the shader clock during
+// each run (s_memtime core-clock ticks against the constant-rate
 // s_memrealtime counter).
 //
 // In the rate probes every lane runs 8 independent dependency chains, so neither one wave's
@@ -26,7 +27,7 @@ constexpr int kUnroll = 8;  // loop body: kUnroll groups of 8 chains
 
 enum Kind {
     kFma = 0, kExp = 1, kMix = 2, kFmac = 3, kMixWaves = 4, kFmaLat = 5, kExpLat = 6,
-    kAddDpp = 7, kMulBcast = 8, kCndmask = 9, kMul = 10
+    kAddDpp = 7, kMulBcast = 8, kCndmask = 9, kMul = 10, kFmaSgpr = 11, kMulSgpr = 12
 };
 
 __device__ inline void fma8(float (&v)[8], float m, float c)
@@ -62,6 +63,17 @@ __device__ inline void mul8(float (&v)[8], float m)
 {
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("v_mul_f32_e32 %0, %1, %0" : "+v"(v[i]) : "v"(m));
+}
+// The same with the multiplier in a scalar register.
+__device__ inline void fma_s8(float (&v)[8], float m, float c)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(v[i]) : "s"(m), "v"(c));
+}
+__device__ inline void mul_s8(float (&v)[8], float m)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("v_mul_f32_e32 %0, %1, %0" : "+v"(v[i]) : "s"(m));
 }
 __device__ inline void exp8(float (&v)[8])
 {
@@ -117,6 +129,8 @@ __global__ __launch_bounds__(512) void probe_kernel(int iters, float seed, float
             if (kKind == kMulBcast) mul_bcast8(v, m);
             if (kKind == kCndmask) cndmask8(v, c);
             if (kKind == kMul) mul8(v, m);
+            if (kKind == kFmaSgpr) fma_s8(v, m, c);
+            if (kKind == kMulSgpr) mul_s8(v, m);
             if (kKind == kFmaLat) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(v[0]) : "v"(m), "v"(c));
@@ -152,7 +166,8 @@ extern "C" {
 //   5 one dependent v_fma_f32 chain per lane; 6 one dependent v_exp_f32 chain per lane
 //     (use one workgroup of 64 threads per SIMD for these two);
 //   7 v_add_f32 with a DPP row_shl source, 8 v_mul_f32 with a DPP row_newbcast source,
-//   9 v_cndmask_b32 (VOP3, SGPR-pair mask), 10 v_mul_f32 (VOP2): 8 chains per lane.
+//   9 v_cndmask_b32 (VOP3, SGPR-pair mask), 10 v_mul_f32 (VOP2), 11 v_fma_f32 and 12
+//   v_mul_f32 with the multiplier in a scalar register: 8 chains per lane.
 // Returns 0 on success.  Outputs:
 //   out[0] seconds of the launch (HIP events)
 //   out[1] lane-instructions executed (an exponential counts as one)
@@ -160,7 +175,7 @@ extern "C" {
 //   out[3] median shader clock over the workgroups in GHz (s_memtime ticks / real time)
 int samba_probe_rates(int kind, int workgroups, int iters, double *out)
 {
-    if (kind < 0 || kind > 10 || workgroups < 1 || iters < 1 || out == nullptr) return 1;
+    if (kind < 0 || kind > 12 || workgroups < 1 || iters < 1 || out == nullptr) return 1;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 2;
     int wall_khz = 0;
@@ -187,6 +202,8 @@ int samba_probe_rates(int kind, int workgroups, int iters, double *out)
         case kMulBcast: probe_kernel<kMulBcast><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         case kCndmask: probe_kernel<kCndmask><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         case kMul: probe_kernel<kMul><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
+        case kFmaSgpr: probe_kernel<kFmaSgpr><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
+        case kMulSgpr: probe_kernel<kMulSgpr><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         default: probe_kernel<kFmac><<<workgroups, kThreads>>>(n, 0.5f, sink, stamps); break;
         }
     };
