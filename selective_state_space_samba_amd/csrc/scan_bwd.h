@@ -13,17 +13,18 @@
 // chunk, channel) gets a lane (one lane per channel, the 16 states in registers, as in the
 // lane prefill kernel), so a training batch of 4 x 4096 tokens x 4096 channels gives 1M
 // lanes.  Both recurrences are linear, so a chunk only needs two carries:
-//   1. local pass (one lane per chunk): the chunk's state from a zero start, H, its
-//      decay sum S = sum_t Delta_t log2(e) (the chunk maps h to exp2(A S) h + H), and its
-//      adjoint from a zero end, E (maps R to exp2(A S) R + E);
-//   2. carry pass (one lane per sequence and channel, sequential over chunks): the true
-//      state entering each chunk and the true adjoint entering it from the right, the
+//   1. local pass (one lane per chunk, one sweep in time order): the chunk's state from a
+//      zero start, H, its decay sum S = sum_t Delta_t log2(e) (the chunk maps h to
+//      exp2(A S) h + H), and its adjoint from a zero end, E (maps R to exp2(A S) R + E),
+//      accumulated forward as a sum of running products of the decay factors;
+//   2. carry pass (one lane per sequence, channel and state, sequential over chunks): the
+//      true state entering each chunk and the true adjoint entering it from the right, the
 //      gradient of h0 falls out at the end;
-//   3. full pass (one lane per chunk): the forward recomputed from the true start (kSub
-//      tokens at a time, the sub-chunk starts kept in registers), then the reverse with
+//   3. full pass (one lane per group of chunks): the forward recomputed from the true start
+//      kSub tokens at a time (two checkpoints per chunk in LDS), then the reverse with
 //      every per-token gradient; dB / dC (sums over channels) are reduced over the wave's
 //      64 channels through LDS and written as per-wave partials; dA, dD, dbias as
-//      per-chunk partials; the conv-output gradient dpre goes to a float32 workspace;
+//      per-group partials; the conv-output gradient dpre goes to a float32 workspace;
 //   4. conv pass: dx (the conv transposed over dpre), dconv0, dconv_w / dconv_b partials;
 //   5. reductions of the partials.
 #pragma once
