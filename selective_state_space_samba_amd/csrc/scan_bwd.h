@@ -932,7 +932,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(BwdArgs a)
     const int n = k & (kMaxState - 1);
     if (n >= a.N) return;
     float acc = 0.0f;
-    for (int wv = 0; wv < a.nwave; ++wv) acc += a.pbc[(t * a.nwave + wv) * kBC + k];
+#pragma unroll 16
+    for (int wv = 0; wv < a.nwave; ++wv) acc += a.pbc[(t * a.nwave + wv) * kBC + k];  // in wave order
     Io::st(k < kMaxState ? a.dB : a.dC, t * a.N + n, acc);
 }
 
@@ -949,29 +950,34 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float *__restrict
     out[static_cast<size_t>(blockIdx.y) * cols + col] = acc;
 }
 
-// Parameters, stage 2: one thread per channel.
+// Parameters, stage 2: one thread per (channel, parameter), the nsplit sums added in order.
 __global__ __launch_bounds__(256) void bwd_reduce_par_kernel(BwdArgs a)
 {
     using namespace bwd;
-    const int d = blockIdx.x * 256 + threadIdx.x;
-    if (d >= a.D) return;
-    float acc[kPar], cw[kConvPar];
-#pragma unroll
-    for (int k = 0; k < kPar; ++k) acc[k] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kConvPar; ++k) cw[k] = 0.0f;
-    for (int sp = 0; sp < kSplit; ++sp) {
-#pragma unroll
-        for (int k = 0; k < kPar; ++k) acc[k] += a.par2[(static_cast<size_t>(sp) * a.D + d) * kPar + k];
-#pragma unroll
-        for (int k = 0; k < kConvPar; ++k) cw[k] += a.conv2[(static_cast<size_t>(sp) * a.D + d) * kConvPar + k];
+    constexpr int kAll = kPar + kConvPar;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.D * kAll) return;
+    const int d = i / kAll, k = i - d * kAll;
+    float acc = 0.0f;
+    if (k < kPar) {
+#pragma unroll 8
+        for (int sp = 0; sp < kSplit; ++sp) acc += a.par2[(static_cast<size_t>(sp) * a.D + d) * kPar + k];
+        if (k < kMaxState) {
+            if (k < a.N) a.dA[static_cast<size_t>(d) * a.N + k] = acc;
+        } else if (k == kMaxState) {
+            a.dD[d] = acc;
+        } else {
+            a.ddt_bias[d] = acc;
+        }
+    } else {
+        const int kc = k - kPar;
+#pragma unroll 8
+        for (int sp = 0; sp < kSplit; ++sp) acc += a.conv2[(static_cast<size_t>(sp) * a.D + d) * kConvPar + kc];
+        if (kc < kConvK)
+            a.dconv_w[static_cast<size_t>(d) * kConvK + kc] = acc;
+        else
+            a.dconv_b[d] = acc;
     }
-    for (int n = 0; n < a.N; ++n) a.dA[static_cast<size_t>(d) * a.N + n] = acc[n];
-    a.dD[d] = acc[kMaxState];
-    a.ddt_bias[d] = acc[kMaxState + 1];
-#pragma unroll
-    for (int k = 0; k < kConvK; ++k) a.dconv_w[static_cast<size_t>(d) * kConvK + k] = cw[k];
-    a.dconv_b[d] = cw[kConvK];
 }
 
 // ---------------------------------------------------------------- host side
@@ -1071,7 +1077,7 @@ inline void launch_backward(BwdArgs a, float *ws, samba_dtype io, hipStream_t st
         bwd_colsum_kernel<<<dim3((ccols + 255) / 256, kSplit), 256, 0, stream>>>(a.pconv, a.nseq * a.nrun, ccols,
                                                                                  kSplit, a.conv2);
     }
-    bwd_reduce_par_kernel<<<(a.D + 255) / 256, 256, 0, stream>>>(a);
+    bwd_reduce_par_kernel<<<(a.D * (kPar + kConvPar) + 255) / 256, 256, 0, stream>>>(a);
 }
 
 }  // namespace samba
