@@ -87,6 +87,18 @@ def test_backward_packed(io):
     check(*run_both(make(2040, (T,), len(lens), 64, 16, io), io, cu=cu, max_seqlen=max(lens)), io)
 
 
+@pytest.mark.parametrize("io,N", [("bf16", 16), ("f32", 16), ("bf16", 7)])
+def test_backward_packed_long(io, N):
+    """Packed sequences long enough for many chunk groups per sequence (groups of 64 tokens
+    cut at sequence ends, full chunks next to partial ones, the carry over tens of chunks), an
+    empty sequence, 136 channels (two full waves and a partial one), and for N = 7 the
+    per-element B / C rows."""
+    lens = [1000, 37, 2049, 0, 513, 1601, 64, 65]
+    cu = synth.cu_from_lengths(lens)
+    T = int(cu[-1])
+    check(*run_both(make(2060 + N, (T,), len(lens), 136, N, io), io, cu=cu, max_seqlen=max(lens)), io)
+
+
 def test_backward_is_deterministic():
     case = make(2050, (2, 70), 2, 128, 16, "bf16")
     a, _ = run_both(case, "bf16")
